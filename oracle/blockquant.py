@@ -1,0 +1,198 @@
+"""32-element block quantization with one fp16 absmax scale (oracle, test only).
+
+Sources:
+* velog.io post "fix KV cache quantization outliers", section "the essence of
+  the problem": the quantization scale is set by the few extreme values of a
+  group, which is why outliers crush the small values (absmax scaling).
+* aiwitness.kr post 1txlhxu, table "Qwen 3.6 27B Q5_K_S + 64k context KLD
+  results": q4_0 / q5_0 / q8_0 caches cost 28.1 / 34.4 / 53.1 % of bf16,
+  i.e. 4.5 / 5.5 / 8.5 bits per value = 32 codes plus one 2-byte scale.
+* aitrends.kr article 92204, glossary entry "Precision Tail": the newest
+  tokens are kept in bf16.
+
+The quantizer is an encoding, so every float32 operation is spelled out and
+the GPU reproduces it bit for bit.  Readings (the pages do not fix these):
+* R5  With a bf16 tail (T > 0) the rotated value is rounded to bf16 before it
+      is quantized, so a token gets the same codes whether or not it passed
+      through the tail.  With T = 0 the float32 value is quantized directly.
+* R6  Symmetric codes c in [-qmax, qmax], qmax = 2^(b-1) - 1; no zero point.
+* R7  scale = fp16_rne(min(absmax / qmax, 65504)), divide correctly rounded.
+* R8  codes = clip(rint(x * r), -qmax, qmax) with r = 1 / fp32(scale)
+      (one correctly rounded divide per block, one multiply per element),
+      rint ties to even.
+* R9  A block whose fp16 scale is 0 gets all-zero codes.
+* R10 Code storage: 8-bit codes are two's-complement bytes.  4-bit codes are
+      offset binary u = c + 8, two per byte, even element in the low nibble.
+      5-bit codes are offset binary u = c + 16: the low four bits form a
+      4-bit nibble plane (d/2 bytes, packed like 4-bit), followed by one
+      little-endian 32-bit word per block holding bit 4 of each code; element
+      w of the block (0..31) owns bit 8*((w%8)//2) + 2*(w//8) + (w%2).
+* R11 Memory layout of a code plane: rows are padded to a multiple of 16
+      bytes and grouped in tiles of 64 tokens; inside a tile, the 16-byte
+      chunk c of the row of token l sits at byte (c*64 + l)*16.  Scale planes
+      are plain [token][d/32] fp16.
+"""
+
+import numpy as np
+
+BLOCK = 32
+QMAX = {4: 7, 5: 15, 8: 127}
+TILE = 64
+CHUNK = 16
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 to bfloat16 with round-to-nearest-even; returns uint16 bits.
+
+    NaN and infinity are outside the contract (reading R9)."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
+    b = b.astype(np.uint64)
+    r = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    """Widen bfloat16 bits to float32 exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def bf16_round(x):
+    """float32 -> nearest bfloat16 value (ties to even), returned as float32."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+def quantize_blocks(xq, bits):
+    """Quantize float32 rows of length d (a multiple of 32), block by block.
+
+    Returns (codes, scales): codes int8 [..., d] in [-qmax, qmax]; scales
+    uint16 [..., d/32] holding fp16 bit patterns.  Steps (readings R6-R9):
+      a   = max |x| over the block                      (exact)
+      s32 = a / qmax                                    (float32, IEEE divide)
+      s16 = fp16_rne(min(s32, 65504))
+      r   = 1 / float32(s16)                            (float32, IEEE divide)
+      c   = clip(rint(float32(x * r)), -qmax, qmax)     (0 if s16 == 0)
+    """
+    if bits not in QMAX:
+        raise ValueError("bits must be 4, 5 or 8")
+    qmax = np.float32(QMAX[bits])
+    x = np.asarray(xq, dtype=np.float32)
+    d = x.shape[-1]
+    if d % BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (d // BLOCK, BLOCK))
+    a = np.max(np.abs(blocks), axis=-1)
+    s32 = a / qmax
+    s32 = np.minimum(s32, np.float32(65504.0))
+    s16 = s32.astype(np.float16)
+    s16f = s16.astype(np.float32)
+    nz = s16f != 0
+    r = np.where(nz, np.float32(1.0) / np.where(nz, s16f, np.float32(1.0)),
+                 np.float32(0.0)).astype(np.float32)
+    prod = (blocks * r[..., None]).astype(np.float32)
+    c = np.clip(np.rint(prod), -qmax, qmax)
+    c = np.where(nz[..., None], c, np.float32(0.0))
+    codes = c.astype(np.int8).reshape(x.shape)
+    return codes, s16.view(np.uint16)
+
+
+def dequantize_blocks(codes, scales_bits):
+    """x_hat = float32(c) * float32(scale): exact in float32 (at most
+    8 + 11 significant bits), so there is one right answer."""
+    c = np.asarray(codes, dtype=np.int8).astype(np.float32)
+    d = c.shape[-1]
+    s = np.asarray(scales_bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+    out = c.reshape(c.shape[:-1] + (d // BLOCK, BLOCK)) * s[..., None]
+    return out.reshape(c.shape).astype(np.float32)
+
+
+def row_bytes(d, bits):
+    """Packed bytes of one head vector: d*bits/8 (reading R10)."""
+    return d * bits // 8
+
+
+def padded_row_bytes(d, bits):
+    """Row bytes rounded up to the 16-byte chunk of the tiled layout (R11)."""
+    r = row_bytes(d, bits)
+    return (r + CHUNK - 1) // CHUNK * CHUNK
+
+
+def _hibit_position(w):
+    """Bit of the 5-bit high-bit word owned by element w of a block (R10)."""
+    return 8 * ((w % 8) // 2) + 2 * (w // 8) + (w % 2)
+
+
+def pack_rows(codes, bits):
+    """Pack int8 codes [..., d] into uint8 rows [..., row_bytes] (reading R10)."""
+    c = np.asarray(codes, dtype=np.int16)
+    d = c.shape[-1]
+    lead = c.shape[:-1]
+    if bits == 8:
+        return c.astype(np.int8).view(np.uint8).reshape(lead + (d,))
+    if bits == 4:
+        u = (c + 8).astype(np.uint8)
+        return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+    if bits == 5:
+        u = (c + 16).astype(np.uint16)
+        lo = (u & 15).astype(np.uint8)
+        nib = (lo[..., 0::2] | (lo[..., 1::2] << 4)).astype(np.uint8)
+        hb = ((u >> 4) & 1).astype(np.uint32)
+        hb = hb.reshape(lead + (d // BLOCK, BLOCK))
+        pos = np.array([_hibit_position(w) for w in range(BLOCK)], dtype=np.uint32)
+        words = np.zeros(lead + (d // BLOCK,), dtype=np.uint32)
+        for w in range(BLOCK):
+            words |= hb[..., w] << pos[w]
+        hi = words.astype("<u4").view(np.uint8).reshape(lead + (d // 8,))
+        return np.concatenate([nib, hi], axis=-1)
+    raise ValueError("bits must be 4, 5 or 8")
+
+
+def unpack_rows(rows, bits, d):
+    """Inverse of pack_rows: uint8 rows -> int8 codes [..., d]."""
+    r = np.asarray(rows, dtype=np.uint8)
+    lead = r.shape[:-1]
+    if bits == 8:
+        return r[..., :d].view(np.int8).copy()
+    if bits == 4:
+        b = r[..., : d // 2]
+        u = np.empty(lead + (d,), dtype=np.int16)
+        u[..., 0::2] = b & 15
+        u[..., 1::2] = b >> 4
+        return (u - 8).astype(np.int8)
+    if bits == 5:
+        b = r[..., : d // 2]
+        lo = np.empty(lead + (d,), dtype=np.int16)
+        lo[..., 0::2] = b & 15
+        lo[..., 1::2] = b >> 4
+        words = np.ascontiguousarray(r[..., d // 2: d // 2 + d // 8]).view("<u4")
+        words = words.reshape(lead + (d // BLOCK,)).astype(np.uint32)
+        hi = np.empty(lead + (d // BLOCK, BLOCK), dtype=np.int16)
+        for w in range(BLOCK):
+            hi[..., w] = (words >> np.uint32(_hibit_position(w))) & 1
+        u = lo + 16 * hi.reshape(lead + (d,))
+        return (u - 16).astype(np.int8)
+    raise ValueError("bits must be 4, 5 or 8")
+
+
+def rows_to_tiled(rows, padded):
+    """Logical rows [n][R] (n a multiple of 64) -> tiled plane bytes (R11).
+
+    Byte (tile*64*padded) + (c*64 + l)*16 + k holds byte c*16 + k of the row of
+    token tile*64 + l."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    n, rlen = rows.shape
+    if n % TILE:
+        raise ValueError("token count must be a multiple of 64")
+    full = np.zeros((n, padded), dtype=np.uint8)
+    full[:, :rlen] = rows
+    nch = padded // CHUNK
+    t = full.reshape(n // TILE, TILE, nch, CHUNK).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def tiled_to_rows(plane, n, padded, rlen):
+    """Inverse of rows_to_tiled for the first n tokens (n a multiple of 64)."""
+    plane = np.asarray(plane, dtype=np.uint8)
+    nch = padded // CHUNK
+    t = plane[: n * padded].reshape(n // TILE, nch, TILE, CHUNK).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(t).reshape(n, padded)[:, :rlen]

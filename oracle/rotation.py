@@ -1,0 +1,81 @@
+"""Normalized Hadamard rotation (oracle, test infrastructure only).
+
+Source: velog.io post "fix KV cache quantization outliers", section
+"Hadamard rotation": Q, K and V are multiplied by a normalized Hadamard
+matrix before K/V enter the cache, and the attention output is rotated back;
+the matrix is orthogonal, so dot products (and hence attention scores) are
+unchanged.  The section "application and background" enables the rotation
+when head_dim is at least 64 and a multiple of 64.
+
+Readings (the page does not fix these):
+* R1  The matrix is Sylvester's construction in natural order with no random
+      sign diagonal: H[i, j] = (-1)^popcount(i & j) / sqrt(d).
+* R3  Normalization is one float32 multiply by fp32(1/sqrt(d)) applied after
+      the unnormalized transform.
+* R4  The float32 fast Walsh-Hadamard transform runs its stages in the order
+      h = 1, 2, 4, ..., d/2 with butterflies (a + b, a - b); the order changes
+      rounding, so it is fixed here and the GPU follows it.
+"""
+
+import numpy as np
+
+
+def hadamard(d):
+    """Dense normalized Sylvester Hadamard matrix in float64 (plain definition).
+
+    H[i, j] = (-1)^popcount(i & j) / sqrt(d); symmetric and orthogonal, so it
+    is its own inverse (velog.io post, section "Hadamard rotation").
+    """
+    if d < 1 or d & (d - 1):
+        raise ValueError("Sylvester Hadamard needs a power-of-two size")
+    i = np.arange(d, dtype=np.int64)
+    anded = i[:, None] & i[None, :]
+    parity = np.zeros_like(anded)
+    x = anded.copy()
+    while np.any(x):
+        parity ^= x & 1
+        x >>= 1
+    return np.where(parity == 1, -1.0, 1.0) / np.sqrt(float(d))
+
+
+def rot_scale_f32(d):
+    """fp32(1/sqrt(d)): the normalization constant of reading R3."""
+    return np.float32(1.0 / np.sqrt(np.float64(d)))
+
+
+def fwht_f32(x):
+    """Unnormalized fast Walsh-Hadamard transform along the last axis, float32.
+
+    Stage order h = 1, 2, ..., d/2 (reading R4); in each stage every index i
+    with (i & h) == 0 pairs with i + h and becomes (x[i] + x[i+h],
+    x[i] - x[i+h]), each rounded to float32.  No fused operations.
+    The result equals sqrt(d) * H @ x up to float32 rounding.
+    """
+    x = np.array(x, dtype=np.float32, copy=True)
+    d = x.shape[-1]
+    if d < 1 or d & (d - 1):
+        raise ValueError("FWHT needs a power-of-two length")
+    lead = x.shape[:-1]
+    h = 1
+    while h < d:
+        v = x.reshape(lead + (d // (2 * h), 2, h))
+        a = v[..., 0, :].copy()
+        b = v[..., 1, :].copy()
+        v[..., 0, :] = a + b
+        v[..., 1, :] = a - b
+        x = v.reshape(lead + (d,))
+        h *= 2
+    return x
+
+
+def rotate_f32(x, enabled=True):
+    """y = fp32(1/sqrt(d)) * FWHT(x) in float32, or x unchanged if disabled.
+
+    velog.io post, section "Hadamard rotation" (rotate before storing);
+    readings R1, R3, R4.  The per-plane switch follows the separate K and V
+    disable variables named in section "application and background".
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if not enabled:
+        return x.copy()
+    return fwht_f32(x) * rot_scale_f32(x.shape[-1])

@@ -1,0 +1,106 @@
+"""Pins for the oracle cache: append semantics, the bf16 precision tail
+(aitrends.kr article 92204, glossary "Precision Tail": newest tokens kept in
+bf16), chunk invariance and layout."""
+
+import numpy as np
+import pytest
+
+from oracle import (OracleCache, rotate_f32, quantize_blocks, pack_rows,
+                    bf16_round, f32_to_bf16_bits, dequantize_reference)
+from oracle.kvcache import planes_to_rows
+
+
+def _data(B, n, H, d, seed=0):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, n, H, d)).astype(np.float32)
+    v = rng.standard_normal((B, n, H, d)).astype(np.float32)
+    k[..., 5] *= 20
+    return k, v
+
+
+def _same(a, b):
+    pa, pb = a.physical(), b.physical()
+    return all(np.array_equal(pa[key], pb[key]) for key in pa)
+
+
+@pytest.mark.parametrize("T", (0, 8, 64))
+@pytest.mark.parametrize("bits", ((4, 4), (8, 4), (5, 8)))
+def test_chunk_invariance(T, bits):
+    B, H, d, n = 2, 2, 64, 150
+    k, v = _data(B, n, H, d, seed=T)
+    one = OracleCache(B, H, d, bits[0], bits[1], T, 192)
+    one.append(k, v, [0, 0], dtype="f32")
+    step = OracleCache(B, H, d, bits[0], bits[1], T, 192)
+    for i in range(n):
+        step.append(k[:, i:i + 1], v[:, i:i + 1], [i, i], dtype="f32")
+    assert _same(one, step)
+    rng = np.random.default_rng(1)
+    cuts = np.sort(rng.choice(np.arange(1, n), size=6, replace=False))
+    rnd = OracleCache(B, H, d, bits[0], bits[1], T, 192)
+    prev = 0
+    for c in list(cuts) + [n]:
+        rnd.append(k[:, prev:c], v[:, prev:c], [prev, prev], dtype="f32")
+        prev = c
+    assert _same(one, rnd)
+
+
+def test_tail_holds_newest_tokens_in_bf16():
+    B, H, d, n, T = 1, 2, 64, 100, 16
+    k, v = _data(B, n, H, d, seed=3)
+    c = OracleCache(B, H, d, 4, 4, T, 128)
+    c.append(k, v, [0], dtype="f32")
+    ph = c.physical()
+    for p in range(n - T, n):
+        want = f32_to_bf16_bits(rotate_f32(k[0, p]))
+        assert np.array_equal(ph["k_tail"][0, :, p % T], want)
+    # older tokens are quantized from the bf16-rounded rotated value
+    rows = planes_to_rows(ph["k_codes"][0, 1], d, 4, n - T)
+    codes, scales = quantize_blocks(bf16_round(rotate_f32(k[0, : n - T, 1])), 4)
+    assert np.array_equal(rows, pack_rows(codes, 4))
+    assert np.array_equal(ph["k_scales"][0, 1, : n - T], scales)
+
+
+def test_no_tail_quantizes_float32_directly():
+    B, H, d, n = 1, 1, 128, 64
+    k, v = _data(B, n, H, d, seed=5)
+    c = OracleCache(B, H, d, 8, 8, 0, 64)
+    c.append(k, v, [0], dtype="f32")
+    rows = planes_to_rows(c.physical()["v_codes"][0, 0], d, 8, n)
+    codes, _ = quantize_blocks(rotate_f32(v[0, :, 0]), 8)
+    assert np.array_equal(rows, pack_rows(codes, 8))
+
+
+def test_bf16_input_widened_exactly():
+    B, H, d, n = 1, 1, 64, 64
+    k, v = _data(B, n, H, d, seed=6)
+    kb, vb = f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    a = OracleCache(B, H, d, 4, 4, 0, 64)
+    a.append(kb, vb, [0], dtype="bf16")
+    b = OracleCache(B, H, d, 4, 4, 0, 64)
+    b.append(bf16_round(k), bf16_round(v), [0], dtype="f32")
+    assert _same(a, b)
+
+
+def test_capacity_is_enforced():
+    c = OracleCache(1, 1, 64, 4, 4, 0, 64)
+    k, v = _data(1, 65, 1, 64)
+    with pytest.raises(ValueError):
+        c.append(k, v, [0], dtype="f32")
+
+
+def test_dequantize_reference_spaces():
+    B, H, d, n, T = 1, 2, 64, 80, 8
+    k, v = _data(B, n, H, d, seed=8)
+    c = OracleCache(B, H, d, 8, 8, T, 128)
+    c.append(k, v, [0], dtype="f32")
+    ph = c.physical()
+    rot = dequantize_reference(ph, 0, 0, 0, n, n, H, d, 8, T, space=0)
+    orig = dequantize_reference(ph, 0, 0, 0, n, n, H, d, 8, T, space=1)
+    # rotated-space values are within half a quantization step of the rotated
+    # input, and the tail rows are the exact bf16 values
+    y = bf16_round(rotate_f32(k[0]))
+    assert np.array_equal(rot[n - T:], y[n - T:])
+    assert np.max(np.abs(rot - y)) < 0.05 * np.max(np.abs(y))
+    # original space is the rotated value rotated again (H is its own inverse)
+    assert np.array_equal(orig, rotate_f32(rot))
+    assert np.max(np.abs(orig - k[0])) < 0.05 * np.max(np.abs(k[0]))
