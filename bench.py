@@ -1,0 +1,266 @@
+"""Benchmark: quantized-KV decode attention on one MI355X.
+
+One step is the decode hot path for one batch: rotate-quantize-append one new
+token per sequence (with tail graduation), then single-query decode attention
+over the whole cache.  Default workload "long": batch 8, 40 query / 8 KV
+heads, head_dim 128, 65536 cached tokens, K 8-bit / V 4-bit 32-element blocks
+with fp16 scales, newest 1024 tokens in a bf16 tail, Hadamard-128 rotation.
+
+Prints one JSON line.  `value` is cache GB/s over the full step (algorithmic
+cache bytes read by the attention / step time).  `roofline` reports the
+split-K attention kernel alone, timed with HIP events recorded on the call's
+stream around that kernel.  `cpu_baseline` times the CPU oracle's decode
+attention on a bounded sample of (sequence, KV head) units of the same cache.
+
+  python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FILL_CHUNK = 8192
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cache_bytes_per_step(w, lens):
+    """Algorithmic bytes one attention call reads: packed codes + fp16 scales
+    of quantized tokens, bf16 K and V rows of tail tokens."""
+    d, T = w["d"], w["tail"]
+    nb = d // 32
+    tot = 0
+    for n in lens:
+        nt = min(n, T) if T > 0 else 0
+        nq = n - nt
+        q_bytes = nq * (d * w["k_bits"] // 8 + d * w["v_bits"] // 8 + 2 * 2 * nb)
+        tot += (q_bytes + nt * 2 * d * 2) * w["Hkv"]
+    return tot
+
+
+def describe(w):
+    return ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %d, K%d V%d, "
+            "bf16 tail %d, %s inputs" % (w["name"], w["B"], w["Hq"], w["Hkv"], w["d"], w["n"],
+                                        w["k_bits"], w["v_bits"], w["tail"], w["dist"]))
+
+
+# ----------------------------------------------------------- CPU baseline
+def _oracle_unit(args):
+    """Time the oracle's decode attention for one (sequence, KV head) unit
+    whose cache the oracle builds itself from the same generator inputs."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    k, v, q, w = args
+    from oracle import OracleCache, decode_reference
+    from oracle.blockquant import bf16_bits_to_f32
+    n, d = k.shape[0], w["d"]
+    G = q.shape[0]
+    c = OracleCache(1, 1, d, w["k_bits"], w["v_bits"], w["tail"], n)
+    c.append(k[None, :, None], v[None, :, None], [0], dtype="bf16")
+    planes = c.physical()
+    t0 = time.perf_counter()
+    decode_reference(planes, bf16_bits_to_f32(q)[None], [n], 1, d, w["k_bits"], w["v_bits"],
+                     w["tail"])
+    return time.perf_counter() - t0, G
+
+
+def cpu_baseline(w, units, k_dev, v_dev, q_host, torch, budget_units):
+    """Oracle decode attention over a sample of units, run in a process pool."""
+    import multiprocessing as mp
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    sample = units[:budget_units]
+    G = w["Hq"] // w["Hkv"]
+    jobs = []
+    for b, g in sample:
+        k = k_dev[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        v = v_dev[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        jobs.append((k, v, q_host[b, g * G:(g + 1) * G], w))
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(min(cores, len(jobs))) as pool:
+        res = pool.map(_oracle_unit, jobs)
+    wall = time.perf_counter() - t0
+    busy = sum(r[0] for r in res)
+    unit_bytes = cache_bytes_per_step(dict(w, B=1, Hkv=1), [w["n"]])
+    # throughput of the timed attention work at the pool's parallelism
+    par = min(cores, len(jobs))
+    gbs = len(jobs) * unit_bytes / (busy / par) / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": par, "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) units at full context %d; float64 "
+                      "attention over the oracle-built cache, %.1f s of CPU time "
+                      "(pool wall %.1f s incl. setup)" % (len(jobs), w["B"] * w["Hkv"],
+                                                         w["n"], busy, wall)}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--no-append", action="store_true", help="skip the bulk append measurement")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library runs the decode hot path on a single "
+              "device (no collectives); run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import decode_attention_rotate_amd as kvq
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = workloads.workload(args.workload)
+    B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
+    total_steps = args.warmup + args.steps
+    max_ctx = n + total_steps + 64
+    cfg = kvq.kvq_config(B, Hkv, d, max_ctx, w["k_bits"], w["v_bits"], w["tail"])
+    cache = kvq.KVCache(cfg, dev)
+    log("workload", describe(w))
+
+    # fill the cache; keep the generated inputs of a few units for the oracle
+    rng = np.random.default_rng(0)
+    units = [(int(rng.integers(B)), int(rng.integers(Hkv))) for _ in range(args.cpu_units)]
+    k_units = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev) if not args.no_cpu_baseline else None
+    v_units = torch.empty_like(k_units) if k_units is not None else None
+    lens = [0] * B
+    t_fill = 0.0
+    fill_tokens = 0
+    for t0 in range(0, n, FILL_CHUNK):
+        t1 = min(n, t0 + FILL_CHUNK)
+        k = workloads.kv_torch(w, 1, t0, t1, dev, torch)
+        v = workloads.kv_torch(w, 2, t0, t1, dev, torch)
+        if k_units is not None:
+            k_units[:, t0:t1].copy_(k)
+            v_units[:, t0:t1].copy_(v)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.kvq_rotate_quantize_append(cfg, cache, k, v, lens)
+        e1.record()
+        torch.cuda.synchronize()
+        t_fill += e0.elapsed_time(e1) * 1e-3
+        fill_tokens += (t1 - t0) * B
+        lens = [x + (t1 - t0) for x in lens]
+        del k, v
+    log("filled %d tokens/sequence, append %.1f Mtok/s" % (n, fill_tokens / t_fill / 1e6))
+
+    # inputs of every step, generated before timing
+    qs = [workloads.q_torch(w, s, dev, torch) for s in range(total_steps)]
+    ks = [workloads.new_tokens_torch(w, 1, s, dev, torch) for s in range(total_steps)]
+    vs = [workloads.new_tokens_torch(w, 2, s, dev, torch) for s in range(total_steps)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(cfg, Hq), dtype=torch.uint8, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+
+    def step(s):
+        kvq.kvq_rotate_quantize_append(cfg, cache, ks[s], vs[s], lens)
+        for b in range(B):
+            lens[b] += 1
+        kvq.kvq_profile_decode_events(ev[s][0], ev[s][1])
+        kvq.kvq_decode_attention(cfg, cache, qs[s], lens, out=out, workspace=ws)
+
+    step_bytes = []
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        step(s)
+        step_bytes.append(cache_bytes_per_step(w, lens))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kvq.kvq_profile_decode_events(None, None)
+    assert torch.isfinite(out).all().item(), "non-finite attention output"
+
+    ms_step = elapsed / args.steps * 1e3
+    avg_bytes = float(np.mean(step_bytes))
+    kern_ms = [kvq.kernel_elapsed_ms(ev[s][0], ev[s][1]) for s in range(args.warmup, total_steps)]
+    kern_avg_ms = float(np.mean(kern_ms))
+    achieved = avg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    value = avg_bytes / (ms_step * 1e-3) / 1e9
+    log("step %.1f us, attention kernel %.1f us (median %.1f), %.0f GB/s kernel, %.0f GB/s step"
+        % (ms_step * 1e3, kern_avg_ms * 1e3, float(np.median(kern_ms)) * 1e3, achieved, value))
+
+    result = {
+        "metric": "Quantized-KV decode attention cache GB/s (decode step: append 1 token + attention)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/u4 codes, fp16 scales, f32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "cache_bytes_per_step": int(avg_bytes),
+                   "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+                   "us_per_step": round(ms_step * 1e3, 2),
+                   "attention_kernel_us": round(kern_avg_ms * 1e3, 2),
+                   "fill_append_mtok_s": round(fill_tokens / t_fill / 1e6, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    q0 = qs[0]
+    del qs, ks, vs
+
+    if not args.no_append:
+        result["append"] = bulk_append(torch, kvq, dev)
+
+    if not args.no_cpu_baseline:
+        q_host = q0.view(torch.int16).cpu().numpy().view(np.uint16)
+        log("cpu baseline on %d units" % len(units))
+        result["cpu_baseline"] = cpu_baseline(w, units, k_units, v_units, q_host, torch, len(units))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bulk_append(torch, kvq, dev):
+    """Rotate-quantize-append of 32768 tokens per sequence in one call:
+    batch 16, 8 KV heads, head_dim 128, K4 V4, no tail."""
+    w = workloads.workload("mid")
+    B, Hkv, d, n = w["B"], w["Hkv"], w["d"], w["n"]
+    cfg = kvq.kvq_config(B, Hkv, d, n, w["k_bits"], w["v_bits"], 0)
+    cache = kvq.KVCache(cfg, dev)
+    k = workloads.kv_torch(w, 1, 0, n, dev, torch)
+    v = workloads.kv_torch(w, 2, 0, n, dev, torch)
+    reps = 5
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 1)]
+    for r in range(reps + 1):
+        evs[r][0].record()
+        kvq.kvq_rotate_quantize_append(cfg, cache, k, v, [0] * B)
+        evs[r][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([evs[r][0].elapsed_time(evs[r][1]) for r in range(1, reps + 1)]))
+    tokens = B * n
+    moved = 2 * B * n * Hkv * d * 2 + 2 * B * n * Hkv * (d * 4 // 8 + 2 * d // 32)
+    res = {"workload": "mid append: batch 16, 8 KV heads, head_dim 128, 32768 new tokens "
+                       "per sequence in one call, K4 V4",
+           "us": round(ms * 1e3, 1), "mtok_s": round(tokens / (ms * 1e-3) / 1e6, 1),
+           "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
+           "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    log("bulk append", res)
+    del k, v, cache
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

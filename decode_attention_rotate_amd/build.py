@@ -1,0 +1,89 @@
+"""Build libkvq.so (HIP for gfx950) in-tree, compiling translation units in
+parallel.  Usage: python -m decode_attention_rotate_amd.build [--jobs N]."""
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libkvq.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # bit-exact quantizer: IEEE float32, no contraction of a*b+c into fma
+    "-ffp-contract=off",
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+]
+DEVICE = [
+    "--offload-arch=" + ARCH,
+    # never emit packed fp32 arithmetic
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def units():
+    """(source, object, extra flags) for every translation unit."""
+    out = []
+    for name in ("append.hip", "dequant.hip", "decode_main.hip"):
+        out.append((os.path.join(CSRC, name), name.replace(".hip", ".o"), DEVICE))
+    for d in (64, 128, 256):
+        for kb in (4, 5, 8):
+            out.append((os.path.join(CSRC, "decode_inst.hip"), "decode_d%d_k%d.o" % (d, kb),
+                        DEVICE + ["-DKVQ_INST_D=%d" % d, "-DKVQ_INST_KB=%d" % kb]))
+    out.append((os.path.join(CSRC, "kvq_host.cpp"), "kvq_host.o", DEVICE + ["-x", "hip"]))
+    return out
+
+
+def _compile(job):
+    src, obj, extra = job
+    cmd = [HIPCC] + COMMON + extra + ["-c", src, "-o", os.path.join(BUILD, obj)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = ("unknown target feature", "packed-fp32-ops", "warning generated")
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if l.strip() and not any(n in l for n in noise))
+    return obj, r.returncode, msgs, cmd
+
+
+def build(jobs=None, verbose=False):
+    """Compile every unit and link libkvq.so; raises on any failure."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError("hipcc not found at %s" % HIPCC)
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(16, os.cpu_count() or 4)
+    failed = []
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for obj, rc, msgs, cmd in ex.map(_compile, units()):
+            if rc != 0:
+                failed.append((obj, msgs, cmd))
+            elif verbose and msgs:
+                print("[%s]\n%s" % (obj, msgs))
+    if failed:
+        raise RuntimeError("\n\n".join("%s failed:\n%s\n%s" % (o, " ".join(c), m) for o, m, c in failed))
+    objs = [os.path.join(BUILD, o) for _, o, _ in units()]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    shutil.move(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(args.jobs, args.verbose))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

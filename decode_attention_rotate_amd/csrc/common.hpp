@@ -1,0 +1,122 @@
+// Device helpers shared by the kvq kernels (gfx950, wave64).
+//
+// The rotation is the normalized Sylvester Hadamard transform (velog.io post
+// "fix KV cache quantization outliers", section "Hadamard rotation"), applied
+// as a float32 fast Walsh-Hadamard transform whose butterfly stages run in the
+// order h = 1, 2, 4, ..., d/2.  The quantizer and the transform must match the
+// CPU reference bit for bit, so everything in this file is compiled with
+// -ffp-contract=off and uses IEEE float32 with denormals preserved.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kTile = 64;     // tokens per tile of a code plane
+constexpr int kChunk = 16;    // bytes per tiled chunk
+constexpr int kBlock = 32;    // elements per quantization block
+
+__host__ __device__ constexpr int row_bytes(int d, int bits) { return d * bits / 8; }
+__host__ __device__ constexpr int padded_row_bytes(int d, int bits) {
+  return (row_bytes(d, bits) + kChunk - 1) / kChunk * kChunk;
+}
+__host__ __device__ constexpr int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
+
+// Byte offset of 16-byte chunk c of token p's row inside one (b, g) plane.
+__host__ __device__ inline size_t chunk_offset(int p, int c, int rpad) {
+  return (size_t)(p / kTile) * kTile * rpad + (size_t)(c * kTile + (p % kTile)) * kChunk;
+}
+
+__device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round-to-nearest-even to bfloat16 (finite inputs).
+__device__ inline uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline float bf16_round(float x) { return __uint_as_float(f32_to_bf16_bits(x) << 16); }
+
+// Value of lane (lane ^ M) within groups of 32 lanes.
+template <int M>
+__device__ inline float xor_lane(float v) {
+  int i = __float_as_int(v);
+  if constexpr (M == 1) {
+    i = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    i = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  } else {
+    static_assert(M == 4 || M == 8 || M == 16, "xor within 32 lanes");
+    i = __builtin_amdgcn_ds_swizzle(i, 0x1F | (M << 10));     // bit-mask mode, xor M
+  }
+  return __int_as_float(i);
+}
+
+// Butterfly stages h = 1..16 on the 32 consecutive elements a lane holds.
+__device__ inline void fwht32_in_lane(float (&x)[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float u = x[i], v = x[i + h];
+        x[i] = u + v;
+        x[i + h] = u - v;
+      }
+    }
+  }
+}
+
+// One butterfly stage across lanes: element bit log2(32*M) lives in lane bit
+// M.  The lane holding the lower index keeps a + b, the other b_low - a_high;
+// adding the sign-flipped own value gives exactly those two results.
+template <int M>
+__device__ inline void fwht_cross_stage(float (&x)[32], int lane) {
+  const uint32_t flip = (lane & M) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float y = xor_lane<M>(x[i]);
+    x[i] = y + __uint_as_float(__float_as_uint(x[i]) ^ flip);
+  }
+}
+
+// Full transform of a d-element row spread over d/32 consecutive lanes, each
+// holding one 32-element block, followed by the normalization multiply.
+template <int D>
+__device__ inline void rotate_row(float (&x)[32], int lane, float cd) {
+  fwht32_in_lane(x);
+  if constexpr (D >= 64) fwht_cross_stage<1>(x, lane);
+  if constexpr (D >= 128) fwht_cross_stage<2>(x, lane);
+  if constexpr (D >= 256) fwht_cross_stage<4>(x, lane);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = x[i] * cd;
+}
+
+// Bit of the 5-bit high-bit word owned by element w (0..31) of a block.
+__host__ __device__ constexpr int hibit_pos(int w) {
+  return 8 * ((w % 8) / 2) + 2 * (w / 8) + (w % 2);
+}
+
+// Quantize one 32-element block: fp16 scale bits and int codes.
+template <int BITS>
+__device__ inline uint32_t quantize_block(const float (&x)[32], int (&c)[32]) {
+  constexpr float qmax = (float)qmax_of(BITS);
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
+  float s32 = a / qmax;                  // correctly rounded divide
+  s32 = fminf(s32, 65504.0f);
+  const _Float16 s16 = (_Float16)s32;    // round to nearest even
+  const float sf = (float)s16;
+  const float r = sf != 0.f ? 1.0f / sf : 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float t = rintf(x[i] * r);
+    c[i] = (int)fminf(fmaxf(t, -qmax), qmax);
+  }
+  return (uint32_t)__builtin_bit_cast(uint16_t, s16);
+}
+
+}  // namespace kvq

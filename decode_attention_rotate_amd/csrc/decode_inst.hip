@@ -1,0 +1,31 @@
+// One instantiation unit of the split-K decode kernel: head_dim KVQ_INST_D and
+// K width KVQ_INST_KB (set by the build), every V width and 1..8 query heads
+// per KV-head chunk.  Split across units so the build compiles in parallel.
+#include "decode_kernels.hpp"
+
+#ifndef KVQ_INST_D
+#error "KVQ_INST_D must be defined"
+#endif
+#ifndef KVQ_INST_KB
+#error "KVQ_INST_KB must be defined"
+#endif
+
+#define KVQ_CAT2(a, b, c) a##_##b##_##c
+#define KVQ_CAT(a, b, c) KVQ_CAT2(a, b, c)
+#define KVQ_TABLE KVQ_CAT(kvq_decode_table, KVQ_INST_D, KVQ_INST_KB)
+
+namespace kvq {
+
+#define KVQ_ROW(VB)                                                                \
+  {launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 1>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 2>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 3>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 4>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 5>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 6>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 7>,                            \
+   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8>}
+
+DecodeLauncher KVQ_TABLE[3][8] = {KVQ_ROW(4), KVQ_ROW(5), KVQ_ROW(8)};
+
+}  // namespace kvq

@@ -1,0 +1,95 @@
+// Dequantize (read-back) kernel: code * fp16 scale for quantized positions,
+// the stored bf16 value for tail positions, optionally rotated back to the
+// original space with the same float32 transform as the append (the
+// normalized Sylvester matrix is its own inverse; velog.io post "fix KV cache
+// quantization outliers", section "Hadamard rotation").
+//
+// Thread mapping as in the append: one lane per 32-element block.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace kvq {
+namespace {
+
+template <int D, int BITS>
+__device__ inline void load_codes(const uint8_t* plane, int p, int j, int (&c)[32]) {
+  constexpr int RP = padded_row_bytes(D, BITS);
+  if constexpr (BITS == 8) {
+    const uint4 v0 = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, 2 * j, RP));
+    const uint4 v1 = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, 2 * j + 1, RP));
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) c[e] = (int)(int8_t)((w[e / 4] >> (8 * (e % 4))) & 0xFF);
+  } else {
+    constexpr int OFF = 1 << (BITS - 1);
+    const uint4 v = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, j, RP));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hw = 0;
+    if constexpr (BITS == 5) {
+      const int byte = D / 2 + 4 * j;
+      hw = *reinterpret_cast<const uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      int u = (int)((w[e / 8] >> (4 * (e % 8))) & 15);
+      if constexpr (BITS == 5) u |= (int)((hw >> hibit_pos(e)) & 1) << 4;
+      c[e] = u - OFF;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  constexpr int LPR = D / kBlock;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = tid % LPR;
+  const int g = blockIdx.y;
+  const int p = a.t0 + blockIdx.x * RPB + tid / LPR;
+  const bool active = p < a.t1;
+  const size_t unit = (size_t)a.b * a.Hkv + g;
+  float x[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) x[e] = 0.f;
+  if (active) {
+    if (p < a.nq) {
+      const uint8_t* plane = a.codes + unit * (size_t)a.cap * padded_row_bytes(D, a.bits);
+      const float s = (float)__builtin_bit_cast(_Float16, a.scales[(unit * a.cap + p) * (D / kBlock) + j]);
+      int c[32];
+      if (a.bits == 4) load_codes<D, 4>(plane, p, j, c);
+      else if (a.bits == 5) load_codes<D, 5>(plane, p, j, c);
+      else load_codes<D, 8>(plane, p, j, c);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = (float)c[e] * s;
+    } else {
+      const uint16_t* row = a.tail + (unit * a.T + p % a.T) * D + kBlock * j;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = bf16_to_f32(row[e]);
+    }
+  }
+  if (a.space == 1 && a.rotate) rotate_row<D>(x, lane, a.cd);
+  if (!active) return;
+  float4* dst = reinterpret_cast<float4*>(a.out + ((size_t)(p - a.t0) * a.Hkv + g) * D + kBlock * j);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dst[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+}
+
+}  // namespace
+
+hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s) {
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  const int rpb = 256 / (D / kBlock);
+  const int n = a.t1 - a.t0;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((n + rpb - 1) / rpb, a.Hkv, 1);
+  switch (D) {
+    case 64: hipLaunchKernelGGL(dequant_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(dequant_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(dequant_kernel<256>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,82 @@
+// Internal interface between the host library and the kernel translation
+// units: argument blocks passed by value to the kernels, and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// ---------------------------------------------------------------- append
+struct AppendArgs {
+  const void* src[2];        // k_new, v_new: [B][n_new][Hkv][D]
+  uint8_t* codes[2];         // tiled code planes
+  uint16_t* scales[2];       // [B][Hkv][cap][D/32] fp16 bits
+  uint16_t* tail[2];         // [B][Hkv][T][D] bf16 bits (unused when T == 0)
+  int32_t bits[2];
+  int32_t rotate[2];
+  int32_t Hkv, n_new, T, cap, dtype;
+  float cd;                  // fp32(1/sqrt(D))
+  int32_t len[KVQ_MAX_BATCH];  // lengths before the append
+};
+hipError_t launch_append(int D, const AppendArgs& a, int B, hipStream_t s);
+
+// ------------------------------------------------------------- dequantize
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* tail;
+  float* out;                // [t1-t0][Hkv][D]
+  int32_t bits, rotate, space, Hkv, T, cap, b, t0, t1, nq;
+  float cd;
+};
+hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- decode
+// Per query head the prep kernel writes kQpStride(D) bytes:
+//   [0, D)          high bytes of the 16-bit fixed-point rotated query,
+//                   in the byte order the K code unpacking produces
+//   [D, 2D)         low bytes, same order
+//   [2D, 2D+D/8)    int32 per block: -offset * sum of the fixed-point query
+//                   (folds offset-binary K codes back to signed codes)
+//   [2D+D/8, +4)    float: fixed-point step * sm_scale * log2(e)
+//   [4D, 8D)        float32 rotated query (used for bf16 tail tokens)
+__host__ __device__ constexpr int qp_stride(int D) { return 8 * D; }
+
+struct PrepArgs {
+  const void* q;             // [B][Hq][D]
+  uint8_t* qp;               // [B][Hq][qp_stride]
+  int32_t Hq, dtype, rotate, k_bits;
+  float cd, sm_scale;
+};
+hipError_t launch_prep(int D, const PrepArgs& a, int B, hipStream_t s);
+
+struct DecodeArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_scales;
+  const uint8_t* v_codes;
+  const uint16_t* v_scales;
+  const uint16_t* k_tail;
+  const uint16_t* v_tail;
+  const uint8_t* qp;         // prep output
+  float* part_ml;            // [B][Hq][S][2]  running max (log2 units), sum
+  float* part_acc;           // [B][Hq][S][D]  unnormalised output, rotated space
+  int32_t Hkv, Hq, G, n_gchunks, T, cap, S, split_tokens;
+  int32_t len[KVQ_MAX_BATCH];
+};
+using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
+// Table lookup for (D, k_bits, v_bits, heads per chunk); nullptr if absent.
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc);
+
+struct CombineArgs {
+  const float* part_ml;
+  const float* part_acc;
+  float* out;                // [B][Hq][D]
+  int32_t Hq, S, rotate;
+  float cd;
+};
+hipError_t launch_combine(int D, const CombineArgs& a, int B, hipStream_t s);
+
+}  // namespace kvq

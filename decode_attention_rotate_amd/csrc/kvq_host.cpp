@@ -1,0 +1,340 @@
+// Host side of the kvq C ABI: argument validation, sizing of cache planes and
+// of the decode workspace, split-K scheduling and kernel launches.
+//
+// Configuration rules: K and V widths are independent (velog.io post "fix KV
+// cache quantization outliers", section "the essence of the problem", the
+// --cache-type-k / --cache-type-v options); rotation defaults to on for
+// head_dim >= 64 and a multiple of 64 and is switchable per plane (same post,
+// section "application and background"); the bf16 tail length is a setting
+// (aitrends.kr article 92204, glossary "Precision Tail").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "kvq.h"
+
+namespace {
+
+using namespace kvq;
+
+constexpr int kTargetWaves = 4096;   // split-K waves per decode launch
+constexpr int kMaxSplits = 1024;
+
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
+
+bool bits_ok(int b) { return b == 4 || b == 5 || b == 8; }
+bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cap_tokens(const kvq_config& c) { return ((int64_t)c.max_ctx + kTile - 1) / kTile * kTile; }
+
+kvq_status check_cfg(const kvq_config* c) {
+  if (!c) return KVQ_ERR_INVALID;
+  if (c->batch < 1 || c->batch > KVQ_MAX_BATCH || c->n_kv_heads < 1 || c->max_ctx < 1 ||
+      c->tail_len < 0 || (c->rotate_k != 0 && c->rotate_k != 1) ||
+      (c->rotate_v != 0 && c->rotate_v != 1))
+    return KVQ_ERR_INVALID;
+  if (!dim_ok(c->head_dim) || !bits_ok(c->k_bits) || !bits_ok(c->v_bits)) return KVQ_ERR_UNSUPPORTED;
+  if (c->n_kv_heads > 65535 / 2) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_config& c, const kvq_cache* k) {
+  if (!k) return KVQ_ERR_INVALID;
+  const void* need[4] = {k->k_codes, k->k_scales, k->v_codes, k->v_scales};
+  for (const void* p : need) {
+    if (!p) return KVQ_ERR_INVALID;
+    if (!aligned16(p)) return KVQ_ERR_ALIGN;
+  }
+  if (c.tail_len > 0) {
+    if (!k->k_tail || !k->v_tail) return KVQ_ERR_INVALID;
+    if (!aligned16(k->k_tail) || !aligned16(k->v_tail)) return KVQ_ERR_ALIGN;
+  }
+  return KVQ_OK;
+}
+
+// Largest divisor of G that is at most 8 (query heads per kernel instance).
+int head_chunk(int G) {
+  for (int c = std::min(G, 8); c >= 1; --c)
+    if (G % c == 0) return c;
+  return 1;
+}
+
+struct Schedule {
+  int gc, nchunk, S, split_tokens;
+};
+
+// Splits per (sequence, KV head, head chunk): enough waves to fill the chip,
+// at least one 64-token tile per split, contexts split at tile boundaries.
+Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
+  Schedule s;
+  const int G = n_q_heads / c.n_kv_heads;
+  s.gc = head_chunk(G);
+  s.nchunk = G / s.gc;
+  const int64_t units = (int64_t)c.batch * c.n_kv_heads * s.nchunk;
+  const int tiles = std::max(1, (max_len + kTile - 1) / kTile);
+  int want = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
+  want = std::min(want, tiles);
+  const int tiles_per = (tiles + want - 1) / want;
+  s.split_tokens = tiles_per * kTile;
+  s.S = (max_len + s.split_tokens - 1) / s.split_tokens;
+  if (s.S < 1) s.S = 1;
+  return s;
+}
+
+// Upper bound of Schedule::S over every length up to max_ctx (S never exceeds
+// the wanted split count, which never exceeds the tile count).
+int max_splits(const kvq_config& c, int n_q_heads) {
+  const int G = n_q_heads / c.n_kv_heads;
+  const int nchunk = G / head_chunk(G);
+  const int64_t units = (int64_t)c.batch * c.n_kv_heads * nchunk;
+  const int tiles = std::max(1, (c.max_ctx + kTile - 1) / kTile);
+  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
+  return (int)std::min<int64_t>(want, tiles);
+}
+
+// Workspace: prep output, then (max, sum) pairs, then partial vectors.
+struct WsLayout {
+  size_t qp, ml, acc, total;
+};
+WsLayout ws_layout(const kvq_config& c, int n_q_heads, int S) {
+  WsLayout w;
+  const size_t heads = (size_t)c.batch * n_q_heads;
+  w.qp = 0;
+  const size_t qp_bytes = heads * qp_stride(c.head_dim);
+  w.ml = (qp_bytes + 255) / 256 * 256;
+  const size_t ml_bytes = heads * (size_t)S * 2 * sizeof(float);
+  w.acc = w.ml + (ml_bytes + 255) / 256 * 256;
+  w.total = w.acc + heads * (size_t)S * c.head_dim * sizeof(float);
+  return w;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t max_ctx) {
+  kvq_config c;
+  c.batch = batch;
+  c.n_kv_heads = n_kv_heads;
+  c.head_dim = head_dim;
+  c.k_bits = 4;
+  c.v_bits = 4;
+  c.tail_len = 0;
+  c.max_ctx = max_ctx;
+  const int on = (head_dim >= 64 && head_dim % 64 == 0) ? 1 : 0;
+  c.rotate_k = on;
+  c.rotate_v = on;
+  return c;
+}
+
+kvq_status kvq_config_check(const kvq_config* cfg) { return check_cfg(cfg); }
+
+size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane) {
+  if (check_cfg(cfg) != KVQ_OK) return 0;
+  const kvq_config& c = *cfg;
+  const size_t units = (size_t)c.batch * c.n_kv_heads;
+  const size_t cap = (size_t)cap_tokens(c);
+  switch (plane) {
+    case KVQ_K_CODES: return units * cap * padded_row_bytes(c.head_dim, c.k_bits);
+    case KVQ_V_CODES: return units * cap * padded_row_bytes(c.head_dim, c.v_bits);
+    case KVQ_K_SCALES:
+    case KVQ_V_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t);
+    case KVQ_K_TAIL:
+    case KVQ_V_TAIL: return units * (size_t)c.tail_len * c.head_dim * sizeof(uint16_t);
+  }
+  return 0;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads) {
+  if (check_cfg(cfg) != KVQ_OK) return 0;
+  if (n_q_heads < cfg->n_kv_heads || n_q_heads % cfg->n_kv_heads != 0) return 0;
+  return ws_layout(*cfg, n_q_heads, max_splits(*cfg, n_q_heads)).total;
+}
+
+kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* cache,
+                                      const void* k_new, const void* v_new, kvq_dtype dtype,
+                                      int32_t n_new, const int32_t* seq_len, void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = *cfg;
+  if ((st = check_cache(c, cache)) != KVQ_OK) return st;
+  if (dtype != KVQ_BF16 && dtype != KVQ_F32) return KVQ_ERR_INVALID;
+  if (n_new < 0 || !seq_len) return KVQ_ERR_INVALID;
+  for (int b = 0; b < c.batch; ++b) {
+    if (seq_len[b] < 0) return KVQ_ERR_INVALID;
+    if ((int64_t)seq_len[b] + n_new > c.max_ctx) return KVQ_ERR_CAPACITY;
+  }
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGN;
+
+  AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.codes[0] = static_cast<uint8_t*>(cache->k_codes);
+  a.codes[1] = static_cast<uint8_t*>(cache->v_codes);
+  a.scales[0] = static_cast<uint16_t*>(cache->k_scales);
+  a.scales[1] = static_cast<uint16_t*>(cache->v_scales);
+  a.tail[0] = static_cast<uint16_t*>(cache->k_tail);
+  a.tail[1] = static_cast<uint16_t*>(cache->v_tail);
+  a.bits[0] = c.k_bits;
+  a.bits[1] = c.v_bits;
+  a.rotate[0] = c.rotate_k;
+  a.rotate[1] = c.rotate_v;
+  a.Hkv = c.n_kv_heads;
+  a.n_new = n_new;
+  a.T = c.tail_len;
+  a.cap = (int32_t)cap_tokens(c);
+  a.dtype = dtype;
+  a.cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  for (int b = 0; b < c.batch; ++b) a.len[b] = seq_len[b];
+  return hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                kvq_dtype dtype, int32_t n_q_heads, float sm_scale,
+                                const int32_t* seq_len, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = *cfg;
+  if ((st = check_cache(c, cache)) != KVQ_OK) return st;
+  if (dtype != KVQ_BF16 && dtype != KVQ_F32) return KVQ_ERR_INVALID;
+  if (!q || !out || !workspace || !seq_len) return KVQ_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (n_q_heads < c.n_kv_heads || n_q_heads % c.n_kv_heads != 0) return KVQ_ERR_INVALID;
+  if ((int64_t)c.batch * n_q_heads > 2147483647 / 8) return KVQ_ERR_INVALID;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  int max_len = 0;
+  for (int b = 0; b < c.batch; ++b) {
+    if (seq_len[b] < 1) return KVQ_ERR_INVALID;
+    if (seq_len[b] > c.max_ctx) return KVQ_ERR_CAPACITY;
+    max_len = std::max(max_len, (int)seq_len[b]);
+  }
+  const Schedule sc = schedule(c, n_q_heads, max_len);
+  const WsLayout wl = ws_layout(c, n_q_heads, sc.S);
+  if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
+  const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc);
+  if (!fn) return KVQ_ERR_UNSUPPORTED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const float cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+
+  PrepArgs pa;
+  pa.q = q;
+  pa.qp = ws + wl.qp;
+  pa.Hq = n_q_heads;
+  pa.dtype = dtype;
+  pa.rotate = c.rotate_k;
+  pa.k_bits = c.k_bits;
+  pa.cd = cd;
+  pa.sm_scale = sm_scale;
+  if ((st = hip_status(launch_prep(c.head_dim, pa, c.batch, s))) != KVQ_OK) return st;
+
+  DecodeArgs da;
+  std::memset(&da, 0, sizeof(da));
+  da.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+  da.k_scales = static_cast<const uint16_t*>(cache->k_scales);
+  da.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+  da.v_scales = static_cast<const uint16_t*>(cache->v_scales);
+  da.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+  da.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+  da.qp = ws + wl.qp;
+  da.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+  da.part_acc = reinterpret_cast<float*>(ws + wl.acc);
+  da.Hkv = c.n_kv_heads;
+  da.Hq = n_q_heads;
+  da.G = n_q_heads / c.n_kv_heads;
+  da.n_gchunks = sc.nchunk;
+  da.T = c.tail_len;
+  da.cap = (int32_t)cap_tokens(c);
+  da.S = sc.S;
+  da.split_tokens = sc.split_tokens;
+  for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
+  const dim3 grid(sc.S, c.n_kv_heads * sc.nchunk, c.batch);
+  if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
+  if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
+  if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
+
+  CombineArgs ca;
+  ca.part_ml = da.part_ml;
+  ca.part_acc = da.part_acc;
+  ca.out = out;
+  ca.Hq = n_q_heads;
+  ca.S = sc.S;
+  ca.rotate = c.rotate_v;
+  ca.cd = cd;
+  return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
+}
+
+kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t which, int32_t b,
+                          int32_t t0, int32_t t1, const int32_t* seq_len, int32_t space,
+                          float* out, void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = *cfg;
+  if ((st = check_cache(c, cache)) != KVQ_OK) return st;
+  if ((which != 0 && which != 1) || (space != 0 && space != 1) || !seq_len)
+    return KVQ_ERR_INVALID;
+  if (b < 0 || b >= c.batch) return KVQ_ERR_INVALID;
+  const int n = seq_len[b];
+  if (n < 0) return KVQ_ERR_INVALID;
+  if (n > c.max_ctx) return KVQ_ERR_CAPACITY;
+  if (t0 < 0 || t0 > t1 || t1 > n) return KVQ_ERR_INVALID;
+  if (t0 == t1) return KVQ_OK;
+  if (!out) return KVQ_ERR_INVALID;
+  if (!aligned16(out)) return KVQ_ERR_ALIGN;
+  DequantArgs a;
+  a.codes = static_cast<const uint8_t*>(which == 0 ? cache->k_codes : cache->v_codes);
+  a.scales = static_cast<const uint16_t*>(which == 0 ? cache->k_scales : cache->v_scales);
+  a.tail = static_cast<const uint16_t*>(which == 0 ? cache->k_tail : cache->v_tail);
+  a.out = out;
+  a.bits = which == 0 ? c.k_bits : c.v_bits;
+  a.rotate = which == 0 ? c.rotate_k : c.rotate_v;
+  a.space = space;
+  a.Hkv = c.n_kv_heads;
+  a.T = c.tail_len;
+  a.cap = (int32_t)cap_tokens(c);
+  a.b = b;
+  a.t0 = t0;
+  a.t1 = t1;
+  a.nq = n - (c.tail_len > 0 ? std::min(n, (int)c.tail_len) : 0);
+  a.cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  return hip_status(launch_dequant(c.head_dim, a, static_cast<hipStream_t>(stream)));
+}
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported head_dim or bit width";
+    case KVQ_ERR_CAPACITY: return "sequence length exceeds max_ctx";
+    case KVQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    case KVQ_ERR_WORKSPACE: return "decode workspace too small";
+  }
+  return "unknown status";
+}
+
+void kvq_profile_decode_events(void* before, void* after) {
+  if (before && after) {
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+  } else {
+    g_ev_before = nullptr;
+    g_ev_after = nullptr;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+/*
+ * kvq — rotated low-bit KV cache and single-query decode attention for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The method (sources are the three public pages this library is built from):
+ *  - Each K/V head vector is multiplied by a normalized Hadamard matrix before
+ *    it is stored, which spreads outlier channels; attention runs on rotated
+ *    q and K (the matrix is orthogonal, so scores are unchanged) and the
+ *    output is rotated back.  velog.io post "fix KV cache quantization
+ *    outliers", section "Hadamard rotation".  Rotation is on by default when
+ *    head_dim >= 64 and a multiple of 64, and can be switched off separately
+ *    for K and V (same post, section "application and background").
+ *  - Rotated vectors are stored as 32-element blocks: one fp16 absmax scale
+ *    plus 4-, 5- or 8-bit codes, i.e. 4.5 / 5.5 / 8.5 bits per value, the
+ *    q4_0 / q5_0 / q8_0 cache sizes (28.1 / 34.4 / 53.1 % of bf16) in the
+ *    table "Qwen 3.6 27B Q5_K_S + 64k context KLD results" of aiwitness.kr
+ *    post 1txlhxu.  K and V pick their widths independently
+ *    (--cache-type-k / --cache-type-v in the velog.io post).
+ *  - An optional bf16 precision tail keeps the newest tokens unquantized
+ *    (aitrends.kr article 92204, glossary entry "Precision Tail").
+ *
+ * Conventions shared by every call:
+ *  - Ownership: the caller allocates and frees every device buffer; the
+ *    library never allocates device memory and keeps no global state, so
+ *    calls are re-entrant.  Host arrays (seq_len) are read during the call
+ *    only.
+ *  - Execution: all device work is queued on `stream` (a hipStream_t passed
+ *    as void*; NULL is the default stream) and is asynchronous.
+ *  - Errors: every argument is validated on the host before any device work
+ *    is queued; a failed validation returns a negative status and queues
+ *    nothing.  A failed kernel launch returns KVQ_ERR_HIP.  Errors raised by
+ *    the device later surface from the HIP runtime on the caller's next
+ *    synchronisation.
+ *  - Device pointers must be 16-byte aligned (KVQ_ERR_ALIGN otherwise).
+ *
+ * Cache memory layout (all planes indexed by sequence b and KV head g,
+ * cap = max_ctx rounded up to a multiple of 64 tokens):
+ *  - code planes (k_codes, v_codes): per (b, g) a block of cap * R bytes,
+ *    where R = head_dim * bits / 8 rounded up to a multiple of 16.  Tokens
+ *    are grouped in tiles of 64; inside a tile, bytes [16c, 16c+16) of the
+ *    row of token l live at byte (c * 64 + l) * 16.  Row encoding:
+ *      8-bit  two's-complement code per element;
+ *      4-bit  u = code + 8, element 2i in the low nibble of byte i,
+ *             element 2i+1 in the high nibble;
+ *      5-bit  u = code + 16: low nibbles packed as 4-bit (head_dim/2 bytes),
+ *             then one little-endian 32-bit word per block holding bit 4 of
+ *             each code; element w of the block owns bit
+ *             8*((w%8)/2) + 2*(w/8) + (w%2).
+ *    Row padding bytes are never read or written.
+ *  - scale planes (k_scales, v_scales): [b][g][cap][head_dim/32] fp16.
+ *  - tail planes (k_tail, v_tail): [b][g][tail_len][head_dim] bf16; position
+ *    p of the newest tail_len positions lives in slot p % tail_len.  NULL is
+ *    allowed when tail_len == 0.
+ *
+ * Quantization of one block of 32 rotated values x (bf16-rounded first when
+ * tail_len > 0, so that a token gets the same codes whether or not it passed
+ * through the tail):
+ *    a = max|x|;  s = fp16_rne(min(a / qmax, 65504));  r = 1 / float(s);
+ *    code = clamp(rint(x * r), -qmax, qmax)   (all codes 0 if s == 0)
+ * with qmax = 7 / 15 / 127, IEEE float32 arithmetic, no fused operations.
+ * The rotation is y = fp32(1/sqrt(d)) * FWHT(x) with the float32 butterfly
+ * stages applied in the order h = 1, 2, 4, ..., d/2.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,      /* null pointer, bad size, bad enum value */
+  KVQ_ERR_UNSUPPORTED = -2,  /* head_dim or bit width the library does not build */
+  KVQ_ERR_CAPACITY = -3,     /* a sequence would exceed max_ctx */
+  KVQ_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned */
+  KVQ_ERR_HIP = -5,          /* the HIP runtime reported an error */
+  KVQ_ERR_WORKSPACE = -6     /* decode workspace smaller than required */
+} kvq_status;
+
+typedef enum kvq_dtype { KVQ_BF16 = 0, KVQ_F32 = 1 } kvq_dtype;
+
+typedef enum kvq_plane {
+  KVQ_K_CODES = 0, KVQ_K_SCALES = 1, KVQ_V_CODES = 2,
+  KVQ_V_SCALES = 3, KVQ_K_TAIL = 4, KVQ_V_TAIL = 5
+} kvq_plane;
+
+/* Largest batch a single call accepts (sequence lengths travel in the
+ * kernel arguments). */
+#define KVQ_MAX_BATCH 256
+
+typedef struct kvq_config {
+  int32_t batch;       /* sequences, 1..KVQ_MAX_BATCH */
+  int32_t n_kv_heads;  /* KV heads per sequence, >= 1 */
+  int32_t head_dim;    /* 64, 128 or 256 */
+  int32_t k_bits;      /* 4, 5 or 8 */
+  int32_t v_bits;      /* 4, 5 or 8 */
+  int32_t tail_len;    /* newest tokens kept in bf16, >= 0 */
+  int32_t max_ctx;     /* capacity per sequence in tokens, >= 1 */
+  int32_t rotate_k;    /* 1: rotate K (and q); 0: store K as is */
+  int32_t rotate_v;    /* 1: rotate V and rotate the output back; 0: neither */
+} kvq_config;
+
+typedef struct kvq_cache {
+  void* k_codes;
+  void* k_scales;
+  void* v_codes;
+  void* v_scales;
+  void* k_tail;  /* may be NULL when tail_len == 0 */
+  void* v_tail;  /* may be NULL when tail_len == 0 */
+} kvq_cache;
+
+/* Defaults: 4-bit K and V, no tail, rotation on iff head_dim >= 64 and
+ * head_dim % 64 == 0 (velog.io post, section "application and background"). */
+kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t max_ctx);
+
+/* KVQ_OK if the configuration is one the library can run. */
+kvq_status kvq_config_check(const kvq_config* cfg);
+
+/* Bytes the caller must allocate for one cache plane; 0 for an invalid
+ * configuration or plane (and for tail planes when tail_len == 0). */
+size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane);
+
+/* Device workspace kvq_decode_attention needs for n_q_heads query heads per
+ * sequence; 0 for invalid arguments.  Depends only on the configuration. */
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads);
+
+/* Rotate, quantize and append n_new tokens to every sequence.
+ *  k_new, v_new: device [batch][n_new][n_kv_heads][head_dim] of `dtype`.
+ *  seq_len:      host [batch], each sequence's length BEFORE the append;
+ *                positions seq_len[b] .. seq_len[b]+n_new-1 are written.
+ *                The caller advances its lengths afterwards.
+ * Positions below (new length - tail_len) are quantized; the newest tail_len
+ * positions are written to the tail ring, and tokens that leave the tail are
+ * quantized from their stored bf16 values in the same call.  n_new == 0 is a
+ * no-op.  Errors: KVQ_ERR_CAPACITY if seq_len[b] + n_new > max_ctx;
+ * KVQ_ERR_INVALID for null pointers, negative lengths or a bad dtype. */
+kvq_status kvq_rotate_quantize_append(const kvq_config* cfg,
+                                      const kvq_cache* cache,
+                                      const void* k_new, const void* v_new,
+                                      kvq_dtype dtype, int32_t n_new,
+                                      const int32_t* seq_len, void* stream);
+
+/* Single-query decode attention over the whole cache of every sequence
+ * (velog.io post, section "Hadamard rotation": rotated q.K scores, softmax,
+ * weighted sum of V, inverse rotation of the result).
+ *  q:        device [batch][n_q_heads][head_dim] of `dtype`; query head h
+ *            reads KV head h / (n_q_heads / n_kv_heads).
+ *  sm_scale: multiplier of q.k before the softmax (1/sqrt(head_dim) is usual).
+ *  seq_len:  host [batch], tokens cached per sequence, 1..max_ctx.
+ *  out:      device [batch][n_q_heads][head_dim] float32, original space.
+ *  workspace/workspace_bytes: device scratch of at least
+ *            kvq_decode_workspace_bytes(cfg, n_q_heads) bytes
+ *            (KVQ_ERR_WORKSPACE otherwise); contents need no initialisation.
+ * Errors: KVQ_ERR_INVALID if n_q_heads is not a positive multiple of
+ * n_kv_heads, a length is 0 or sm_scale is not finite; KVQ_ERR_CAPACITY if a
+ * length exceeds max_ctx. */
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                const void* q, kvq_dtype dtype,
+                                int32_t n_q_heads, float sm_scale,
+                                const int32_t* seq_len, float* out,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Read back positions [t0, t1) of sequence b from the K (which = 0) or V
+ * (which = 1) cache as float32 [t1-t0][n_kv_heads][head_dim]: code * scale
+ * for quantized positions, the stored bf16 value for tail positions.
+ * space 0 returns the rotated values; space 1 rotates them back (the same
+ * float32 transform as the append, since the matrix is its own inverse).
+ * seq_len is the host length array; 0 <= t0 <= t1 <= seq_len[b]. */
+kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache,
+                          int32_t which, int32_t b, int32_t t0, int32_t t1,
+                          const int32_t* seq_len, int32_t space, float* out,
+                          void* stream);
+
+/* Static text for a status code. */
+const char* kvq_status_str(kvq_status status);
+
+/* Instrumentation: when both are non-NULL, later kvq_decode_attention calls
+ * on this host thread record `before` immediately before and `after`
+ * immediately after the split-K attention kernel on the call's stream, so
+ * that kernel can be timed on its own.  Both are hipEvent_t passed as void*;
+ * the caller owns them.  NULL, NULL switches recording off. */
+void kvq_profile_decode_events(void* before, void* after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

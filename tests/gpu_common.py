@@ -1,0 +1,103 @@
+"""Helpers for the GPU parity tests: run the HIP path and the CPU oracle on
+the same seeded inputs and compare.  Imported by test_gpu_*.py only."""
+
+import sys
+
+import numpy as np
+import torch
+
+import decode_attention_rotate_amd as kvq
+from oracle import OracleCache, decode_reference
+from oracle.blockquant import bf16_bits_to_f32
+
+DEV = "cuda"
+
+
+def say(*msg):
+    """Name the GPU step about to run, flushed, so a crash log shows it."""
+    print("[gpu]", *msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(x, dtype):
+    """numpy inputs (bf16 bit patterns or float32) -> device tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def to_values(x, dtype):
+    """numpy inputs -> float32 values (bf16 widened exactly)."""
+    return bf16_bits_to_f32(x) if dtype == "bf16" else np.asarray(x, np.float32)
+
+
+def gpu_planes(cache, cfg):
+    """Device planes as numpy arrays shaped like OracleCache.physical()."""
+    B, H, d, T = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.tail_len
+    cap = (cfg.max_ctx + 63) // 64 * 64
+    out = {}
+    for p in ("k", "v"):
+        codes = cache[p + "_codes"].cpu().numpy()
+        out[p + "_codes"] = codes.reshape(B, H, -1)
+        out[p + "_scales"] = cache[p + "_scales"].cpu().numpy().view(np.uint16).reshape(B, H, cap, d // 32)
+        if T > 0:
+            out[p + "_tail"] = cache[p + "_tail"].cpu().numpy().view(np.uint16).reshape(B, H, T, d)
+        else:
+            out[p + "_tail"] = np.zeros((B, H, 0, d), np.uint16)
+    return out
+
+
+class Pair:
+    """A device cache and the oracle cache fed the same appends."""
+
+    def __init__(self, B, H, d, kb, vb, T, max_ctx, rotate_k=True, rotate_v=True):
+        self.cfg = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T, rotate_k, rotate_v)
+        self.cache = kvq.KVCache(self.cfg, DEV)
+        self.orc = OracleCache(B, H, d, kb, vb, T, max_ctx, rotate_k, rotate_v)
+        self.lens = np.zeros(B, dtype=np.int64)
+
+    def append(self, k, v, dtype, lens=None):
+        lens = self.lens if lens is None else np.asarray(lens, dtype=np.int64)
+        say("append", self.cfg, "n_new=%d" % k.shape[1], "lens=%s" % list(lens))
+        kvq.kvq_rotate_quantize_append(self.cfg, self.cache, to_device(k, dtype),
+                                       to_device(v, dtype), lens)
+        torch.cuda.synchronize()
+        self.orc.append(k, v, lens, dtype=dtype)
+        self.lens = lens + k.shape[1]
+
+    def compare_planes(self):
+        got = gpu_planes(self.cache, self.cfg)
+        want = self.orc.physical()
+        for key in want:
+            a, b = got[key], want[key]
+            assert a.shape == b.shape, key
+            if not np.array_equal(a, b):
+                bad = np.argwhere(a != b)
+                raise AssertionError("%s differs at %d places, first %s: gpu %s oracle %s"
+                                     % (key, len(bad), bad[0], a[tuple(bad[0])], b[tuple(bad[0])]))
+        return got
+
+    def decode(self, q, dtype, lens=None, sm_scale=None):
+        lens = self.lens if lens is None else lens
+        say("decode", self.cfg, "Hq=%d" % q.shape[1], "lens=%s" % list(lens))
+        out = kvq.kvq_decode_attention(self.cfg, self.cache, to_device(q, dtype), lens,
+                                       sm_scale=sm_scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+
+def attention_errors(got, planes, qv, lens, cfg, sm_scale=None, heads=None):
+    """Per-(b, h) relative L2 error of got against the float64 oracle
+    evaluated on the given (device-produced) planes."""
+    ref = decode_reference(planes, qv, lens, cfg.n_kv_heads, cfg.head_dim, cfg.k_bits,
+                           cfg.v_bits, cfg.tail_len, sm_scale=sm_scale,
+                           rotate_k=bool(cfg.rotate_k), rotate_v=bool(cfg.rotate_v),
+                           heads=heads)
+    errs = {}
+    B, Hq, _ = qv.shape
+    for b in range(B):
+        for h in range(Hq):
+            if heads is not None and (b, h) not in set(heads):
+                continue
+            errs[(b, h)] = np.linalg.norm(got[b, h] - ref[b, h]) / np.linalg.norm(ref[b, h])
+    return errs

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvq.h declares, sizes planes as the block format prescribes, and
+rejects bad arguments on the host before any device work is queued.
+
+The cases here only use argument combinations that fail validation, so no
+HIP call is ever reached."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+kvq = pytest.importorskip("decode_attention_rotate_amd")
+from decode_attention_rotate_amd import _capi  # noqa: E402
+
+if not os.path.exists(_capi.LIB_PATH):
+    pytest.skip("libkvq.so not built", allow_module_level=True)
+
+L = _capi.lib()
+FAKE = 0x10000          # aligned, never dereferenced (validation fails first)
+FAKE_MISALIGNED = 0x10008
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text))
+
+
+def test_exports_every_declared_function():
+    declared = _header_functions()
+    assert declared == set(_capi.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings():
+    for code in range(-6, 1):
+        assert isinstance(kvq.kvq_status_str(code), str) and kvq.kvq_status_str(code)
+
+
+@pytest.mark.parametrize("d,rot", [(64, 1), (128, 1), (256, 1), (32, 0), (96, 0), (192, 1)])
+def test_default_rotation_rule(d, rot):
+    # velog.io post, section "application and background": on for head_dim
+    # >= 64 and a multiple of 64
+    c = kvq.kvq_config_default(2, 4, d, 1000)
+    assert (c.rotate_k, c.rotate_v) == (rot, rot)
+    assert (c.k_bits, c.v_bits, c.tail_len) == (4, 4, 0)
+
+
+def test_config_check():
+    c = kvq.kvq_config_default(2, 4, 128, 1000)
+    assert kvq.kvq_config_check(c) == 0
+    for field, val, want in (("head_dim", 192, -2), ("head_dim", 32, -2), ("k_bits", 6, -2),
+                             ("v_bits", 3, -2), ("batch", 0, -1), ("batch", 257, -1),
+                             ("tail_len", -1, -1), ("max_ctx", 0, -1), ("rotate_k", 2, -1)):
+        bad = kvq.kvq_config_default(2, 4, 128, 1000)
+        setattr(bad, field, val)
+        assert kvq.kvq_config_check(bad) == want, field
+
+
+@pytest.mark.parametrize("d", (64, 128, 256))
+@pytest.mark.parametrize("kb,vb", ((4, 4), (8, 4), (5, 4), (8, 8), (5, 5)))
+def test_plane_bytes(d, kb, vb):
+    B, H, max_ctx, T = 3, 2, 1000, 16
+    c = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T)
+    cap = 1024
+    pad = lambda r: (r + 15) // 16 * 16
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_CODES) == B * H * cap * pad(d * kb // 8)
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_V_CODES) == B * H * cap * pad(d * vb // 8)
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_SCALES) == B * H * cap * (d // 32) * 2
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_TAIL) == B * H * T * d * 2
+    # codes + scales per token-head: 32*b/8 + 2 bytes per 32 elements
+    for b, plane in ((kb, kvq.KVQ_K_CODES), (vb, kvq.KVQ_V_CODES)):
+        if (d * b // 8) % 16 == 0:
+            per_tok = (kvq.kvq_plane_bytes(c, plane) + kvq.kvq_plane_bytes(c, kvq.KVQ_K_SCALES)) / (B * H * cap)
+            assert per_tok == (d // 32) * (32 * b // 8 + 2)
+
+
+def test_workspace_bytes():
+    c = kvq.kvq_config(8, 8, 128, 65536, 8, 4, 1024)
+    ws = kvq.kvq_decode_workspace_bytes(c, 40)
+    assert ws > 8 * 40 * 128 * 4
+    assert kvq.kvq_decode_workspace_bytes(c, 12) == 0     # not a multiple of 8
+    assert kvq.kvq_decode_workspace_bytes(c, 4) == 0
+
+
+def _cache(ptr=FAKE, tail=FAKE):
+    return _capi.KvqCache(ptr, FAKE, FAKE, FAKE, tail, tail)
+
+
+def _lens(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def _append(c, cache, n_new, lens, k=FAKE, v=FAKE, dtype=0):
+    return L.kvq_rotate_quantize_append(ctypes.byref(c), ctypes.byref(cache), k, v, dtype,
+                                        n_new, lens, None)
+
+
+def test_append_validation():
+    c = kvq.kvq_config(2, 2, 128, 100, 4, 4, 0)
+    assert _append(c, _cache(), 10, _lens(91, 0)) == _capi.KVQ_ERR_CAPACITY
+    assert _append(c, _cache(), 1, _lens(-1, 0)) == _capi.KVQ_ERR_INVALID
+    assert _append(c, _cache(), -1, _lens(0, 0)) == _capi.KVQ_ERR_INVALID
+    assert _append(c, _cache(0), 1, _lens(0, 0)) == _capi.KVQ_ERR_INVALID
+    assert _append(c, _cache(FAKE_MISALIGNED), 1, _lens(0, 0)) == _capi.KVQ_ERR_ALIGN
+    assert _append(c, _cache(), 1, _lens(0, 0), k=FAKE_MISALIGNED) == _capi.KVQ_ERR_ALIGN
+    assert _append(c, _cache(), 1, _lens(0, 0), k=0) == _capi.KVQ_ERR_INVALID
+    assert _append(c, _cache(), 1, _lens(0, 0), dtype=7) == _capi.KVQ_ERR_INVALID
+    assert _append(c, _cache(), 0, _lens(0, 0)) == _capi.KVQ_OK      # no-op, no device work
+    ct = kvq.kvq_config(2, 2, 128, 100, 4, 4, 8)
+    assert _append(ct, _cache(tail=0), 1, _lens(0, 0)) == _capi.KVQ_ERR_INVALID
+    bad = kvq.kvq_config_default(2, 2, 128, 100)
+    bad.k_bits = 3
+    assert _append(bad, _cache(), 1, _lens(0, 0)) == _capi.KVQ_ERR_UNSUPPORTED
+
+
+def _decode(c, hq, lens, ws_bytes=1 << 40, sm=0.1, q=FAKE, out=FAKE, cache=None):
+    cache = cache or _cache()
+    return L.kvq_decode_attention(ctypes.byref(c), ctypes.byref(cache), q, 0, hq, sm, lens,
+                                  out, FAKE, ws_bytes, None)
+
+
+def test_decode_validation():
+    c = kvq.kvq_config(2, 4, 128, 100, 8, 4, 0)
+    assert _decode(c, 6, _lens(5, 5)) == _capi.KVQ_ERR_INVALID      # 6 % 4 != 0
+    assert _decode(c, 2, _lens(5, 5)) == _capi.KVQ_ERR_INVALID
+    assert _decode(c, 8, _lens(0, 5)) == _capi.KVQ_ERR_INVALID      # empty sequence
+    assert _decode(c, 8, _lens(5, 101)) == _capi.KVQ_ERR_CAPACITY
+    assert _decode(c, 8, _lens(5, 5), sm=float("nan")) == _capi.KVQ_ERR_INVALID
+    assert _decode(c, 8, _lens(5, 5), ws_bytes=100) == _capi.KVQ_ERR_WORKSPACE
+    assert _decode(c, 8, _lens(5, 5), q=FAKE_MISALIGNED, ws_bytes=100) == _capi.KVQ_ERR_ALIGN
+    assert _decode(c, 8, _lens(5, 5), out=0) == _capi.KVQ_ERR_INVALID
+
+
+def test_dequantize_validation():
+    c = kvq.kvq_config(2, 4, 128, 100, 8, 4, 0)
+    lens = _lens(10, 20)
+    deq = lambda which, b, t0, t1, space=0, out=FAKE: L.kvq_dequantize(
+        ctypes.byref(c), ctypes.byref(_cache()), which, b, t0, t1, lens, space, out, None)
+    assert deq(2, 0, 0, 5) == _capi.KVQ_ERR_INVALID
+    assert deq(0, 2, 0, 5) == _capi.KVQ_ERR_INVALID
+    assert deq(0, 0, 5, 4) == _capi.KVQ_ERR_INVALID
+    assert deq(0, 0, 0, 11) == _capi.KVQ_ERR_INVALID
+    assert deq(0, 0, 0, 5, space=3) == _capi.KVQ_ERR_INVALID
+    assert deq(0, 0, 0, 5, out=FAKE_MISALIGNED) == _capi.KVQ_ERR_ALIGN
+    assert deq(0, 0, 0, 5, out=0) == _capi.KVQ_ERR_INVALID
+    assert deq(0, 0, 3, 3, out=0) == _capi.KVQ_OK                    # empty range

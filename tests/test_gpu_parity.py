@@ -1,0 +1,180 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+* Append: code, scale and tail planes byte-identical to the oracle's (the
+  quantizer is an encoding, so bit-exactness is the bar).
+* Dequantize: float32 output bit-identical to the oracle's on the device
+  cache (rotated and original space).
+* Decode attention: relative L2 error <= 1e-3 per (sequence, query head)
+  against the float64 oracle evaluated on the device-produced cache.
+
+Sizes span several 64-token tiles, several splits and ragged tails; the
+workload shapes (head_dim, GQA ratio, bit widths, tail) follow workloads.py
+with shorter contexts so the oracle finishes in seconds."""
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_common import Pair, say, to_device, to_values, attention_errors, gpu_planes
+from oracle import dequantize_reference
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+APPEND_CASES = [
+    # d, kb, vb, T, dtype, B, H, chunks, rotate
+    (64, 4, 4, 0, "f32", 1, 1, [256], True),
+    (128, 8, 8, 0, "bf16", 1, 8, [300, 1, 1, 211], True),
+    (128, 4, 4, 0, "bf16", 2, 8, [130, 70], True),
+    (128, 8, 4, 16, "bf16", 2, 8, [100, 1, 1, 40], True),
+    (128, 8, 4, 64, "bf16", 1, 4, [10, 200, 1, 70], True),
+    (256, 5, 4, 0, "bf16", 2, 4, [129, 63], True),
+    (256, 8, 5, 8, "f32", 1, 2, [5, 90, 3], True),
+    (64, 5, 8, 4, "bf16", 2, 2, [3, 3, 70], True),
+    (128, 5, 5, 0, "f32", 1, 2, [65], True),
+    (128, 4, 8, 0, "bf16", 1, 2, [80], False),
+    (256, 4, 4, 32, "bf16", 1, 2, [40, 40], False),
+]
+
+
+def _case_id(c):
+    d, kb, vb, T, dt, B, H, ch, rot = c
+    return "d%d-k%d-v%d-T%d-%s-B%d-H%d-%s" % (d, kb, vb, T, dt, B, H, "rot" if rot else "norot")
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[_case_id(c) for c in APPEND_CASES])
+def test_append_bit_exact(case):
+    d, kb, vb, T, dtype, B, H, chunks, rot = case
+    n = sum(chunks)
+    pair = Pair(B, H, d, kb, vb, T, n + 7, rot, rot)
+    seed = 0
+    for c in chunks:
+        seed += 1
+        k = workloads.adversarial_numpy(seed, (B, c, H, d), dtype)
+        v = workloads.adversarial_numpy(1000 + seed, (B, c, H, d), dtype)
+        pair.append(k, v, dtype)
+    pair.compare_planes()
+
+
+@pytest.mark.parametrize("case", APPEND_CASES[:8], ids=[_case_id(c) for c in APPEND_CASES[:8]])
+def test_dequantize_bit_exact(case):
+    import torch
+    import decode_attention_rotate_amd as kvq
+    d, kb, vb, T, dtype, B, H, chunks, rot = case
+    n = sum(chunks)
+    pair = Pair(B, H, d, kb, vb, T, n, rot, rot)
+    k = workloads.adversarial_numpy(7, (B, n, H, d), dtype)
+    v = workloads.adversarial_numpy(8, (B, n, H, d), dtype)
+    pair.append(k, v, dtype)
+    planes = gpu_planes(pair.cache, pair.cfg)
+    for which, bits in ((0, kb), (1, vb)):
+        for space in (0, 1):
+            for b in range(B):
+                for t0, t1 in ((0, n), (n // 3, n - 1)):
+                    say("dequantize", which, b, t0, t1, space)
+                    got = kvq.kvq_dequantize(pair.cfg, pair.cache, which, b, t0, t1,
+                                             pair.lens, space).cpu().numpy()
+                    torch.cuda.synchronize()
+                    want = dequantize_reference(planes, which, b, t0, t1, n, H, d, bits, T,
+                                                space, rotate=rot)
+                    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+                        (which, space, b, t0, t1)
+
+
+def _fill(pair, w, n_list, dtype, seed0=0):
+    """Append workload tokens so sequence b ends with length n_list[b]:
+    one append for everyone, then a second append that restarts the shorter
+    sequences (a sequence given length 0 starts afresh)."""
+    B = len(n_list)
+    nmax = max(n_list)
+    k = workloads.kv_numpy(w, 1, 0, nmax)
+    v = workloads.kv_numpy(w, 2, 0, nmax)
+    short = [n for n in n_list if n < nmax]
+    if not short:
+        pair.append(k, v, dtype)
+        return
+    m = min(short)
+    assert all(x in (nmax, m) for x in n_list), "two distinct lengths supported"
+    pair.append(k[:, : nmax - m], v[:, : nmax - m], dtype)
+    lens = [nmax - m if n == nmax else 0 for n in n_list]
+    pair.append(k[:, nmax - m:], v[:, nmax - m:], dtype, lens=lens)
+
+
+ATTN_CASES = [
+    # name, workload overrides, lengths
+    ("tiny", dict(), [256]),
+    ("small", dict(), [4096]),
+    ("mid", dict(B=2), [1000, 333]),
+    ("long", dict(B=2, tail=1024), [3000, 1500]),
+    ("long", dict(B=2, tail=16), [700, 700]),
+    ("long", dict(B=1, tail=64), [40]),
+    ("huge", dict(B=2), [2000, 129]),
+    ("small", dict(Hq=24), [513]),            # G = 3
+    ("small", dict(Hq=48), [200]),            # G = 6
+    ("small", dict(Hq=56), [130]),            # G = 7
+    ("small", dict(Hq=96, B=2), [100, 64]),   # G = 12: two chunks of 6
+    ("small", dict(Hq=8), [1]),               # G = 1, one token
+    ("tiny", dict(B=2, k_bits=8, v_bits=5), [64, 63]),
+    ("huge", dict(B=1, Hq=8, k_bits=4, v_bits=8, tail=100), [300]),
+]
+
+
+@pytest.mark.parametrize("name,over,lens", ATTN_CASES,
+                         ids=["%s-%d" % (c[0], i) for i, c in enumerate(ATTN_CASES)])
+def test_decode_attention(name, over, lens):
+    w = workloads.workload(name, **over)
+    w["B"] = len(lens)
+    d, dtype = w["d"], w["dtype"]
+    pair = Pair(w["B"], w["Hkv"], d, w["k_bits"], w["v_bits"], w["tail"], max(lens) + 5)
+    _fill(pair, w, lens, dtype)
+    assert list(pair.lens) == lens
+    q = workloads.q_numpy(w)
+    got = pair.decode(q, dtype)
+    planes = gpu_planes(pair.cache, pair.cfg)
+    errs = attention_errors(got, planes, to_values(q, dtype), lens, pair.cfg)
+    worst = max(errs.values())
+    say("worst rel L2 %.3e" % worst)
+    assert worst <= TOL, sorted(errs.items(), key=lambda kv: -kv[1])[:3]
+
+
+def test_decode_rotation_flags_and_scale():
+    w = workloads.workload("small", B=2, Hq=16)
+    for rk, rv in ((False, True), (True, False), (False, False)):
+        pair = Pair(2, 8, 128, 8, 4, 32, 600, rk, rv)
+        _fill(pair, w, [520, 520], "bf16")
+        q = workloads.q_numpy(w)
+        got = pair.decode(q, "bf16", sm_scale=0.05)
+        planes = gpu_planes(pair.cache, pair.cfg)
+        errs = attention_errors(got, planes, to_values(q, "bf16"), [520, 520], pair.cfg,
+                                sm_scale=0.05)
+        assert max(errs.values()) <= TOL, (rk, rv)
+
+
+def test_decode_fp32_query_and_repeat_calls():
+    w = workloads.workload("mid", B=2, dtype="f32")
+    pair = Pair(2, 8, 128, 4, 4, 0, 1100)
+    _fill(pair, w, [1100, 1100], "f32")
+    q = workloads.q_numpy(w)
+    a = pair.decode(q, "f32")
+    b = pair.decode(q, "f32")
+    assert np.array_equal(a, b)       # deterministic
+    planes = gpu_planes(pair.cache, pair.cfg)
+    errs = attention_errors(a, planes, to_values(q, "f32"), [1100, 1100], pair.cfg)
+    assert max(errs.values()) <= TOL
+
+
+def test_decode_steps_with_single_token_appends():
+    # the decode step as a serving loop runs it: append one token, attend
+    w = workloads.workload("long", B=2, tail=32)
+    pair = Pair(2, 8, 128, 8, 4, 32, 400)
+    _fill(pair, w, [300, 300], "bf16")
+    for step in range(3):
+        k = workloads.new_tokens_numpy(w, 1, step)
+        v = workloads.new_tokens_numpy(w, 2, step)
+        pair.append(k, v, "bf16")
+        q = workloads.q_numpy(w, step)
+        got = pair.decode(q, "bf16")
+        planes = pair.compare_planes()
+        errs = attention_errors(got, planes, to_values(q, "bf16"), list(pair.lens), pair.cfg)
+        assert max(errs.values()) <= TOL

@@ -180,3 +180,23 @@ def new_tokens_torch(w, role, step, device, torch, n_new=1):
     x = x * torch.from_numpy(outlier_scale(w, role)).to(device)
     dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     return x.to(dt).contiguous()
+
+
+def adversarial_numpy(seed, shape, dtype="bf16"):
+    """Rows that stress the block quantizer: normal rows with outliers, all-zero
+    rows, rows so small the fp16 scale underflows or is subnormal, rows large
+    enough to saturate the fp16 scale, and rows with exact ties after scaling.
+    shape = (B, n, H, d).  Returns bf16 bits or float32 like kv_numpy."""
+    rng = np.random.default_rng((99, seed))
+    x = rng.standard_normal(shape, dtype=np.float32)
+    x[..., 3] *= 20.0
+    flat = x.reshape(-1, shape[-1])
+    kinds = rng.integers(0, 8, size=flat.shape[0])
+    flat[kinds == 1] = 0.0
+    flat[kinds == 2] *= np.float32(1e-30)
+    flat[kinds == 3] *= np.float32(2.0 ** -18)
+    flat[kinds == 4] *= np.float32(3e5)
+    ints = rng.integers(-15, 16, size=flat.shape).astype(np.float32) * np.float32(0.5)
+    flat[kinds == 5] = ints[kinds == 5]
+    x = flat.reshape(shape)
+    return to_bf16_bits(x) if dtype == "bf16" else x
