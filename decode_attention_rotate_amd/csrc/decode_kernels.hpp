@@ -39,8 +39,19 @@ using sgpr_f32 = const float __attribute__((address_space(4)))*;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Relative cost of a 64-token tile: quantized codes vs bf16 tail rows.
+constexpr int kCostQ = 2;
+constexpr int kCostT = 5;
+
+// Occupancy target of the split-K kernel (waves per SIMD); bounds the
+// registers the scheduler may use.
+#ifndef KVQ_SPLIT_WAVES_PER_EU
+#define KVQ_SPLIT_WAVES_PER_EU 2
+#endif
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-__device__ inline uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Maximum / sum over the 64 lanes, result in every lane.
 __device__ inline float wave_max(float v) {
@@ -96,17 +107,30 @@ __device__ inline void unpack_k(const uint32_t* kw, uint32_t (&kb)[D / 4]) {
 template <int VB>
 struct VTok;
 
+// Byte k of token A in the low half and byte k of token B in the high half.
+__device__ inline uint32_t pair_bytes(uint32_t b, uint32_t a, int k) {
+  return __builtin_amdgcn_perm(b, a, (uint32_t)k | (0x0Cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0Cu << 24));
+}
+
+// (x & mask) | magic as one v_and_or_b32; magic lives in a VGPR.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  return (x & mask) | magic;
+}
+
 template <>
 struct VTok<4> {
-  uint32_t n;  // 8 nibbles
-  __device__ inline void pairs(const VTok& B, h2_t (&c)[8]) const {
-    const uint32_t x1 = __builtin_amdgcn_perm(B.n, n, 0x05040100u);
-    const uint32_t x2 = __builtin_amdgcn_perm(B.n, n, 0x07060302u);
-    const h2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  uint32_t n;  // 8 nibbles: element i in bits 4i..4i+3
+  // Even elements become exact fp16 codes c; odd elements become 16*c
+  // (nibble kept in mantissa bits 4..7), undone once when partials are stored.
+  static constexpr bool kOddTimes16 = true;
+  __device__ inline void pairs(const VTok& B, h2_t (&c)[8], uint32_t magic) const {
+    const h2_t bias_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2_t bias_hi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[i] = as_h2(((x1 >> (4 * i)) & 0x000F000Fu) | 0x64006400u) + bias;
-      c[4 + i] = as_h2(((x2 >> (4 * i)) & 0x000F000Fu) | 0x64006400u) + bias;
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t p = pair_bytes(B.n, n, k);
+      c[2 * k] = as_h2(and_or(p, 0x000F000Fu, magic)) + bias_lo;
+      c[2 * k + 1] = as_h2(and_or(p, 0x00F000F0u, magic)) + bias_hi;
     }
   }
 };
@@ -114,13 +138,13 @@ struct VTok<4> {
 template <>
 struct VTok<8> {
   uint32_t b0, b1;  // 8 signed bytes
-  __device__ inline void pairs(const VTok& B, h2_t (&c)[8]) const {
+  static constexpr bool kOddTimes16 = false;
+  __device__ inline void pairs(const VTok& B, h2_t (&c)[8], uint32_t) const {
     const h2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t sel = (uint32_t)i | (0x0Cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0Cu << 24);
-      c[i] = as_h2(__builtin_amdgcn_perm(B.b0, b0, sel) ^ 0x64806480u) + bias;
-      c[4 + i] = as_h2(__builtin_amdgcn_perm(B.b1, b1, sel) ^ 0x64806480u) + bias;
+    for (int k = 0; k < 4; ++k) {
+      c[k] = as_h2(pair_bytes(B.b0, b0, k) ^ 0x64806480u) + bias;
+      c[4 + k] = as_h2(pair_bytes(B.b1, b1, k) ^ 0x64806480u) + bias;
     }
   }
 };
@@ -130,7 +154,8 @@ struct VTok<5> {
   uint32_t n;   // 8 nibbles
   uint32_t hw;  // high-bit word of the block
   int gq;       // which 8-element group of the block this lane owns
-  __device__ inline void pairs(const VTok& B, h2_t (&c)[8]) const {
+  static constexpr bool kOddTimes16 = false;
+  __device__ inline void pairs(const VTok& B, h2_t (&c)[8], uint32_t) const {
     const uint32_t x1 = __builtin_amdgcn_perm(B.n, n, 0x05040100u);
     const uint32_t x2 = __builtin_amdgcn_perm(B.n, n, 0x07060302u);
     const h2_t bias = {(_Float16)-1040.0f, (_Float16)-1040.0f};
@@ -160,7 +185,7 @@ struct TileRegs {
 };
 
 template <int D, int KB, int VB, int G>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WAVES_PER_EU))) void decode_split_kernel(DecodeArgs a) {
   constexpr int NB = D / kBlock;
   constexpr int RKP = padded_row_bytes(D, KB);
   constexpr int RVP = padded_row_bytes(D, VB);
@@ -172,6 +197,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   constexpr int QPS = qp_stride(D);
   using Regs = TileRegs<D, KB, VB>;
 
+  // per head: D/4 dwords of high query bytes, D/4 of low bytes, NB block
+  // corrections, the fixed-point score multiplier; padded to 16 bytes
+  constexpr int QCK = D / 2 + NB;
+  constexpr int QLD = (QCK + 1 + 3) / 4 * 4;
+  __shared__ __align__(16) uint32_t qlds[G][QLD];
   __shared__ __align__(16) uint32_t wlds[G][NB][32];
   __shared__ float plds[G][64];
 
@@ -184,8 +214,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int T = a.T;
   const int nt = T > 0 ? min(n, T) : 0;
   const int nq = n - nt;
-  const int p0 = split * a.split_tokens;
-  const int p1 = min(n, p0 + a.split_tokens);
+  // Work split by cost, not by token count: a 64-token tile of quantized
+  // codes weighs kCostQ, a tile of bf16 tail tokens kCostT (it carries about
+  // 2.5x the bytes).  Split s of S takes the cost interval [s*C/S, (s+1)*C/S)
+  // of this sequence; boundaries fall on tile edges of each region.
+  const int ctq = (nq + kTile - 1) / kTile;       // quantized tiles
+  const int ctt = (nt + kTile - 1) / kTile;       // tail tiles
+  const int64_t C = (int64_t)kCostQ * ctq + (int64_t)kCostT * ctt;
+  const int64_t c0 = C * split / a.S, c1 = C * (split + 1) / a.S;
+  auto q_tiles = [&](int64_t c) {
+    const int64_t t = c / kCostQ;
+    return (int)(t < ctq ? t : ctq);
+  };
+  auto t_tiles = [&](int64_t c) {
+    const int64_t r = (c - (int64_t)kCostQ * ctq) / kCostT;
+    return r <= 0 ? 0 : (int)(r < ctt ? r : ctt);
+  };
+  const int qa = q_tiles(c0) * kTile, qb = min(nq, q_tiles(c1) * kTile);
+  const int ta = nq + t_tiles(c0) * kTile, tb = min(n, nq + t_tiles(c1) * kTile);
   const size_t unit = (size_t)b * a.Hkv + g;
 
   const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
@@ -200,6 +246,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int kq = lane / NSLOT;
   const int hidx = ((lane % NSLOT) * NPAIR + (kq >> 1)) * 2 + (kq & 1);
 
+  for (int i = lane; i < G * (QCK + 1); i += 64) {
+    const int h = i / (QCK + 1), k = i % (QCK + 1);
+    qlds[h][k] = reinterpret_cast<const uint32_t*>(qp0 + (size_t)h * QPS)[k];
+  }
+  __syncthreads();
+
   float m[G], ls[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -211,6 +263,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   // Online-softmax step shared by the quantized and the tail loops:
   // x holds this lane's scores (log2 units, -inf for masked lanes).
+  // Online-softmax step shared by the quantized and the tail loops:
+  // x holds this lane's scores (log2 units, -inf for masked lanes).  The
+  // running maxima only move when some lane exceeds them (a wave-uniform
+  // branch); the rescale of the accumulators is applied unconditionally so
+  // the common path carries no register shuffles.
   auto softmax_update = [&](float (&x)[G], float (&p)[G]) {
     bool need = false;
 #pragma unroll
@@ -220,10 +277,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       for (int h = 0; h < G; ++h) {
         const float mn = fmaxf(m[h], wave_max(x[h]));
         const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+        m[h] = mn;
         ls[h] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-        m[h] = mn;
       }
     }
 #pragma unroll
@@ -234,16 +291,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   };
 
   // ------------------------------------------------ quantized positions
-  const int qa = p0, qb = min(p1, nq);
   if (qa < qb) {
     const int last = (qb - 1) / kTile * kTile;
+    // per-lane byte offsets inside a tile; the tile base is uniform
+    const uint32_t k_off = lane * kChunk;
+    const uint32_t s_off = lane * NB * 2;
+    uint32_t v_off, vh_off = 0;
+    if constexpr (VB == 8) {
+      v_off = ((eg / 2) * kTile + slot) * kChunk + (eg % 2) * 8;
+    } else {
+      v_off = ((eg / 4) * kTile + slot) * kChunk + (eg % 4) * 4;
+      const int byte = D / 2 + 4 * jv;
+      vh_off = ((byte / kChunk) * kTile + slot) * kChunk + byte % kChunk;
+    }
+
     auto load_tile = [&](Regs& r, int t0) {
       const uint8_t* kt = kpl + (size_t)(t0 / kTile) * kTile * RKP;
 #pragma unroll
       for (int c = 0; c < NCK; ++c)
-        r.kc[c] = *reinterpret_cast<const uint4*>(kt + (size_t)(c * kTile + lane) * kChunk);
-      const uint16_t* ks = ksc + (size_t)(t0 + lane) * NB;
-      const uint16_t* vs = vsc + (size_t)(t0 + lane) * NB;
+        r.kc[c] = *reinterpret_cast<const uint4*>(kt + c * kTile * kChunk + k_off);
+      const uint8_t* ks = reinterpret_cast<const uint8_t*>(ksc + (size_t)t0 * NB) + s_off;
+      const uint8_t* vs = reinterpret_cast<const uint8_t*>(vsc + (size_t)t0 * NB) + s_off;
       if constexpr (NB == 2) {
         r.ks[0] = *reinterpret_cast<const uint32_t*>(ks);
         r.vs[0] = *reinterpret_cast<const uint32_t*>(vs);
@@ -260,17 +328,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       const uint8_t* vt = vpl + (size_t)(t0 / kTile) * kTile * RVP;
 #pragma unroll
       for (int k = 0; k < TPS; ++k) {
-        const int t = k * NSLOT + slot;
+        const uint8_t* vk = vt + k * NSLOT * kChunk;
         if constexpr (VB == 4) {
-          r.v[k].n = *reinterpret_cast<const uint32_t*>(vt + (size_t)((eg / 4) * kTile + t) * kChunk + (eg % 4) * 4);
+          r.v[k].n = *reinterpret_cast<const uint32_t*>(vk + v_off);
         } else if constexpr (VB == 8) {
-          const uint2 v = *reinterpret_cast<const uint2*>(vt + (size_t)((eg / 2) * kTile + t) * kChunk + (eg % 2) * 8);
+          const uint2 v = *reinterpret_cast<const uint2*>(vk + v_off);
           r.v[k].b0 = v.x; r.v[k].b1 = v.y;
         } else {
-          r.v[k].n = *reinterpret_cast<const uint32_t*>(vt + (size_t)((eg / 4) * kTile + t) * kChunk + (eg % 4) * 4);
-          constexpr int hb0 = D / 2;
-          const int byte = hb0 + 4 * jv;
-          r.v[k].hw = *reinterpret_cast<const uint32_t*>(vt + (size_t)((byte / kChunk) * kTile + t) * kChunk + byte % kChunk);
+          r.v[k].n = *reinterpret_cast<const uint32_t*>(vk + v_off);
+          r.v[k].hw = *reinterpret_cast<const uint32_t*>(vk + vh_off);
           r.v[k].gq = eg % 4;
         }
       }
@@ -292,30 +358,43 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         ksf[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.ks[j / 2] >> (16 * (j % 2))));
         vsf[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.vs[j / 2] >> (16 * (j % 2))));
       }
-      // scalar-load the fixed-point query for each head (kept out of the
-      // loop-invariant set so it does not pin hundreds of SGPRs)
-      const uint8_t* qbase = qp0;
-      asm volatile("" : "+s"(qbase));
+      // Query bytes come from LDS (same address in every lane: a broadcast).
+      // The read of block b is tied (empty asm on an opaque offset) to the
+      // result of block b-2, so at most about three blocks of query bytes are
+      // live: the reads run two blocks ahead of their use and cannot all be
+      // hoisted to the top of the tile.
+      int qz = 0;
+      int ring[2] = {0, 0};
+      float s[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma unroll
+      for (int bi = 0; bi < G * NB; ++bi) {
+        const int h = bi / NB, j = bi % NB;
+        asm volatile("" : "+s"(qz) : "v"(ring[bi % 2]));
+        const uint32_t* qh = &qlds[h][0] + qz;
+        const uint4 h0 = *reinterpret_cast<const uint4*>(qh + 8 * j);
+        const uint4 h1 = *reinterpret_cast<const uint4*>(qh + 8 * j + 4);
+        const uint4 l0 = *reinterpret_cast<const uint4*>(qh + D / 4 + 8 * j);
+        const uint4 l1 = *reinterpret_cast<const uint4*>(qh + D / 4 + 8 * j + 4);
+        const uint32_t qhi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t qlo[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        int ahi = 0, alo = (int)qh[D / 2 + j];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          ahi = __builtin_amdgcn_sdot4((int)qhi[w], (int)kb[8 * j + w], ahi, false);
+          alo = __builtin_amdgcn_sdot4((int)qlo[w], (int)kb[8 * j + w], alo, false);
+        }
+        const int dj = ahi * 256 + alo;
+        ring[bi % 2] = dj;
+        s[h] = __builtin_fmaf(ksf[j], (float)dj, s[h]);
+      }
       float x[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const uint8_t* qh8 = qbase + (size_t)h * QPS;
-        const sgpr_i32 qhi = (sgpr_i32)(qh8);
-        const sgpr_i32 qlo = (sgpr_i32)(qh8 + D);
-        const sgpr_i32 corr = (sgpr_i32)(qh8 + 2 * D);
-        const float ck = *(sgpr_f32)(qh8 + 2 * D + D / 8);
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          int ahi = 0, alo = corr[j];
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            ahi = __builtin_amdgcn_sdot4((int)qhi[8 * j + w], (int)kb[8 * j + w], ahi, false);
-            alo = __builtin_amdgcn_sdot4((int)qlo[8 * j + w], (int)kb[8 * j + w], alo, false);
-          }
-          s = __builtin_fmaf(ksf[j], (float)(ahi * 256 + alo), s);
-        }
-        x[h] = valid ? s * ck : -INFINITY;
+        float xv = s[h] * __uint_as_float(qlds[h][QCK + qz]);
+        asm volatile("" : "+v"(xv));   // computed in every lane: a select, not a branch
+        x[h] = valid ? xv : -INFINITY;
       }
       float p[G];
       softmax_update(x, p);
@@ -329,20 +408,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
       }
       __syncthreads();
+      uint32_t magic = 0x64006400u;
+      asm volatile("" : "+v"(magic));
 #pragma unroll
-      for (int q4 = 0; q4 < NPAIR; q4 += 4) {
-        uint4 wq[G];
+      for (int q2 = 0; q2 < NPAIR; q2 += 2) {
+        u32x2 wq[G];
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          wq[h] = *reinterpret_cast<const uint4*>(&wlds[h][jv][slot * NPAIR + q4]);
+          wq[h] = *reinterpret_cast<const u32x2*>(&wlds[h][jv][slot * NPAIR + q2]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
           h2_t c[8];
-          r.v[2 * (q4 + u)].pairs(r.v[2 * (q4 + u) + 1], c);
+          r.v[2 * (q2 + u)].pairs(r.v[2 * (q2 + u) + 1], c, magic);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const uint32_t wsel = u == 0 ? wq[h].x : u == 1 ? wq[h].y : u == 2 ? wq[h].z : wq[h].w;
-            const h2_t wp = as_h2(wsel);
+            const h2_t wp = as_h2(wq[h][u]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_amdgcn_fdot2(wp, c[e], acc[h][e], false);
           }
@@ -360,10 +440,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       load_tile(ra, min(t1 + kTile, last));
       compute_tile(rb, t1);
     }
+    if constexpr (VTok<VB>::kOddTimes16) {
+      // odd elements were accumulated as 16*c (see VTok<4>); the tail loop
+      // below accumulates plain values, so undo the factor before it runs
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 1; e < 8; e += 2) acc[h][e] *= 0.0625f;
+      }
+    }
   }
 
   // ------------------------------------------------ bf16 tail positions
-  const int ta = max(p0, nq), tb = p1;
   if (ta < tb) {
     const uint16_t* ktl = a.k_tail + unit * (size_t)T * D;
     const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;

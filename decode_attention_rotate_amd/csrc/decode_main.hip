@@ -99,35 +99,56 @@ __global__ __launch_bounds__(64) void prep_kernel(PrepArgs a) {
   }
 }
 
+// One 256-thread block per (sequence, query head).  Thread t owns output
+// element t % D and visits the splits s = t / D, t / D + 256/D, ...; the
+// per-split weights 2^(m_s - M) follow the log-sum-exp merge.
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int P = 256 / D;       // split phases handled in parallel
+  __shared__ float red[256];
   __shared__ float o[D];
   const int t = threadIdx.x;
   const int bh = blockIdx.x;
   const float* ml = a.part_ml + (size_t)bh * a.S * 2;
   const float* acc = a.part_acc + (size_t)bh * a.S * D;
-  float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f;
-  float v[D / 64];
-#pragma unroll
-  for (int k = 0; k < D / 64; ++k) v[k] = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    const float m = ml[2 * s];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += w * ml[2 * s + 1];
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) v[k] += w * acc[(size_t)s * D + t + 64 * k];
+  float mloc = -INFINITY;
+  for (int s = t; s < a.S; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
+  red[t] = mloc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
   }
-  const float inv = 1.0f / L;
+  const float M = red[0];
+  __syncthreads();
+  const int e = t % D, ph = t / D;
+  float v = 0.f, lsum = 0.f;
+  for (int s = ph; s < a.S; s += P) {
+    const float m = ml[2 * s];
+    const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
+    v += wgt * acc[(size_t)s * D + e];
+    lsum += wgt * ml[2 * s + 1];
+  }
+  red[t] = v;
+  __syncthreads();
+  if (t < D) {
+    float tot = 0.f;
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) o[t + 64 * k] = v[k] * inv;
+    for (int k = 0; k < P; ++k) tot += red[t + k * D];
+    o[t] = tot;
+  }
+  __syncthreads();
+  red[t] = e == 0 ? lsum : 0.f;
+  __syncthreads();
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < P; ++k) L += red[k * D];
+  const float inv = 1.0f / L;
   __syncthreads();
   if (a.rotate) {
     for (int h = 1; h < D; h <<= 1) {
-      for (int k = t; k < D / 2; k += 64) {
-        const int i = (k / h) * 2 * h + (k % h);
+      if (t < D / 2) {
+        const int i = (t / h) * 2 * h + (t % h);
         const float u = o[i], w = o[i + h];
         o[i] = u + w;
         o[i + h] = u - w;
@@ -135,8 +156,8 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
       __syncthreads();
     }
   }
-  const float scale = a.rotate ? a.cd : 1.0f;
-  for (int e = t; e < D; e += 64) a.out[(size_t)bh * D + e] = o[e] * scale;
+  const float scale = (a.rotate ? a.cd : 1.0f) * inv;
+  if (t < D) a.out[(size_t)bh * D + t] = o[t] * scale;
 }
 
 }  // namespace
@@ -157,9 +178,9 @@ hipError_t launch_combine(int D, const CombineArgs& a, int B, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   const dim3 grid(B * a.Hq);
   switch (D) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(64), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(64), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -63,7 +63,7 @@ struct DecodeArgs {
   const uint8_t* qp;         // prep output
   float* part_ml;            // [B][Hq][S][2]  running max (log2 units), sum
   float* part_acc;           // [B][Hq][S][D]  unnormalised output, rotated space
-  int32_t Hkv, Hq, G, n_gchunks, T, cap, S, split_tokens;
+  int32_t Hkv, Hq, G, n_gchunks, T, cap, S;
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);

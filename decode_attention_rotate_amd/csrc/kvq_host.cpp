@@ -67,11 +67,12 @@ int head_chunk(int G) {
 }
 
 struct Schedule {
-  int gc, nchunk, S, split_tokens;
+  int gc, nchunk, S;
 };
 
 // Splits per (sequence, KV head, head chunk): enough waves to fill the chip,
-// at least one 64-token tile per split, contexts split at tile boundaries.
+// at most one split per 64-token tile of the longest sequence.  The kernel
+// divides each sequence's work among the S splits by cost.
 Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
   Schedule s;
   const int G = n_q_heads / c.n_kv_heads;
@@ -79,12 +80,8 @@ Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
   s.nchunk = G / s.gc;
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * s.nchunk;
   const int tiles = std::max(1, (max_len + kTile - 1) / kTile);
-  int want = (int)std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
-  want = std::min(want, tiles);
-  const int tiles_per = (tiles + want - 1) / want;
-  s.split_tokens = tiles_per * kTile;
-  s.S = (max_len + s.split_tokens - 1) / s.split_tokens;
-  if (s.S < 1) s.S = 1;
+  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
+  s.S = (int)std::min<int64_t>(want, tiles);
   return s;
 }
 
@@ -260,7 +257,6 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.T = c.tail_len;
   da.cap = (int32_t)cap_tokens(c);
   da.S = sc.S;
-  da.split_tokens = sc.split_tokens;
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
   const dim3 grid(sc.S, c.n_kv_heads * sc.nchunk, c.batch);
   if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
