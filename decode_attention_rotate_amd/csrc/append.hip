@@ -1,4 +1,4 @@
-// Rotate-quantize-append kernel.
+// Rotate-quantize-append kernels.
 //
 // Each new K/V head vector is rotated by the normalized Hadamard matrix
 // (velog.io post "fix KV cache quantization outliers", section "Hadamard
@@ -7,15 +7,24 @@
 // context KLD results") or, for the newest tail_len positions, stored in the
 // bf16 precision tail (aitrends.kr article 92204, glossary "Precision Tail").
 //
-// Thread mapping: one lane per 32-element block, D/32 consecutive lanes per
-// head vector, so a 256-thread block covers 256*32/D consecutive tokens of one
-// (sequence, KV head, plane).  The in-lane butterfly stages h = 1..16 run in
-// registers, the remaining stages cross lanes with DPP / ds_swizzle, and the
-// block absmax and the codes never leave the lane.
+// An append of n_new tokens to a sequence of length len runs two launches:
+//  1. quant: positions [q0, q1) become quantized, where q0/q1 are the first
+//     non-tail position before/after the append (q0 = len, q1 = len + n_new
+//     without a tail).  A position below len is read back from its tail slot
+//     (it is leaving the tail), any other one is rotated from the input.
+//     Work goes in groups of eight 8-aligned positions, because V codes of
+//     eight consecutive tokens share one word of the element-major V tiles:
+//     the group's codes meet in LDS and are packed there, merging with the
+//     bytes of positions outside [q0, q1) that the group's words also hold.
+//  2. tail: the newest min(n_new, T) positions are rotated and written to
+//     their ring slots p % T.  This runs after (1), which has read every slot
+//     it overwrites.
 //
-// Tail ring: a new tail token at position p goes to slot p % T; the token it
-// displaces (if it is leaving the tail in this call) is read and quantized by
-// the same thread first, so no slot is read after it is overwritten.
+// Thread mapping: one lane per 32-element block, D/32 consecutive lanes per
+// head vector, so a 256-thread block covers 256*32/D consecutive positions of
+// one (sequence, KV head, plane).  The in-lane butterfly stages h = 1..16 run
+// in registers, the remaining stages cross lanes with DPP / ds_swizzle, and
+// the block absmax and the codes never leave the lane.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,13 +54,24 @@ __device__ inline void load_row_block(const void* src, int dtype, size_t elem_of
   }
 }
 
-// Quantize block j of the row of position p and store codes and scale.
+__device__ inline void load_bf16_block(const uint16_t* row, float (&x)[32]) {
+  const uint4* src = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = src[q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[q * 8 + 2 * k] = __uint_as_float(w[k] << 16);
+      x[q * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+}
+
+// K codes of block j of position p, row layout (tiled 16-byte chunks).
 template <int D, int BITS>
-__device__ inline void quantize_store(const float (&x)[32], uint8_t* plane, uint16_t* scale_row,
-                                      int p, int j) {
+__device__ inline void store_k_row(const int (&c)[32], uint8_t* plane, int p, int j) {
   constexpr int RP = padded_row_bytes(D, BITS);
-  int c[32];
-  scale_row[j] = (uint16_t)quantize_block<BITS>(x, c);
   if constexpr (BITS == 8) {
     uint32_t w[8];
 #pragma unroll
@@ -82,34 +102,96 @@ __device__ inline void quantize_store(const float (&x)[32], uint8_t* plane, uint
 }
 
 template <int D>
-__device__ inline void quantize_store_bits(int bits, const float (&x)[32], uint8_t* plane,
-                                           uint16_t* scale_row, int p, int j) {
-  if (bits == 4) quantize_store<D, 4>(x, plane, scale_row, p, j);
-  else if (bits == 5) quantize_store<D, 5>(x, plane, scale_row, p, j);
-  else quantize_store<D, 8>(x, plane, scale_row, p, j);
+__device__ inline uint32_t quantize_k(int bits, const float (&x)[32], int (&c)[32], bool active,
+                                      uint8_t* plane, int p, int j) {
+  uint32_t s;
+  if (bits == 4) {
+    s = quantize_block<4>(x, c);
+    if (active) store_k_row<D, 4>(c, plane, p, j);
+  } else if (bits == 5) {
+    s = quantize_block<5>(x, c);
+    if (active) store_k_row<D, 5>(c, plane, p, j);
+  } else {
+    s = quantize_block<8>(x, c);
+    if (active) store_k_row<D, 8>(c, plane, p, j);
+  }
+  return s;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+__device__ inline uint32_t quantize_any(int bits, const float (&x)[32], int (&c)[32]) {
+  if (bits == 4) return quantize_block<4>(x, c);
+  if (bits == 5) return quantize_block<5>(x, c);
+  return quantize_block<8>(x, c);
+}
+
+// Merge the slots of one V item whose bit is set in `mask` into memory.
+// u holds the offset codes of slots 0..7 in bytes 0..7.
+template <int D, int BITS>
+__device__ inline void store_v_item(uint8_t* tile, int item, uint64_t u, uint32_t mask) {
+  if constexpr (BITS == 8) {
+    uint64_t* dst = reinterpret_cast<uint64_t*>(tile) + item;
+    if (mask != 0xFFu) {
+      uint64_t keep = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (!(mask & (1u << k))) keep |= (uint64_t)0xFF << (8 * k);
+      u = (u & ~keep) | (*dst & keep);
+    }
+    *dst = u;
+  } else {
+    uint32_t w = 0, hi = 0, keep = 0, keep_hi = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = (uint32_t)(u >> (8 * k)) & 0xFFu;
+      w |= (v & 15u) << (4 * v_nibble(k));
+      hi |= ((v >> 4) & 1u) << v_nibble(k);
+      if (!(mask & (1u << k))) {
+        keep |= 15u << (4 * v_nibble(k));
+        keep_hi |= 1u << v_nibble(k);
+      }
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile) + item;
+    if (keep) w = (w & ~keep) | (*dst & keep);
+    *dst = w;
+    if constexpr (BITS == 5) {
+      uint8_t* dh = tile + 32 * D + item;
+      if (keep_hi) hi = (hi & ~keep_hi) | (*dh & keep_hi);
+      *dh = (uint8_t)hi;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a) {
   constexpr int LPR = D / kBlock;
-  constexpr int RPB = 256 / LPR;
+  constexpr int RPB = 256 / LPR;   // positions per block, a multiple of 8
+  constexpr int NGRP = RPB / 8;
+  __shared__ __align__(16) uint8_t vlds[NGRP * D * 8];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = tid % LPR;
   const int g = blockIdx.y;
   const int b = blockIdx.z >> 1;
   const int pl = blockIdx.z & 1;
-  const int i = blockIdx.x * RPB + tid / LPR;
-  const bool active = i < a.n_new;
   const int len = a.len[b];
   const int T = a.T;
   const int n1 = len + a.n_new;
-  const int q_end = T > 0 ? n1 - T : n1;
+  const int q0 = T > 0 ? max(0, len - T) : len;
+  const int q1 = T > 0 ? max(0, n1 - T) : n1;
+  const int blk0 = (q0 & ~7) + blockIdx.x * RPB;
+  if (blk0 >= q1) return;                       // uniform over the block
+  const int rho = tid / LPR;
+  const int p = blk0 + rho;
+  const bool active = p >= q0 && p < q1;
+  const bool from_ring = active && p < len;     // leaving the tail (T > 0)
   const int Hkv = a.Hkv;
+  const size_t unit = (size_t)b * Hkv + g;
 
   float x[32];
-  if (active) {
-    const size_t off = ((size_t)(b * (size_t)a.n_new + i) * Hkv + g) * D + (size_t)kBlock * j;
+  if (active && !from_ring) {
+    const size_t off = ((size_t)(b * (size_t)a.n_new + (p - len)) * Hkv + g) * D + (size_t)kBlock * j;
     load_row_block(a.src[pl], a.dtype, off, x);
   } else {
 #pragma unroll
@@ -121,37 +203,79 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = bf16_round(x[e]);
   }
-  if (!active) return;
+  if (from_ring) load_bf16_block(a.tail[pl] + (unit * T + p % T) * D + kBlock * j, x);
 
-  const size_t unit = (size_t)b * Hkv + g;
   const int bits = a.bits[pl];
-  uint8_t* plane = a.codes[pl] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
   uint16_t* scales = a.scales[pl] + unit * (size_t)a.cap * (D / kBlock);
-  const int p = len + i;
-  if (p < q_end) {
-    quantize_store_bits<D>(bits, x, plane, scales + (size_t)p * (D / kBlock), p, j);
+  int c[32];
+  if (pl == 0) {
+    uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
+    const uint32_t s = quantize_k<D>(bits, x, c, active, plane, p, j);
+    if (active) scales[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
     return;
   }
-  const int slot = p % T;
-  uint16_t* tail_row = a.tail[pl] + (unit * T + slot) * D + kBlock * j;
-  const int o0 = len > T ? len - T : 0;
-  const int pg = o0 + (slot - o0 % T + T) % T;   // old occupant of the slot
-  if (pg < len && pg < q_end) {
-    float y[32];
-    const uint4* src = reinterpret_cast<const uint4*>(tail_row);
+
+  // V: codes of the block's positions meet in LDS as bytes [group][e][slot]
+  const uint32_t s = quantize_any<D>(bits, x, c);
+  if (active) {
+    scales[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
+    const int off = 1 << (bits - 1);
+    uint8_t* dst = vlds + ((rho / 8) * D + kBlock * j) * 8 + rho % 8;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = src[q];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        y[q * 8 + 2 * k] = __uint_as_float(w[k] << 16);
-        y[q * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
-    }
-    quantize_store_bits<D>(bits, y, plane, scales + (size_t)pg * (D / kBlock), pg, j);
+    for (int e = 0; e < 32; ++e) dst[8 * e] = (uint8_t)(c[e] + off);
   }
-  uint4* dst = reinterpret_cast<uint4*>(tail_row);
+  __syncthreads();
+
+  constexpr int NN = D / 16;
+  uint8_t* vplane = a.codes[1] + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, bits);
+  for (int it = tid; it < NGRP * D; it += 256) {
+    const int grp = it / D, idx = it % D;
+    const int e = 16 * (idx % NN) + idx / NN;   // consecutive threads: consecutive items
+    const int p0 = blk0 + 8 * grp;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (p0 + k >= q0 && p0 + k < q1) mask |= 1u << k;
+    if (!mask) continue;
+    const uint64_t u = *reinterpret_cast<const uint64_t*>(vlds + (grp * D + e) * 8);
+    uint8_t* tile = vplane + (size_t)(p0 / kTile) * v_tile_bytes(D, bits);
+    const int item = v_item(D, p0 % kTile, e);
+    if (bits == 4) store_v_item<D, 4>(tile, item, u, mask);
+    else if (bits == 5) store_v_item<D, 5>(tile, item, u, mask);
+    else store_v_item<D, 8>(tile, item, u, mask);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
+  constexpr int LPR = D / kBlock;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = tid % LPR;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z >> 1;
+  const int pl = blockIdx.z & 1;
+  const int len = a.len[b];
+  const int T = a.T;
+  const int n1 = len + a.n_new;
+  const int t0 = max(len, n1 - T);
+  const int p = t0 + blockIdx.x * RPB + tid / LPR;
+  const bool active = p < n1;
+  const int Hkv = a.Hkv;
+
+  float x[32];
+  if (active) {
+    const size_t off = ((size_t)(b * (size_t)a.n_new + (p - len)) * Hkv + g) * D + (size_t)kBlock * j;
+    load_row_block(a.src[pl], a.dtype, off, x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = 0.f;
+  }
+  if (a.rotate[pl]) rotate_row<D>(x, lane, a.cd);
+  if (!active) return;
+  const size_t unit = (size_t)b * Hkv + g;
+  uint4* dst = reinterpret_cast<uint4*>(a.tail[pl] + (unit * T + p % T) * D + kBlock * j);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t w[4];
@@ -162,19 +286,35 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+template <int D>
+hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
+  constexpr int RPB = 256 / (D / kBlock);
+  int quant_blocks = 0;
+  for (int b = 0; b < B; ++b) {
+    const int len = a.len[b], n1 = len + a.n_new;
+    const int q0 = a.T > 0 ? max(0, len - a.T) : len;
+    const int q1 = a.T > 0 ? max(0, n1 - a.T) : n1;
+    if (q1 > q0) quant_blocks = max(quant_blocks, (q1 - (q0 & ~7) + RPB - 1) / RPB);
+  }
+  if (quant_blocks > 0)
+    hipLaunchKernelGGL(append_quant_kernel<D>, dim3(quant_blocks, a.Hkv, 2 * B), dim3(256), 0, s, a);
+  const int n_tail = a.T > 0 ? min(a.n_new, a.T) : 0;
+  if (n_tail > 0)
+    hipLaunchKernelGGL(append_tail_kernel<D>, dim3((n_tail + RPB - 1) / RPB, a.Hkv, 2 * B),
+                       dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_append(int D, const AppendArgs& a, int B, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  const int rpb = 256 / (D / kBlock);
-  const dim3 grid((a.n_new + rpb - 1) / rpb, a.Hkv, 2 * B);
   switch (D) {
-    case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(append_kernel<128>, grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(append_kernel<256>, grid, dim3(256), 0, s, a); break;
+    case 64: return launch_append_d<64>(a, B, s);
+    case 128: return launch_append_d<128>(a, B, s);
+    case 256: return launch_append_d<256>(a, B, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -30,6 +30,20 @@ __host__ __device__ inline size_t chunk_offset(int p, int c, int rpad) {
   return (size_t)(p / kTile) * kTile * rpad + (size_t)(c * kTile + (p % kTile)) * kChunk;
 }
 
+// V code planes are stored element-major per 64-token tile, so that the
+// codes of one element for eight consecutive tokens sit in one item (the
+// shape of one lane's P.V matrix-core operand).  Token t (0..63) and element
+// e of a tile belong to item v_item(d, t, e), slot t % 8:
+//   4-bit: one 32-bit word per item, u = c + 8 of slot k in nibble v_nibble(k)
+//   8-bit: eight bytes per item, u = c + 128 of slot k in byte k
+//   5-bit: the 4-bit words of u & 15 for every item (32*d bytes), then one
+//          byte per item whose bit v_nibble(k) is bit 4 of u.
+__host__ __device__ constexpr int v_tile_bytes(int d, int bits) { return kTile * d * bits / 8; }
+__host__ __device__ constexpr int v_item(int d, int t, int e) {
+  return ((t / 32) * 64 + 16 * ((t % 32) / 8) + e % 16) * (d / 16) + e / 16;
+}
+__host__ __device__ constexpr int v_nibble(int k) { return 4 * (k % 2) + k / 2; }
+
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // Round-to-nearest-even to bfloat16 (finite inputs).

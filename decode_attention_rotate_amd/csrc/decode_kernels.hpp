@@ -7,25 +7,28 @@
 // rotates the result back.  Newest tokens may sit unquantized in a bf16 tail
 // (aitrends.kr article 92204, glossary "Precision Tail").
 //
-// One wave handles one (sequence b, KV head g, chunk of G query heads, split
-// of the context) and streams every cache byte of its split exactly once.
-// Each tile of 64 tokens runs in two layouts:
-//  * Q.K, one token per lane.  K codes come in 16-byte chunks laid out so that
-//    chunk c of the 64 tokens of a tile is 1 KB of contiguous memory.  The
-//    query is held as a 16-bit fixed-point number split into two int8 planes
-//    (high and low byte), read with scalar loads, so each group of four codes
-//    costs two v_dot4_i32_i8 per head with no code conversion.  Offset-binary
-//    4/5-bit codes are folded back to signed codes through a per-block
-//    correction that initialises the accumulator.  Per block:
-//      score += scale_k[j] * float(256 * dot(q_hi, u) + dot(q_lo, u) + corr_j)
-//  * P.V, eight output elements per lane (D/8 lanes per token).  The softmax
-//    weight of each token, already multiplied by the token's per-block V
-//    scale and rounded to fp16, moves through LDS; two tokens' codes are
-//    interleaved with v_perm into fp16 pairs (magic-number conversion, then an
-//    exact subtraction of the bias) and v_dot2_f32_f16 accumulates both tokens
-//    into a float32 accumulator in one instruction.
-// The online softmax keeps one running maximum per head for the whole wave
-// and rescales only when some lane's score exceeds it.
+// One wave handles one (sequence b, KV head g, chunk of G <= 8 query heads,
+// split of the context) and streams every cache byte of its split once.  The
+// G query heads share each K/V row, so both contractions of a step of 32
+// tokens run on the matrix cores (16x16x32 MFMA; lane l owns A row l%16 and
+// B column l%16, k-slots 8*(l/16)..+7, and output rows 4*(l/16)..+3):
+//  * Q.K, v_mfma_i32_16x16x32_i8 per 16 tokens and 32-element block.  A rows
+//    are the query of each head in 16-bit fixed point, split into a high-byte
+//    row and a low-byte row; B columns are the int8 codes of 16 tokens, read
+//    straight from the row layout (4/5-bit codes widened to bytes, their
+//    offset folded in per block).  A lane gets the high and low sums of two
+//    heads for one token, combines them exactly in int32 and applies the
+//    token's fp16 block scale:
+//      score += scale_k * float(256 * sum(q_hi * c) + sum(q_lo * c))
+//  * Online softmax in log2 units, rescaling only when a running max grows.
+//  * P.V, v_mfma_f32_16x16x32_f16 per 32 tokens and 16 output elements.  A
+//    rows are the weights p * scale_v of each head (rounded once to fp16,
+//    moved from score layout to operand layout through LDS); B columns are
+//    V codes of one element for 8 consecutive tokens, which the element-major
+//    V tiles store together: nibbles / bytes become exact fp16 integers with
+//    one v_and_or (or v_perm) per pair plus one packed fp16 add.
+// bf16 tail tokens take a float32 VALU path with its own softmax state, which
+// is merged with the quantized part before the partials are written.
 #pragma once
 
 #include "common.hpp"
@@ -34,10 +37,15 @@
 namespace kvq {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-using sgpr_i32 = const int32_t __attribute__((address_space(4)))*;
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 using sgpr_f32 = const float __attribute__((address_space(4)))*;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kStep = 32;   // tokens per step of the quantized loop
 
 // Relative cost of a 64-token tile: quantized codes vs bf16 tail rows.
 constexpr int kCostQ = 2;
@@ -49,9 +57,8 @@ constexpr int kCostT = 5;
 #define KVQ_SPLIT_WAVES_PER_EU 2
 #endif
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 __device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+__device__ inline uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Maximum / sum over the 64 lanes, result in every lane.
 __device__ inline float wave_max(float v) {
@@ -75,137 +82,133 @@ __device__ inline float wave_sum(float v) {
   return lo + hi;
 }
 
-// K codes of one token unpacked into D/4 dwords of byte-sized values in the
-// order the prep kernel lays out the query bytes.
-template <int D, int KB>
-__device__ inline void unpack_k(const uint32_t* kw, uint32_t (&kb)[D / 4]) {
-  if constexpr (KB == 8) {
-#pragma unroll
-    for (int w = 0; w < D / 4; ++w) kb[w] = kw[w];
-  } else {
-#pragma unroll
-    for (int w = 0; w < D / 8; ++w) {
-      uint32_t lo = kw[w] & 0x0F0F0F0Fu;
-      uint32_t hi = (kw[w] >> 4) & 0x0F0F0F0Fu;
-      if constexpr (KB == 5) {
-        const uint32_t hw = kw[D / 8 + w / 4];
-        const int gq = w % 4;
-        const int sl = 4 - 2 * gq, sh = 3 - 2 * gq;
-        const uint32_t tl = sl >= 0 ? (hw << sl) : (hw >> (-sl));
-        const uint32_t th = sh >= 0 ? (hw << sh) : (hw >> (-sh));
-        lo |= tl & 0x10101010u;
-        hi |= th & 0x10101010u;
-      }
-      kb[2 * w] = lo;
-      kb[2 * w + 1] = hi;
-    }
-  }
+// Rotation by N lanes inside each row of 16 lanes (DPP row_ror).
+template <int N>
+__device__ inline float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+__device__ inline float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
 }
 
-// Eight fp16 code pairs (token A in the low half, token B in the high half)
-// for the eight elements a P.V lane owns.
-template <int VB>
-struct VTok;
-
-// Byte k of token A in the low half and byte k of token B in the high half.
-__device__ inline uint32_t pair_bytes(uint32_t b, uint32_t a, int k) {
-  return __builtin_amdgcn_perm(b, a, (uint32_t)k | (0x0Cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0Cu << 24));
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) { return (x & mask) | bits; }
+__device__ inline uint32_t rotr(uint32_t x, uint32_t s) { return __builtin_amdgcn_alignbit(x, x, s); }
+__device__ inline float half_of(uint32_t w, int hi) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(hi ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-// (x & mask) | magic as one v_and_or_b32; magic lives in a VGPR.
-__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  return (x & mask) | magic;
-}
-
-template <>
-struct VTok<4> {
-  uint32_t n;  // 8 nibbles: element i in bits 4i..4i+3
-  // Even elements become exact fp16 codes c; odd elements become 16*c
-  // (nibble kept in mantissa bits 4..7), undone once when partials are stored.
-  static constexpr bool kOddTimes16 = true;
-  __device__ inline void pairs(const VTok& B, h2_t (&c)[8], uint32_t magic) const {
-    const h2_t bias_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    const h2_t bias_hi = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t p = pair_bytes(B.n, n, k);
-      c[2 * k] = as_h2(and_or(p, 0x000F000Fu, magic)) + bias_lo;
-      c[2 * k + 1] = as_h2(and_or(p, 0x00F000F0u, magic)) + bias_hi;
-    }
-  }
-};
-
-template <>
-struct VTok<8> {
-  uint32_t b0, b1;  // 8 signed bytes
-  static constexpr bool kOddTimes16 = false;
-  __device__ inline void pairs(const VTok& B, h2_t (&c)[8], uint32_t) const {
-    const h2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      c[k] = as_h2(pair_bytes(B.b0, b0, k) ^ 0x64806480u) + bias;
-      c[4 + k] = as_h2(pair_bytes(B.b1, b1, k) ^ 0x64806480u) + bias;
-    }
-  }
-};
-
-template <>
-struct VTok<5> {
-  uint32_t n;   // 8 nibbles
-  uint32_t hw;  // high-bit word of the block
-  int gq;       // which 8-element group of the block this lane owns
-  static constexpr bool kOddTimes16 = false;
-  __device__ inline void pairs(const VTok& B, h2_t (&c)[8], uint32_t) const {
-    const uint32_t x1 = __builtin_amdgcn_perm(B.n, n, 0x05040100u);
-    const uint32_t x2 = __builtin_amdgcn_perm(B.n, n, 0x07060302u);
-    const h2_t bias = {(_Float16)-1040.0f, (_Float16)-1040.0f};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t x = e < 4 ? x1 : x2;
-      const uint32_t nib = (x >> (4 * (e % 4))) & 0x000F000Fu;
-      const int i = e / 2, nb = e % 2;
-      const uint32_t sel = (uint32_t)i | (0x0Cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0Cu << 24);
-      const uint32_t hb = __builtin_amdgcn_perm(B.hw, hw, sel);   // bit 2*gq+nb of each half
-      const int sh = 4 - 2 * gq - nb;
-      const uint32_t hbs = sh >= 0 ? (hb << sh) : (hb >> (-sh));
-      c[e] = as_h2(nib | (hbs & 0x00100010u) | 0x64006400u) + bias;
-    }
-  }
-};
-
+// Cache bytes of one 32-token step held in registers.
 template <int D, int KB, int VB>
-struct TileRegs {
+struct StepRegs {
   static constexpr int NB = D / kBlock;
-  static constexpr int NCK = padded_row_bytes(D, KB) / kChunk;
-  static constexpr int TPS = D / 8;   // tokens per P.V slot in a tile
-  uint4 kc[NCK];
-  uint32_t ks[NB / 2];   // fp16 K scales of this lane's token
-  uint32_t vs[NB / 2];   // fp16 V scales of this lane's token
-  VTok<VB> v[TPS];
+  static constexpr int NN = D / 16;
+  static constexpr int NSW = (NB + 1) / 2;   // 32-bit words of fp16 scales per token
+  u32x2 k8[KB == 8 ? 2 * NB : 1];            // [m][blk] 8 code bytes
+  uint32_t k4[KB == 8 ? 1 : 2 * NB];         // [m][blk] 8 code nibbles
+  uint32_t kh[KB == 5 ? 2 * NB : 1];         // [m][blk] 5-bit high-bit word
+  uint32_t ks[2][NSW], vs[2][NSW];           // [m] fp16 scales of this lane's token
+  u32x4 v[VB == 8 ? NN / 2 : NN / 4];        // V items (4 or 8 bytes each)
+  uint32_t vh[VB == 5 ? NN / 4 : 1];         // 5-bit high-bit bytes
 };
+
+// B operand of Q.K for 16 tokens and one block: 8 int8 codes of this lane's
+// token in the k-slot order of the query bytes (4/5-bit: elements
+// 0,2,4,6,1,3,5,7 of the lane's group of 8, widened to bytes).
+template <int D, int KB, int VB>
+__device__ inline long k_operand(const StepRegs<D, KB, VB>& R, int i, uint32_t rot_lo, uint32_t rot_hi) {
+  if constexpr (KB == 8) {
+    return __builtin_bit_cast(long, R.k8[i]);
+  } else {
+    const uint32_t x = R.k4[i];
+    uint32_t lo = x & 0x0F0F0F0Fu;
+    uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+    if constexpr (KB == 5) {
+      lo |= rotr(R.kh[i], rot_lo) & 0x10101010u;
+      hi |= rotr(R.kh[i], rot_hi) & 0x10101010u;
+    }
+    return (long)(((uint64_t)hi << 32) | lo);
+  }
+}
+
+// B operand of P.V for output elements 16*nb..+15: this lane's element for
+// the 8 tokens of its k-slots, as exact fp16 codes.
+template <int D, int KB, int VB>
+__device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t magic) {
+  const h2_t one16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  if constexpr (VB == 8) {
+    const u32x4 q = R.v[nb / 2];
+    const uint32_t x0 = (nb % 2) ? q[2] : q[0];
+    const uint32_t x1 = (nb % 2) ? q[3] : q[1];
+    const uint32_t c64 = 0x64646464u;
+    const h2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const h2_t d0 = as_h2(__builtin_amdgcn_perm(c64, x0, 0x04010400u)) + bias;
+    const h2_t d1 = as_h2(__builtin_amdgcn_perm(c64, x0, 0x04030402u)) + bias;
+    const h2_t d2 = as_h2(__builtin_amdgcn_perm(c64, x1, 0x04010400u)) + bias;
+    const h2_t d3 = as_h2(__builtin_amdgcn_perm(c64, x1, 0x04030402u)) + bias;
+    return h8_t{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+  } else {
+    const uint32_t x = R.v[nb / 4][nb % 4];
+    const uint32_t x8 = x >> 8;
+    uint32_t w0 = and_or(x, 0x000F000Fu, magic);
+    uint32_t w1 = and_or(x, 0x00F000F0u, magic);
+    uint32_t w2 = and_or(x8, 0x000F000Fu, magic);
+    uint32_t w3 = and_or(x8, 0x00F000F0u, magic);
+    _Float16 b_lo, b_hi;
+    if constexpr (VB == 5) {
+      const uint32_t hb = (R.vh[nb / 4] >> (8 * (nb % 4))) & 0xFFu;
+      const uint32_t y = (hb << 4) | (hb << 16);
+      w0 |= y & 0x00100010u;
+      w1 |= (y << 3) & 0x01000100u;
+      w2 |= (y >> 2) & 0x00100010u;
+      w3 |= (y << 1) & 0x01000100u;
+      b_lo = (_Float16)-1040.0f;
+      b_hi = (_Float16)-80.0f;
+    } else {
+      b_lo = (_Float16)-1032.0f;
+      b_hi = (_Float16)-72.0f;
+    }
+    const h2_t bl = {b_lo, b_lo}, bh = {b_hi, b_hi};
+    const h2_t d0 = as_h2(w0) + bl;
+    const h2_t d1 = as_h2(w1) * one16 + bh;
+    const h2_t d2 = as_h2(w2) + bl;
+    const h2_t d3 = as_h2(w3) * one16 + bh;
+    return h8_t{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+  }
+}
 
 template <int D, int KB, int VB, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WAVES_PER_EU))) void decode_split_kernel(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
   constexpr int NB = D / kBlock;
+  constexpr int NN = D / 16;
+  constexpr int NSW = (NB + 1) / 2;
   constexpr int RKP = padded_row_bytes(D, KB);
-  constexpr int RVP = padded_row_bytes(D, VB);
-  constexpr int NCK = RKP / kChunk;
-  constexpr int LPRV = D / 8;
-  constexpr int NSLOT = 64 / LPRV;
-  constexpr int TPS = 64 / NSLOT;
-  constexpr int NPAIR = TPS / 2;
+  constexpr int VTB = v_tile_bytes(D, VB);
   constexpr int QPS = qp_stride(D);
-  using Regs = TileRegs<D, KB, VB>;
+  constexpr int LPRV = D / 8;           // tail P.V: lanes per token
+  constexpr int NSLOT = 64 / LPRV;      // tail P.V: tokens in flight
+  constexpr int TPS = 64 / NSLOT;
+  constexpr int WROW = 48;              // fp16 per LDS weight row: 32 tokens + pad
+  using Regs = StepRegs<D, KB, VB>;
 
-  // per head: D/4 dwords of high query bytes, D/4 of low bytes, NB block
-  // corrections, the fixed-point score multiplier; padded to 16 bytes
-  constexpr int QCK = D / 2 + NB;
-  constexpr int QLD = (QCK + 1 + 3) / 4 * 4;
-  __shared__ __align__(16) uint32_t qlds[G][QLD];
-  __shared__ __align__(16) uint32_t wlds[G][NB][32];
+  __shared__ __align__(16) _Float16 wl[NB][8][WROW];
+  __shared__ float alds[16];
+  __shared__ float mls[G][2];
+  __shared__ __align__(16) float accl[G][D];
   __shared__ float plds[G][64];
 
   const int lane = threadIdx.x;
+  const int col = lane & 15;
+  const int r = lane >> 4;
   const int split = blockIdx.x;
   const int g = blockIdx.y / a.n_gchunks;
   const int h0 = g * a.G + (blockIdx.y % a.n_gchunks) * G;
@@ -215,11 +218,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   const int nt = T > 0 ? min(n, T) : 0;
   const int nq = n - nt;
   // Work split by cost, not by token count: a 64-token tile of quantized
-  // codes weighs kCostQ, a tile of bf16 tail tokens kCostT (it carries about
-  // 2.5x the bytes).  Split s of S takes the cost interval [s*C/S, (s+1)*C/S)
-  // of this sequence; boundaries fall on tile edges of each region.
-  const int ctq = (nq + kTile - 1) / kTile;       // quantized tiles
-  const int ctt = (nt + kTile - 1) / kTile;       // tail tiles
+  // codes weighs kCostQ, a tile of bf16 tail tokens kCostT.  Split s of S
+  // takes the cost interval [s*C/S, (s+1)*C/S) of this sequence; boundaries
+  // fall on tile edges of each region.
+  const int ctq = (nq + kTile - 1) / kTile;
+  const int ctt = (nt + kTile - 1) / kTile;
   const int64_t C = (int64_t)kCostQ * ctq + (int64_t)kCostT * ctt;
   const int64_t c0 = C * split / a.S, c1 = C * (split + 1) / a.S;
   auto q_tiles = [&](int64_t c) {
@@ -227,8 +230,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
     return (int)(t < ctq ? t : ctq);
   };
   auto t_tiles = [&](int64_t c) {
-    const int64_t r = (c - (int64_t)kCostQ * ctq) / kCostT;
-    return r <= 0 ? 0 : (int)(r < ctt ? r : ctt);
+    const int64_t rr = (c - (int64_t)kCostQ * ctq) / kCostT;
+    return rr <= 0 ? 0 : (int)(rr < ctt ? rr : ctt);
   };
   const int qa = q_tiles(c0) * kTile, qb = min(nq, q_tiles(c1) * kTile);
   const int ta = nq + t_tiles(c0) * kTile, tb = min(n, nq + t_tiles(c1) * kTile);
@@ -236,222 +239,233 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
 
   const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
   const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * NB;
-  const uint8_t* vpl = a.v_codes + unit * (size_t)a.cap * RVP;
+  const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
   const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * NB;
   const uint8_t* qp0 = a.qp + ((size_t)b * a.Hq + h0) * QPS;
 
-  const int slot = lane / LPRV;
-  const int eg = lane % LPRV;
-  const int jv = eg / 4;
-  const int kq = lane / NSLOT;
-  const int hidx = ((lane % NSLOT) * NPAIR + (kq >> 1)) * 2 + (kq & 1);
+  if (lane < 16) alds[lane] = 1.f;
 
-  for (int i = lane; i < G * (QCK + 1); i += 64) {
-    const int h = i / (QCK + 1), k = i % (QCK + 1);
-    qlds[h][k] = reinterpret_cast<const uint32_t*>(qp0 + (size_t)h * QPS)[k];
-  }
-  __syncthreads();
-
-  float m[G], ls[G], acc[G][8];
+  // this lane's score heads (Q.K output rows 4r..4r+3 = hi/lo of hA, hB)
+  const int hA = 2 * r, hB = 2 * r + 1;
+  const bool okA = hA < G, okB = hB < G;
+  float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
+  f4_t acc[NN];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    ls[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-
-  // Online-softmax step shared by the quantized and the tail loops:
-  // x holds this lane's scores (log2 units, -inf for masked lanes).
-  // Online-softmax step shared by the quantized and the tail loops:
-  // x holds this lane's scores (log2 units, -inf for masked lanes).  The
-  // running maxima only move when some lane exceeds them (a wave-uniform
-  // branch); the rescale of the accumulators is applied unconditionally so
-  // the common path carries no register shuffles.
-  auto softmax_update = [&](float (&x)[G], float (&p)[G]) {
-    bool need = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) need |= x[h] > m[h];
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], wave_max(x[h]));
-        const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
-        m[h] = mn;
-        ls[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      p[h] = __builtin_amdgcn_exp2f(x[h] - m[h]);
-      ls[h] += p[h];
-    }
-  };
+  for (int i = 0; i < NN; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   // ------------------------------------------------ quantized positions
   if (qa < qb) {
-    const int last = (qb - 1) / kTile * kTile;
-    // per-lane byte offsets inside a tile; the tile base is uniform
-    const uint32_t k_off = lane * kChunk;
-    const uint32_t s_off = lane * NB * 2;
-    uint32_t v_off, vh_off = 0;
-    if constexpr (VB == 8) {
-      v_off = ((eg / 2) * kTile + slot) * kChunk + (eg % 2) * 8;
-    } else {
-      v_off = ((eg / 4) * kTile + slot) * kChunk + (eg % 4) * 4;
-      const int byte = D / 2 + 4 * jv;
-      vh_off = ((byte / kChunk) * kTile + slot) * kChunk + byte % kChunk;
+    // A operand of Q.K: row col = head col/2, high (even) or low (odd) bytes
+    long qop[NB];
+    {
+      const bool qrow = col < 2 * G;
+      const uint8_t* qrow_p = qp0 + (size_t)(col / 2) * QPS + (col % 2) * D + 8 * r;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) qop[j] = qrow ? *reinterpret_cast<const long*>(qrow_p + kBlock * j) : 0;
     }
-
-    auto load_tile = [&](Regs& r, int t0) {
-      const uint8_t* kt = kpl + (size_t)(t0 / kTile) * kTile * RKP;
+    const float ckA = okA ? *reinterpret_cast<const float*>(qp0 + (size_t)hA * QPS + 2 * D + D / 8) : 0.f;
+    const float ckB = okB ? *reinterpret_cast<const float*>(qp0 + (size_t)hB * QPS + 2 * D + D / 8) : 0.f;
+    int corrA[KB == 8 ? 1 : NB], corrB[KB == 8 ? 1 : NB];
+    if constexpr (KB != 8) {
 #pragma unroll
-      for (int c = 0; c < NCK; ++c)
-        r.kc[c] = *reinterpret_cast<const uint4*>(kt + c * kTile * kChunk + k_off);
-      const uint8_t* ks = reinterpret_cast<const uint8_t*>(ksc + (size_t)t0 * NB) + s_off;
-      const uint8_t* vs = reinterpret_cast<const uint8_t*>(vsc + (size_t)t0 * NB) + s_off;
-      if constexpr (NB == 2) {
-        r.ks[0] = *reinterpret_cast<const uint32_t*>(ks);
-        r.vs[0] = *reinterpret_cast<const uint32_t*>(vs);
-      } else if constexpr (NB == 4) {
-        const uint2 k2 = *reinterpret_cast<const uint2*>(ks);
-        const uint2 v2 = *reinterpret_cast<const uint2*>(vs);
-        r.ks[0] = k2.x; r.ks[1] = k2.y; r.vs[0] = v2.x; r.vs[1] = v2.y;
-      } else {
-        const uint4 k4 = *reinterpret_cast<const uint4*>(ks);
-        const uint4 v4 = *reinterpret_cast<const uint4*>(vs);
-        r.ks[0] = k4.x; r.ks[1] = k4.y; r.ks[2] = k4.z; r.ks[3] = k4.w;
-        r.vs[0] = v4.x; r.vs[1] = v4.y; r.vs[2] = v4.z; r.vs[3] = v4.w;
+      for (int j = 0; j < NB; ++j) {
+        corrA[j] = okA ? reinterpret_cast<const int*>(qp0 + (size_t)hA * QPS + 2 * D)[j] : 0;
+        corrB[j] = okB ? reinterpret_cast<const int*>(qp0 + (size_t)hB * QPS + 2 * D)[j] : 0;
       }
-      const uint8_t* vt = vpl + (size_t)(t0 / kTile) * kTile * RVP;
+    }
+    // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
+    // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word
+    const uint32_t rot_lo = (uint32_t)(2 * r + 28) & 31u;   // rotate left by 4 - 2r
+    const uint32_t rot_hi = (uint32_t)(2 * r + 29) & 31u;   // rotate left by 3 - 2r
+    uint32_t magic = 0x64006400u;
+    asm volatile("" : "+v"(magic));
+
+    // per-lane byte offsets inside a tile; the tile base is uniform
+    const uint32_t k_off = KB == 8 ? (uint32_t)((((r >> 1) * kTile + col) * kChunk) + 8 * (r & 1))
+                                   : (uint32_t)(col * kChunk + 4 * r);
+    const uint32_t v_off = (uint32_t)(lane * NN * (VB == 8 ? 8 : 4));
+    const uint32_t vh_off = (uint32_t)(32 * D + lane * NN);
+    const int last = (qb - 1) / kStep * kStep;
+
+    auto load_step = [&](Regs& R, int s0) {
+      const int j2 = (s0 / kStep) & 1;
+      const uint8_t* kt = kpl + (size_t)(s0 / kTile) * kTile * RKP + j2 * kStep * kChunk;
 #pragma unroll
-      for (int k = 0; k < TPS; ++k) {
-        const uint8_t* vk = vt + k * NSLOT * kChunk;
-        if constexpr (VB == 4) {
-          r.v[k].n = *reinterpret_cast<const uint32_t*>(vk + v_off);
-        } else if constexpr (VB == 8) {
-          const uint2 v = *reinterpret_cast<const uint2*>(vk + v_off);
-          r.v[k].b0 = v.x; r.v[k].b1 = v.y;
-        } else {
-          r.v[k].n = *reinterpret_cast<const uint32_t*>(vk + v_off);
-          r.v[k].hw = *reinterpret_cast<const uint32_t*>(vk + vh_off);
-          r.v[k].gq = eg % 4;
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if constexpr (KB == 8) {
+            R.k8[m * NB + j] = *reinterpret_cast<const u32x2*>(kt + (2 * j * kTile + 16 * m) * kChunk + k_off);
+          } else {
+            R.k4[m * NB + j] = *reinterpret_cast<const uint32_t*>(kt + (j * kTile + 16 * m) * kChunk + k_off);
+            if constexpr (KB == 5) {
+              const int cb = D / 32 + j / 4;
+              R.kh[m * NB + j] = *reinterpret_cast<const uint32_t*>(
+                  kt + (cb * kTile + 16 * m + col) * kChunk + 4 * (j % 4));
+            }
+          }
         }
+        const size_t tok = (size_t)s0 + 16 * m + col;
+        const uint32_t* ksp = reinterpret_cast<const uint32_t*>(ksc + tok * NB);
+        const uint32_t* vsp = reinterpret_cast<const uint32_t*>(vsc + tok * NB);
+        if constexpr (NSW == 1) {
+          R.ks[m][0] = ksp[0];
+          R.vs[m][0] = vsp[0];
+        } else if constexpr (NSW == 2) {
+          const u32x2 k2 = *reinterpret_cast<const u32x2*>(ksp);
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(vsp);
+          R.ks[m][0] = k2[0]; R.ks[m][1] = k2[1];
+          R.vs[m][0] = v2[0]; R.vs[m][1] = v2[1];
+        } else {
+          const u32x4 k4 = *reinterpret_cast<const u32x4*>(ksp);
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(vsp);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { R.ks[m][q] = k4[q]; R.vs[m][q] = v4[q]; }
+        }
+      }
+      const uint8_t* vt = vpl + (size_t)(s0 / kTile) * VTB;
+      const uint8_t* vj = vt + (size_t)j2 * 64 * NN * (VB == 8 ? 8 : 4) + v_off;
+#pragma unroll
+      for (int q = 0; q < (VB == 8 ? NN / 2 : NN / 4); ++q) R.v[q] = reinterpret_cast<const u32x4*>(vj)[q];
+      if constexpr (VB == 5) {
+        const uint8_t* hj = vt + (size_t)j2 * 64 * NN + vh_off;
+#pragma unroll
+        for (int q = 0; q < NN / 4; ++q) R.vh[q] = reinterpret_cast<const uint32_t*>(hj)[q];
       }
     };
 
-    auto compute_tile = [&](const Regs& r, int t0) {
-      const bool valid = t0 + lane < qb;
-      uint32_t kw[NCK * 4];
-#pragma unroll
-      for (int c = 0; c < NCK; ++c) {
-        kw[4 * c] = r.kc[c].x; kw[4 * c + 1] = r.kc[c].y;
-        kw[4 * c + 2] = r.kc[c].z; kw[4 * c + 3] = r.kc[c].w;
-      }
-      uint32_t kb[D / 4];
-      unpack_k<D, KB>(kw, kb);
-      float ksf[NB], vsf[NB];
+    auto compute_step = [&](const Regs& R, int s0) {
+      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements
+      i4_t dq[2 * NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        ksf[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.ks[j / 2] >> (16 * (j % 2))));
-        vsf[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(r.vs[j / 2] >> (16 * (j % 2))));
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          dq[m * NB + j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+              qop[j], k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi), i4_t{0, 0, 0, 0}, 0, 0, 0);
       }
-      // Query bytes come from LDS (same address in every lane: a broadcast).
-      // The read of block b is tied (empty asm on an opaque offset) to the
-      // result of block b-2, so at most about three blocks of query bytes are
-      // live: the reads run two blocks ahead of their use and cannot all be
-      // hoisted to the top of the tile.
-      int qz = 0;
-      int ring[2] = {0, 0};
-      float s[G];
+      float sA[2], sB[2];
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = 0.f;
-#pragma unroll
-      for (int bi = 0; bi < G * NB; ++bi) {
-        const int h = bi / NB, j = bi % NB;
-        asm volatile("" : "+s"(qz) : "v"(ring[bi % 2]));
-        const uint32_t* qh = &qlds[h][0] + qz;
-        const uint4 h0 = *reinterpret_cast<const uint4*>(qh + 8 * j);
-        const uint4 h1 = *reinterpret_cast<const uint4*>(qh + 8 * j + 4);
-        const uint4 l0 = *reinterpret_cast<const uint4*>(qh + D / 4 + 8 * j);
-        const uint4 l1 = *reinterpret_cast<const uint4*>(qh + D / 4 + 8 * j + 4);
-        const uint32_t qhi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-        const uint32_t qlo[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        int ahi = 0, alo = (int)qh[D / 2 + j];
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          ahi = __builtin_amdgcn_sdot4((int)qhi[w], (int)kb[8 * j + w], ahi, false);
-          alo = __builtin_amdgcn_sdot4((int)qlo[w], (int)kb[8 * j + w], alo, false);
-        }
-        const int dj = ahi * 256 + alo;
-        ring[bi % 2] = dj;
-        s[h] = __builtin_fmaf(ksf[j], (float)dj, s[h]);
-      }
-      float x[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float xv = s[h] * __uint_as_float(qlds[h][QCK + qz]);
-        asm volatile("" : "+v"(xv));   // computed in every lane: a select, not a branch
-        x[h] = valid ? xv : -INFINITY;
-      }
-      float p[G];
-      softmax_update(x, p);
-      __syncthreads();
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int m = 0; m < 2; ++m) {
+        sA[m] = 0.f;
+        sB[m] = 0.f;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const float wv = valid ? p[h] * vsf[j] : 0.f;
-          reinterpret_cast<_Float16*>(&wlds[h][j][0])[hidx] = (_Float16)wv;
+          const i4_t d = dq[m * NB + j];
+          int vA = (d[0] << 8) + d[1];
+          int vB = (d[2] << 8) + d[3];
+          if constexpr (KB != 8) {
+            vA += corrA[j];
+            vB += corrB[j];
+          }
+          const float ks = half_of(R.ks[m][j / 2], j % 2);
+          sA[m] = __builtin_fmaf(ks, (float)vA, sA[m]);
+          sB[m] = __builtin_fmaf(ks, (float)vB, sB[m]);
+        }
+      }
+      // online softmax (log2 units); masked tokens score -inf
+      bool valid[2];
+      float xA[2], xB[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        valid[m] = s0 + 16 * m + col < qb;
+        float ya = sA[m] * ckA, yb = sB[m] * ckB;
+        asm volatile("" : "+v"(ya), "+v"(yb));   // selects, not branches
+        xA[m] = valid[m] && okA ? ya : -INFINITY;
+        xB[m] = valid[m] && okB ? yb : -INFINITY;
+      }
+      const float nA = fmaxf(mA, row16_max(fmaxf(xA[0], xA[1])));
+      const float nB = fmaxf(mB, row16_max(fmaxf(xB[0], xB[1])));
+      if (__builtin_amdgcn_ballot_w64(nA > mA || nB > mB) != 0) {
+        const float aA = nA > mA ? __builtin_amdgcn_exp2f(mA - nA) : 1.f;
+        const float aB = nB > mB ? __builtin_amdgcn_exp2f(mB - nB) : 1.f;
+        mA = nA;
+        mB = nB;
+        lA *= aA;
+        lB *= aB;
+        __syncthreads();
+        if (col == 0) {
+          alds[hA] = aA;
+          alds[hB] = aB;
+        }
+        __syncthreads();
+        const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]);
+#pragma unroll
+        for (int i = 0; i < NN; ++i) acc[i] *= al;
+      }
+      float pA[2], pB[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        pA[m] = __builtin_amdgcn_exp2f(xA[m] - mA);
+        pB[m] = __builtin_amdgcn_exp2f(xB[m] - mB);
+      }
+      lA += pA[0] + pA[1];
+      lB += pB[0] + pB[1];
+      // weights p * scale_v in fp16, moved to the A-operand layout via LDS
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float vs = half_of(R.vs[m][j / 2], j % 2);
+          const int t = 16 * m + col;
+          if (okA) wl[j][hA][t] = valid[m] ? (_Float16)(pA[m] * vs) : (_Float16)0.f;
+          if (okB) wl[j][hB][t] = valid[m] ? (_Float16)(pB[m] * vs) : (_Float16)0.f;
         }
       }
       __syncthreads();
-      uint32_t magic = 0x64006400u;
-      asm volatile("" : "+v"(magic));
+      const int hr = col < G ? col : 0;
+      h8_t wa[NB];
 #pragma unroll
-      for (int q2 = 0; q2 < NPAIR; q2 += 2) {
-        u32x2 wq[G];
+      for (int j = 0; j < NB; ++j) wa[j] = *reinterpret_cast<const h8_t*>(&wl[j][hr][8 * r]);
+      // P.V on the matrix cores: NN products of 16 heads x 32 tokens x 16 elements
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-          wq[h] = *reinterpret_cast<const u32x2*>(&wlds[h][jv][slot * NPAIR + q2]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          h2_t c[8];
-          r.v[2 * (q2 + u)].pairs(r.v[2 * (q2 + u) + 1], c, magic);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const h2_t wp = as_h2(wq[h][u]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_amdgcn_fdot2(wp, c[e], acc[h][e], false);
-          }
-        }
-      }
+      for (int i = 0; i < NN; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[i / 2], v_operand<D, KB, VB>(R, i, magic),
+                                                        acc[i], 0, 0, 0);
     };
 
     Regs ra, rb;
-    load_tile(ra, qa);
-    for (int t = qa; t < qb; t += 2 * kTile) {
-      const int t1 = t + kTile;
-      load_tile(rb, min(t1, last));
-      compute_tile(ra, t);
-      if (t1 >= qb) break;
-      load_tile(ra, min(t1 + kTile, last));
-      compute_tile(rb, t1);
-    }
-    if constexpr (VTok<VB>::kOddTimes16) {
-      // odd elements were accumulated as 16*c (see VTok<4>); the tail loop
-      // below accumulates plain values, so undo the factor before it runs
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 1; e < 8; e += 2) acc[h][e] *= 0.0625f;
-      }
+    load_step(ra, qa);
+    for (int s = qa; s < qb; s += 2 * kStep) {
+      const int s1 = s + kStep;
+      load_step(rb, min(s1, last));
+      compute_step(ra, s);
+      if (s1 >= qb) break;
+      load_step(ra, min(s1 + kStep, last));
+      compute_step(rb, s1);
     }
   }
 
+  // quantized-part state, per head, into LDS
+  lA = row16_sum(lA);
+  lB = row16_sum(lB);
+  __syncthreads();
+  if (col == 0) {
+    if (okA) { mls[hA][0] = mA; mls[hA][1] = lA; }
+    if (okB) { mls[hB][0] = mB; mls[hB][1] = lB; }
+  }
+#pragma unroll
+  for (int i = 0; i < NN; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = 4 * r + k;
+      if (h < G) accl[h][16 * i + col] = acc[i][k];
+    }
+  }
+  __syncthreads();
+
   // ------------------------------------------------ bf16 tail positions
+  const int slot = lane / LPRV;
+  const int eg = lane % LPRV;
+  float tm[G], tl[G], tacc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    tm[h] = -INFINITY;
+    tl[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tacc[h][e] = 0.f;
+  }
   if (ta < tb) {
     const uint16_t* ktl = a.k_tail + unit * (size_t)T * D;
     const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;
@@ -482,21 +496,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
           for (int e = 0; e < 8; ++e) s[h] = __builtin_fmaf(qr[8 * c + e], kf[e], s[h]);
         }
       }
-      float x[G], p[G];
+      float p[G];
+      bool need = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float cs = *(sgpr_f32)(qbase + (size_t)h * QPS + 2 * D + D / 8 + 4);
-        x[h] = valid ? s[h] * cs : -INFINITY;
+        s[h] = valid ? s[h] * cs : -INFINITY;
+        need |= s[h] > tm[h];
       }
-      softmax_update(x, p);
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float mn = fmaxf(tm[h], wave_max(s[h]));
+          const float alpha = mn > tm[h] ? __builtin_amdgcn_exp2f(tm[h] - mn) : 1.f;
+          tm[h] = mn;
+          tl[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tacc[h][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        p[h] = __builtin_amdgcn_exp2f(s[h] - tm[h]);
+        tl[h] += p[h];
+      }
       __syncthreads();
 #pragma unroll
       for (int h = 0; h < G; ++h) plds[h][lane] = p[h];
       __syncthreads();
 #pragma unroll 4
       for (int k = 0; k < TPS; ++k) {
-        const int tl = k * NSLOT + slot;
-        const int tt = t0 + tl;
+        const int tk = k * NSLOT + slot;
+        const int tt = t0 + tk;
         const int sv = (tt < tb ? tt : t0) % T;
         const uint4 vv = *reinterpret_cast<const uint4*>(vtl + (size_t)sv * D + 8 * eg);
         const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
@@ -508,39 +539,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float ph = plds[h][tl];
+          const float ph = plds[h][tk];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(ph, vf[e], acc[h][e]);
+          for (int e = 0; e < 8; ++e) tacc[h][e] = __builtin_fmaf(ph, vf[e], tacc[h][e]);
         }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) tl[h] = wave_sum(tl[h]);
+#pragma unroll
+    for (int sft = LPRV; sft < 64; sft <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tacc[h][e] += __shfl_xor(tacc[h][e], sft);
       }
     }
   }
 
   // ------------------------------------------------ partial results
-#pragma unroll
-  for (int h = 0; h < G; ++h) ls[h] = wave_sum(ls[h]);
-#pragma unroll
-  for (int s = LPRV; s < 64; s <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], s);
-    }
-  }
   const size_t row0 = ((size_t)b * a.Hq + h0) * a.S + split;
   if (lane < LPRV) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      const float mq = mls[h][0], lq = mls[h][1];
+      const float M = fmaxf(mq, tm[h]);
+      const float aq = mq > -INFINITY ? __builtin_amdgcn_exp2f(mq - M) : 0.f;
+      const float at = tm[h] > -INFINITY ? __builtin_amdgcn_exp2f(tm[h] - M) : 0.f;
+      const float4 q0 = *reinterpret_cast<const float4*>(&accl[h][8 * eg]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&accl[h][8 * eg + 4]);
       float4* dst = reinterpret_cast<float4*>(a.part_acc + (row0 + (size_t)h * a.S) * D + 8 * eg);
-      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      a.part_ml[(row0 + (size_t)h * a.S) * 2] = m[h];
-      a.part_ml[(row0 + (size_t)h * a.S) * 2 + 1] = ls[h];
+      dst[0] = make_float4(q0.x * aq + tacc[h][0] * at, q0.y * aq + tacc[h][1] * at,
+                           q0.z * aq + tacc[h][2] * at, q0.w * aq + tacc[h][3] * at);
+      dst[1] = make_float4(q1.x * aq + tacc[h][4] * at, q1.y * aq + tacc[h][5] * at,
+                           q1.z * aq + tacc[h][6] * at, q1.w * aq + tacc[h][7] * at);
+      if (lane == 0) {
+        a.part_ml[(row0 + (size_t)h * a.S) * 2] = M;
+        a.part_ml[(row0 + (size_t)h * a.S) * 2 + 1] = lq * aq + tl[h] * at;
+      }
     }
   }
 }

@@ -4,7 +4,8 @@
 // normalized Sylvester matrix is its own inverse; velog.io post "fix KV cache
 // quantization outliers", section "Hadamard rotation").
 //
-// Thread mapping as in the append: one lane per 32-element block.
+// K codes are read from their row layout, V codes from the element-major
+// tiles.  Thread mapping as in the append: one lane per 32-element block.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,6 +39,27 @@ __device__ inline void load_codes(const uint8_t* plane, int p, int j, int (&c)[3
   }
 }
 
+// V codes of elements 32j..32j+31 of token p from the element-major tiles.
+template <int D, int BITS>
+__device__ inline void load_v_codes(const uint8_t* plane, int p, int j, int (&c)[32]) {
+  constexpr int OFF = 1 << (BITS - 1);
+  const uint8_t* tile = plane + (size_t)(p / kTile) * v_tile_bytes(D, BITS);
+  const int t = p % kTile, k = t % 8;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int item = v_item(D, t, kBlock * j + i);
+    int u;
+    if constexpr (BITS == 8) {
+      u = tile[item * 8 + k];
+    } else {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(tile)[item];
+      u = (int)((w >> (4 * v_nibble(k))) & 15u);
+      if constexpr (BITS == 5) u |= (int)((tile[32 * D + item] >> v_nibble(k)) & 1u) << 4;
+    }
+    c[i] = u - OFF;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   constexpr int LPR = D / kBlock;
@@ -54,12 +76,19 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int e = 0; e < 32; ++e) x[e] = 0.f;
   if (active) {
     if (p < a.nq) {
-      const uint8_t* plane = a.codes + unit * (size_t)a.cap * padded_row_bytes(D, a.bits);
       const float s = (float)__builtin_bit_cast(_Float16, a.scales[(unit * a.cap + p) * (D / kBlock) + j]);
       int c[32];
-      if (a.bits == 4) load_codes<D, 4>(plane, p, j, c);
-      else if (a.bits == 5) load_codes<D, 5>(plane, p, j, c);
-      else load_codes<D, 8>(plane, p, j, c);
+      if (a.which == 0) {
+        const uint8_t* plane = a.codes + unit * (size_t)a.cap * padded_row_bytes(D, a.bits);
+        if (a.bits == 4) load_codes<D, 4>(plane, p, j, c);
+        else if (a.bits == 5) load_codes<D, 5>(plane, p, j, c);
+        else load_codes<D, 8>(plane, p, j, c);
+      } else {
+        const uint8_t* plane = a.codes + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, a.bits);
+        if (a.bits == 4) load_v_codes<D, 4>(plane, p, j, c);
+        else if (a.bits == 5) load_v_codes<D, 5>(plane, p, j, c);
+        else load_v_codes<D, 8>(plane, p, j, c);
+      }
 #pragma unroll
       for (int e = 0; e < 32; ++e) x[e] = (float)c[e] * s;
     } else {

@@ -29,6 +29,7 @@ struct DequantArgs {
   const uint16_t* scales;
   const uint16_t* tail;
   float* out;                // [t1-t0][Hkv][D]
+  int32_t which;              // 0 = K (row layout), 1 = V (element-major tiles)
   int32_t bits, rotate, space, Hkv, T, cap, b, t0, t1, nq;
   float cd;
 };

@@ -142,7 +142,7 @@ size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane) {
   const size_t cap = (size_t)cap_tokens(c);
   switch (plane) {
     case KVQ_K_CODES: return units * cap * padded_row_bytes(c.head_dim, c.k_bits);
-    case KVQ_V_CODES: return units * cap * padded_row_bytes(c.head_dim, c.v_bits);
+    case KVQ_V_CODES: return units * (cap / kTile) * v_tile_bytes(c.head_dim, c.v_bits);
     case KVQ_K_SCALES:
     case KVQ_V_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t);
     case KVQ_K_TAIL:
@@ -296,6 +296,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t
   a.scales = static_cast<const uint16_t*>(which == 0 ? cache->k_scales : cache->v_scales);
   a.tail = static_cast<const uint16_t*>(which == 0 ? cache->k_tail : cache->v_tail);
   a.out = out;
+  a.which = which;
   a.bits = which == 0 ? c.k_bits : c.v_bits;
   a.rotate = which == 0 ? c.rotate_k : c.rotate_v;
   a.space = space;

@@ -51,7 +51,7 @@ def dequantize_unit(planes, b, g, n, d, k_bits, v_bits, tail_len):
         x = np.zeros((n, d), dtype=np.float64)
         if nq > 0:
             x[:nq] = dequantize_rows(planes[p + "_codes"][b, g],
-                                     planes[p + "_scales"][b, g], d, bits, nq)
+                                     planes[p + "_scales"][b, g], d, bits, nq, p)
         for pos in range(nq, n):
             x[pos] = bf16_bits_to_f32(planes[p + "_tail"][b, g, pos % T])
         out.append(x)
@@ -104,7 +104,7 @@ def dequantize_reference(planes, which, b, t0, t1, n, n_kv_heads, d, bits,
     for g in range(n_kv_heads):
         if nq > 0:
             rows = dequantize_rows(planes[p + "_codes"][b, g],
-                                   planes[p + "_scales"][b, g], d, bits, nq)
+                                   planes[p + "_scales"][b, g], d, bits, nq, p)
         for pos in range(t0, t1):
             if pos < nq:
                 out[pos - t0, g] = rows[pos]

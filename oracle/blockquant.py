@@ -27,10 +27,19 @@ the GPU reproduces it bit for bit.  Readings (the pages do not fix these):
       4-bit nibble plane (d/2 bytes, packed like 4-bit), followed by one
       little-endian 32-bit word per block holding bit 4 of each code; element
       w of the block (0..31) owns bit 8*((w%8)//2) + 2*(w//8) + (w%2).
-* R11 Memory layout of a code plane: rows are padded to a multiple of 16
+* R11 Memory layout of a K code plane: rows are padded to a multiple of 16
       bytes and grouped in tiles of 64 tokens; inside a tile, the 16-byte
       chunk c of the row of token l sits at byte (c*64 + l)*16.  Scale planes
       are plain [token][d/32] fp16.
+* R11 V code planes keep the same codes but store each 64-token tile
+      element-major, so that the eight codes of one element for eight
+      consecutive tokens sit together: token t, element e of a tile belong to
+      item ((t//32)*64 + 16*((t%32)//8) + e%16) * (d//16) + e//16, slot
+      k = t%8 of that item.  4-bit: one little-endian 32-bit word per item,
+      u = c + 8 of slot k in nibble 4*(k%2) + k//2.  8-bit: eight bytes per
+      item, u = c + 128 in byte k.  5-bit: the 4-bit words of u & 15 for all
+      items (32*d bytes per tile), then one byte per item whose bit
+      4*(k%2) + k//2 is bit 4 of u.
 """
 
 import numpy as np
@@ -196,3 +205,84 @@ def tiled_to_rows(plane, n, padded, rlen):
     nch = padded // CHUNK
     t = plane[: n * padded].reshape(n // TILE, nch, TILE, CHUNK).transpose(0, 2, 1, 3)
     return np.ascontiguousarray(t).reshape(n, padded)[:, :rlen]
+
+
+def v_tile_bytes(d, bits):
+    """Bytes of one 64-token tile of a V code plane (reading R11)."""
+    return TILE * d * bits // 8
+
+
+def _v_item_index(d):
+    """Token and element index arrays [2][64][d//16][8] of the V tile items
+    (reading R11): item (j, lane, n), slot k holds token 32j + 8*(lane//16) + k
+    and element 16n + lane % 16."""
+    nn = d // 16
+    j = np.arange(2)[:, None, None, None]
+    lane = np.arange(64)[None, :, None, None]
+    n = np.arange(nn)[None, None, :, None]
+    k = np.arange(8)[None, None, None, :]
+    t = 32 * j + 8 * (lane // 16) + k + 0 * n
+    e = 16 * n + lane % 16 + 0 * k + 0 * j
+    return t, e
+
+
+# nibble (and high bit) position of slot k inside a 4-bit word / 5-bit byte
+_V_NIBBLE = np.array([4 * (k % 2) + k // 2 for k in range(8)], dtype=np.uint32)
+
+
+def codes_to_vtiles(codes, bits):
+    """Int codes [n][d] (n a multiple of 64) -> V code plane bytes (R10, R11)."""
+    c = np.asarray(codes, dtype=np.int16)
+    return offset_codes_to_vtiles(c + (1 << (bits - 1)), bits)
+
+
+def offset_codes_to_vtiles(u, bits):
+    """Offset codes u = c + 2^(bits-1) [n][d] -> V code plane bytes.  Every
+    stored code has u >= 1, so u = 0 marks a slot that was never written and
+    becomes zero bits, as in a zero-filled plane."""
+    u = np.asarray(u, dtype=np.int16)
+    n, d = u.shape
+    if n % TILE:
+        raise ValueError("token count must be a multiple of 64")
+    t, e = _v_item_index(d)
+    u = u.reshape(n // TILE, TILE, d)
+    items = u[:, t, e].astype(np.uint32)          # [tiles][2][64][d/16][8]
+    nt = n // TILE
+    if bits == 8:
+        return items.astype(np.uint8).reshape(-1)
+    if bits not in (4, 5):
+        raise ValueError("bits must be 4, 5 or 8")
+    words = np.zeros(items.shape[:-1], dtype=np.uint32)
+    for k in range(8):
+        words |= (items[..., k] & 15) << (4 * _V_NIBBLE[k])
+    nib = words.astype("<u4").view(np.uint8).reshape(nt, -1)
+    if bits == 4:
+        return nib.reshape(-1)
+    hi = np.zeros(items.shape[:-1], dtype=np.uint32)
+    for k in range(8):
+        hi |= ((items[..., k] >> 4) & 1) << _V_NIBBLE[k]
+    return np.concatenate([nib, hi.astype(np.uint8).reshape(nt, -1)], axis=1).reshape(-1)
+
+
+def vtiles_to_codes(plane, n, d, bits):
+    """Inverse of codes_to_vtiles for the first n tokens (n a multiple of 64)."""
+    plane = np.asarray(plane, dtype=np.uint8)
+    nt = n // TILE
+    tb = v_tile_bytes(d, bits)
+    tiles = plane[: nt * tb].reshape(nt, tb)
+    shape = (nt, 2, 64, d // 16)
+    if bits == 8:
+        items = tiles.reshape(shape + (8,)).astype(np.int16)
+    elif bits in (4, 5):
+        words = np.ascontiguousarray(tiles[:, : 32 * d]).view("<u4").reshape(shape).astype(np.uint32)
+        items = np.stack([(words >> (4 * _V_NIBBLE[k])) & 15 for k in range(8)], axis=-1)
+        if bits == 5:
+            hi = tiles[:, 32 * d:].reshape(shape).astype(np.uint32)
+            items = items | np.stack([((hi >> _V_NIBBLE[k]) & 1) << 4 for k in range(8)], axis=-1)
+        items = items.astype(np.int16)
+    else:
+        raise ValueError("bits must be 4, 5 or 8")
+    t, e = _v_item_index(d)
+    u = np.zeros((nt, TILE, d), dtype=np.int16)
+    u[:, t, e] = items
+    return (u.reshape(n, d) - (1 << (bits - 1))).astype(np.int8)

@@ -24,6 +24,7 @@ from .rotation import rotate_f32
 from .blockquant import (
     BLOCK, TILE, quantize_blocks, dequantize_blocks, pack_rows, unpack_rows,
     row_bytes, padded_row_bytes, rows_to_tiled, tiled_to_rows,
+    offset_codes_to_vtiles, vtiles_to_codes, v_tile_bytes,
     f32_to_bf16_bits, bf16_bits_to_f32,
 )
 
@@ -56,6 +57,9 @@ class OracleCache:
         for p in ("k", "v"):
             self.rows[p] = np.zeros((batch, n_kv_heads, self.cap,
                                      row_bytes(head_dim, self.bits[p])), np.uint8)
+        # V codes as offset codes u = c + 2^(bits-1) (u = 0: never written)
+        self.v_u = np.zeros((batch, n_kv_heads, self.cap, head_dim), np.uint8)
+        for p in ("k", "v"):
             self.scales[p] = np.zeros((batch, n_kv_heads, self.cap, nb), np.uint16)
             self.tail[p] = np.zeros((batch, n_kv_heads, max(self.T, 0), head_dim), np.uint16)
 
@@ -98,17 +102,27 @@ class OracleCache:
         codes, scales = quantize_blocks(xq, bits)   # [H][d], [H][d/32]
         self.rows[p][b, :, pos, :] = pack_rows(codes, bits)
         self.scales[p][b, :, pos, :] = scales
+        if p == "v":
+            self.v_u[b, :, pos, :] = codes.astype(np.int16) + (1 << (bits - 1))
 
     def physical(self):
-        """Planes in the device byte layout (reading R11)."""
+        """Planes in the device byte layout (reading R11): K rows tiled in
+        16-byte chunks, V codes in element-major tiles."""
         out = {}
         for p in ("k", "v"):
             bits = self.bits[p]
-            pad = padded_row_bytes(self.d, bits)
-            planes = np.zeros((self.B, self.H, self.cap * pad), np.uint8)
-            for b in range(self.B):
-                for g in range(self.H):
-                    planes[b, g] = rows_to_tiled(self.rows[p][b, g], pad)
+            if p == "k":
+                pad = padded_row_bytes(self.d, bits)
+                planes = np.zeros((self.B, self.H, self.cap * pad), np.uint8)
+                for b in range(self.B):
+                    for g in range(self.H):
+                        planes[b, g] = rows_to_tiled(self.rows[p][b, g], pad)
+            else:
+                planes = np.zeros((self.B, self.H, self.cap // TILE * v_tile_bytes(self.d, bits)),
+                                  np.uint8)
+                for b in range(self.B):
+                    for g in range(self.H):
+                        planes[b, g] = offset_codes_to_vtiles(self.v_u[b, g], bits)
             out[p + "_codes"] = planes
             out[p + "_scales"] = self.scales[p].copy()
             out[p + "_tail"] = self.tail[p].copy()
@@ -116,13 +130,21 @@ class OracleCache:
 
 
 def planes_to_rows(codes_plane, d, bits, n):
-    """Physical code plane of one (b, g) -> logical rows of the first n tokens."""
+    """Physical K code plane of one (b, g) -> logical rows of the first n tokens."""
     pad = padded_row_bytes(d, bits)
     n_t = (n + TILE - 1) // TILE * TILE
     return tiled_to_rows(codes_plane, n_t, pad, row_bytes(d, bits))[:n]
 
 
-def dequantize_rows(codes_plane, scales_plane, d, bits, n):
+def plane_codes(codes_plane, d, bits, n, which):
+    """Int codes [n][d] of the first n tokens of one (b, g) plane; which is
+    "k" (row layout) or "v" (element-major tiles)."""
+    if which == "k":
+        return unpack_rows(planes_to_rows(codes_plane, d, bits, n), bits, d)
+    n_t = (n + TILE - 1) // TILE * TILE
+    return vtiles_to_codes(codes_plane, n_t, d, bits)[:n]
+
+
+def dequantize_rows(codes_plane, scales_plane, d, bits, n, which):
     """Dequantized values (rotated space, float32) of quantized rows [0, n)."""
-    rows = planes_to_rows(codes_plane, d, bits, n)
-    return dequantize_blocks(unpack_rows(rows, bits, d), scales_plane[:n])
+    return dequantize_blocks(plane_codes(codes_plane, d, bits, n, which), scales_plane[:n])

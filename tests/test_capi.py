@@ -71,12 +71,13 @@ def test_plane_bytes(d, kb, vb):
     cap = 1024
     pad = lambda r: (r + 15) // 16 * 16
     assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_CODES) == B * H * cap * pad(d * kb // 8)
-    assert kvq.kvq_plane_bytes(c, kvq.KVQ_V_CODES) == B * H * cap * pad(d * vb // 8)
+    # V codes sit in element-major 64-token tiles with no row padding
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_V_CODES) == B * H * cap * d * vb // 8
     assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_SCALES) == B * H * cap * (d // 32) * 2
     assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_TAIL) == B * H * T * d * 2
     # codes + scales per token-head: 32*b/8 + 2 bytes per 32 elements
     for b, plane in ((kb, kvq.KVQ_K_CODES), (vb, kvq.KVQ_V_CODES)):
-        if (d * b // 8) % 16 == 0:
+        if (d * b // 8) % 16 == 0 or plane == kvq.KVQ_V_CODES:
             per_tok = (kvq.kvq_plane_bytes(c, plane) + kvq.kvq_plane_bytes(c, kvq.KVQ_K_SCALES)) / (B * H * cap)
             assert per_tok == (d // 32) * (32 * b // 8 + 2)
 

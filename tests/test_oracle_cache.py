@@ -7,7 +7,8 @@ import pytest
 
 from oracle import (OracleCache, rotate_f32, quantize_blocks, pack_rows,
                     bf16_round, f32_to_bf16_bits, dequantize_reference)
-from oracle.kvcache import planes_to_rows
+from oracle.kvcache import planes_to_rows, plane_codes
+from oracle.blockquant import codes_to_vtiles, vtiles_to_codes, v_tile_bytes
 
 
 def _data(B, n, H, d, seed=0):
@@ -65,9 +66,9 @@ def test_no_tail_quantizes_float32_directly():
     k, v = _data(B, n, H, d, seed=5)
     c = OracleCache(B, H, d, 8, 8, 0, 64)
     c.append(k, v, [0], dtype="f32")
-    rows = planes_to_rows(c.physical()["v_codes"][0, 0], d, 8, n)
+    got = plane_codes(c.physical()["v_codes"][0, 0], d, 8, n, "v")
     codes, _ = quantize_blocks(rotate_f32(v[0, :, 0]), 8)
-    assert np.array_equal(rows, pack_rows(codes, 8))
+    assert np.array_equal(got, codes)
 
 
 def test_bf16_input_widened_exactly():
@@ -104,3 +105,46 @@ def test_dequantize_reference_spaces():
     # original space is the rotated value rotated again (H is its own inverse)
     assert np.array_equal(orig, rotate_f32(rot))
     assert np.max(np.abs(orig - k[0])) < 0.05 * np.max(np.abs(k[0]))
+
+
+# ---------------------------------------------------------------- V tile layout
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [4, 5, 8])
+def test_v_tiles_round_trip_and_size(d, bits):
+    qmax = (1 << (bits - 1)) - 1
+    rng = np.random.default_rng(d * 10 + bits)
+    codes = rng.integers(-qmax, qmax + 1, size=(128, d)).astype(np.int8)
+    plane = codes_to_vtiles(codes, bits)
+    assert plane.size == 2 * v_tile_bytes(d, bits) == 2 * 64 * d * bits // 8
+    assert np.array_equal(vtiles_to_codes(plane, 128, d, bits), codes)
+
+
+def _one_code_plane(d, bits, t, e, c):
+    codes = np.zeros((64, d), dtype=np.int8)
+    codes[t, e] = c
+    base = codes_to_vtiles(np.zeros((64, d), dtype=np.int8), bits)
+    return codes_to_vtiles(codes, bits), base
+
+
+def test_v_tile_positions_by_hand():
+    # d = 64, token 9, element 20: half j = 0, lane group 1, slot 1; element
+    # group 1, lane 16 + 4 = 20; item (0*64 + 20) * 4 + 1 = 81.
+    # 4-bit: word 81, nibble 4*(1 % 2) + 1 // 2 = 4 -> byte 326, low nibble.
+    plane, base = _one_code_plane(64, 4, 9, 20, 5)
+    diff = np.nonzero(plane != base)[0]
+    assert list(diff) == [326] and plane[326] == ((5 + 8) | (8 << 4))
+    # 8-bit: byte 81*8 + 1 = 649 holds c + 128.
+    plane, base = _one_code_plane(64, 8, 9, 20, -3)
+    diff = np.nonzero(plane != base)[0]
+    assert list(diff) == [649] and plane[649] == 125
+    # 5-bit: u = 16 - 9 = 7 -> nibble 7 in byte 326 (low); its high bit (0,
+    # where every zero code has 1) is bit 4 of byte 32*64 + 81 = 2129.
+    plane, base = _one_code_plane(64, 5, 9, 20, -9)
+    diff = np.nonzero(plane != base)[0]
+    assert list(diff) == [326, 2129]
+    assert plane[326] & 15 == 7 and base[2129] == 0xFF and plane[2129] == 0xEF
+    # token 45 (j 1, lane group 1, slot 5), element 3 (group 0, lane 19):
+    # item (64 + 19) * 4 + 0 = 332; 4-bit nibble 4*1 + 2 = 6 -> byte 1331, low.
+    plane, base = _one_code_plane(64, 4, 45, 3, -7)
+    diff = np.nonzero(plane != base)[0]
+    assert list(diff) == [1331] and plane[1331] & 15 == 1
