@@ -27,8 +27,9 @@
 //    V codes of one element for 8 consecutive tokens, which the element-major
 //    V tiles store together: nibbles / bytes become exact fp16 integers with
 //    one v_and_or (or v_perm) per pair plus one packed fp16 add.
-// bf16 tail tokens take a float32 VALU path with its own softmax state, which
-// is merged with the quantized part before the partials are written.
+// bf16 tail tokens run the same steps on bf16 matrix products, with the
+// float32 query and weights split into high and low bf16 parts, and share
+// the online-softmax state of the quantized tokens.
 #pragma once
 
 #include "common.hpp"
@@ -38,11 +39,11 @@ namespace kvq {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-using sgpr_f32 = const float __attribute__((address_space(4)))*;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kStep = 32;   // tokens per step of the quantized loop
@@ -60,38 +61,19 @@ constexpr int kCostT = 5;
 __device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 __device__ inline uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
-// Maximum / sum over the 64 lanes, result in every lane.
-__device__ inline float wave_max(float v) {
-  v = fmaxf(v, xor_lane<1>(v));
-  v = fmaxf(v, xor_lane<2>(v));
-  v = fmaxf(v, xor_lane<4>(v));
-  v = fmaxf(v, xor_lane<8>(v));
-  v = fmaxf(v, xor_lane<16>(v));
-  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  return fmaxf(lo, hi);
-}
-__device__ inline float wave_sum(float v) {
-  v += xor_lane<1>(v);
-  v += xor_lane<2>(v);
-  v += xor_lane<4>(v);
-  v += xor_lane<8>(v);
-  v += xor_lane<16>(v);
-  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  return lo + hi;
-}
+// Larger of two scores; no NaN handling (scores are finite or -inf).
+__device__ inline float fmax_fast(float a, float b) { return a > b ? a : b; }
 
 // Rotation by N lanes inside each row of 16 lanes (DPP row_ror).
 template <int N>
 __device__ inline float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xF, 0xF, false));
 }
 __device__ inline float row16_max(float v) {
-  v = fmaxf(v, row_ror<8>(v));
-  v = fmaxf(v, row_ror<4>(v));
-  v = fmaxf(v, row_ror<2>(v));
-  return fmaxf(v, row_ror<1>(v));
+  v = fmax_fast(v, row_ror<8>(v));
+  v = fmax_fast(v, row_ror<4>(v));
+  v = fmax_fast(v, row_ror<2>(v));
+  return fmax_fast(v, row_ror<1>(v));
 }
 __device__ inline float row16_sum(float v) {
   v += row_ror<8>(v);
@@ -194,17 +176,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   constexpr int RKP = padded_row_bytes(D, KB);
   constexpr int VTB = v_tile_bytes(D, VB);
   constexpr int QPS = qp_stride(D);
-  constexpr int LPRV = D / 8;           // tail P.V: lanes per token
-  constexpr int NSLOT = 64 / LPRV;      // tail P.V: tokens in flight
-  constexpr int TPS = 64 / NSLOT;
-  constexpr int WROW = 48;              // fp16 per LDS weight row: 32 tokens + pad
+  // LDS weight rows of 32 tokens (+ pad), 16-bit: row 8*j + h holds head h's
+  // weights for V block j; the tail keeps the low bf16 parts of its weights
+  // in rows LOROW + h; row ZROW stays zero (A rows 8..15 of quantized steps).
+  constexpr int WROW = 48;
+  constexpr int LOROW = 8 * NB;
+  constexpr int ZROW = 8 * NB + 8;
   using Regs = StepRegs<D, KB, VB>;
 
-  __shared__ __align__(16) _Float16 wl[NB][8][WROW];
-  __shared__ float alds[16];
-  __shared__ float mls[G][2];
-  __shared__ __align__(16) float accl[G][D];
-  __shared__ float plds[G][64];
+  __shared__ __align__(16) uint16_t wl[(8 * NB + 9) * WROW];
+  __shared__ __align__(16) float alds[16];
 
   const int lane = threadIdx.x;
   const int col = lane & 15;
@@ -236,13 +217,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   const int qa = q_tiles(c0) * kTile, qb = min(nq, q_tiles(c1) * kTile);
   const int ta = nq + t_tiles(c0) * kTile, tb = min(n, nq + t_tiles(c1) * kTile);
   const size_t unit = (size_t)b * a.Hkv + g;
-
-  const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
-  const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * NB;
-  const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
-  const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * NB;
   const uint8_t* qp0 = a.qp + ((size_t)b * a.Hq + h0) * QPS;
 
+  for (int i = lane; i < WROW; i += 64) wl[ZROW * WROW + i] = 0;
   if (lane < 16) alds[lane] = 1.f;
 
   // this lane's score heads (Q.K output rows 4r..4r+3 = hi/lo of hA, hB)
@@ -253,8 +230,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
 #pragma unroll
   for (int i = 0; i < NN; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Online softmax over this lane's scores (log2 units, -inf when masked).
+  // The running maxima only move, and the accumulators are only rescaled,
+  // when some score exceeds them (a wave-uniform branch); every weight stays
+  // at most 1.
+  auto softmax = [&](const float (&xA)[2], const float (&xB)[2], float (&pA)[2], float (&pB)[2]) {
+    const bool up = xA[0] > mA || xA[1] > mA || xB[0] > mB || xB[1] > mB;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float nA = fmax_fast(mA, row16_max(fmax_fast(xA[0], xA[1])));
+      const float nB = fmax_fast(mB, row16_max(fmax_fast(xB[0], xB[1])));
+      const float aA = nA > mA ? __builtin_amdgcn_exp2f(mA - nA) : 1.f;
+      const float aB = nB > mB ? __builtin_amdgcn_exp2f(mB - nB) : 1.f;
+      mA = nA;
+      mB = nB;
+      lA *= aA;
+      lB *= aB;
+      __syncthreads();
+      if (col == 0) {
+        alds[hA] = aA;
+        alds[hB] = aB;
+        alds[8 + hA] = aA;
+        alds[8 + hB] = aB;
+      }
+      __syncthreads();
+      const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]);
+#pragma unroll
+      for (int i = 0; i < NN; ++i) acc[i] *= al;
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      pA[m] = __builtin_amdgcn_exp2f(xA[m] - mA);
+      pB[m] = __builtin_amdgcn_exp2f(xB[m] - mB);
+    }
+    lA += pA[0] + pA[1];
+    lB += pB[0] + pB[1];
+  };
+
   // ------------------------------------------------ quantized positions
   if (qa < qb) {
+    const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
+    const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * NB;
+    const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
+    const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * NB;
     // A operand of Q.K: row col = head col/2, high (even) or low (odd) bytes
     long qop[NB];
     {
@@ -336,22 +353,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
 
     auto compute_step = [&](const Regs& R, int s0) {
       // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements
-      i4_t dq[2 * NB];
+      float sA[2] = {0.f, 0.f}, sB[2] = {0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-          dq[m * NB + j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+        for (int m = 0; m < 2; ++m) {
+          const i4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
               qop[j], k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi), i4_t{0, 0, 0, 0}, 0, 0, 0);
-      }
-      float sA[2], sB[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        sA[m] = 0.f;
-        sB[m] = 0.f;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const i4_t d = dq[m * NB + j];
           int vA = (d[0] << 8) + d[1];
           int vB = (d[2] << 8) + d[3];
           if constexpr (KB != 8) {
@@ -363,9 +371,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
           sB[m] = __builtin_fmaf(ks, (float)vB, sB[m]);
         }
       }
-      // online softmax (log2 units); masked tokens score -inf
       bool valid[2];
-      float xA[2], xB[2];
+      float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         valid[m] = s0 + 16 * m + col < qb;
@@ -374,34 +381,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
         xA[m] = valid[m] && okA ? ya : -INFINITY;
         xB[m] = valid[m] && okB ? yb : -INFINITY;
       }
-      const float nA = fmaxf(mA, row16_max(fmaxf(xA[0], xA[1])));
-      const float nB = fmaxf(mB, row16_max(fmaxf(xB[0], xB[1])));
-      if (__builtin_amdgcn_ballot_w64(nA > mA || nB > mB) != 0) {
-        const float aA = nA > mA ? __builtin_amdgcn_exp2f(mA - nA) : 1.f;
-        const float aB = nB > mB ? __builtin_amdgcn_exp2f(mB - nB) : 1.f;
-        mA = nA;
-        mB = nB;
-        lA *= aA;
-        lB *= aB;
-        __syncthreads();
-        if (col == 0) {
-          alds[hA] = aA;
-          alds[hB] = aB;
-        }
-        __syncthreads();
-        const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]);
-#pragma unroll
-        for (int i = 0; i < NN; ++i) acc[i] *= al;
-      }
-      float pA[2], pB[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        pA[m] = __builtin_amdgcn_exp2f(xA[m] - mA);
-        pB[m] = __builtin_amdgcn_exp2f(xB[m] - mB);
-      }
-      lA += pA[0] + pA[1];
-      lB += pB[0] + pB[1];
+      softmax(xA, xB, pA, pB);
       // weights p * scale_v in fp16, moved to the A-operand layout via LDS
+      // (rows of heads >= G receive values nobody reads back into results)
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -409,20 +391,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
         for (int m = 0; m < 2; ++m) {
           const float vs = half_of(R.vs[m][j / 2], j % 2);
           const int t = 16 * m + col;
-          if (okA) wl[j][hA][t] = valid[m] ? (_Float16)(pA[m] * vs) : (_Float16)0.f;
-          if (okB) wl[j][hB][t] = valid[m] ? (_Float16)(pB[m] * vs) : (_Float16)0.f;
+          const _Float16 wA = valid[m] ? (_Float16)(pA[m] * vs) : (_Float16)0.f;
+          const _Float16 wB = valid[m] ? (_Float16)(pB[m] * vs) : (_Float16)0.f;
+          wl[(8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, wA);
+          wl[(8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, wB);
         }
       }
       __syncthreads();
-      const int hr = col < G ? col : 0;
-      h8_t wa[NB];
+      // P.V on the matrix cores: NN products of 16 rows x 32 tokens x 16 elements
 #pragma unroll
-      for (int j = 0; j < NB; ++j) wa[j] = *reinterpret_cast<const h8_t*>(&wl[j][hr][8 * r]);
-      // P.V on the matrix cores: NN products of 16 heads x 32 tokens x 16 elements
+      for (int j = 0; j < NB; ++j) {
+        const int row = col < 8 ? 8 * j + col : ZROW;
+        const h8_t wa = *reinterpret_cast<const h8_t*>(&wl[row * WROW + 8 * r]);
 #pragma unroll
-      for (int i = 0; i < NN; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa[i / 2], v_operand<D, KB, VB>(R, i, magic),
-                                                        acc[i], 0, 0, 0);
+        for (int i = 2 * j; i < 2 * j + 2; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, v_operand<D, KB, VB>(R, i, magic), acc[i], 0, 0, 0);
+      }
     };
 
     Regs ra, rb;
@@ -437,146 +421,115 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
     }
   }
 
-  // quantized-part state, per head, into LDS
-  lA = row16_sum(lA);
-  lB = row16_sum(lB);
-  __syncthreads();
-  if (col == 0) {
-    if (okA) { mls[hA][0] = mA; mls[hA][1] = lA; }
-    if (okB) { mls[hB][0] = mB; mls[hB][1] = lB; }
-  }
-#pragma unroll
-  for (int i = 0; i < NN; ++i) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int h = 4 * r + k;
-      if (h < G) accl[h][16 * i + col] = acc[i][k];
-    }
-  }
-  __syncthreads();
-
   // ------------------------------------------------ bf16 tail positions
-  const int slot = lane / LPRV;
-  const int eg = lane % LPRV;
-  float tm[G], tl[G], tacc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    tm[h] = -INFINITY;
-    tl[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tacc[h][e] = 0.f;
-  }
+  // Same steps on bf16 rows with bf16 matrix products.  The float32 query
+  // and the weights are each split into a high and a low bf16 part, so the
+  // products carry about 16 significant bits: query parts are A rows 2h /
+  // 2h+1 of Q.K, weight parts are A rows h / 8+h of P.V (rows 8..15 of the
+  // accumulators are added to rows 0..7 at the end).  K rows come straight
+  // from the ring; each lane gathers its element of 8 V rows.
   if (ta < tb) {
     const uint16_t* ktl = a.k_tail + unit * (size_t)T * D;
     const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;
-    for (int t0 = ta; t0 < tb; t0 += kTile) {
-      const int t = t0 + lane;
-      const bool valid = t < tb;
-      const int sl = (valid ? t : t0) % T;
-      const uint16_t* krow = ktl + (size_t)sl * D;
-      const uint8_t* qbase = qp0;
-      asm volatile("" : "+s"(qbase));
-      float s[G];
+    bf8_t qt[NB];
+    {
+      const bool qrow = col < 2 * G;
+      const float* qr = reinterpret_cast<const float*>(qp0 + (size_t)(col / 2) * QPS + 4 * D) + 8 * r;
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = 0.f;
+      for (int j = 0; j < NB; ++j) {
 #pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 8 * c);
-        const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
-        float kf[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          kf[2 * k] = __uint_as_float(w4[k] << 16);
-          kf[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const sgpr_f32 qr = (sgpr_f32)(qbase + (size_t)h * QPS + 4 * D);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[h] = __builtin_fmaf(qr[8 * c + e], kf[e], s[h]);
-        }
-      }
-      float p[G];
-      bool need = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float cs = *(sgpr_f32)(qbase + (size_t)h * QPS + 2 * D + D / 8 + 4);
-        s[h] = valid ? s[h] * cs : -INFINITY;
-        need |= s[h] > tm[h];
-      }
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float mn = fmaxf(tm[h], wave_max(s[h]));
-          const float alpha = mn > tm[h] ? __builtin_amdgcn_exp2f(tm[h] - mn) : 1.f;
-          tm[h] = mn;
-          tl[h] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) tacc[h][e] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        p[h] = __builtin_amdgcn_exp2f(s[h] - tm[h]);
-        tl[h] += p[h];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int h = 0; h < G; ++h) plds[h][lane] = p[h];
-      __syncthreads();
-#pragma unroll 4
-      for (int k = 0; k < TPS; ++k) {
-        const int tk = k * NSLOT + slot;
-        const int tt = t0 + tk;
-        const int sv = (tt < tb ? tt : t0) % T;
-        const uint4 vv = *reinterpret_cast<const uint4*>(vtl + (size_t)sv * D + 8 * eg);
-        const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-        float vf[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          vf[2 * q] = __uint_as_float(w4[q] << 16);
-          vf[2 * q + 1] = __uint_as_float(w4[q] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float ph = plds[h][tk];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) tacc[h][e] = __builtin_fmaf(ph, vf[e], tacc[h][e]);
+        for (int e = 0; e < 8; ++e) {
+          const float f = qrow ? qr[kBlock * j + e] : 0.f;
+          const uint32_t hi = f32_to_bf16_bits(f);
+          const uint32_t lo = f32_to_bf16_bits(f - __uint_as_float(hi << 16));
+          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)((col & 1) ? lo : hi));
         }
       }
     }
+    const float csA = okA ? *reinterpret_cast<const float*>(qp0 + (size_t)hA * QPS + 2 * D + D / 8 + 4) : 0.f;
+    const float csB = okB ? *reinterpret_cast<const float*>(qp0 + (size_t)hB * QPS + 2 * D + D / 8 + 4) : 0.f;
+    for (int s0 = ta; s0 < tb; s0 += kStep) {
+      f4_t d[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int h = 0; h < G; ++h) tl[h] = wave_sum(tl[h]);
+      for (int m = 0; m < 2; ++m) {
+        const int tok = s0 + 16 * m + col;
+        const uint16_t* krow = ktl + (size_t)((tok < tb ? tok : ta) % T) * D + 8 * r;
 #pragma unroll
-    for (int sft = LPRV; sft < 64; sft <<= 1) {
+        for (int j = 0; j < NB; ++j)
+          d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt[j], *reinterpret_cast<const bf8_t*>(krow + kBlock * j),
+                                                          d[m], 0, 0, 0);
+      }
+      bool valid[2];
+      float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int m = 0; m < 2; ++m) {
+        valid[m] = s0 + 16 * m + col < tb;
+        float ya = (d[m][0] + d[m][1]) * csA, yb = (d[m][2] + d[m][3]) * csB;
+        asm volatile("" : "+v"(ya), "+v"(yb));
+        xA[m] = valid[m] && okA ? ya : -INFINITY;
+        xB[m] = valid[m] && okB ? yb : -INFINITY;
+      }
+      softmax(xA, xB, pA, pB);
+      __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tacc[h][e] += __shfl_xor(tacc[h][e], sft);
+      for (int m = 0; m < 2; ++m) {
+        const int t = 16 * m + col;
+        const float wA = valid[m] ? pA[m] : 0.f;
+        const float wB = valid[m] ? pB[m] : 0.f;
+        const uint32_t hiA = f32_to_bf16_bits(wA), hiB = f32_to_bf16_bits(wB);
+        wl[hA * WROW + t] = (uint16_t)hiA;
+        wl[hB * WROW + t] = (uint16_t)hiB;
+        wl[(LOROW + hA) * WROW + t] = (uint16_t)f32_to_bf16_bits(wA - __uint_as_float(hiA << 16));
+        wl[(LOROW + hB) * WROW + t] = (uint16_t)f32_to_bf16_bits(wB - __uint_as_float(hiB << 16));
+      }
+      __syncthreads();
+      const int row = col < 8 ? col : LOROW + col - 8;
+      const bf8_t wa = *reinterpret_cast<const bf8_t*>(&wl[row * WROW + 8 * r]);
+      size_t voff[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int tok = s0 + 8 * r + k;
+        voff[k] = (size_t)((tok < tb ? tok : ta) % T) * D + col;
+      }
+#pragma unroll
+      for (int i = 0; i < NN; ++i) {
+        bf8_t vb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vb[k] = __builtin_bit_cast(__bf16, vtl[voff[k] + 16 * i]);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, vb, acc[i], 0, 0, 0);
       }
     }
   }
 
   // ------------------------------------------------ partial results
-  const size_t row0 = ((size_t)b * a.Hq + h0) * a.S + split;
-  if (lane < LPRV) {
+  // rows h and 8+h of the accumulators belong to head h
+  lA = row16_sum(lA);
+  lB = row16_sum(lB);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mq = mls[h][0], lq = mls[h][1];
-      const float M = fmaxf(mq, tm[h]);
-      const float aq = mq > -INFINITY ? __builtin_amdgcn_exp2f(mq - M) : 0.f;
-      const float at = tm[h] > -INFINITY ? __builtin_amdgcn_exp2f(tm[h] - M) : 0.f;
-      const float4 q0 = *reinterpret_cast<const float4*>(&accl[h][8 * eg]);
-      const float4 q1 = *reinterpret_cast<const float4*>(&accl[h][8 * eg + 4]);
-      float4* dst = reinterpret_cast<float4*>(a.part_acc + (row0 + (size_t)h * a.S) * D + 8 * eg);
-      dst[0] = make_float4(q0.x * aq + tacc[h][0] * at, q0.y * aq + tacc[h][1] * at,
-                           q0.z * aq + tacc[h][2] * at, q0.w * aq + tacc[h][3] * at);
-      dst[1] = make_float4(q1.x * aq + tacc[h][4] * at, q1.y * aq + tacc[h][5] * at,
-                           q1.z * aq + tacc[h][6] * at, q1.w * aq + tacc[h][7] * at);
-      if (lane == 0) {
-        a.part_ml[(row0 + (size_t)h * a.S) * 2] = M;
-        a.part_ml[(row0 + (size_t)h * a.S) * 2 + 1] = lq * aq + tl[h] * at;
+  for (int i = 0; i < NN; ++i) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[i][k] += __shfl_xor(acc[i][k], 32);
+  }
+  const size_t row0 = ((size_t)b * a.Hq + h0) * a.S + split;
+  if (r < 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int h = 4 * r + k;
+      if (h < G) {
+        float* dst = a.part_acc + (row0 + (size_t)h * a.S) * D + col;
+#pragma unroll
+        for (int i = 0; i < NN; ++i) dst[16 * i] = acc[i][k];
       }
+    }
+  }
+  if (col == 0) {
+    if (okA) {
+      a.part_ml[(row0 + (size_t)hA * a.S) * 2] = mA;
+      a.part_ml[(row0 + (size_t)hA * a.S) * 2 + 1] = lA;
+    }
+    if (okB) {
+      a.part_ml[(row0 + (size_t)hB * a.S) * 2] = mB;
+      a.part_ml[(row0 + (size_t)hB * a.S) * 2 + 1] = lB;
     }
   }
 }
