@@ -22,7 +22,7 @@ namespace {
 
 using namespace kvq;
 
-constexpr int kTargetWaves = 4096;   // split-K waves per decode launch
+constexpr int kTargetWaves = 2048;   // split-K waves per decode launch: two per SIMD
 constexpr int kMaxSplits = 1024;
 
 thread_local hipEvent_t g_ev_before = nullptr;
