@@ -7,9 +7,10 @@ heads, head_dim 128, 65536 cached tokens, K 8-bit / V 4-bit 32-element blocks
 with fp16 scales, newest 1024 tokens in a bf16 tail, Hadamard-128 rotation.
 
 Prints one JSON line.  `value` is cache GB/s over the full step (algorithmic
-cache bytes read by the attention / step time).  `roofline` reports the
-split-K attention kernel alone, timed with HIP events recorded on the call's
-stream around that kernel.  `cpu_baseline` times the CPU oracle's decode
+cache bytes read by the attention / step time, over the timed steps).
+`roofline` reports the split-K attention kernel alone, timed with HIP events
+that the library records on the call's stream around that kernel during a
+second run of as many steps (the event records stay out of the timed loop).  `cpu_baseline` times the CPU oracle's decode
 attention on a bounded sample of (sequence, KV head) units of the same cache.
 
   python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
@@ -167,7 +168,10 @@ def main():
     torch.cuda.set_device(0)
     w = workloads.workload(args.workload)
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
-    total_steps = args.warmup + args.steps
+    # warm-up, timed steps, then as many steps again with HIP events around
+    # the split kernel (kept out of the timed loop: event records sit between
+    # kernels on the stream)
+    total_steps = args.warmup + 2 * args.steps
     max_ctx = n + total_steps + 64
     cfg = kvq.kvq_config(B, Hkv, d, max_ctx, w["k_bits"], w["v_bits"], w["tail"])
     cache = kvq.KVCache(cfg, dev)
@@ -213,31 +217,37 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
 
-    def step(s):
+    def step(s, events):
         kvq.kvq_rotate_quantize_append(cfg, cache, ks[s], vs[s], lens)
         for b in range(B):
             lens[b] += 1
-        kvq.kvq_profile_decode_events(ev[s][0], ev[s][1])
+        if events:
+            kvq.kvq_profile_decode_events(ev[s][0], ev[s][1])
         kvq.kvq_decode_attention(cfg, cache, qs[s], lens, out=out, workspace=ws)
 
     step_bytes = []
     for s in range(args.warmup):
-        step(s)
+        step(s, False)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        step(s)
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s, False)
         step_bytes.append(cache_bytes_per_step(w, lens))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    kern_bytes = []
+    for s in range(args.warmup + args.steps, total_steps):
+        step(s, True)
+        kern_bytes.append(cache_bytes_per_step(w, lens))
+    torch.cuda.synchronize()
     kvq.kvq_profile_decode_events(None, None)
     assert torch.isfinite(out).all().item(), "non-finite attention output"
 
     ms_step = elapsed / args.steps * 1e3
     avg_bytes = float(np.mean(step_bytes))
-    kern_ms = [kvq.kernel_elapsed_ms(ev[s][0], ev[s][1]) for s in range(args.warmup, total_steps)]
+    kern_ms = [kvq.kernel_elapsed_ms(ev[s][0], ev[s][1]) for s in range(args.warmup + args.steps, total_steps)]
     kern_avg_ms = float(np.mean(kern_ms))
-    achieved = avg_bytes / (kern_avg_ms * 1e-3) / 1e9
+    achieved = float(np.mean(kern_bytes)) / (kern_avg_ms * 1e-3) / 1e9
     value = avg_bytes / (ms_step * 1e-3) / 1e9
     log("step %.1f us, attention kernel %.1f us (median %.1f), %.0f GB/s kernel, %.0f GB/s step"
         % (ms_step * 1e3, kern_avg_ms * 1e3, float(np.median(kern_ms)) * 1e3, achieved, value))

@@ -7,7 +7,9 @@
 // context KLD results") or, for the newest tail_len positions, stored in the
 // bf16 precision tail (aitrends.kr article 92204, glossary "Precision Tail").
 //
-// An append of n_new tokens to a sequence of length len runs two launches:
+// An append of n_new tokens to a sequence of length len runs in two steps
+// (two launches, or one block per (sequence, KV head, plane) with a barrier
+// between the steps when n_new is small):
 //  1. quant: positions [q0, q1) become quantized, where q0/q1 are the first
 //     non-tail position before/after the append (q0 = len, q1 = len + n_new
 //     without a tail).  A position below len is read back from its tail slot
@@ -162,25 +164,36 @@ __device__ inline void store_v_item(uint8_t* tile, int item, uint64_t u, uint32_
   }
 }
 
+// Positions [q0, q1) that become quantized and the first position of the
+// tail after the append of sequence b.
+struct AppendRange {
+  int len, n1, q0, q1, t0;
+};
+__device__ inline AppendRange append_range(const AppendArgs& a, int b) {
+  AppendRange r;
+  r.len = a.len[b];
+  r.n1 = r.len + a.n_new;
+  const int T = a.T;
+  r.q0 = T > 0 ? max(0, r.len - T) : r.len;
+  r.q1 = T > 0 ? max(0, r.n1 - T) : r.n1;
+  r.t0 = max(r.len, r.n1 - T);
+  return r;
+}
+
+// Quantize the positions of block bx of [q0 & ~7, q1) (RPB per block) for
+// plane pl of (b, g).  Called by all 256 threads; contains barriers.
 template <int D>
-__global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a) {
+__device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, uint8_t* vlds) {
   constexpr int LPR = D / kBlock;
   constexpr int RPB = 256 / LPR;   // positions per block, a multiple of 8
   constexpr int NGRP = RPB / 8;
-  __shared__ __align__(16) uint8_t vlds[NGRP * D * 8];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = tid % LPR;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z >> 1;
-  const int pl = blockIdx.z & 1;
-  const int len = a.len[b];
+  const AppendRange rg = append_range(a, b);
+  const int len = rg.len, q0 = rg.q0, q1 = rg.q1;
   const int T = a.T;
-  const int n1 = len + a.n_new;
-  const int q0 = T > 0 ? max(0, len - T) : len;
-  const int q1 = T > 0 ? max(0, n1 - T) : n1;
-  const int blk0 = (q0 & ~7) + blockIdx.x * RPB;
+  const int blk0 = (q0 & ~7) + bx * RPB;
   if (blk0 >= q1) return;                       // uniform over the block
   const int rho = tid / LPR;
   const int p = blk0 + rho;
@@ -246,21 +259,19 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a) {
   }
 }
 
+// Rotate the new positions of block bx of [t0, n1) and write them to their
+// tail slots (plane pl of (b, g)).
 template <int D>
-__global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
+__device__ void tail_part(const AppendArgs& a, int bx, int g, int b, int pl) {
   constexpr int LPR = D / kBlock;
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = tid % LPR;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z >> 1;
-  const int pl = blockIdx.z & 1;
-  const int len = a.len[b];
+  const AppendRange rg = append_range(a, b);
+  const int len = rg.len, n1 = rg.n1;
   const int T = a.T;
-  const int n1 = len + a.n_new;
-  const int t0 = max(len, n1 - T);
-  const int p = t0 + blockIdx.x * RPB + tid / LPR;
+  const int p = rg.t0 + bx * RPB + tid / LPR;
   const bool active = p < n1;
   const int Hkv = a.Hkv;
 
@@ -287,8 +298,35 @@ __global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
 }
 
 template <int D>
+__global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a) {
+  __shared__ __align__(16) uint8_t vlds[256 * kBlock];
+  quant_part<D>(a, blockIdx.x, blockIdx.y, blockIdx.z >> 1, blockIdx.z & 1, vlds);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
+  tail_part<D>(a, blockIdx.x, blockIdx.y, blockIdx.z >> 1, blockIdx.z & 1);
+}
+
+// Appends small enough for one block per (b, g, plane): quantize, then (after
+// a barrier, so every displaced slot has been read) write the tail.
+template <int D>
+__global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
+  __shared__ __align__(16) uint8_t vlds[256 * kBlock];
+  const int g = blockIdx.y, b = blockIdx.z >> 1, pl = blockIdx.z & 1;
+  quant_part<D>(a, 0, g, b, pl, vlds);
+  __syncthreads();
+  if (a.T > 0) tail_part<D>(a, 0, g, b, pl);
+}
+
+template <int D>
 hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
   constexpr int RPB = 256 / (D / kBlock);
+  if (a.n_new <= RPB - 7) {
+    // [q0 & ~7, q1) spans at most n_new + 7 positions and the tail at most n_new
+    hipLaunchKernelGGL(append_small_kernel<D>, dim3(1, a.Hkv, 2 * B), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   int quant_blocks = 0;
   for (int b = 0; b < B; ++b) {
     const int len = a.len[b], n1 = len + a.n_new;

@@ -177,7 +177,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   constexpr int NSW = (NB + 1) / 2;
   constexpr int RKP = padded_row_bytes(D, KB);
   constexpr int VTB = v_tile_bytes(D, VB);
-  constexpr int QPS = qp_stride(D);
   // LDS weight rows of 32 tokens (+ pad), 16-bit: row 8*j + h holds head h's
   // weights for V block j; the tail keeps the low bf16 parts of its weights
   // in rows LOROW + h; row ZROW stays zero (A rows 8..15 of quantized steps).
@@ -219,7 +218,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   const int qa = q_tiles(c0) * kTile, qb = min(nq, q_tiles(c1) * kTile);
   const int ta = nq + t_tiles(c0) * kTile, tb = min(n, nq + t_tiles(c1) * kTile);
   const size_t unit = (size_t)b * a.Hkv + g;
-  const uint8_t* qp0 = a.qp + ((size_t)b * a.Hq + h0) * QPS;
 
   for (int i = lane; i < WROW; i += 64) wl[ZROW * WROW + i] = 0;
   if (lane < 16) alds[lane] = 1.f;
@@ -231,6 +229,78 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   f4_t acc[NN];
 #pragma unroll
   for (int i = 0; i < NN; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Query of this lane's A row in registers: row col < 2G is head h0 + col/2;
+  // the lane holds elements 32j + 8r + i (j < NB, i < 8), rotated in float32
+  // with the butterfly stages in the order h = 1, 2, 4, ..., D/2 (h = 8, 16
+  // exchange values with lanes 16 and 32 apart).  Rows >= 2G read head 0.
+  auto load_query = [&](float (&f)[NB][8]) {
+    const int hq = col < 2 * G ? col / 2 : 0;
+    const size_t off = ((size_t)b * a.Hq + h0 + hq) * D + 8 * r;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (a.q_dtype == KVQ_BF16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off + kBlock * j);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          f[j][2 * k] = __uint_as_float(w4[k] << 16);
+          f[j][2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+        }
+      } else {
+        const float4* v = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off + kBlock * j);
+        const float4 x0 = v[0], x1 = v[1];
+        f[j][0] = x0.x; f[j][1] = x0.y; f[j][2] = x0.z; f[j][3] = x0.w;
+        f[j][4] = x1.x; f[j][5] = x1.y; f[j][6] = x1.z; f[j][7] = x1.w;
+      }
+    }
+    if (!a.rotate_k) return;
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if ((i & h) == 0) {
+            const float u = f[j][i], v = f[j][i + h];
+            f[j][i] = u + v;
+            f[j][i + h] = u - v;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh <<= 1) {
+      const uint32_t flip = (lane & sh) ? 0x80000000u : 0u;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float y = __shfl_xor(f[j][i], sh);
+          f[j][i] = y + __uint_as_float(__float_as_uint(f[j][i]) ^ flip);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 1; h < NB; h <<= 1) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if ((j & h) == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float u = f[j][i], v = f[j + h][i];
+            f[j][i] = u + v;
+            f[j + h][i] = u - v;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[j][i] = f[j][i] * a.cd;
+    }
+  };
 
   // Online softmax over this lane's scores (log2 units, -inf when masked).
   // The running maxima only move, and the accumulators are only rescaled,
@@ -274,24 +344,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
     const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * NB;
     const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
     const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * NB;
-    // A operand of Q.K: row col = head col/2, high (even) or low (odd) bytes
+    // A operand of Q.K: the rotated query in 16-bit fixed point (step
+    // amax / 32639 per head), high bytes in even rows, low bytes in odd rows;
+    // 4/5-bit codes widen to bytes in the order 0,2,4,6,1,3,5,7 of each group
+    // of 8, so the query bytes follow that order.  Offset-binary codes need a
+    // per-block correction -offset * sum(q_int), applied with the block scale.
     long qop[NB];
-    {
-      const bool qrow = col < 2 * G;
-      const uint8_t* qrow_p = qp0 + (size_t)(col / 2) * QPS + (col % 2) * D + 8 * r;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) qop[j] = qrow ? *reinterpret_cast<const long*>(qrow_p + kBlock * j) : 0;
-    }
-    const float ckA = okA ? *reinterpret_cast<const float*>(qp0 + (size_t)hA * QPS + 2 * D + D / 8) : 0.f;
-    const float ckB = okB ? *reinterpret_cast<const float*>(qp0 + (size_t)hB * QPS + 2 * D + D / 8) : 0.f;
+    float ckA, ckB;
     int corrA[KB == 8 ? 1 : NB], corrB[KB == 8 ? 1 : NB];
-    if constexpr (KB != 8) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        corrA[j] = okA ? reinterpret_cast<const int*>(qp0 + (size_t)hA * QPS + 2 * D)[j] : 0;
-        corrB[j] = okB ? reinterpret_cast<const int*>(qp0 + (size_t)hB * QPS + 2 * D)[j] : 0;
-      }
-    }
     // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
     // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word
     const uint32_t rot_lo = (uint32_t)(2 * r + 28) & 31u;   // rotate left by 4 - 2r
@@ -412,7 +472,54 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
     };
 
     Regs ra, rb;
-    load_step(ra, qa);
+    load_step(ra, qa);   // in flight while the query operands are built
+    {
+      float f[NB][8];
+      load_query(f);
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[j][i]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float step = amax > 0.f ? amax / 32639.0f : 1.0f;
+      const float inv = 1.0f / step;
+      const float ck = step * a.sm_scale * kLog2e;
+      ckA = __shfl(ck, 4 * r);
+      ckB = __shfl(ck, 4 * r + 2);
+      ckA = okA ? ckA : 0.f;
+      ckB = okB ? ckB : 0.f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        int v[8];
+        int bsum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          int x = (int)rintf(f[j][i] * inv);
+          x = x > 32639 ? 32639 : (x < -32639 ? -32639 : x);
+          v[i] = x;
+          bsum += x;
+        }
+        uint64_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = KB == 8 ? i : (i < 4 ? 2 * i : 2 * (i - 4) + 1);
+          const int hi = (v[e] + 128) >> 8;
+          const int byte = (col & 1) ? v[e] - 256 * hi : hi;
+          w |= (uint64_t)(uint8_t)(int8_t)byte << (8 * i);
+        }
+        qop[j] = col < 2 * G ? (long)w : 0;
+        if constexpr (KB != 8) {
+          bsum += __shfl_xor(bsum, 16);
+          bsum += __shfl_xor(bsum, 32);
+          const int corr = -(1 << (KB - 1)) * bsum;
+          corrA[j] = okA ? __shfl(corr, 4 * r) : 0;
+          corrB[j] = okB ? __shfl(corr, 4 * r + 2) : 0;
+        }
+      }
+    }
     for (int s = qa; s < qb; s += 2 * kStep) {
       const int s1 = s + kStep;
       load_step(rb, min(s1, last));
@@ -435,21 +542,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
     const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;
     bf8_t qt[NB];
     {
-      const bool qrow = col < 2 * G;
-      const float* qr = reinterpret_cast<const float*>(qp0 + (size_t)(col / 2) * QPS + 4 * D) + 8 * r;
+      float f[NB][8];
+      load_query(f);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float f = qrow ? qr[kBlock * j + e] : 0.f;
-          const uint32_t hi = f32_to_bf16_bits(f);
-          const uint32_t lo = f32_to_bf16_bits(f - __uint_as_float(hi << 16));
-          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)((col & 1) ? lo : hi));
+          const uint32_t hi = f32_to_bf16_bits(f[j][e]);
+          const uint32_t lo = f32_to_bf16_bits(f[j][e] - __uint_as_float(hi << 16));
+          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(col < 2 * G ? ((col & 1) ? lo : hi) : 0u));
         }
       }
     }
-    const float csA = okA ? *reinterpret_cast<const float*>(qp0 + (size_t)hA * QPS + 2 * D + D / 8 + 4) : 0.f;
-    const float csB = okB ? *reinterpret_cast<const float*>(qp0 + (size_t)hB * QPS + 2 * D + D / 8 + 4) : 0.f;
+    const float csA = okA ? a.sm_scale * kLog2e : 0.f;
+    const float csB = okB ? a.sm_scale * kLog2e : 0.f;
     for (int s0 = ta; s0 < tb; s0 += kStep) {
       f4_t d[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll

@@ -1,13 +1,10 @@
-// Decode attention: query preparation, split combination and the table of
-// split-K kernel instantiations.
+// Decode attention: split combination and the table of split-K kernel
+// instantiations.
 //
-// Query preparation rotates each query by the normalized Hadamard matrix
-// (velog.io post "fix KV cache quantization outliers", section "Hadamard
-// rotation": Q is rotated like K so their dot products are unchanged) and
-// converts it into the 16-bit fixed-point form the split kernel consumes.
 // Combination merges the per-split (max, sum, weighted V) triples with the
-// log-sum-exp rule and rotates the result back to the original space (same
-// section: the attention result is inverse-rotated).
+// log-sum-exp rule and rotates the result back to the original space
+// (velog.io post "fix KV cache quantization outliers", section "Hadamard
+// rotation": the attention result is inverse-rotated).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,103 +30,62 @@ DecodeLauncher decode_launcher(int D, int kb, int vb, int gc) {
 
 namespace {
 
-// Byte position of query element e in the K-order layout: 8-bit codes are
-// consumed in natural order; 4/5-bit codes are unpacked per 8-element group
-// into (even elements, odd elements) byte vectors.
-__device__ inline int kbyte_pos(int e, int kbits) {
-  if (kbits == 8) return e;
-  const int w = e / 8, i = (e % 8) / 2, nib = e % 2;
-  return (2 * w + nib) * 4 + i;
-}
-
-template <int D>
-__global__ __launch_bounds__(64) void prep_kernel(PrepArgs a) {
-  __shared__ float q[D];
-  __shared__ int qi[D];
+// Block-wide reductions of a 256-thread block (4 waves).
+__device__ inline float block_max(float v, float* red) {
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
   const int t = threadIdx.x;
-  const int bh = blockIdx.x;     // b * Hq + h
-  for (int e = t; e < D; e += 64) {
-    const size_t off = (size_t)bh * D + e;
-    q[e] = a.dtype == KVQ_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[off])
-                               : static_cast<const float*>(a.q)[off];
-  }
   __syncthreads();
-  if (a.rotate) {
-    for (int h = 1; h < D; h <<= 1) {
-      for (int k = t; k < D / 2; k += 64) {
-        const int i = (k / h) * 2 * h + (k % h);
-        const float u = q[i], v = q[i + h];
-        q[i] = u + v;
-        q[i + h] = u - v;
-      }
-      __syncthreads();
-    }
-    for (int e = t; e < D; e += 64) q[e] = q[e] * a.cd;
-    __syncthreads();
-  }
-  float amax = 0.f;
-  for (int e = t; e < D; e += 64) amax = fmaxf(amax, fabsf(q[e]));
-  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  // 16-bit fixed point: |q_int| <= 127*256 + 127 so both bytes fit in int8
-  const float step = amax > 0.f ? amax / 32639.0f : 1.0f;
-  const float inv = 1.0f / step;
-  uint8_t* out = a.qp + (size_t)bh * qp_stride(D);
-  for (int e = t; e < D; e += 64) {
-    int v = (int)rintf(q[e] * inv);
-    v = v > 32639 ? 32639 : (v < -32639 ? -32639 : v);
-    qi[e] = v;
-    const int hi = (v + 128) >> 8;
-    const int lo = v - hi * 256;
-    const int pos = kbyte_pos(e, a.k_bits);
-    out[pos] = (uint8_t)(int8_t)hi;
-    out[D + pos] = (uint8_t)(int8_t)lo;
-    reinterpret_cast<float*>(out + 4 * D)[e] = q[e];
-  }
+  if ((t & 63) == 0) red[t >> 6] = v;
   __syncthreads();
-  const int offs = a.k_bits == 8 ? 0 : (1 << (a.k_bits - 1));
-  if (t < D / kBlock) {
-    int s = 0;
-    for (int e = 0; e < kBlock; ++e) s += qi[t * kBlock + e];
-    reinterpret_cast<int*>(out + 2 * D)[t] = -offs * s;
-  }
-  if (t == 0) {
-    float* f = reinterpret_cast<float*>(out + 2 * D + D / 8);
-    f[0] = step * a.sm_scale * 1.4426950408889634f;
-    f[1] = a.sm_scale * 1.4426950408889634f;
-  }
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ inline float block_sum(float v, float* red) {
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+  const int t = threadIdx.x;
+  __syncthreads();
+  if ((t & 63) == 0) red[t >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// One 256-thread block per (sequence, query head).  Thread t owns output
-// element t % D and visits the splits s = t / D, t / D + 256/D, ...; the
-// per-split weights 2^(m_s - M) follow the log-sum-exp merge.
+// One 256-thread block per (sequence, query head), log-sum-exp merge of the
+// S split partials: M = max m_s, w_s = 2^(m_s - M), out = sum w_s acc_s /
+// sum w_s l_s, then the inverse rotation.  The weights go to LDS once;
+// thread t then sums element t % D over the splits s = t / D (mod 256 / D)
+// with several loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int P = 256 / D;       // split phases handled in parallel
+  constexpr int U = 4;             // independent partial sums per thread
+  __shared__ float wgt[kMaxSplitsDevice];
   __shared__ float red[256];
   __shared__ float o[D];
   const int t = threadIdx.x;
   const int bh = blockIdx.x;
-  const float* ml = a.part_ml + (size_t)bh * a.S * 2;
-  const float* acc = a.part_acc + (size_t)bh * a.S * D;
+  const int S = a.S;
+  const float* ml = a.part_ml + (size_t)bh * S * 2;
+  const float* acc = a.part_acc + (size_t)bh * S * D;
   float mloc = -INFINITY;
-  for (int s = t; s < a.S; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
-  red[t] = mloc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  const int e = t % D, ph = t / D;
-  float v = 0.f, lsum = 0.f;
-  for (int s = ph; s < a.S; s += P) {
+  for (int s = t; s < S; s += 256) mloc = fmaxf(mloc, ml[2 * s]);
+  const float M = block_max(mloc, red);
+  float lsum = 0.f;
+  for (int s = t; s < S; s += 256) {
     const float m = ml[2 * s];
-    const float wgt = m == -INFINITY ? 0.f : exp2f(m - M);
-    v += wgt * acc[(size_t)s * D + e];
-    lsum += wgt * ml[2 * s + 1];
+    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+    wgt[s] = w;
+    lsum += w * ml[2 * s + 1];
   }
-  red[t] = v;
+  const float L = block_sum(lsum, red);   // its barriers also publish wgt
+  const int e = t % D, ph = t / D;
+  float v[U] = {};
+  int s = ph;
+  for (; s + (U - 1) * P < S; s += U * P) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] += wgt[s + u * P] * acc[(size_t)(s + u * P) * D + e];
+  }
+  for (; s < S; s += P) v[0] += wgt[s] * acc[(size_t)s * D + e];
+  __syncthreads();                        // every thread has read red[0..3]
+  red[t] = (v[0] + v[1]) + (v[2] + v[3]);
   __syncthreads();
   if (t < D) {
     float tot = 0.f;
@@ -137,13 +93,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int k = 0; k < P; ++k) tot += red[t + k * D];
     o[t] = tot;
   }
-  __syncthreads();
-  red[t] = e == 0 ? lsum : 0.f;
-  __syncthreads();
-  float L = 0.f;
-#pragma unroll
-  for (int k = 0; k < P; ++k) L += red[k * D];
-  const float inv = 1.0f / L;
   __syncthreads();
   if (a.rotate) {
     for (int h = 1; h < D; h <<= 1) {
@@ -156,23 +105,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       __syncthreads();
     }
   }
-  const float scale = (a.rotate ? a.cd : 1.0f) * inv;
+  const float scale = (a.rotate ? a.cd : 1.0f) / L;
   if (t < D) a.out[(size_t)bh * D + t] = o[t] * scale;
 }
 
 }  // namespace
-
-hipError_t launch_prep(int D, const PrepArgs& a, int B, hipStream_t s) {
-  (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  const dim3 grid(B * a.Hq);
-  switch (D) {
-    case 64: hipLaunchKernelGGL(prep_kernel<64>, grid, dim3(64), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(prep_kernel<128>, grid, dim3(64), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(prep_kernel<256>, grid, dim3(64), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_combine(int D, const CombineArgs& a, int B, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls

@@ -36,24 +36,6 @@ struct DequantArgs {
 hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
-// Per query head the prep kernel writes kQpStride(D) bytes:
-//   [0, D)          high bytes of the 16-bit fixed-point rotated query,
-//                   in the byte order the K code unpacking produces
-//   [D, 2D)         low bytes, same order
-//   [2D, 2D+D/8)    int32 per block: -offset * sum of the fixed-point query
-//                   (folds offset-binary K codes back to signed codes)
-//   [2D+D/8, +4)    float: fixed-point step * sm_scale * log2(e)
-//   [4D, 8D)        float32 rotated query (used for bf16 tail tokens)
-__host__ __device__ constexpr int qp_stride(int D) { return 8 * D; }
-
-struct PrepArgs {
-  const void* q;             // [B][Hq][D]
-  uint8_t* qp;               // [B][Hq][qp_stride]
-  int32_t Hq, dtype, rotate, k_bits;
-  float cd, sm_scale;
-};
-hipError_t launch_prep(int D, const PrepArgs& a, int B, hipStream_t s);
-
 struct DecodeArgs {
   const uint8_t* k_codes;
   const uint16_t* k_scales;
@@ -61,15 +43,20 @@ struct DecodeArgs {
   const uint16_t* v_scales;
   const uint16_t* k_tail;
   const uint16_t* v_tail;
-  const uint8_t* qp;         // prep output
+  const void* q;             // [B][Hq][D] bf16 or float32, original space
   float* part_ml;            // [B][Hq][S][2]  running max (log2 units), sum
   float* part_acc;           // [B][Hq][S][D]  unnormalised output, rotated space
   int32_t Hkv, Hq, G, n_gchunks, T, cap, S;
+  int32_t q_dtype, rotate_k;
+  float cd, sm_scale;        // fp32(1/sqrt(D)); softmax scale
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
 // Table lookup for (D, k_bits, v_bits, heads per chunk); nullptr if absent.
 DecodeLauncher decode_launcher(int D, int kb, int vb, int gc);
+
+// Largest split count the host schedules (bounds the combine kernel's LDS).
+constexpr int kMaxSplitsDevice = 1024;
 
 struct CombineArgs {
   const float* part_ml;

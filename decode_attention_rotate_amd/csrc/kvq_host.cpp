@@ -23,7 +23,7 @@ namespace {
 using namespace kvq;
 
 constexpr int kTargetWaves = 2048;   // split-K waves per decode launch: two per SIMD
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = kMaxSplitsDevice;
 
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
@@ -96,16 +96,14 @@ int max_splits(const kvq_config& c, int n_q_heads) {
   return (int)std::min<int64_t>(want, tiles);
 }
 
-// Workspace: prep output, then (max, sum) pairs, then partial vectors.
+// Workspace: (max, sum) pairs, then partial vectors, per split.
 struct WsLayout {
-  size_t qp, ml, acc, total;
+  size_t ml, acc, total;
 };
 WsLayout ws_layout(const kvq_config& c, int n_q_heads, int S) {
   WsLayout w;
   const size_t heads = (size_t)c.batch * n_q_heads;
-  w.qp = 0;
-  const size_t qp_bytes = heads * qp_stride(c.head_dim);
-  w.ml = (qp_bytes + 255) / 256 * 256;
+  w.ml = 0;
   const size_t ml_bytes = heads * (size_t)S * 2 * sizeof(float);
   w.acc = w.ml + (ml_bytes + 255) / 256 * 256;
   w.total = w.acc + heads * (size_t)S * c.head_dim * sizeof(float);
@@ -228,17 +226,6 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const float cd = (float)(1.0 / std::sqrt((double)c.head_dim));
 
-  PrepArgs pa;
-  pa.q = q;
-  pa.qp = ws + wl.qp;
-  pa.Hq = n_q_heads;
-  pa.dtype = dtype;
-  pa.rotate = c.rotate_k;
-  pa.k_bits = c.k_bits;
-  pa.cd = cd;
-  pa.sm_scale = sm_scale;
-  if ((st = hip_status(launch_prep(c.head_dim, pa, c.batch, s))) != KVQ_OK) return st;
-
   DecodeArgs da;
   std::memset(&da, 0, sizeof(da));
   da.k_codes = static_cast<const uint8_t*>(cache->k_codes);
@@ -247,7 +234,11 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.v_scales = static_cast<const uint16_t*>(cache->v_scales);
   da.k_tail = static_cast<const uint16_t*>(cache->k_tail);
   da.v_tail = static_cast<const uint16_t*>(cache->v_tail);
-  da.qp = ws + wl.qp;
+  da.q = q;
+  da.q_dtype = dtype;
+  da.rotate_k = c.rotate_k;
+  da.cd = cd;
+  da.sm_scale = sm_scale;
   da.part_ml = reinterpret_cast<float*>(ws + wl.ml);
   da.part_acc = reinterpret_cast<float*>(ws + wl.acc);
   da.Hkv = c.n_kv_heads;
