@@ -7,8 +7,13 @@
 // rotates the result back.  Newest tokens may sit unquantized in a bf16 tail
 // (aitrends.kr article 92204, glossary "Precision Tail").
 //
-// One wave handles one (sequence b, KV head g, chunk of G <= 8 query heads,
-// split of the context) and streams every cache byte of its split once.  The
+// Work unit: one (sequence b, KV head g, chunk of G <= 8 query heads); S
+// waves share a unit and stream each of its cache bytes once.  Workgroups of
+// 8 waves (one per compute unit at 2 waves per SIMD) take contiguous ranges
+// of the unit's quantized tiles, and inside a workgroup each wave takes the
+// next tile from an LDS counter, so waves the compute unit happens to serve
+// less do less of the work.  Each wave keeps one online-softmax state in its
+// own LDS rows and registers and writes one partial.  The
 // G query heads share each K/V row, so both contractions of a step of 32
 // tokens run on the matrix cores (16x16x32 MFMA; lane l owns A row l%16 and
 // B column l%16, k-slots 8*(l/16)..+7, and output rows 4*(l/16)..+3):
@@ -48,12 +53,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kStep = 32;   // tokens per step of the quantized loop
 
-// Relative time of a 64-token tile: quantized codes vs bf16 tail rows (the
-// tail carries 2.5x the bytes and gathers its V operands element by element;
-// the ratio is measured on the 64k-context K8/V4 shape).
-constexpr int kCostQ = 2;
-constexpr int kCostT = 10;
-
 // Occupancy target of the split-K kernel (waves per SIMD); bounds the
 // registers the scheduler may use.
 #ifndef KVQ_SPLIT_WAVES_PER_EU
@@ -61,6 +60,14 @@ constexpr int kCostT = 10;
 #endif
 
 __device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+// Orders this wave's LDS accesses around a point (each wave of the split
+// kernel owns its LDS rows; no other wave waits).
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 __device__ inline uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Larger of two scores; no NaN handling (scores are finite or -inf).
@@ -170,7 +177,7 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t 
 }
 
 template <int D, int KB, int VB, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WAVES_PER_EU))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WAVES_PER_EU))) void decode_split_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
@@ -185,13 +192,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   constexpr int ZROW = 8 * NB + 8;
   using Regs = StepRegs<D, KB, VB>;
 
-  __shared__ __align__(16) uint16_t wl[(8 * NB + 9) * WROW];
-  __shared__ __align__(16) float alds[16];
+  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9) * WROW];
+  __shared__ __align__(16) float alds_all[kGroupWaves][16];
+  __shared__ uint32_t tile_ctr;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int col = lane & 15;
   const int r = lane >> 4;
-  const int split = blockIdx.x;
+  const int split = blockIdx.x * kGroupWaves + wv;   // this wave's partial slot
+  uint16_t* wl = wl_all[wv];
+  float* alds = alds_all[wv];
+  if (threadIdx.x == 0) tile_ctr = 0u;
+  __syncthreads();
   const int g = blockIdx.y / a.n_gchunks;
   const int h0 = g * a.G + (blockIdx.y % a.n_gchunks) * G;
   const int b = blockIdx.z;
@@ -199,24 +212,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
   const int T = a.T;
   const int nt = T > 0 ? min(n, T) : 0;
   const int nq = n - nt;
-  // Work split by cost, not by token count: a 64-token tile of quantized
-  // codes weighs kCostQ, a tile of bf16 tail tokens kCostT.  Split s of S
-  // takes the cost interval [s*C/S, (s+1)*C/S) of this sequence; boundaries
-  // fall on tile edges of each region.
+  // Quantized tiles: workgroup wg of NG takes the contiguous range
+  // [ctq*wg/NG, ctq*(wg+1)/NG) and its waves pull tiles from it one at a
+  // time, so they finish together however the compute unit schedules them.
+  // bf16 tail tiles (few, each worth several quantized tiles) are dealt out
+  // round-robin: tile k to workgroup k mod NG, wave (k / NG) mod kGroupWaves.
   const int ctq = (nq + kTile - 1) / kTile;
   const int ctt = (nt + kTile - 1) / kTile;
-  const int64_t C = (int64_t)kCostQ * ctq + (int64_t)kCostT * ctt;
-  const int64_t c0 = C * split / a.S, c1 = C * (split + 1) / a.S;
-  auto q_tiles = [&](int64_t c) {
-    const int64_t t = c / kCostQ;
-    return (int)(t < ctq ? t : ctq);
-  };
-  auto t_tiles = [&](int64_t c) {
-    const int64_t rr = (c - (int64_t)kCostQ * ctq) / kCostT;
-    return rr <= 0 ? 0 : (int)(rr < ctt ? rr : ctt);
-  };
-  const int qa = q_tiles(c0) * kTile, qb = min(nq, q_tiles(c1) * kTile);
-  const int ta = nq + t_tiles(c0) * kTile, tb = min(n, nq + t_tiles(c1) * kTile);
+  const int NG = (int)gridDim.x;
+  const int wq0 = (int)((int64_t)ctq * blockIdx.x / NG), wq1 = (int)((int64_t)ctq * (blockIdx.x + 1) / NG);
   const size_t unit = (size_t)b * a.Hkv + g;
 
   for (int i = lane; i < WROW; i += 64) wl[ZROW * WROW + i] = 0;
@@ -317,14 +321,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
       mB = nB;
       lA *= aA;
       lB *= aB;
-      __syncthreads();
+      wave_sync();
       if (col == 0) {
         alds[hA] = aA;
         alds[hB] = aB;
         alds[8 + hA] = aA;
         alds[8 + hB] = aB;
       }
-      __syncthreads();
+      wave_sync();
       const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]);
 #pragma unroll
       for (int i = 0; i < NN; ++i) acc[i] *= al;
@@ -338,8 +342,91 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
     lB += pB[0] + pB[1];
   };
 
+  // ------------------------------------------------ bf16 tail positions
+  // Same steps on bf16 rows with bf16 matrix products.  The float32 query
+  // and the weights are each split into a high and a low bf16 part, so the
+  // products carry about 16 significant bits: query parts are A rows 2h /
+  // 2h+1 of Q.K, weight parts are A rows h / 8+h of P.V (rows 8..15 of the
+  // accumulators are added to rows 0..7 at the end).  K rows come straight
+  // from the ring; each lane gathers its element of 8 V rows.
+  const int tk0 = (int)blockIdx.x + NG * wv;
+  if (tk0 < ctt) {
+    const uint16_t* ktl = a.k_tail + unit * (size_t)T * D;
+    const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;
+    bf8_t qt[NB];
+    {
+      float f[NB][8];
+      load_query(f);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t hi = f32_to_bf16_bits(f[j][e]);
+          const uint32_t lo = f32_to_bf16_bits(f[j][e] - __uint_as_float(hi << 16));
+          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(col < 2 * G ? ((col & 1) ? lo : hi) : 0u));
+        }
+      }
+    }
+    const float csA = okA ? a.sm_scale * kLog2e : 0.f;
+    const float csB = okB ? a.sm_scale * kLog2e : 0.f;
+    for (int kt = tk0; kt < ctt; kt += NG * kGroupWaves) {
+    const int ta = nq + kt * kTile, tb = min(n, ta + kTile);
+    for (int s0 = ta; s0 < tb; s0 += kStep) {
+      f4_t d[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int tok = s0 + 16 * m + col;
+        const uint16_t* krow = ktl + (size_t)((tok < tb ? tok : ta) % T) * D + 8 * r;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt[j], *reinterpret_cast<const bf8_t*>(krow + kBlock * j),
+                                                          d[m], 0, 0, 0);
+      }
+      bool valid[2];
+      float xA[2], xB[2], pA[2], pB[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        valid[m] = s0 + 16 * m + col < tb;
+        float ya = (d[m][0] + d[m][1]) * csA, yb = (d[m][2] + d[m][3]) * csB;
+        asm volatile("" : "+v"(ya), "+v"(yb));
+        xA[m] = valid[m] && okA ? ya : -INFINITY;
+        xB[m] = valid[m] && okB ? yb : -INFINITY;
+      }
+      softmax(xA, xB, pA, pB);
+      wave_sync();
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int t = 16 * m + col;
+        const float wA = valid[m] ? pA[m] : 0.f;
+        const float wB = valid[m] ? pB[m] : 0.f;
+        const uint32_t hiA = f32_to_bf16_bits(wA), hiB = f32_to_bf16_bits(wB);
+        wl[hA * WROW + t] = (uint16_t)hiA;
+        wl[hB * WROW + t] = (uint16_t)hiB;
+        wl[(LOROW + hA) * WROW + t] = (uint16_t)f32_to_bf16_bits(wA - __uint_as_float(hiA << 16));
+        wl[(LOROW + hB) * WROW + t] = (uint16_t)f32_to_bf16_bits(wB - __uint_as_float(hiB << 16));
+      }
+      wave_sync();
+      const int row = col < 8 ? col : LOROW + col - 8;
+      const bf8_t wa = *reinterpret_cast<const bf8_t*>(&wl[row * WROW + 8 * r]);
+      size_t voff[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int tok = s0 + 8 * r + k;
+        voff[k] = (size_t)((tok < tb ? tok : ta) % T) * D + col;
+      }
+#pragma unroll
+      for (int i = 0; i < NN; ++i) {
+        bf8_t vb;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vb[k] = __builtin_bit_cast(__bf16, vtl[voff[k] + 16 * i]);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, vb, acc[i], 0, 0, 0);
+      }
+    }
+    }
+  }
+
   // ------------------------------------------------ quantized positions
-  if (qa < qb) {
+  if (wq0 < wq1) {
     const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
     const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * NB;
     const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
@@ -364,7 +451,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
                                    : (uint32_t)(col * kChunk + 4 * r);
     const uint32_t v_off = (uint32_t)(lane * NN * (VB == 8 ? 8 : 4));
     const uint32_t vh_off = (uint32_t)(32 * D + lane * NN);
-    const int last = (qb - 1) / kStep * kStep;
 
     auto load_step = [&](Regs& R, int s0) {
       const int j2 = (s0 / kStep) & 1;
@@ -437,7 +523,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
       float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        valid[m] = s0 + 16 * m + col < qb;
+        valid[m] = s0 + 16 * m + col < nq;
         float ya = sA[m] * ckA, yb = sB[m] * ckB;
         asm volatile("" : "+v"(ya), "+v"(yb));   // selects, not branches
         xA[m] = valid[m] && okA ? ya : -INFINITY;
@@ -446,7 +532,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
       softmax(xA, xB, pA, pB);
       // weights p * scale_v in fp16, moved to the A-operand layout via LDS
       // (rows of heads >= G receive values nobody reads back into results)
-      __syncthreads();
+      wave_sync();
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -459,7 +545,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
           wl[(8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, wB);
         }
       }
-      __syncthreads();
+      wave_sync();
       // P.V on the matrix cores: NN products of 16 rows x 32 tokens x 16 elements
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -471,8 +557,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
       }
     };
 
-    Regs ra, rb;
-    load_step(ra, qa);   // in flight while the query operands are built
+    // Tiles of [wq0, wq1) come from the workgroup's LDS counter, one tile
+    // ahead: the second half of a tile and the first half of the next one
+    // load while the half before computes.
+    auto grab_issue = [&]() {
+      uint32_t v = 0;
+      if (lane == 0) v = atomicAdd(&tile_ctr, 1u);
+      return v;
+    };
+    auto grab_read = [&](uint32_t v) { return wq0 + (int)__builtin_amdgcn_readfirstlane(v); };
+    int t_cur = grab_read(grab_issue());
+    if (t_cur < wq1) {
+      int t_nxt = grab_read(grab_issue());
+      Regs ra, rb;
+      load_step(ra, t_cur * kTile);   // in flight while the query operands are built
     {
       float f[NB][8];
       load_query(f);
@@ -520,91 +618,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
         }
       }
     }
-    for (int s = qa; s < qb; s += 2 * kStep) {
-      const int s1 = s + kStep;
-      load_step(rb, min(s1, last));
-      compute_step(ra, s);
-      if (s1 >= qb) break;
-      load_step(ra, min(s1 + kStep, last));
-      compute_step(rb, s1);
-    }
-  }
-
-  // ------------------------------------------------ bf16 tail positions
-  // Same steps on bf16 rows with bf16 matrix products.  The float32 query
-  // and the weights are each split into a high and a low bf16 part, so the
-  // products carry about 16 significant bits: query parts are A rows 2h /
-  // 2h+1 of Q.K, weight parts are A rows h / 8+h of P.V (rows 8..15 of the
-  // accumulators are added to rows 0..7 at the end).  K rows come straight
-  // from the ring; each lane gathers its element of 8 V rows.
-  if (ta < tb) {
-    const uint16_t* ktl = a.k_tail + unit * (size_t)T * D;
-    const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;
-    bf8_t qt[NB];
-    {
-      float f[NB][8];
-      load_query(f);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t hi = f32_to_bf16_bits(f[j][e]);
-          const uint32_t lo = f32_to_bf16_bits(f[j][e] - __uint_as_float(hi << 16));
-          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(col < 2 * G ? ((col & 1) ? lo : hi) : 0u));
-        }
-      }
-    }
-    const float csA = okA ? a.sm_scale * kLog2e : 0.f;
-    const float csB = okB ? a.sm_scale * kLog2e : 0.f;
-    for (int s0 = ta; s0 < tb; s0 += kStep) {
-      f4_t d[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int tok = s0 + 16 * m + col;
-        const uint16_t* krow = ktl + (size_t)((tok < tb ? tok : ta) % T) * D + 8 * r;
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt[j], *reinterpret_cast<const bf8_t*>(krow + kBlock * j),
-                                                          d[m], 0, 0, 0);
-      }
-      bool valid[2];
-      float xA[2], xB[2], pA[2], pB[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        valid[m] = s0 + 16 * m + col < tb;
-        float ya = (d[m][0] + d[m][1]) * csA, yb = (d[m][2] + d[m][3]) * csB;
-        asm volatile("" : "+v"(ya), "+v"(yb));
-        xA[m] = valid[m] && okA ? ya : -INFINITY;
-        xB[m] = valid[m] && okB ? yb : -INFINITY;
-      }
-      softmax(xA, xB, pA, pB);
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int t = 16 * m + col;
-        const float wA = valid[m] ? pA[m] : 0.f;
-        const float wB = valid[m] ? pB[m] : 0.f;
-        const uint32_t hiA = f32_to_bf16_bits(wA), hiB = f32_to_bf16_bits(wB);
-        wl[hA * WROW + t] = (uint16_t)hiA;
-        wl[hB * WROW + t] = (uint16_t)hiB;
-        wl[(LOROW + hA) * WROW + t] = (uint16_t)f32_to_bf16_bits(wA - __uint_as_float(hiA << 16));
-        wl[(LOROW + hB) * WROW + t] = (uint16_t)f32_to_bf16_bits(wB - __uint_as_float(hiB << 16));
-      }
-      __syncthreads();
-      const int row = col < 8 ? col : LOROW + col - 8;
-      const bf8_t wa = *reinterpret_cast<const bf8_t*>(&wl[row * WROW + 8 * r]);
-      size_t voff[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int tok = s0 + 8 * r + k;
-        voff[k] = (size_t)((tok < tb ? tok : ta) % T) * D + col;
-      }
-#pragma unroll
-      for (int i = 0; i < NN; ++i) {
-        bf8_t vb;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) vb[k] = __builtin_bit_cast(__bf16, vtl[voff[k] + 16 * i]);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, vb, acc[i], 0, 0, 0);
+      while (true) {
+        const uint32_t t_aft_v = grab_issue();
+        load_step(rb, t_cur * kTile + kStep);
+        compute_step(ra, t_cur * kTile);
+        if (t_nxt < wq1) load_step(ra, t_nxt * kTile);
+        compute_step(rb, t_cur * kTile + kStep);
+        const int t_aft = grab_read(t_aft_v);
+        if (t_nxt >= wq1) break;
+        t_cur = t_nxt;
+        t_nxt = t_aft;
       }
     }
   }
@@ -645,7 +668,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WA
 template <int D, int KB, int VB, int G>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G>), grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G>), grid, dim3(64 * kGroupWaves), 0, s, a);
   return hipGetLastError();
 }
 

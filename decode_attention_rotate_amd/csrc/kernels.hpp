@@ -36,6 +36,14 @@ struct DequantArgs {
 hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
+// Waves per workgroup of the split-K kernel.  The waves of a workgroup share
+// one contiguous range of a unit's quantized tiles and take them from an LDS
+// counter; the split count S is a multiple of this.
+#ifndef KVQ_SPLIT_GROUP_WAVES
+#define KVQ_SPLIT_GROUP_WAVES 8
+#endif
+constexpr int kGroupWaves = KVQ_SPLIT_GROUP_WAVES;
+
 struct DecodeArgs {
   const uint8_t* k_codes;
   const uint16_t* k_scales;

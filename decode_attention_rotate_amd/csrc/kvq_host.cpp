@@ -81,7 +81,7 @@ Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * s.nchunk;
   const int tiles = std::max(1, (max_len + kTile - 1) / kTile);
   const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
-  s.S = (int)std::min<int64_t>(want, tiles);
+  s.S = (int)((std::min<int64_t>(want, tiles) + kGroupWaves - 1) / kGroupWaves * kGroupWaves);
   return s;
 }
 
@@ -93,7 +93,7 @@ int max_splits(const kvq_config& c, int n_q_heads) {
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * nchunk;
   const int tiles = std::max(1, (c.max_ctx + kTile - 1) / kTile);
   const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
-  return (int)std::min<int64_t>(want, tiles);
+  return (int)((std::min<int64_t>(want, tiles) + kGroupWaves - 1) / kGroupWaves * kGroupWaves);
 }
 
 // Workspace: (max, sum) pairs, then partial vectors, per split.
@@ -249,7 +249,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.cap = (int32_t)cap_tokens(c);
   da.S = sc.S;
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
-  const dim3 grid(sc.S, c.n_kv_heads * sc.nchunk, c.batch);
+  const dim3 grid(sc.S / kGroupWaves, c.n_kv_heads * sc.nchunk, c.batch);
   if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
   if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
   if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;

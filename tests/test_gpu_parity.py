@@ -158,7 +158,11 @@ def test_decode_fp32_query_and_repeat_calls():
     q = workloads.q_numpy(w)
     a = pair.decode(q, "f32")
     b = pair.decode(q, "f32")
-    assert np.array_equal(a, b)       # deterministic
+    # the waves of a workgroup take tiles dynamically, so the float32
+    # summation order and the running maximum each fp16 weight is rounded
+    # against can change between calls: repeats agree to rounding
+    rel = np.linalg.norm(a - b, axis=-1) / np.linalg.norm(a, axis=-1)
+    assert np.max(rel) <= 1e-4, np.max(rel)
     planes = gpu_planes(pair.cache, pair.cfg)
     errs = attention_errors(a, planes, to_values(q, "f32"), [1100, 1100], pair.cfg)
     assert max(errs.values()) <= TOL
