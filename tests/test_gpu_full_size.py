@@ -1,0 +1,150 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration that
+bench.py times: the cache is filled with 8192-token appends, then decode steps
+append one token and attend.  The oracle checks sampled outputs one by one:
+
+* codes and fp16 scales of sampled 64-token windows of sampled (sequence, KV
+  head) units, bit-exact against the oracle quantizer applied to the same
+  input values (rotation, bf16 rounding when there is a tail, absmax blocks);
+* the bf16 tail rows of those units, bit-exact;
+* the attention outputs of those units' query heads, relative L2 <= 1e-3
+  against the float64 oracle evaluated on the device cache of the unit, after
+  the fill and after a decode step.
+
+Inputs come from the device generators of workloads.py; the windows the oracle
+needs are regenerated and copied to the host."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+import decode_attention_rotate_amd as kvq
+from gpu_common import say
+from oracle import rotate_f32, quantize_blocks, decode_reference
+from oracle.blockquant import (bf16_round, bf16_bits_to_f32, f32_to_bf16_bits, padded_row_bytes,
+                               v_tile_bytes)
+from oracle.kvcache import plane_codes
+
+pytestmark = pytest.mark.gpu
+
+FILL = 8192
+TOL = 1e-3
+DEV = "cuda"
+
+# workload, sampled (sequence, KV head) units
+CASES = [
+    ("mid", [(3, 5), (15, 0)]),
+    ("long", [(2, 7), (7, 1)]),
+    ("huge", [(0, 3), (31, 1)]),
+]
+
+
+def host_values(t):
+    """Device bf16/fp32 tensor -> float32 numpy values."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.float().cpu().numpy()
+
+
+def unit_planes(cache, cfg, b, g):
+    """Device planes of unit (b, g) shaped as a one-sequence, one-head cache."""
+    B, H, d, T = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.tail_len
+    cap = (cfg.max_ctx + 63) // 64 * 64
+    out = {}
+    for p in ("k", "v"):
+        out[p + "_codes"] = cache[p + "_codes"].view(B, H, -1)[b, g].cpu().numpy()[None, None]
+        sc = cache[p + "_scales"].view(B, H, -1)[b, g].cpu().numpy().view(np.uint16)
+        out[p + "_scales"] = sc.reshape(1, 1, cap, d // 32)
+        if T > 0:
+            tl = cache[p + "_tail"].view(B, H, -1)[b, g].cpu().numpy().view(np.uint16)
+            out[p + "_tail"] = tl.reshape(1, 1, T, d)
+        else:
+            out[p + "_tail"] = np.zeros((1, 1, 0, d), np.uint16)
+    return out
+
+
+def window_codes(planes, p, d, bits, t0, t1):
+    """Codes of tokens [t0, t1) (t0 a multiple of 64) of a unit plane."""
+    tile = 64 * padded_row_bytes(d, bits) if p == "k" else v_tile_bytes(d, bits)
+    plane = planes[p + "_codes"][0, 0]
+    sub = plane[(t0 // 64) * tile: ((t1 + 63) // 64) * tile]
+    return plane_codes(sub, d, bits, t1 - t0, p)
+
+
+def check_unit_bytes(w, planes, b, g, n):
+    """Bit-exact codes, scales and tail rows of unit (b, g) on sampled windows."""
+    d, T = w["d"], w["tail"]
+    nt = min(n, T) if T > 0 else 0
+    nq = n - nt
+    starts = sorted({0, (nq // 2) // 64 * 64, max(0, (nq - 64) // 64 * 64)})
+    for role, p, bits in ((1, "k", w["k_bits"]), (2, "v", w["v_bits"])):
+        for t0 in starts:
+            t1 = min(nq, t0 + 64)
+            if t1 <= t0:
+                continue
+            x = host_values(workloads.kv_torch(w, role, t0, t1, DEV, torch)[b, :, g])
+            y = rotate_f32(x)
+            if T > 0:
+                y = bf16_round(y)
+            codes, scales = quantize_blocks(y, bits)
+            got = window_codes(planes, p, d, bits, t0, t1)
+            assert np.array_equal(got, codes), (p, b, g, t0, t1)
+            assert np.array_equal(planes[p + "_scales"][0, 0, t0:t1], scales), (p, b, g, t0)
+        if nt:
+            x = host_values(workloads.kv_torch(w, role, nq, n, DEV, torch)[b, :, g])
+            want = f32_to_bf16_bits(rotate_f32(x))
+            slots = np.arange(nq, n) % T
+            assert np.array_equal(planes[p + "_tail"][0, 0, slots], want), (p, b, g, "tail")
+
+
+def check_unit_attention(w, cache, cfg, out, q, b, g, n):
+    G = w["Hq"] // w["Hkv"]
+    planes = unit_planes(cache, cfg, b, g)
+    qv = host_values(q[b, g * G:(g + 1) * G])[None]
+    ref = decode_reference(planes, qv, [n], 1, w["d"], w["k_bits"], w["v_bits"], w["tail"])
+    got = out[b, g * G:(g + 1) * G].cpu().numpy()
+    err = np.linalg.norm(got - ref[0], axis=-1) / np.linalg.norm(ref[0], axis=-1)
+    say("unit", (b, g), "worst rel L2 %.3e" % err.max())
+    assert err.max() <= TOL, (b, g, err)
+    return planes
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,units", CASES, ids=[c[0] for c in CASES])
+def test_full_size_sampled(name, units):
+    w = workloads.workload(name)
+    B, Hkv, Hq, d, n = w["B"], w["Hkv"], w["Hq"], w["d"], w["n"]
+    steps = 2
+    cfg = kvq.kvq_config(B, Hkv, d, n + steps + 64, w["k_bits"], w["v_bits"], w["tail"])
+    cache = kvq.KVCache(cfg, DEV)
+    lens = [0] * B
+    for t0 in range(0, n, FILL):
+        t1 = min(n, t0 + FILL)
+        say(name, "fill", t0, t1)
+        k = workloads.kv_torch(w, 1, t0, t1, DEV, torch)
+        v = workloads.kv_torch(w, 2, t0, t1, DEV, torch)
+        kvq.kvq_rotate_quantize_append(cfg, cache, k, v, lens)
+        lens = [x + (t1 - t0) for x in lens]
+        del k, v
+    torch.cuda.synchronize()
+    ws = torch.zeros(kvq.kvq_decode_workspace_bytes(cfg, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+
+    say(name, "decode after fill")
+    q = workloads.q_torch(w, 0, DEV, torch)
+    kvq.kvq_decode_attention(cfg, cache, q, lens, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for b, g in units:
+        planes = check_unit_attention(w, cache, cfg, out, q, b, g, n)
+        check_unit_bytes(w, planes, b, g, n)
+
+    for s in range(1, steps + 1):
+        say(name, "decode step", s)
+        kvq.kvq_rotate_quantize_append(cfg, cache, workloads.new_tokens_torch(w, 1, s, DEV, torch),
+                                       workloads.new_tokens_torch(w, 2, s, DEV, torch), lens)
+        lens = [x + 1 for x in lens]
+        q = workloads.q_torch(w, s, DEV, torch)
+        kvq.kvq_decode_attention(cfg, cache, q, lens, out=out, workspace=ws)
+        torch.cuda.synchronize()
+    for b, g in units:
+        check_unit_attention(w, cache, cfg, out, q, b, g, n + steps)
