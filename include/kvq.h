@@ -157,7 +157,7 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg,
  *            kvq_decode_workspace_bytes(cfg, n_q_heads) bytes
  *            (KVQ_ERR_WORKSPACE otherwise); contents need no initialisation.
  * The waves that share a (sequence, KV head) take its tiles dynamically, so
- * two calls on the same inputs agree to rounding (about 1e-5 relative), not
+ * two calls on the same inputs agree to rounding (about 1e-4 relative), not
  * bit for bit.
  * Errors: KVQ_ERR_INVALID if n_q_heads is not a positive multiple of
  * n_kv_heads, a length is 0 or sm_scale is not finite; KVQ_ERR_CAPACITY if a

@@ -160,12 +160,15 @@ def test_decode_fp32_query_and_repeat_calls():
     b = pair.decode(q, "f32")
     # the waves of a workgroup take tiles dynamically, so the float32
     # summation order and the running maximum each fp16 weight is rounded
-    # against can change between calls: repeats agree to rounding
+    # against can change between calls: both calls must meet the bar, and
+    # agree with each other to it
     rel = np.linalg.norm(a - b, axis=-1) / np.linalg.norm(a, axis=-1)
-    assert np.max(rel) <= 1e-4, np.max(rel)
+    say("repeat calls differ by rel L2 %.3e" % np.max(rel))
+    assert np.max(rel) <= TOL, np.max(rel)
     planes = gpu_planes(pair.cache, pair.cfg)
-    errs = attention_errors(a, planes, to_values(q, "f32"), [1100, 1100], pair.cfg)
-    assert max(errs.values()) <= TOL
+    for out in (a, b):
+        errs = attention_errors(out, planes, to_values(q, "f32"), [1100, 1100], pair.cfg)
+        assert max(errs.values()) <= TOL
 
 
 def test_decode_steps_with_single_token_appends():
@@ -182,3 +185,25 @@ def test_decode_steps_with_single_token_appends():
         planes = pair.compare_planes()
         errs = attention_errors(got, planes, to_values(q, "bf16"), list(pair.lens), pair.cfg)
         assert max(errs.values()) <= TOL
+
+
+def test_decode_reuses_one_workspace():
+    # one caller-owned workspace serves calls of different head counts and
+    # lengths: nothing in it may carry over from one call into the next
+    import torch
+    import decode_attention_rotate_amd as kvq
+    w = workloads.workload("long", B=2, tail=64)
+    pair = Pair(2, 8, 128, 8, 4, 64, 3000)
+    _fill(pair, w, [2500, 900], "bf16")
+    need = max(kvq.kvq_decode_workspace_bytes(pair.cfg, hq) for hq in (40, 16, 96))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    planes = gpu_planes(pair.cache, pair.cfg)
+    for call, hq in enumerate((40, 16, 96, 40)):
+        q = workloads.q_numpy(dict(w, Hq=hq), call)
+        qt = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).to("cuda")
+        say("decode with shared workspace", call, hq)
+        got = kvq.kvq_decode_attention(pair.cfg, pair.cache, qt, list(pair.lens), workspace=ws)
+        torch.cuda.synchronize()
+        errs = attention_errors(got.cpu().numpy(), planes, to_values(q, "bf16"), list(pair.lens),
+                                pair.cfg)
+        assert max(errs.values()) <= TOL, (call, hq, max(errs.values()))
