@@ -9,7 +9,8 @@
 //
 // Work unit: one (sequence b, KV head g, chunk of G <= 8 query heads); S
 // waves share a unit and stream each of its cache bytes once.  Workgroups of
-// 8 waves (one per compute unit at 2 waves per SIMD) take contiguous ranges
+// 8 waves at d <= 128 (2 per SIMD), 4 at d = 256 (1 per SIMD, for registers),
+// one per compute unit, take contiguous ranges
 // of the unit's quantized tiles, and inside a workgroup each wave takes the
 // next tile from an LDS counter, so waves the compute unit happens to serve
 // less do less of the work.  Each wave keeps one online-softmax state in its
@@ -52,12 +53,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kStep = 32;   // tokens per step of the quantized loop
-
-// Occupancy target of the split-K kernel (waves per SIMD); bounds the
-// registers the scheduler may use.
-#ifndef KVQ_SPLIT_WAVES_PER_EU
-#define KVQ_SPLIT_WAVES_PER_EU 2
-#endif
 
 __device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
@@ -169,16 +164,22 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t 
     }
     const h2_t bl = {b_lo, b_lo}, bh = {b_hi, b_hi};
     const h2_t d0 = as_h2(w0) + bl;
-    const h2_t d1 = as_h2(w1) * one16 + bh;
+    const h2_t d1 = __builtin_elementwise_fma(as_h2(w1), one16, bh);   // exact
     const h2_t d2 = as_h2(w2) + bl;
-    const h2_t d3 = as_h2(w3) * one16 + bh;
+    const h2_t d3 = __builtin_elementwise_fma(as_h2(w3), one16, bh);
     return h8_t{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
   }
 }
 
 template <int D, int KB, int VB, int G>
-__global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_eu(KVQ_SPLIT_WAVES_PER_EU))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * split_group_waves(D))
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D), split_waves_per_simd(D))))
+void decode_split_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
+  constexpr int kGroupWaves = split_group_waves(D);
+  // tiles whose bytes a wave keeps in registers ahead of the one computing:
+  // at one wave per SIMD (d = 256) the wave alone must cover the latency
+  constexpr int kAhead = split_waves_per_simd(D) == 1 ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
   constexpr int NSW = (NB + 1) / 2;
@@ -229,7 +230,10 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
   // this lane's score heads (Q.K output rows 4r..4r+3 = hi/lo of hA, hB)
   const int hA = 2 * r, hB = 2 * r + 1;
   const bool okA = hA < G, okB = hB < G;
-  float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
+  // running maxima start at -inf for present heads (the first step of a wave
+  // always has a valid token) and at 0 for absent ones, so every masked
+  // score, whose value is -inf, gets weight exp2(-inf - m) = 0
+  float mA = okA ? -INFINITY : 0.f, mB = okB ? -INFINITY : 0.f, lA = 0.f, lB = 0.f;
   f4_t acc[NN];
 #pragma unroll
   for (int i = 0; i < NN; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -435,10 +439,11 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
     // amax / 32639 per head), high bytes in even rows, low bytes in odd rows;
     // 4/5-bit codes widen to bytes in the order 0,2,4,6,1,3,5,7 of each group
     // of 8, so the query bytes follow that order.  Offset-binary codes need a
-    // per-block correction -offset * sum(q_int), applied with the block scale.
+    // per-block correction -offset * sum(q_int), which seeds the low-byte rows
+    // of the integer accumulators: cq[j] = {0, corr_hA, 0, corr_hB}.
     long qop[NB];
     float ckA, ckB;
-    int corrA[KB == 8 ? 1 : NB], corrB[KB == 8 ? 1 : NB];
+    i4_t cq[KB == 8 ? 1 : NB];
     // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
     // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word
     const uint32_t rot_lo = (uint32_t)(2 * r + 28) & 31u;   // rotate left by 4 - 2r
@@ -507,31 +512,27 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const i4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-              qop[j], k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi), i4_t{0, 0, 0, 0}, 0, 0, 0);
-          int vA = (d[0] << 8) + d[1];
-          int vB = (d[2] << 8) + d[3];
-          if constexpr (KB != 8) {
-            vA += corrA[j];
-            vB += corrB[j];
-          }
+              qop[j], k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi),
+              KB == 8 ? i4_t{0, 0, 0, 0} : cq[KB == 8 ? 0 : j], 0, 0, 0);
+          const int vA = (d[0] << 8) + d[1];
+          const int vB = (d[2] << 8) + d[3];
           const float ks = half_of(R.ks[m][j / 2], j % 2);
           sA[m] = __builtin_fmaf(ks, (float)vA, sA[m]);
           sB[m] = __builtin_fmaf(ks, (float)vB, sB[m]);
         }
       }
-      bool valid[2];
       float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        valid[m] = s0 + 16 * m + col < nq;
+        const bool valid = s0 + 16 * m + col < nq;
         float ya = sA[m] * ckA, yb = sB[m] * ckB;
         asm volatile("" : "+v"(ya), "+v"(yb));   // selects, not branches
-        xA[m] = valid[m] && okA ? ya : -INFINITY;
-        xB[m] = valid[m] && okB ? yb : -INFINITY;
+        xA[m] = valid && okA ? ya : -INFINITY;
+        xB[m] = valid && okB ? yb : -INFINITY;
       }
       softmax(xA, xB, pA, pB);
-      // weights p * scale_v in fp16, moved to the A-operand layout via LDS
-      // (rows of heads >= G receive values nobody reads back into results)
+      // weights p * scale_v in fp16 (0 for masked tokens and absent heads),
+      // moved to the A-operand layout via LDS
       wave_sync();
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -539,8 +540,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
         for (int m = 0; m < 2; ++m) {
           const float vs = half_of(R.vs[m][j / 2], j % 2);
           const int t = 16 * m + col;
-          const _Float16 wA = valid[m] ? (_Float16)(pA[m] * vs) : (_Float16)0.f;
-          const _Float16 wB = valid[m] ? (_Float16)(pB[m] * vs) : (_Float16)0.f;
+          const _Float16 wA = (_Float16)(pA[m] * vs);
+          const _Float16 wB = (_Float16)(pB[m] * vs);
           wl[(8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, wA);
           wl[(8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, wB);
         }
@@ -566,12 +567,8 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
       return v;
     };
     auto grab_read = [&](uint32_t v) { return wq0 + (int)__builtin_amdgcn_readfirstlane(v); };
-    int t_cur = grab_read(grab_issue());
-    if (t_cur < wq1) {
-      int t_nxt = grab_read(grab_issue());
-      Regs ra, rb;
-      load_step(ra, t_cur * kTile);   // in flight while the query operands are built
-    {
+    // query operands, built while the first loads are in flight
+    auto prep_query = [&]() {
       float f[NB][8];
       load_query(f);
       float amax = 0.f;
@@ -613,21 +610,59 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
           bsum += __shfl_xor(bsum, 16);
           bsum += __shfl_xor(bsum, 32);
           const int corr = -(1 << (KB - 1)) * bsum;
-          corrA[j] = okA ? __shfl(corr, 4 * r) : 0;
-          corrB[j] = okB ? __shfl(corr, 4 * r + 2) : 0;
+          cq[KB == 8 ? 0 : j] = i4_t{0, okA ? __shfl(corr, 4 * r) : 0, 0, okB ? __shfl(corr, 4 * r + 2) : 0};
         }
       }
-    }
-      while (true) {
-        const uint32_t t_aft_v = grab_issue();
-        load_step(rb, t_cur * kTile + kStep);
-        compute_step(ra, t_cur * kTile);
-        if (t_nxt < wq1) load_step(ra, t_nxt * kTile);
-        compute_step(rb, t_cur * kTile + kStep);
-        const int t_aft = grab_read(t_aft_v);
-        if (t_nxt >= wq1) break;
-        t_cur = t_nxt;
-        t_nxt = t_aft;
+    };
+    if constexpr (kAhead == 1) {
+      int t_cur = grab_read(grab_issue());
+      if (t_cur < wq1) {
+        int t_nxt = grab_read(grab_issue());
+        Regs ra, rb;
+        load_step(ra, t_cur * kTile);
+        prep_query();
+        while (true) {
+          const uint32_t t_aft_v = grab_issue();
+          load_step(rb, t_cur * kTile + kStep);
+          compute_step(ra, t_cur * kTile);
+          if (t_nxt < wq1) load_step(ra, t_nxt * kTile);
+          compute_step(rb, t_cur * kTile + kStep);
+          const int t_aft = grab_read(t_aft_v);
+          if (t_nxt >= wq1) break;
+          t_cur = t_nxt;
+          t_nxt = t_aft;
+        }
+      }
+    } else {
+      // two tiles (four steps) in registers: while one step computes, the
+      // next three are loaded or in flight
+      int t0 = grab_read(grab_issue());
+      if (t0 < wq1) {
+        int t1 = grab_read(grab_issue());
+        Regs ra0, rb0, ra1, rb1;
+        load_step(ra0, t0 * kTile);
+        load_step(rb0, t0 * kTile + kStep);
+        if (t1 < wq1) {
+          load_step(ra1, t1 * kTile);
+          load_step(rb1, t1 * kTile + kStep);
+        }
+        prep_query();
+        while (true) {
+          const int t2 = grab_read(grab_issue());
+          compute_step(ra0, t0 * kTile);
+          if (t2 < wq1) load_step(ra0, t2 * kTile);
+          compute_step(rb0, t0 * kTile + kStep);
+          if (t2 < wq1) load_step(rb0, t2 * kTile + kStep);
+          if (t1 >= wq1) break;
+          const int t3 = grab_read(grab_issue());
+          compute_step(ra1, t1 * kTile);
+          if (t3 < wq1) load_step(ra1, t3 * kTile);
+          compute_step(rb1, t1 * kTile + kStep);
+          if (t3 < wq1) load_step(rb1, t3 * kTile + kStep);
+          if (t2 >= wq1) break;
+          t0 = t2;
+          t1 = t3;
+        }
       }
     }
   }
@@ -668,7 +703,7 @@ __global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_e
 template <int D, int KB, int VB, int G>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G>), grid, dim3(64 * kGroupWaves), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G>), grid, dim3(64 * split_group_waves(D)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -36,13 +36,17 @@ struct DequantArgs {
 hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
-// Waves per workgroup of the split-K kernel.  The waves of a workgroup share
-// one contiguous range of a unit's quantized tiles and take them from an LDS
-// counter; the split count S is a multiple of this.
-#ifndef KVQ_SPLIT_GROUP_WAVES
-#define KVQ_SPLIT_GROUP_WAVES 8
-#endif
-constexpr int kGroupWaves = KVQ_SPLIT_GROUP_WAVES;
+// Resident waves per SIMD the split-K kernel is built for, by head_dim.
+// A wave holds two 32-token steps of cache bytes and D/16 accumulator tiles
+// in registers: at d <= 128 that fits the 256 registers of two waves per
+// SIMD; at d = 256 it needs about 300, which one wave per SIMD (512
+// registers, half of them AGPRs) allows.
+constexpr int split_waves_per_simd(int D) { return D >= 256 ? 1 : 2; }
+// Waves per workgroup: one workgroup fills a compute unit's four SIMDs at
+// that occupancy.  The waves of a workgroup share one contiguous range of a
+// unit's quantized tiles and take them from an LDS counter; the split count
+// S is a multiple of this.
+constexpr int split_group_waves(int D) { return 4 * split_waves_per_simd(D); }
 
 struct DecodeArgs {
   const uint8_t* k_codes;

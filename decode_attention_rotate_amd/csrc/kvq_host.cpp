@@ -22,7 +22,9 @@ namespace {
 
 using namespace kvq;
 
-constexpr int kTargetWaves = 2048;   // split-K waves per decode launch: two per SIMD
+// Split-K waves per decode launch: one resident round on 256 compute units
+// of 4 SIMDs at the kernel's occupancy.
+int target_waves(int D) { return 256 * 4 * split_waves_per_simd(D); }
 constexpr int kMaxSplits = kMaxSplitsDevice;
 
 thread_local hipEvent_t g_ev_before = nullptr;
@@ -80,8 +82,9 @@ Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
   s.nchunk = G / s.gc;
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * s.nchunk;
   const int tiles = std::max(1, (max_len + kTile - 1) / kTile);
-  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
-  s.S = (int)((std::min<int64_t>(want, tiles) + kGroupWaves - 1) / kGroupWaves * kGroupWaves);
+  const int64_t tw = target_waves(c.head_dim), gw = split_group_waves(c.head_dim);
+  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (tw + units - 1) / units));
+  s.S = (int)((std::min<int64_t>(want, tiles) + gw - 1) / gw * gw);
   return s;
 }
 
@@ -92,8 +95,9 @@ int max_splits(const kvq_config& c, int n_q_heads) {
   const int nchunk = G / head_chunk(G);
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * nchunk;
   const int tiles = std::max(1, (c.max_ctx + kTile - 1) / kTile);
-  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (kTargetWaves + units - 1) / units));
-  return (int)((std::min<int64_t>(want, tiles) + kGroupWaves - 1) / kGroupWaves * kGroupWaves);
+  const int64_t tw = target_waves(c.head_dim), gw = split_group_waves(c.head_dim);
+  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (tw + units - 1) / units));
+  return (int)((std::min<int64_t>(want, tiles) + gw - 1) / gw * gw);
 }
 
 // Workspace: (max, sum) pairs, then partial vectors, per split.
@@ -249,7 +253,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.cap = (int32_t)cap_tokens(c);
   da.S = sc.S;
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
-  const dim3 grid(sc.S / kGroupWaves, c.n_kv_heads * sc.nchunk, c.batch);
+  const dim3 grid(sc.S / split_group_waves(c.head_dim), c.n_kv_heads * sc.nchunk, c.batch);
   if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
   if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
   if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
