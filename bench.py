@@ -10,10 +10,14 @@ Prints one JSON line.  `value` is cache GB/s over the full step (algorithmic
 cache bytes read by the attention / step time, over the timed steps).
 `roofline` reports the split-K attention kernel alone, timed with HIP events
 that the library records on the call's stream around that kernel during a
-second run of as many steps (the event records stay out of the timed loop).  `cpu_baseline` times the CPU oracle's decode
-attention on a bounded sample of (sequence, KV head) units of the same cache.
+second run of as many steps (the event records stay out of the timed loop).
+`secondary` gives p10 / median / p90 of that kernel and of the one-token
+append, and the same step on a cache with rotation disabled.  `cpu_baseline`
+times the CPU oracle's decode attention on a bounded sample of (sequence, KV
+head) units of the same cache.
 
   python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+                  [--no-append] [--no-rotation-off]
 """
 
 import argparse
@@ -141,6 +145,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=64,
                     help="(sequence, KV head) units the CPU oracle times (all when >= batch * KV heads)")
     ap.add_argument("--no-append", action="store_true", help="skip the bulk append measurement")
+    ap.add_argument("--no-rotation-off", action="store_true",
+                    help="skip the secondary run with rotation disabled")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -168,87 +174,23 @@ def main():
     torch.cuda.set_device(0)
     w = workloads.workload(args.workload)
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
-    # warm-up, timed steps, then as many steps again with HIP events around
-    # the split kernel (kept out of the timed loop: event records sit between
-    # kernels on the stream)
-    total_steps = args.warmup + 2 * args.steps
-    max_ctx = n + total_steps + 64
-    cfg = kvq.kvq_config(B, Hkv, d, max_ctx, w["k_bits"], w["v_bits"], w["tail"])
-    cache = kvq.KVCache(cfg, dev)
     log("workload", describe(w))
 
-    # fill the cache; keep the generated inputs of a few units for the oracle
+    # (sequence, KV head) units whose inputs the CPU oracle gets
     all_units = [(b, g) for b in range(B) for g in range(Hkv)]
     if args.cpu_units >= len(all_units):
         units = all_units
     else:
         pick = np.random.default_rng(0).choice(len(all_units), args.cpu_units, replace=False)
         units = [all_units[i] for i in sorted(pick)]
-    k_units = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev) if not args.no_cpu_baseline else None
-    v_units = torch.empty_like(k_units) if k_units is not None else None
-    lens = [0] * B
-    t_fill = 0.0
-    fill_tokens = 0
-    for t0 in range(0, n, FILL_CHUNK):
-        t1 = min(n, t0 + FILL_CHUNK)
-        k = workloads.kv_torch(w, 1, t0, t1, dev, torch)
-        v = workloads.kv_torch(w, 2, t0, t1, dev, torch)
-        if k_units is not None:
-            k_units[:, t0:t1].copy_(k)
-            v_units[:, t0:t1].copy_(v)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        kvq.kvq_rotate_quantize_append(cfg, cache, k, v, lens)
-        e1.record()
-        torch.cuda.synchronize()
-        t_fill += e0.elapsed_time(e1) * 1e-3
-        fill_tokens += (t1 - t0) * B
-        lens = [x + (t1 - t0) for x in lens]
-        del k, v
-    log("filled %d tokens/sequence, append %.1f Mtok/s" % (n, fill_tokens / t_fill / 1e6))
+    keep = None if args.no_cpu_baseline else {}
 
-    # inputs of every step, generated before timing
-    qs = [workloads.q_torch(w, s, dev, torch) for s in range(total_steps)]
-    ks = [workloads.new_tokens_torch(w, 1, s, dev, torch) for s in range(total_steps)]
-    vs = [workloads.new_tokens_torch(w, 2, s, dev, torch) for s in range(total_steps)]
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.kvq_decode_workspace_bytes(cfg, Hq), dtype=torch.uint8, device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(total_steps)]
-
-    def step(s, events):
-        kvq.kvq_rotate_quantize_append(cfg, cache, ks[s], vs[s], lens)
-        for b in range(B):
-            lens[b] += 1
-        if events:
-            kvq.kvq_profile_decode_events(ev[s][0], ev[s][1])
-        kvq.kvq_decode_attention(cfg, cache, qs[s], lens, out=out, workspace=ws)
-
-    step_bytes = []
-    for s in range(args.warmup):
-        step(s, False)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.warmup, args.warmup + args.steps):
-        step(s, False)
-        step_bytes.append(cache_bytes_per_step(w, lens))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    kern_bytes = []
-    for s in range(args.warmup + args.steps, total_steps):
-        step(s, True)
-        kern_bytes.append(cache_bytes_per_step(w, lens))
-    torch.cuda.synchronize()
-    kvq.kvq_profile_decode_events(None, None)
-    assert torch.isfinite(out).all().item(), "non-finite attention output"
-
-    ms_step = elapsed / args.steps * 1e3
-    avg_bytes = float(np.mean(step_bytes))
-    kern_ms = [kvq.kernel_elapsed_ms(ev[s][0], ev[s][1]) for s in range(args.warmup + args.steps, total_steps)]
+    run = decode_run(torch, kvq, w, dev, args.warmup, args.steps, True, keep)
+    ms_step = run["ms_step"]
+    value = run["bytes_step"] / (ms_step * 1e-3) / 1e9
+    kern_ms = run["kern_ms"]
     kern_avg_ms = float(np.mean(kern_ms))
-    achieved = float(np.mean(kern_bytes)) / (kern_avg_ms * 1e-3) / 1e9
-    value = avg_bytes / (ms_step * 1e-3) / 1e9
+    achieved = run["bytes_kern"] / (kern_avg_ms * 1e-3) / 1e9
     log("step %.1f us, attention kernel %.1f us (median %.1f), %.0f GB/s kernel, %.0f GB/s step"
         % (ms_step * 1e3, kern_avg_ms * 1e3, float(np.median(kern_ms)) * 1e3, achieved, value))
 
@@ -265,17 +207,32 @@ def main():
         "vs_baseline": None,
         "dtype": "int8/u4 codes, fp16 scales, f32 accumulation",
         "data": "synthetic",
-        "config": {"workload": describe(w), "cache_bytes_per_step": int(avg_bytes),
+        "config": {"workload": describe(w), "cache_bytes_per_step": int(run["bytes_step"]),
                    "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
                    "us_per_step": round(ms_step * 1e3, 2),
                    "attention_kernel_us": round(kern_avg_ms * 1e3, 2),
-                   "fill_append_mtok_s": round(fill_tokens / t_fill / 1e6, 1)},
+                   "fill_append_mtok_s": round(run["fill_mtok_s"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload)},
+        "secondary": {"attention_kernel_us": percentiles(kern_ms),
+                      "single_token_append_us": percentiles(run["app_ms"])},
     }
-    q0 = qs[0]
-    del qs, ks, vs
+    q0 = run["q0"]
+    del run
+
+    if not args.no_rotation_off:
+        # the same step with rotation disabled for K and V (no query rotation,
+        # no inverse rotation of the output, no rotation in the append)
+        off = decode_run(torch, kvq, w, dev, args.warmup, args.steps, False, None)
+        result["secondary"]["rotation_off"] = {
+            "us_per_step": round(off["ms_step"] * 1e3, 2),
+            "attention_kernel_us": percentiles(off["kern_ms"]),
+            "single_token_append_us": percentiles(off["app_ms"]),
+            "step_slowdown_of_rotation_pct": round(100 * (ms_step / off["ms_step"] - 1), 2)}
+        log("rotation off: step %.1f us" % (off["ms_step"] * 1e3))
+        del off
+
 
     if not args.no_append:
         result["append"] = bulk_append(torch, kvq, dev)
@@ -283,9 +240,103 @@ def main():
     if not args.no_cpu_baseline:
         q_host = q0.view(torch.int16).cpu().numpy().view(np.uint16)
         log("cpu baseline on %d units" % len(units))
-        result["cpu_baseline"] = cpu_baseline(w, units, k_units, v_units, q_host, torch, len(units))
+        result["cpu_baseline"] = cpu_baseline(w, units, keep["k"], keep["v"], q_host, torch, len(units))
     print(json.dumps(result), flush=True)
     return 0
+
+
+def percentiles(ms):
+    """p10 / median / p90 of a list of durations in ms, in us."""
+    p = np.percentile(np.asarray(ms) * 1e3, [10, 50, 90])
+    return {"p10": round(float(p[0]), 2), "median": round(float(p[1]), 2),
+            "p90": round(float(p[2]), 2)}
+
+
+def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep):
+    """Fill a cache for workload w, then run warm-up steps, `steps` timed
+    steps, and as many steps again with HIP events around the split kernel
+    (recorded by the library on the call's stream) and around the append
+    (kept out of the timed loop: event records sit between kernels).  When
+    `keep` is a dict it receives the bf16 K and V inputs for the oracle."""
+    B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
+    total_steps = warmup + 2 * steps
+    cfg = kvq.kvq_config(B, Hkv, d, n + total_steps + 64, w["k_bits"], w["v_bits"], w["tail"],
+                         rotate_k=rotate, rotate_v=rotate)
+    cache = kvq.KVCache(cfg, dev)
+    if keep is not None:
+        keep["k"] = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev)
+        keep["v"] = torch.empty_like(keep["k"])
+    lens = [0] * B
+    t_fill = 0.0
+    for t0 in range(0, n, FILL_CHUNK):
+        t1 = min(n, t0 + FILL_CHUNK)
+        k = workloads.kv_torch(w, 1, t0, t1, dev, torch)
+        v = workloads.kv_torch(w, 2, t0, t1, dev, torch)
+        if keep is not None:
+            keep["k"][:, t0:t1].copy_(k)
+            keep["v"][:, t0:t1].copy_(v)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.kvq_rotate_quantize_append(cfg, cache, k, v, lens)
+        e1.record()
+        torch.cuda.synchronize()
+        t_fill += e0.elapsed_time(e1) * 1e-3
+        lens = [x + (t1 - t0) for x in lens]
+        del k, v
+    fill_mtok_s = n * B / t_fill / 1e6
+    log("filled %d tokens/sequence (rotation %s), append %.1f Mtok/s"
+        % (n, "on" if rotate else "off", fill_mtok_s))
+
+    # inputs of every step, generated before timing
+    qs = [workloads.q_torch(w, s, dev, torch) for s in range(total_steps)]
+    ks = [workloads.new_tokens_torch(w, 1, s, dev, torch) for s in range(total_steps)]
+    vs = [workloads.new_tokens_torch(w, 2, s, dev, torch) for s in range(total_steps)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_decode_workspace_bytes(cfg, Hq), dtype=torch.uint8, device=dev)
+
+    def new_events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [new_events() for _ in range(total_steps)]
+    ev_app = [new_events() for _ in range(total_steps)]
+
+    def step(s, events):
+        if events:
+            ev_app[s][0].record()
+        kvq.kvq_rotate_quantize_append(cfg, cache, ks[s], vs[s], lens)
+        if events:
+            ev_app[s][1].record()
+        for b in range(B):
+            lens[b] += 1
+        if events:
+            kvq.kvq_profile_decode_events(ev[s][0], ev[s][1])
+        kvq.kvq_decode_attention(cfg, cache, qs[s], lens, out=out, workspace=ws)
+
+    step_bytes = []
+    for s in range(warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(warmup, warmup + steps):
+        step(s, False)
+        step_bytes.append(cache_bytes_per_step(w, lens))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kern_bytes = []
+    for s in range(warmup + steps, total_steps):
+        step(s, True)
+        kern_bytes.append(cache_bytes_per_step(w, lens))
+    torch.cuda.synchronize()
+    kvq.kvq_profile_decode_events(None, None)
+    assert torch.isfinite(out).all().item(), "non-finite attention output"
+    timed = range(warmup + steps, total_steps)
+    res = {"ms_step": elapsed / steps * 1e3, "bytes_step": float(np.mean(step_bytes)),
+           "bytes_kern": float(np.mean(kern_bytes)),
+           "kern_ms": [kvq.kernel_elapsed_ms(ev[s][0], ev[s][1]) for s in timed],
+           "app_ms": [ev_app[s][0].elapsed_time(ev_app[s][1]) for s in timed],
+           "fill_mtok_s": fill_mtok_s, "q0": qs[0]}
+    del cache, qs, ks, vs
+    return res
 
 
 def bulk_append(torch, kvq, dev):
