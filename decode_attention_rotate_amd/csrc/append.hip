@@ -9,7 +9,8 @@
 //
 // An append of n_new tokens to a sequence of length len runs in two steps
 // (two launches, or one block per (sequence, KV head, plane) with a barrier
-// between the steps when n_new is small):
+// between the steps when n_new is small; one token per sequence has a kernel
+// of its own, below):
 //  1. quant: positions [q0, q1) become quantized, where q0/q1 are the first
 //     non-tail position before/after the append (q0 = len, q1 = len + n_new
 //     without a tail).  A position below len is read back from its tail slot
@@ -319,9 +320,106 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   if (a.T > 0) tail_part<D>(a, 0, g, b, pl);
 }
 
+// One new token per sequence (a decode step), one wave per (b, g, plane).
+// Lanes [0, LPR) hold the new token's blocks and rotate them; lanes
+// [32, 32 + LPR) hold the row leaving the bf16 tail, when there is one.  The
+// position that becomes quantized is the new token itself without a tail,
+// the leaving row with one.  Every global load (input row, ring row, the V
+// items the quantized codes merge into) is issued before any arithmetic, so
+// the wave waits for memory once; the new row overwrites the ring slot the
+// leaving row was read from only after a barrier.
+template <int D>
+__global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
+  constexpr int LPR = D / kBlock;
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x, b = blockIdx.y, pl = blockIdx.z;
+  const int j = lane % LPR;
+  const AppendRange rg = append_range(a, b);
+  const int len = rg.len, T = a.T;
+  const bool new_lane = lane < LPR;
+  const bool ring_lane = T > 0 && rg.q1 > rg.q0 && lane >= 32 && lane < 32 + LPR;
+  const bool q_lane = rg.q1 > rg.q0 && (T > 0 ? ring_lane : new_lane);
+  const int pq = rg.q0;                          // the quantized position
+  const size_t unit = (size_t)b * a.Hkv + g;
+  const int bits = a.bits[pl];
+
+  float x[32], y[32];
+  if (new_lane) {
+    load_row_block(a.src[pl], a.dtype, ((size_t)b * a.Hkv + g) * D + (size_t)kBlock * j, x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = 0.f;
+  }
+  if (ring_lane) {
+    load_bf16_block(a.tail[pl] + (unit * T + pq % T) * D + kBlock * j, y);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) y[e] = 0.f;
+  }
+  // V items of this lane's 32 elements at the quantized position
+  uint8_t* vtile = a.codes[1] + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, bits) +
+                   (size_t)(pq / kTile) * v_tile_bytes(D, bits);
+  uint32_t oldw[32];
+  uint8_t oldh[32];
+  if (pl == 1 && q_lane && bits != 8) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int item = v_item(D, pq % kTile, kBlock * j + i);
+      oldw[i] = reinterpret_cast<const uint32_t*>(vtile)[item];
+      oldh[i] = bits == 5 ? vtile[32 * D + item] : 0;
+    }
+  }
+
+  if (a.rotate[pl]) rotate_row<D>(x, lane, a.cd);   // every lane takes part
+  if (q_lane) {
+    float z[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) z[e] = T > 0 ? y[e] : x[e];
+    uint16_t* scales = a.scales[pl] + unit * (size_t)a.cap * (D / kBlock);
+    int c[32];
+    if (pl == 0) {
+      uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
+      scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_k<D>(bits, z, c, true, plane, pq, j);
+    } else {
+      scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_any<D>(bits, z, c);
+      const int k = pq % 8, off = 1 << (bits - 1);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int item = v_item(D, pq % kTile, kBlock * j + i);
+        const uint32_t u = (uint32_t)(c[i] + off);
+        if (bits == 8) {
+          vtile[8 * item + k] = (uint8_t)u;
+        } else {
+          const int nb = v_nibble(k);
+          reinterpret_cast<uint32_t*>(vtile)[item] = (oldw[i] & ~(15u << (4 * nb))) | ((u & 15u) << (4 * nb));
+          if (bits == 5)
+            vtile[32 * D + item] = (uint8_t)((oldh[i] & ~(1u << nb)) | (((u >> 4) & 1u) << nb));
+        }
+      }
+    }
+  }
+  if (T == 0) return;
+  __syncthreads();   // the ring row has been read
+  if (new_lane) {
+    uint4* dst = reinterpret_cast<uint4*>(a.tail[pl] + (unit * T + len % T) * D + kBlock * j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = f32_to_bf16_bits(x[q * 8 + 2 * k]) | (f32_to_bf16_bits(x[q * 8 + 2 * k + 1]) << 16);
+      dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
   constexpr int RPB = 256 / (D / kBlock);
+  if (a.n_new == 1) {
+    hipLaunchKernelGGL(append_one_kernel<D>, dim3(a.Hkv, B, 2), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.n_new <= RPB - 7) {
     // [q0 & ~7, q1) spans at most n_new + 7 positions and the tail at most n_new
     hipLaunchKernelGGL(append_small_kernel<D>, dim3(1, a.Hkv, 2 * B), dim3(256), 0, s, a);

@@ -68,6 +68,18 @@ int head_chunk(int G) {
   return 1;
 }
 
+// Splits per unit: enough waves for one resident round, at most one per
+// 64-token tile of the longest sequence, a multiple of the workgroup size and
+// at most kMaxSplits.  Non-decreasing in max_len.
+int split_count(int D, int64_t units, int max_len) {
+  const int64_t tiles = std::max(1, (max_len + kTile - 1) / kTile);
+  const int64_t gw = split_group_waves(D);
+  const int64_t want = std::max<int64_t>(1, (target_waves(D) + units - 1) / units);
+  int64_t S = (std::min(want, tiles) + gw - 1) / gw * gw;
+  if (S > kMaxSplits) S = kMaxSplits / gw * gw;
+  return (int)S;
+}
+
 struct Schedule {
   int gc, nchunk, S;
 };
@@ -81,10 +93,7 @@ Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
   s.gc = head_chunk(G);
   s.nchunk = G / s.gc;
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * s.nchunk;
-  const int tiles = std::max(1, (max_len + kTile - 1) / kTile);
-  const int64_t tw = target_waves(c.head_dim), gw = split_group_waves(c.head_dim);
-  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (tw + units - 1) / units));
-  s.S = (int)((std::min<int64_t>(want, tiles) + gw - 1) / gw * gw);
+  s.S = split_count(c.head_dim, units, max_len);
   return s;
 }
 
@@ -94,10 +103,7 @@ int max_splits(const kvq_config& c, int n_q_heads) {
   const int G = n_q_heads / c.n_kv_heads;
   const int nchunk = G / head_chunk(G);
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * nchunk;
-  const int tiles = std::max(1, (c.max_ctx + kTile - 1) / kTile);
-  const int64_t tw = target_waves(c.head_dim), gw = split_group_waves(c.head_dim);
-  const int64_t want = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, (tw + units - 1) / units));
-  return (int)((std::min<int64_t>(want, tiles) + gw - 1) / gw * gw);
+  return split_count(c.head_dim, units, c.max_ctx);
 }
 
 // Workspace: (max, sum) pairs, then partial vectors, per split.

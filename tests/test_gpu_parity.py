@@ -57,6 +57,42 @@ def test_append_bit_exact(case):
     pair.compare_planes()
 
 
+ONE_TOKEN_CASES = [
+    # d, kb, vb, T, dtype, B, H, rotate
+    (64, 4, 8, 0, "f32", 2, 2, True),
+    (128, 5, 4, 8, "bf16", 2, 2, True),
+    (256, 8, 5, 3, "f32", 1, 2, True),
+    (128, 4, 5, 0, "bf16", 1, 2, False),
+    (128, 8, 4, 64, "bf16", 3, 1, True),
+    (256, 4, 4, 1, "bf16", 1, 1, True),
+]
+
+
+@pytest.mark.parametrize("case", ONE_TOKEN_CASES,
+                         ids=[_case_id(c[:7] + ([1], c[7])) for c in ONE_TOKEN_CASES])
+def test_one_token_appends_bit_exact(case):
+    # decode-step appends, one token per sequence per call: 75 calls cross
+    # 8-token V groups, a 64-token tile and every tail slot; then sequence 0
+    # rolls back to an unaligned length and appends again, so codes merge
+    # into V words that hold older codes
+    d, kb, vb, T, dtype, B, H, rot = case
+    pair = Pair(B, H, d, kb, vb, T, 120, rot, rot)
+    pair.append(workloads.adversarial_numpy(1, (B, 13, H, d), dtype),
+                workloads.adversarial_numpy(2, (B, 13, H, d), dtype), dtype)
+    for s in range(75):
+        pair.append(workloads.adversarial_numpy(100 + s, (B, 1, H, d), dtype),
+                    workloads.adversarial_numpy(300 + s, (B, 1, H, d), dtype), dtype)
+    pair.compare_planes()
+    lens = list(pair.lens)
+    lens[0] = 37
+    pair.append(workloads.adversarial_numpy(500, (B, 1, H, d), dtype),
+                workloads.adversarial_numpy(501, (B, 1, H, d), dtype), dtype, lens=lens)
+    for s in range(5):
+        pair.append(workloads.adversarial_numpy(510 + s, (B, 1, H, d), dtype),
+                    workloads.adversarial_numpy(520 + s, (B, 1, H, d), dtype), dtype)
+    pair.compare_planes()
+
+
 @pytest.mark.parametrize("case", APPEND_CASES[:8], ids=[_case_id(c) for c in APPEND_CASES[:8]])
 def test_dequantize_bit_exact(case):
     import torch
