@@ -45,13 +45,13 @@ from .blockquant import (
 )
 from .kvcache import OracleCache
 from .attention import (softmax_attention, decode_reference, dequantize_unit,
-                        dequantize_reference)
+                        dequantize_reference, prefill_reference)
 
 __all__ = [
     "hadamard", "rot_scale_f32", "fwht_f32", "rotate_f32",
     "QMAX", "BLOCK", "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "quantize_blocks", "dequantize_blocks", "pack_rows", "unpack_rows",
     "row_bytes", "padded_row_bytes", "rows_to_tiled", "tiled_to_rows",
-    "OracleCache", "softmax_attention", "decode_reference", "dequantize_unit",
+    "OracleCache", "softmax_attention", "decode_reference", "prefill_reference", "dequantize_unit",
     "dequantize_reference",
 ]

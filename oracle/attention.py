@@ -1,4 +1,4 @@
-"""Single-query decode attention over the rotated quantized cache (oracle).
+"""Decode and chunked-prefill attention over the rotated quantized cache (oracle).
 
 Source: velog.io post "fix KV cache quantization outliers", section
 "Hadamard rotation": attention runs on the rotated Q and K (the Hadamard
@@ -17,6 +17,13 @@ Readings:
 * R14 The output is float32-valued, in the original (unrotated) space.
 * R15 rotate_k off: neither q nor K is rotated; rotate_v off: V is not
       rotated and the output is not rotated back.
+* R19 Chunked prefill (prompt processing, whose rotation cost the velog.io
+      post reports in section "compute cost and speed"): the n_q queries of a
+      chunk are the last n_q positions of the sequence, already appended;
+      query i sits at position p = n - n_q + i and attends to positions
+      0..p (causal), reading the cache as it stands after the whole chunk
+      was appended (a token that left the tail during the chunk is read
+      quantized).
 """
 
 import numpy as np
@@ -86,6 +93,41 @@ def decode_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
             qr = H @ q[b, h] if rotate_k else q[b, h]
             o = softmax_attention(qr, K, V, sm_scale)
             out[b, h] = H @ o if rotate_v else o
+    return out
+
+
+def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
+                      tail_len, sm_scale=None, rotate_k=True, rotate_v=True,
+                      rows=None):
+    """Reference output [B][n_q][Hq][d] (float64) of chunked prefill attention.
+
+    q: float values [B][n_q][Hq][d], the queries of the last n_q positions of
+    each sequence (R19); lens[b] >= n_q is the length after the chunk.
+    rows: optional iterable of (b, i, h) triples to evaluate; others stay NaN."""
+    q = np.asarray(q, dtype=np.float64)
+    B, n_q, Hq, _ = q.shape
+    G = Hq // n_kv_heads
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    H = hadamard(d)
+    out = np.full((B, n_q, Hq, d), np.nan)
+    want = set(rows) if rows is not None else None
+    cache = {}
+    for b in range(B):
+        n = int(lens[b])
+        for i in range(n_q):
+            p = n - n_q + i
+            for h in range(Hq):
+                if want is not None and (b, i, h) not in want:
+                    continue
+                g = h // G
+                if (b, g) not in cache:
+                    cache[(b, g)] = dequantize_unit(planes, b, g, n, d, k_bits, v_bits,
+                                                    tail_len)
+                K, V = cache[(b, g)]
+                qr = H @ q[b, i, h] if rotate_k else q[b, i, h]
+                o = softmax_attention(qr, K[:p + 1], V[:p + 1], sm_scale)
+                out[b, i, h] = H @ o if rotate_v else o
     return out
 
 
