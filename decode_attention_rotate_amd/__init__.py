@@ -25,7 +25,8 @@ __all__ = [
     "kvq_config_default", "kvq_config_check", "kvq_plane_bytes",
     "kvq_decode_workspace_bytes", "kvq_rotate_quantize_append",
     "kvq_decode_attention", "kvq_dequantize", "kvq_status_str",
-    "kvq_profile_decode_events", "LIB_PATH",
+    "kvq_profile_decode_events", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
+    "LIB_PATH",
 ]
 
 
@@ -184,6 +185,36 @@ def kvq_decode_attention(cfg, cache, q, seq_len, sm_scale=None, out=None,
         float(sm_scale), _lens(seq_len, cfg.batch), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _capi.check(st, "kvq_decode_attention")
+    return out
+
+
+def kvq_prefill_workspace_bytes(cfg, n_q_heads, n_q):
+    return _capi.lib().kvq_prefill_workspace_bytes(ctypes.byref(cfg), n_q_heads, n_q)
+
+
+def kvq_prefill_attention(cfg, cache, q, seq_len, sm_scale=None, out=None,
+                          workspace=None, stream=None):
+    """Chunked prefill attention for q [B][n_q][Hq][d], the queries of the
+    last n_q positions of each sequence (already appended); returns float32
+    [B][n_q][Hq][d]."""
+    torch = _torch()
+    _device_tensor(q, "q")
+    B, n_q, Hq, d = q.shape
+    if (B, d) != (cfg.batch, cfg.head_dim):
+        raise ValueError("q shape %s does not match the configuration" % (tuple(q.shape),))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=q.device)
+    _device_tensor(out, "out")
+    need = kvq_prefill_workspace_bytes(cfg, Hq, n_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = _capi.lib().kvq_prefill_attention(
+        ctypes.byref(cfg), ctypes.byref(cache.struct), q.data_ptr(), _dtype_code(q), Hq, n_q,
+        float(sm_scale), _lens(seq_len, cfg.batch), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _capi.check(st, "kvq_prefill_attention")
     return out
 
 

@@ -27,7 +27,8 @@ EXPORTS = (
     "kvq_config_default", "kvq_config_check", "kvq_plane_bytes",
     "kvq_decode_workspace_bytes", "kvq_rotate_quantize_append",
     "kvq_decode_attention", "kvq_dequantize", "kvq_status_str",
-    "kvq_profile_decode_events",
+    "kvq_profile_decode_events", "kvq_prefill_workspace_bytes",
+    "kvq_prefill_attention",
 )
 
 
@@ -80,6 +81,9 @@ def lib():
             "kvq_rotate_quantize_append": (I32, [CFG, CACHE, vp, vp, I32, I32, P(I32), vp]),
             "kvq_decode_attention": (I32, [CFG, CACHE, vp, I32, I32, ctypes.c_float, P(I32),
                                            vp, vp, SZ, vp]),
+            "kvq_prefill_workspace_bytes": (SZ, [CFG, I32, I32]),
+            "kvq_prefill_attention": (I32, [CFG, CACHE, vp, I32, I32, I32, ctypes.c_float,
+                                            P(I32), vp, vp, SZ, vp]),
             "kvq_dequantize": (I32, [CFG, CACHE, I32, I32, I32, I32, P(I32), I32, vp, vp]),
             "kvq_status_str": (ctypes.c_char_p, [I32]),
             "kvq_profile_decode_events": (None, [vp, vp]),

@@ -1,6 +1,7 @@
 // One instantiation unit of the split-K decode kernel: head_dim KVQ_INST_D and
 // K width KVQ_INST_KB (set by the build), every V width and 1..8 query heads
-// per KV-head chunk.  Split across units so the build compiles in parallel.
+// per KV-head chunk, plus the chunked-prefill variant per V width.  Split
+// across units so the build compiles in parallel.
 #include "decode_kernels.hpp"
 
 #ifndef KVQ_INST_D
@@ -13,6 +14,7 @@
 #define KVQ_CAT2(a, b, c) a##_##b##_##c
 #define KVQ_CAT(a, b, c) KVQ_CAT2(a, b, c)
 #define KVQ_TABLE KVQ_CAT(kvq_decode_table, KVQ_INST_D, KVQ_INST_KB)
+#define KVQ_PF_TABLE KVQ_CAT(kvq_prefill_table, KVQ_INST_D, KVQ_INST_KB)
 
 namespace kvq {
 
@@ -27,5 +29,10 @@ namespace kvq {
    launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8>}
 
 DecodeLauncher KVQ_TABLE[3][8] = {KVQ_ROW(4), KVQ_ROW(5), KVQ_ROW(8)};
+
+// chunked prefill, indexed by v_bits 4/5/8
+DecodeLauncher KVQ_PF_TABLE[3] = {launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 4, 8, true>,
+                                  launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 5, 8, true>,
+                                  launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 8, 8, true>};
 
 }  // namespace kvq

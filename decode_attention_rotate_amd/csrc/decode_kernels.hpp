@@ -171,15 +171,27 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t 
   }
 }
 
-template <int D, int KB, int VB, int G>
+// PF = false: decode, one query per sequence; a wave's rows are the G <= 8
+// query heads of one chunk of a KV head's group.
+// PF = true: chunked prefill (G = 8): the rows of a KV head g are the pairs
+// (query i, head h of g's group), numbered v = i * Gq + h, and the 8 waves of
+// a workgroup own 8 consecutive rows each.  Row (i, h) sits at position
+// n - n_q + i and sees positions up to there.  All waves of a workgroup walk
+// the same tiles, so each cache byte comes from HBM once per workgroup (the
+// other waves find it in L1 / L2).
+template <int D, int KB, int VB, int G, bool PF>
 __global__ __launch_bounds__(64 * split_group_waves(D))
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D), split_waves_per_simd(D))))
 void decode_split_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
+  static_assert(!PF || G == 8, "prefill waves own 8 rows");
   constexpr int kGroupWaves = split_group_waves(D);
   // tiles whose bytes a wave keeps in registers ahead of the one computing:
-  // at one wave per SIMD (d = 256) the wave alone must cover the latency
-  constexpr int kAhead = split_waves_per_simd(D) == 1 ? 2 : 1;
+  // at one wave per SIMD (d = 256) the wave alone must cover the latency, so
+  // it keeps two where four step buffers fit the 512 registers with at most
+  // a few spilled (4-bit K or 4-bit V; decode only, a prefill wave holds
+  // more state)
+  constexpr int kAhead = split_waves_per_simd(D) == 1 && !PF && (KB == 4 || VB == 4) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
   constexpr int NSW = (NB + 1) / 2;
@@ -201,23 +213,44 @@ void decode_split_kernel(DecodeArgs a) {
   const int wv = threadIdx.x >> 6;
   const int col = lane & 15;
   const int r = lane >> 4;
-  const int split = blockIdx.x * kGroupWaves + wv;   // this wave's partial slot
+  // this wave's partial slot
+  const int split = PF ? (int)blockIdx.x : (int)blockIdx.x * kGroupWaves + wv;
   uint16_t* wl = wl_all[wv];
   float* alds = alds_all[wv];
   if (threadIdx.x == 0) tile_ctr = 0u;
   __syncthreads();
-  const int g = blockIdx.y / a.n_gchunks;
-  const int h0 = g * a.G + (blockIdx.y % a.n_gchunks) * G;
+  const int g = PF ? (int)blockIdx.y / a.n_rb : (int)blockIdx.y / a.n_gchunks;
+  const int h0 = g * a.G + (PF ? 0 : ((int)blockIdx.y % a.n_gchunks) * G);
   const int b = blockIdx.z;
   const int n = a.len[b];
+  // rows of this wave (prefill): vbase .. vbase + 7 of the R rows of (b, g)
+  const int R = PF ? a.n_q * a.G : G;
+  const int vbase = PF ? (((int)blockIdx.y % a.n_rb) * kGroupWaves + wv) * 8 : 0;
+  if (PF && vbase >= R) return;   // no barrier follows
+  // row k of the wave: present?, index of its query / output vector among
+  // the [B][n_q][Hq] (decode: [B][Hq]) ones, last position it sees
+  auto row_ok = [&](int k) { return PF ? vbase + k < R : k < G; };
+  auto row_vec = [&](int k) -> size_t {
+    if constexpr (PF) {
+      const int v = vbase + k, i = v / a.G;
+      return ((size_t)b * a.n_q + i) * a.Hq + h0 + (v - i * a.G);
+    } else {
+      return (size_t)b * a.Hq + h0 + k;
+    }
+  };
+  auto row_lim = [&](int k) { return PF ? n - a.n_q + (vbase + k) / a.G : n - 1; };
+  // last position any row of the wave sees (rows are in position order)
+  const int wlim = row_lim(min(7, R - 1 - vbase));
   const int T = a.T;
   const int nt = T > 0 ? min(n, T) : 0;
   const int nq = n - nt;
   // Quantized tiles: workgroup wg of NG takes the contiguous range
   // [ctq*wg/NG, ctq*(wg+1)/NG) and its waves pull tiles from it one at a
-  // time, so they finish together however the compute unit schedules them.
-  // bf16 tail tiles (few, each worth several quantized tiles) are dealt out
-  // round-robin: tile k to workgroup k mod NG, wave (k / NG) mod kGroupWaves.
+  // time, so they finish together however the compute unit schedules them
+  // (prefill: every wave takes every tile of the range, up to its rows' last
+  // position).  bf16 tail tiles (few, each worth several quantized tiles) are
+  // dealt out round-robin: tile k to workgroup k mod NG, wave (k / NG) mod
+  // kGroupWaves (prefill: to every wave of workgroup k mod NG).
   const int ctq = (nq + kTile - 1) / kTile;
   const int ctt = (nt + kTile - 1) / kTile;
   const int NG = (int)gridDim.x;
@@ -229,22 +262,24 @@ void decode_split_kernel(DecodeArgs a) {
 
   // this lane's score heads (Q.K output rows 4r..4r+3 = hi/lo of hA, hB)
   const int hA = 2 * r, hB = 2 * r + 1;
-  const bool okA = hA < G, okB = hB < G;
-  // running maxima start at -inf for present heads (the first step of a wave
-  // always has a valid token) and at 0 for absent ones, so every masked
-  // score, whose value is -inf, gets weight exp2(-inf - m) = 0
-  float mA = okA ? -INFINITY : 0.f, mB = okB ? -INFINITY : 0.f, lA = 0.f, lB = 0.f;
+  const bool okA = row_ok(hA), okB = row_ok(hB);
+  const int limA = row_lim(hA), limB = row_lim(hB);
+  // running maxima start at -1e30 for present heads (a finite floor: a
+  // prefill row may see no token of a whole split) and at 0 for absent ones,
+  // so every masked score, whose value is -inf, gets weight exp2(-inf - m) = 0
+  float mA = okA ? -1e30f : 0.f, mB = okB ? -1e30f : 0.f, lA = 0.f, lB = 0.f;
   f4_t acc[NN];
 #pragma unroll
   for (int i = 0; i < NN; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Query of this lane's A row in registers: row col < 2G is head h0 + col/2;
-  // the lane holds elements 32j + 8r + i (j < NB, i < 8), rotated in float32
-  // with the butterfly stages in the order h = 1, 2, 4, ..., D/2 (h = 8, 16
-  // exchange values with lanes 16 and 32 apart).  Rows >= 2G read head 0.
+  // Query of this lane's A row in registers: row col < 2G is the wave's row
+  // col/2; the lane holds elements 32j + 8r + i (j < NB, i < 8), rotated in
+  // float32 with the butterfly stages in the order h = 1, 2, 4, ..., D/2
+  // (h = 8, 16 exchange values with lanes 16 and 32 apart).  Lanes of absent
+  // rows read row 0.
   auto load_query = [&](float (&f)[NB][8]) {
-    const int hq = col < 2 * G ? col / 2 : 0;
-    const size_t off = ((size_t)b * a.Hq + h0 + hq) * D + 8 * r;
+    const int hq = col < 2 * G && row_ok(col / 2) ? col / 2 : 0;
+    const size_t off = row_vec(hq) * D + 8 * r;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (a.q_dtype == KVQ_BF16) {
@@ -353,7 +388,7 @@ void decode_split_kernel(DecodeArgs a) {
   // 2h+1 of Q.K, weight parts are A rows h / 8+h of P.V (rows 8..15 of the
   // accumulators are added to rows 0..7 at the end).  K rows come straight
   // from the ring; each lane gathers its element of 8 V rows.
-  const int tk0 = (int)blockIdx.x + NG * wv;
+  const int tk0 = (int)blockIdx.x + (PF ? 0 : NG * wv);
   if (tk0 < ctt) {
     const uint16_t* ktl = a.k_tail + unit * (size_t)T * D;
     const uint16_t* vtl = a.v_tail + unit * (size_t)T * D;
@@ -367,15 +402,16 @@ void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) {
           const uint32_t hi = f32_to_bf16_bits(f[j][e]);
           const uint32_t lo = f32_to_bf16_bits(f[j][e] - __uint_as_float(hi << 16));
-          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(col < 2 * G ? ((col & 1) ? lo : hi) : 0u));
+          qt[j][e] = __builtin_bit_cast(__bf16, (uint16_t)(col < 2 * G && row_ok(col / 2) ? ((col & 1) ? lo : hi) : 0u));
         }
       }
     }
     const float csA = okA ? a.sm_scale * kLog2e : 0.f;
     const float csB = okB ? a.sm_scale * kLog2e : 0.f;
-    for (int kt = tk0; kt < ctt; kt += NG * kGroupWaves) {
+    for (int kt = tk0; kt < ctt; kt += NG * (PF ? 1 : kGroupWaves)) {
     const int ta = nq + kt * kTile, tb = min(n, ta + kTile);
-    for (int s0 = ta; s0 < tb; s0 += kStep) {
+    if (PF && ta > wlim) break;
+    for (int s0 = ta; s0 < tb && (!PF || s0 <= wlim); s0 += kStep) {
       f4_t d[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -386,23 +422,25 @@ void decode_split_kernel(DecodeArgs a) {
           d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt[j], *reinterpret_cast<const bf8_t*>(krow + kBlock * j),
                                                           d[m], 0, 0, 0);
       }
-      bool valid[2];
+      bool vA[2], vB[2];
       float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        valid[m] = s0 + 16 * m + col < tb;
+        const int tok = s0 + 16 * m + col;
+        vA[m] = tok < tb && (!PF || tok <= limA);
+        vB[m] = tok < tb && (!PF || tok <= limB);
         float ya = (d[m][0] + d[m][1]) * csA, yb = (d[m][2] + d[m][3]) * csB;
         asm volatile("" : "+v"(ya), "+v"(yb));
-        xA[m] = valid[m] && okA ? ya : -INFINITY;
-        xB[m] = valid[m] && okB ? yb : -INFINITY;
+        xA[m] = vA[m] && okA ? ya : -INFINITY;
+        xB[m] = vB[m] && okB ? yb : -INFINITY;
       }
       softmax(xA, xB, pA, pB);
       wave_sync();
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int t = 16 * m + col;
-        const float wA = valid[m] ? pA[m] : 0.f;
-        const float wB = valid[m] ? pB[m] : 0.f;
+        const float wA = vA[m] ? pA[m] : 0.f;
+        const float wB = vB[m] ? pB[m] : 0.f;
         const uint32_t hiA = f32_to_bf16_bits(wA), hiB = f32_to_bf16_bits(wB);
         wl[hA * WROW + t] = (uint16_t)hiA;
         wl[hB * WROW + t] = (uint16_t)hiB;
@@ -441,9 +479,16 @@ void decode_split_kernel(DecodeArgs a) {
     // of 8, so the query bytes follow that order.  Offset-binary codes need a
     // per-block correction -offset * sum(q_int), which seeds the low-byte rows
     // of the integer accumulators: cq[j] = {0, corr_hA, 0, corr_hB}.
+    // Prefill extends the query to 24 bits: a second product per block takes
+    // the residual byte rint(256 * (q / step - q_int)) in the odd rows (so its
+    // sums land in the same lanes), with its own offset correction.  Rows
+    // whose output nearly cancels need those bits on heavy-tailed data.
+    constexpr bool kQX = PF;
     long qop[NB];
+    long qres[kQX ? NB : 1];
     float ckA, ckB;
     i4_t cq[KB == 8 ? 1 : NB];
+    i4_t cq2[kQX && KB != 8 ? NB : 1];
     // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
     // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word
     const uint32_t rot_lo = (uint32_t)(2 * r + 28) & 31u;   // rotate left by 4 - 2r
@@ -511,24 +556,33 @@ void decode_split_kernel(DecodeArgs a) {
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
+          const long kop = k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi);
           const i4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-              qop[j], k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi),
-              KB == 8 ? i4_t{0, 0, 0, 0} : cq[KB == 8 ? 0 : j], 0, 0, 0);
+              qop[j], kop, KB == 8 ? i4_t{0, 0, 0, 0} : cq[KB == 8 ? 0 : j], 0, 0, 0);
           const int vA = (d[0] << 8) + d[1];
           const int vB = (d[2] << 8) + d[3];
           const float ks = half_of(R.ks[m][j / 2], j % 2);
-          sA[m] = __builtin_fmaf(ks, (float)vA, sA[m]);
-          sB[m] = __builtin_fmaf(ks, (float)vB, sB[m]);
+          float fA = (float)vA, fB = (float)vB;
+          if constexpr (kQX) {
+            const i4_t e = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                qres[j], kop, KB == 8 ? i4_t{0, 0, 0, 0} : cq2[KB == 8 ? 0 : j], 0, 0, 0);
+            fA = __builtin_fmaf((float)e[1], 0.00390625f, fA);
+            fB = __builtin_fmaf((float)e[3], 0.00390625f, fB);
+          }
+          sA[m] = __builtin_fmaf(ks, fA, sA[m]);
+          sB[m] = __builtin_fmaf(ks, fB, sB[m]);
         }
       }
       float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const bool valid = s0 + 16 * m + col < nq;
+        const int tok = s0 + 16 * m + col;
+        const bool validA = tok < nq && (!PF || tok <= limA);
+        const bool validB = tok < nq && (!PF || tok <= limB);
         float ya = sA[m] * ckA, yb = sB[m] * ckB;
         asm volatile("" : "+v"(ya), "+v"(yb));   // selects, not branches
-        xA[m] = valid && okA ? ya : -INFINITY;
-        xB[m] = valid && okB ? yb : -INFINITY;
+        xA[m] = validA && okA ? ya : -INFINITY;
+        xB[m] = validB && okB ? yb : -INFINITY;
       }
       softmax(xA, xB, pA, pB);
       // weights p * scale_v in fp16 (0 for masked tokens and absent heads),
@@ -561,12 +615,20 @@ void decode_split_kernel(DecodeArgs a) {
     // Tiles of [wq0, wq1) come from the workgroup's LDS counter, one tile
     // ahead: the second half of a tile and the first half of the next one
     // load while the half before computes.
+    uint32_t pf_next = 0;
     auto grab_issue = [&]() {
       uint32_t v = 0;
-      if (lane == 0) v = atomicAdd(&tile_ctr, 1u);
+      if constexpr (PF) {
+        v = pf_next++;
+      } else {
+        if (lane == 0) v = atomicAdd(&tile_ctr, 1u);
+      }
       return v;
     };
-    auto grab_read = [&](uint32_t v) { return wq0 + (int)__builtin_amdgcn_readfirstlane(v); };
+    auto grab_read = [&](uint32_t v) {
+      const int t = wq0 + (int)__builtin_amdgcn_readfirstlane(v);
+      return PF && t * kTile > wlim ? wq1 : t;   // past the rows' last position
+    };
     // query operands, built while the first loads are in flight
     auto prep_query = [&]() {
       float f[NB][8];
@@ -588,29 +650,45 @@ void decode_split_kernel(DecodeArgs a) {
       ckB = okB ? ckB : 0.f;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        int v[8];
-        int bsum = 0;
+        int v[8], res[8];
+        int bsum = 0, rsum = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          int x = (int)rintf(f[j][i] * inv);
+          const float t = f[j][i] * inv;
+          int x = (int)rintf(t);
           x = x > 32639 ? 32639 : (x < -32639 ? -32639 : x);
           v[i] = x;
           bsum += x;
+          if constexpr (kQX) {
+            int y = (int)rintf((t - (float)x) * 256.0f);
+            y = y > 127 ? 127 : (y < -127 ? -127 : y);
+            res[i] = y;
+            rsum += y;
+          }
         }
-        uint64_t w = 0;
+        uint64_t w = 0, wr = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int e = KB == 8 ? i : (i < 4 ? 2 * i : 2 * (i - 4) + 1);
           const int hi = (v[e] + 128) >> 8;
           const int byte = (col & 1) ? v[e] - 256 * hi : hi;
           w |= (uint64_t)(uint8_t)(int8_t)byte << (8 * i);
+          if constexpr (kQX) wr |= (uint64_t)(uint8_t)(int8_t)res[e] << (8 * i);
         }
-        qop[j] = col < 2 * G ? (long)w : 0;
+        const bool row_here = col < 2 * G && row_ok(col / 2);
+        qop[j] = row_here ? (long)w : 0;
+        if constexpr (kQX) qres[j] = row_here && (col & 1) ? (long)wr : 0;
         if constexpr (KB != 8) {
           bsum += __shfl_xor(bsum, 16);
           bsum += __shfl_xor(bsum, 32);
           const int corr = -(1 << (KB - 1)) * bsum;
           cq[KB == 8 ? 0 : j] = i4_t{0, okA ? __shfl(corr, 4 * r) : 0, 0, okB ? __shfl(corr, 4 * r + 2) : 0};
+          if constexpr (kQX) {
+            rsum += __shfl_xor(rsum, 16);
+            rsum += __shfl_xor(rsum, 32);
+            const int corr2 = -(1 << (KB - 1)) * rsum;
+            cq2[KB == 8 ? 0 : j] = i4_t{0, okA ? __shfl(corr2, 4 * r) : 0, 0, okB ? __shfl(corr2, 4 * r + 2) : 0};
+          }
         }
       }
     };
@@ -676,13 +754,12 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[i][k] += __shfl_xor(acc[i][k], 32);
   }
-  const size_t row0 = ((size_t)b * a.Hq + h0) * a.S + split;
   if (r < 2) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int h = 4 * r + k;
-      if (h < G) {
-        float* dst = a.part_acc + (row0 + (size_t)h * a.S) * D + col;
+      if (row_ok(h)) {
+        float* dst = a.part_acc + (row_vec(h) * a.S + split) * D + col;
 #pragma unroll
         for (int i = 0; i < NN; ++i) dst[16 * i] = acc[i][k];
       }
@@ -690,20 +767,20 @@ void decode_split_kernel(DecodeArgs a) {
   }
   if (col == 0) {
     if (okA) {
-      a.part_ml[(row0 + (size_t)hA * a.S) * 2] = mA;
-      a.part_ml[(row0 + (size_t)hA * a.S) * 2 + 1] = lA;
+      a.part_ml[(row_vec(hA) * a.S + split) * 2] = mA;
+      a.part_ml[(row_vec(hA) * a.S + split) * 2 + 1] = lA;
     }
     if (okB) {
-      a.part_ml[(row0 + (size_t)hB * a.S) * 2] = mB;
-      a.part_ml[(row0 + (size_t)hB * a.S) * 2 + 1] = lB;
+      a.part_ml[(row_vec(hB) * a.S + split) * 2] = mB;
+      a.part_ml[(row_vec(hB) * a.S + split) * 2 + 1] = lB;
     }
   }
 }
 
-template <int D, int KB, int VB, int G>
+template <int D, int KB, int VB, int G, bool PF = false>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G>), grid, dim3(64 * split_group_waves(D)), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF>), grid, dim3(64 * split_group_waves(D)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Decode attention: split combination and the table of split-K kernel
-// instantiations.
+// Decode and prefill attention: split combination and the tables of split-K
+// kernel instantiations.
 //
 // Combination merges the per-split (max, sum, weighted V) triples with the
 // log-sum-exp rule and rotates the result back to the original space
@@ -11,7 +11,8 @@
 namespace kvq {
 
 // Tables defined by the instantiation units, indexed [v_bits 4/5/8][G-1].
-#define KVQ_DECLARE_TABLE(D, KB) extern DecodeLauncher kvq_decode_table_##D##_##KB[3][8];
+#define KVQ_DECLARE_TABLE(D, KB) extern DecodeLauncher kvq_decode_table_##D##_##KB[3][8]; \
+  extern DecodeLauncher kvq_prefill_table_##D##_##KB[3];
 KVQ_DECLARE_TABLE(64, 4) KVQ_DECLARE_TABLE(64, 5) KVQ_DECLARE_TABLE(64, 8)
 KVQ_DECLARE_TABLE(128, 4) KVQ_DECLARE_TABLE(128, 5) KVQ_DECLARE_TABLE(128, 8)
 KVQ_DECLARE_TABLE(256, 4) KVQ_DECLARE_TABLE(256, 5) KVQ_DECLARE_TABLE(256, 8)
@@ -21,6 +22,17 @@ DecodeLauncher decode_launcher(int D, int kb, int vb, int gc) {
   const int vi = vb == 4 ? 0 : vb == 5 ? 1 : vb == 8 ? 2 : -1;
   if (vi < 0 || gc < 1 || gc > 8) return nullptr;
 #define KVQ_PICK(DD, KK) if (D == DD && kb == KK) return kvq_decode_table_##DD##_##KK[vi][gc - 1];
+  KVQ_PICK(64, 4) KVQ_PICK(64, 5) KVQ_PICK(64, 8)
+  KVQ_PICK(128, 4) KVQ_PICK(128, 5) KVQ_PICK(128, 8)
+  KVQ_PICK(256, 4) KVQ_PICK(256, 5) KVQ_PICK(256, 8)
+#undef KVQ_PICK
+  return nullptr;
+}
+
+DecodeLauncher prefill_launcher(int D, int kb, int vb) {
+  const int vi = vb == 4 ? 0 : vb == 5 ? 1 : vb == 8 ? 2 : -1;
+  if (vi < 0) return nullptr;
+#define KVQ_PICK(DD, KK) if (D == DD && kb == KK) return kvq_prefill_table_##DD##_##KK[vi];
   KVQ_PICK(64, 4) KVQ_PICK(64, 5) KVQ_PICK(64, 8)
   KVQ_PICK(128, 4) KVQ_PICK(128, 5) KVQ_PICK(128, 8)
   KVQ_PICK(256, 4) KVQ_PICK(256, 5) KVQ_PICK(256, 8)

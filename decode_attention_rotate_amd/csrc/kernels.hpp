@@ -59,6 +59,7 @@ struct DecodeArgs {
   float* part_ml;            // [B][Hq][S][2]  running max (log2 units), sum
   float* part_acc;           // [B][Hq][S][D]  unnormalised output, rotated space
   int32_t Hkv, Hq, G, n_gchunks, T, cap, S;
+  int32_t n_q, n_rb;         // prefill: queries per sequence, 64-row blocks per KV head
   int32_t q_dtype, rotate_k;
   float cd, sm_scale;        // fp32(1/sqrt(D)); softmax scale
   int32_t len[KVQ_MAX_BATCH];
@@ -66,6 +67,8 @@ struct DecodeArgs {
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
 // Table lookup for (D, k_bits, v_bits, heads per chunk); nullptr if absent.
 DecodeLauncher decode_launcher(int D, int kb, int vb, int gc);
+// The prefill variant of the split kernel for (D, k_bits, v_bits).
+DecodeLauncher prefill_launcher(int D, int kb, int vb);
 
 // Largest split count the host schedules (bounds the combine kernel's LDS).
 constexpr int kMaxSplitsDevice = 1024;

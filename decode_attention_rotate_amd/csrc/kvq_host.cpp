@@ -106,6 +106,25 @@ int max_splits(const kvq_config& c, int n_q_heads) {
   return split_count(c.head_dim, units, c.max_ctx);
 }
 
+// Chunked prefill: the n_q * G rows of a KV head go in blocks of 8 rows per
+// wave of a workgroup; each row block is split along the cache into S
+// ranges, enough workgroups for one per compute unit (256), at most one per
+// 64-token tile of the longest sequence.  Non-decreasing in max_len.
+struct PrefillSchedule {
+  int n_rb, S;
+};
+PrefillSchedule prefill_schedule(const kvq_config& c, int n_q_heads, int n_q, int max_len) {
+  PrefillSchedule p;
+  const int64_t G = n_q_heads / c.n_kv_heads;
+  const int64_t rows_per_block = 8 * split_group_waves(c.head_dim);
+  p.n_rb = (int)(((int64_t)n_q * G + rows_per_block - 1) / rows_per_block);
+  const int64_t blocks = (int64_t)c.batch * c.n_kv_heads * p.n_rb;
+  const int64_t tiles = std::max(1, (max_len + kTile - 1) / kTile);
+  const int64_t want = std::max<int64_t>(1, (256 + blocks - 1) / blocks);
+  p.S = (int)std::min<int64_t>(std::min<int64_t>(want, tiles), kMaxSplits);
+  return p;
+}
+
 // Workspace: (max, sum) pairs, then partial vectors, per split.
 struct WsLayout {
   size_t ml, acc, total;
@@ -270,6 +289,86 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   ca.out = out;
   ca.Hq = n_q_heads;
   ca.S = sc.S;
+  ca.rotate = c.rotate_v;
+  ca.cd = cd;
+  return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
+}
+
+size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads, int32_t n_q) {
+  if (check_cfg(cfg) != KVQ_OK) return 0;
+  if (n_q_heads < cfg->n_kv_heads || n_q_heads % cfg->n_kv_heads != 0 || n_q < 1) return 0;
+  if ((int64_t)n_q * n_q_heads > 2147483647 / 8) return 0;
+  const PrefillSchedule p = prefill_schedule(*cfg, n_q_heads, n_q, cfg->max_ctx);
+  return ws_layout(*cfg, n_q * n_q_heads, p.S).total;
+}
+
+kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                 kvq_dtype dtype, int32_t n_q_heads, int32_t n_q, float sm_scale,
+                                 const int32_t* seq_len, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = *cfg;
+  if ((st = check_cache(c, cache)) != KVQ_OK) return st;
+  if (dtype != KVQ_BF16 && dtype != KVQ_F32) return KVQ_ERR_INVALID;
+  if (!q || !out || !workspace || !seq_len) return KVQ_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (n_q_heads < c.n_kv_heads || n_q_heads % c.n_kv_heads != 0 || n_q < 1) return KVQ_ERR_INVALID;
+  if ((int64_t)c.batch * n_q * n_q_heads > 2147483647 / 8) return KVQ_ERR_INVALID;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  int max_len = 0;
+  for (int b = 0; b < c.batch; ++b) {
+    if (seq_len[b] < n_q) return KVQ_ERR_INVALID;
+    if (seq_len[b] > c.max_ctx) return KVQ_ERR_CAPACITY;
+    max_len = std::max(max_len, (int)seq_len[b]);
+  }
+  const PrefillSchedule ps = prefill_schedule(c, n_q_heads, n_q, max_len);
+  if ((int64_t)c.n_kv_heads * ps.n_rb > 65535) return KVQ_ERR_INVALID;
+  const WsLayout wl = ws_layout(c, n_q * n_q_heads, ps.S);
+  if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
+  const DecodeLauncher fn = prefill_launcher(c.head_dim, c.k_bits, c.v_bits);
+  if (!fn) return KVQ_ERR_UNSUPPORTED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const float cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+
+  DecodeArgs da;
+  std::memset(&da, 0, sizeof(da));
+  da.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+  da.k_scales = static_cast<const uint16_t*>(cache->k_scales);
+  da.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+  da.v_scales = static_cast<const uint16_t*>(cache->v_scales);
+  da.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+  da.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+  da.q = q;
+  da.q_dtype = dtype;
+  da.rotate_k = c.rotate_k;
+  da.cd = cd;
+  da.sm_scale = sm_scale;
+  da.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+  da.part_acc = reinterpret_cast<float*>(ws + wl.acc);
+  da.Hkv = c.n_kv_heads;
+  da.Hq = n_q_heads;
+  da.G = n_q_heads / c.n_kv_heads;
+  da.n_gchunks = 1;
+  da.T = c.tail_len;
+  da.cap = (int32_t)cap_tokens(c);
+  da.S = ps.S;
+  da.n_q = n_q;
+  da.n_rb = ps.n_rb;
+  for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
+  const dim3 grid(ps.S, c.n_kv_heads * ps.n_rb, c.batch);
+  if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
+  if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
+  if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
+
+  CombineArgs ca;
+  ca.part_ml = da.part_ml;
+  ca.part_acc = da.part_acc;
+  ca.out = out;
+  ca.Hq = n_q * n_q_heads;   // rows [B][n_q][Hq] are combined like heads
+  ca.S = ps.S;
   ca.rotate = c.rotate_v;
   ca.cd = cd;
   return hip_status(launch_combine(c.head_dim, ca, c.batch, s));

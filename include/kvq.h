@@ -169,6 +169,43 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* Workspace bytes kvq_prefill_attention needs for n_q_heads query heads and
+ * n_q queries per sequence at any length up to cfg->max_ctx; 0 if the
+ * arguments are invalid. */
+size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads,
+                                   int32_t n_q);
+
+/* Chunked prefill (prompt processing) attention over the cache: the n_q
+ * queries of each sequence are its last n_q positions, whose K/V a previous
+ * kvq_rotate_quantize_append stored; query i sits at position
+ * seq_len[b] - n_q + i and attends causally to positions 0..that position,
+ * reading the cache as it stands (a position that left the bf16 tail during
+ * the chunk is read quantized).  Per query the steps are those of
+ * kvq_decode_attention (velog.io post "fix KV cache quantization outliers",
+ * section "Hadamard rotation"; the post's section "compute cost and speed"
+ * reports the rotation's cost on prompt processing).
+ *  q:        device [batch][n_q][n_q_heads][head_dim] of `dtype`.
+ *  n_q:      queries per sequence, 1 <= n_q <= seq_len[b] for every b.
+ *  sm_scale: multiplier of q.k before the softmax.
+ *  seq_len:  host [batch], tokens cached per sequence (the chunk included).
+ *  out:      device [batch][n_q][n_q_heads][head_dim] float32, original space.
+ *  workspace/workspace_bytes: device scratch of at least
+ *            kvq_prefill_workspace_bytes(cfg, n_q_heads, n_q) bytes
+ *            (KVQ_ERR_WORKSPACE otherwise), owned by the caller; contents
+ *            need no initialisation.
+ * Results are deterministic.  kvq_profile_decode_events instruments this
+ * call's split kernel too.
+ * Errors: KVQ_ERR_INVALID if n_q_heads is not a positive multiple of
+ * n_kv_heads, n_q < 1, a length is below n_q, sm_scale is not finite or the
+ * rows of one KV head exceed 65535 blocks of 64; KVQ_ERR_CAPACITY if a length
+ * exceeds max_ctx. */
+kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                 const void* q, kvq_dtype dtype,
+                                 int32_t n_q_heads, int32_t n_q, float sm_scale,
+                                 const int32_t* seq_len, float* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Read back positions [t0, t1) of sequence b from the K (which = 0) or V
  * (which = 1) cache as float32 [t1-t0][n_kv_heads][head_dim]: code * scale
  * for quantized positions, the stored bf16 value for tail positions.

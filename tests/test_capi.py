@@ -152,3 +152,29 @@ def test_dequantize_validation():
     assert deq(0, 0, 0, 5, out=FAKE_MISALIGNED) == _capi.KVQ_ERR_ALIGN
     assert deq(0, 0, 0, 5, out=0) == _capi.KVQ_ERR_INVALID
     assert deq(0, 0, 3, 3, out=0) == _capi.KVQ_OK                    # empty range
+
+
+def test_prefill_workspace_bytes():
+    c = kvq.kvq_config(1, 8, 128, 65536, 8, 4, 1024)
+    ws = kvq.kvq_prefill_workspace_bytes(c, 40, 512)
+    assert ws >= 512 * 40 * (128 + 2) * 4                   # at least one split per row
+    assert kvq.kvq_prefill_workspace_bytes(c, 40, 1) <= ws
+    assert kvq.kvq_prefill_workspace_bytes(c, 12, 16) == 0    # not a multiple of 8
+    assert kvq.kvq_prefill_workspace_bytes(c, 40, 0) == 0
+
+
+def _prefill(c, hq, n_q, lens, ws_bytes=1 << 40, sm=0.1, q=FAKE, out=FAKE):
+    return L.kvq_prefill_attention(ctypes.byref(c), ctypes.byref(_cache()), q, 0, hq, n_q, sm,
+                                   lens, out, FAKE, ws_bytes, None)
+
+
+def test_prefill_validation():
+    c = kvq.kvq_config(2, 4, 128, 100, 8, 4, 0)
+    assert _prefill(c, 6, 4, _lens(5, 5)) == _capi.KVQ_ERR_INVALID    # 6 % 4 != 0
+    assert _prefill(c, 8, 0, _lens(5, 5)) == _capi.KVQ_ERR_INVALID    # no query
+    assert _prefill(c, 8, 6, _lens(5, 9)) == _capi.KVQ_ERR_INVALID    # length below n_q
+    assert _prefill(c, 8, 4, _lens(5, 101)) == _capi.KVQ_ERR_CAPACITY
+    assert _prefill(c, 8, 4, _lens(5, 5), sm=float("inf")) == _capi.KVQ_ERR_INVALID
+    assert _prefill(c, 8, 4, _lens(5, 5), ws_bytes=100) == _capi.KVQ_ERR_WORKSPACE
+    assert _prefill(c, 8, 4, _lens(5, 5), q=FAKE_MISALIGNED) == _capi.KVQ_ERR_ALIGN
+    assert _prefill(c, 8, 4, _lens(5, 5), out=0) == _capi.KVQ_ERR_INVALID

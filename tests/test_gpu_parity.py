@@ -16,7 +16,7 @@ import pytest
 
 import workloads
 from gpu_common import Pair, say, to_device, to_values, attention_errors, gpu_planes
-from oracle import dequantize_reference
+from oracle import dequantize_reference, prefill_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -243,3 +243,72 @@ def test_decode_reuses_one_workspace():
         errs = attention_errors(got.cpu().numpy(), planes, to_values(q, "bf16"), list(pair.lens),
                                 pair.cfg)
         assert max(errs.values()) <= TOL, (call, hq, max(errs.values()))
+
+
+PREFILL_CASES = [
+    # name, workload overrides, lengths before the chunk, n_q
+    ("tiny", dict(), [0], 64),                          # from scratch: a full causal square
+    ("long", dict(B=2, tail=1024), [700, 300], 40),     # the chunk stays in the bf16 tail
+    ("long", dict(B=1, tail=16), [500], 50),            # tokens leave the tail during the chunk
+    ("mid", dict(B=2), [300, 0], 37),                   # no tail, ragged, one from scratch
+    ("huge", dict(B=1, Hq=8), [200], 70),               # d256, 5-bit K
+    ("small", dict(Hq=24), [0], 129),                   # G = 3, several row blocks
+    ("small", dict(Hq=56, dtype="f32"), [100], 10),     # G = 7, float32 queries
+    ("tiny", dict(B=2, k_bits=8, v_bits=5, tail=8), [64, 1], 3),
+]
+
+
+def _prefill_case(w, before, n_q, rot=True):
+    B = len(before)
+    w["B"] = B
+    d, dtype = w["d"], w["dtype"]
+    pair = Pair(B, w["Hkv"], d, w["k_bits"], w["v_bits"], w["tail"], max(before) + n_q + 5, rot, rot)
+    if max(before) > 0:
+        _fill(pair, w, before, dtype)
+    k = workloads.kv_numpy(w, 1, 20000, 20000 + n_q)
+    v = workloads.kv_numpy(w, 2, 20000, 20000 + n_q)
+    pair.append(k, v, dtype)
+    return pair
+
+
+@pytest.mark.parametrize("name,over,before,n_q", PREFILL_CASES,
+                         ids=["%s-%d" % (c[0], i) for i, c in enumerate(PREFILL_CASES)])
+def test_prefill_attention(name, over, before, n_q):
+    import decode_attention_rotate_amd as kvq
+    w = workloads.workload(name, **over)
+    pair = _prefill_case(w, before, n_q)
+    lens = list(pair.lens)
+    q = workloads.prefill_q_numpy(w, n_q)
+    say("prefill", name, "n_q=%d" % n_q, "lens=%s" % lens)
+    got = kvq.kvq_prefill_attention(pair.cfg, pair.cache, to_device(q, w["dtype"]), lens)
+    got = got.cpu().numpy().astype(np.float64)
+    planes = gpu_planes(pair.cache, pair.cfg)
+    ref = prefill_reference(planes, to_values(q, w["dtype"]), lens, w["Hkv"], w["d"],
+                            w["k_bits"], w["v_bits"], w["tail"])
+    err = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    say("prefill worst rel L2 %.3e" % err.max())
+    assert err.max() <= TOL, np.unravel_index(np.argmax(err), err.shape)
+
+
+def test_prefill_one_query_and_rotation_off():
+    # one query is a decode step; with rotation off the oracle skips both
+    # rotations and so must the kernel
+    import decode_attention_rotate_amd as kvq
+    w = workloads.workload("long", B=2, tail=32)
+    pair = _prefill_case(w, [400, 90], 1)
+    q = workloads.prefill_q_numpy(w, 1)
+    qd = to_device(q, "bf16")
+    pre = kvq.kvq_prefill_attention(pair.cfg, pair.cache, qd, list(pair.lens)).cpu().numpy()
+    dec = kvq.kvq_decode_attention(pair.cfg, pair.cache, qd[:, 0].contiguous(),
+                                   list(pair.lens)).cpu().numpy()
+    rel = np.linalg.norm(pre[:, 0] - dec, axis=-1) / np.linalg.norm(dec, axis=-1)
+    assert rel.max() <= TOL, rel.max()
+    w2 = workloads.workload("small", B=1, Hq=16)
+    pair2 = _prefill_case(w2, [150], 33, rot=False)
+    q2 = workloads.prefill_q_numpy(w2, 33)
+    got = kvq.kvq_prefill_attention(pair2.cfg, pair2.cache, to_device(q2, "bf16"),
+                                    list(pair2.lens)).cpu().numpy().astype(np.float64)
+    ref = prefill_reference(gpu_planes(pair2.cache, pair2.cfg), to_values(q2, "bf16"),
+                            list(pair2.lens), 8, 128, 8, 8, 0, rotate_k=False, rotate_v=False)
+    err = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    assert err.max() <= TOL, err.max()

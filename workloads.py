@@ -121,6 +121,13 @@ def q_numpy(w, step=0):
     return to_bf16_bits(x) if w["dtype"] == "bf16" else x
 
 
+def prefill_q_numpy(w, n_q, step=0):
+    """Queries [B][n_q][Hq][d] of a prompt chunk (float32 or bf16 bits)."""
+    rng = np.random.default_rng((w["idx"], 5, step))
+    x = _draw(rng, w["dist"], (w["B"], n_q, w["Hq"], w["d"]))
+    return to_bf16_bits(x) if w["dtype"] == "bf16" else x
+
+
 def new_tokens_numpy(w, role, step, n_new=1):
     """Tokens appended at decode step `step`: [B][n_new][Hkv][d]."""
     rng = np.random.default_rng((w["idx"], 4, role, step))
@@ -168,6 +175,15 @@ def q_torch(w, step, device, torch):
     gen = torch.Generator(device=device)
     gen.manual_seed(((w["idx"] * 8 + 3) << 32) + step)
     x = _torch_draw(torch, gen, w["dist"], (w["B"], w["Hq"], w["d"]), device)
+    dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+    return x.to(dt).contiguous()
+
+
+def prefill_q_torch(w, n_q, step, device, torch):
+    """Device-side queries [B][n_q][Hq][d] of a prompt chunk."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(((w["idx"] * 8 + 5) << 32) + step)
+    x = _torch_draw(torch, gen, w["dist"], (w["B"], n_q, w["Hq"], w["d"]), device)
     dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     return x.to(dt).contiguous()
 
