@@ -147,6 +147,9 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the bulk append measurement")
     ap.add_argument("--no-rotation-off", action="store_true",
                     help="skip the secondary run with rotation disabled")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the chunked-prefill measurement (for profiling) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -172,6 +175,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps(prefill_bench(torch, kvq, dev)), flush=True)
+        return 0
     w = workloads.workload(args.workload)
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     log("workload", describe(w))
@@ -236,6 +242,8 @@ def main():
 
     if not args.no_append:
         result["append"] = bulk_append(torch, kvq, dev)
+    if not args.no_prefill:
+        result["prefill"] = prefill_bench(torch, kvq, dev)
 
     if not args.no_cpu_baseline:
         q_host = q0.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -336,6 +344,68 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep):
            "app_ms": [ev_app[s][0].elapsed_time(ev_app[s][1]) for s in timed],
            "fill_mtok_s": fill_mtok_s, "q0": qs[0]}
     del cache, qs, ks, vs
+    return res
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_bench(torch, kvq, dev, n_q=512):
+    """Chunked prefill at the long workload's shape with batch 1: append a
+    chunk of n_q tokens after 65536 - n_q cached ones, then attend its n_q
+    queries causally over the cache.  Algorithmic work: 4 * d flops per
+    (query head, visible position) pair (Q.K and P.V multiply-adds)."""
+    w = workloads.workload("long", B=1)
+    B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
+    n0 = n - n_q
+    cfg = kvq.kvq_config(B, Hkv, d, n, w["k_bits"], w["v_bits"], w["tail"])
+    cache = kvq.KVCache(cfg, dev)
+    for t0 in range(0, n0, FILL_CHUNK):
+        t1 = min(n0, t0 + FILL_CHUNK)
+        kvq.kvq_rotate_quantize_append(cfg, cache, workloads.kv_torch(w, 1, t0, t1, dev, torch),
+                                       workloads.kv_torch(w, 2, t0, t1, dev, torch), [t0])
+    k = workloads.kv_torch(w, 1, n0, n, dev, torch)
+    v = workloads.kv_torch(w, 2, n0, n, dev, torch)
+    q = workloads.prefill_q_torch(w, n_q, 0, dev, torch)
+    out = torch.empty((B, n_q, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.kvq_prefill_workspace_bytes(cfg, Hq, n_q), dtype=torch.uint8, device=dev)
+    reps = 5
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(3 * (reps + 1))]
+    app_ms, att_ms, kern_ms = [], [], []
+    for r in range(reps + 1):
+        e = ev[3 * r: 3 * r + 3]
+        e[0][0].record()
+        kvq.kvq_rotate_quantize_append(cfg, cache, k, v, [n0])
+        e[0][1].record()
+        e[1][0].record()
+        kvq.kvq_prefill_attention(cfg, cache, q, [n], out=out, workspace=ws)
+        e[1][1].record()
+        kvq.kvq_profile_decode_events(e[2][0], e[2][1])
+        kvq.kvq_prefill_attention(cfg, cache, q, [n], out=out, workspace=ws)
+        kvq.kvq_profile_decode_events(None, None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "non-finite prefill output"
+    for r in range(1, reps + 1):
+        e = ev[3 * r: 3 * r + 3]
+        app_ms.append(e[0][0].elapsed_time(e[0][1]))
+        att_ms.append(e[1][0].elapsed_time(e[1][1]))
+        kern_ms.append(kvq.kernel_elapsed_ms(e[2][0], e[2][1]))
+    visible = sum(n0 + i + 1 for i in range(n_q))
+    flops = 4.0 * d * Hq * B * visible
+    att = float(np.median(att_ms))
+    kern = float(np.median(kern_ms))
+    app = float(np.median(app_ms))
+    res = {"workload": "prefill: batch 1, 40 query / 8 KV heads, head_dim 128, K8 V4, bf16 tail "
+                       "1024, chunk of %d tokens appended after %d cached, causal attention of "
+                       "its %d queries" % (n_q, n0, n_q),
+           "append_us": round(app * 1e3, 1), "attention_us": round(att * 1e3, 1),
+           "split_kernel_us": round(kern * 1e3, 1),
+           "query_tokens_per_s": round(n_q * B / ((att + app) * 1e-3), 1),
+           "algorithmic_tflops": round(flops / (kern * 1e-3) / 1e12, 2),
+           "pct_f16_mfma_peak": round(100 * flops / (kern * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 2)}
+    log("prefill", res)
+    del cache, k, v, q, out, ws
     return res
 
 
