@@ -17,7 +17,7 @@ Readings:
 * R14 The output is float32-valued, in the original (unrotated) space.
 * R15 rotate_k off: neither q nor K is rotated; rotate_v off: V is not
       rotated and the output is not rotated back.
-* R19 Chunked prefill (prompt processing, whose rotation cost the velog.io
+* R20 Chunked prefill (prompt processing, whose rotation cost the velog.io
       post reports in section "compute cost and speed"): the n_q queries of a
       chunk are the last n_q positions of the sequence, already appended;
       query i sits at position p = n - n_q + i and attends to positions
@@ -102,7 +102,7 @@ def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
     """Reference output [B][n_q][Hq][d] (float64) of chunked prefill attention.
 
     q: float values [B][n_q][Hq][d], the queries of the last n_q positions of
-    each sequence (R19); lens[b] >= n_q is the length after the chunk.
+    each sequence (R20); lens[b] >= n_q is the length after the chunk.
     rows: optional iterable of (b, i, h) triples to evaluate; others stay NaN."""
     q = np.asarray(q, dtype=np.float64)
     B, n_q, Hq, _ = q.shape

@@ -1,4 +1,4 @@
-"""Pins for the oracle's chunked-prefill attention (reading R19: the chunk's
+"""Pins for the oracle's chunked-prefill attention (reading R20: the chunk's
 queries are the last n_q positions and attend causally to the cache as it
 stands after the chunk was appended; prompt processing is the cost the
 velog.io post "fix KV cache quantization outliers" reports in section
