@@ -37,7 +37,8 @@ only by this specification plus those invariants; the pages print no worked
 example or test vector (parity unpinned against any external implementation).
 """
 
-from .rotation import hadamard, rot_scale_f32, fwht_f32, rotate_f32
+from .rotation import (hadamard, rot_scale_f32, fwht_f32, rotate_f32, unrotate_f32,
+                       hadamard_signs, rotation_matrix, splitmix64)
 from .blockquant import (
     QMAX, BLOCK, bf16_round, bf16_bits_to_f32, f32_to_bf16_bits,
     quantize_blocks, dequantize_blocks, pack_rows, unpack_rows,
@@ -48,7 +49,8 @@ from .attention import (softmax_attention, decode_reference, dequantize_unit,
                         dequantize_reference, prefill_reference)
 
 __all__ = [
-    "hadamard", "rot_scale_f32", "fwht_f32", "rotate_f32",
+    "hadamard", "rot_scale_f32", "fwht_f32", "rotate_f32", "unrotate_f32",
+    "hadamard_signs", "rotation_matrix", "splitmix64",
     "QMAX", "BLOCK", "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "quantize_blocks", "dequantize_blocks", "pack_rows", "unpack_rows",
     "row_bytes", "padded_row_bytes", "rows_to_tiled", "tiled_to_rows",

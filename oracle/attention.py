@@ -28,7 +28,7 @@ Readings:
 
 import numpy as np
 
-from .rotation import hadamard, rotate_f32
+from .rotation import rotation_matrix, unrotate_f32, hadamard_signs
 from .blockquant import bf16_bits_to_f32
 from .kvcache import dequantize_rows
 
@@ -67,17 +67,19 @@ def dequantize_unit(planes, b, g, n, d, k_bits, v_bits, tail_len):
 
 def decode_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
                      tail_len, sm_scale=None, rotate_k=True, rotate_v=True,
-                     heads=None):
+                     heads=None, sign_seed=0):
     """Reference output [B][Hq][d] (float64) of decode attention.
 
     q: float values [B][Hq][d] (already widened from bf16 if needed).
-    heads: optional iterable of (b, h) pairs to evaluate; others stay NaN."""
+    heads: optional iterable of (b, h) pairs to evaluate; others stay NaN.
+    sign_seed: the randomized-sign rotation R = H diag(s) of reading R21
+    (0: H); q is rotated by R and the output by R^T."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, _ = q.shape
     G = Hq // n_kv_heads
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(d)
-    H = hadamard(d)
+    H = rotation_matrix(d, sign_seed)
     out = np.full((B, Hq, d), np.nan)
     want = set(heads) if heads is not None else None
     cache = {}
@@ -92,24 +94,25 @@ def decode_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
             K, V = cache[(b, g)]
             qr = H @ q[b, h] if rotate_k else q[b, h]
             o = softmax_attention(qr, K, V, sm_scale)
-            out[b, h] = H @ o if rotate_v else o
+            out[b, h] = H.T @ o if rotate_v else o
     return out
 
 
 def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
                       tail_len, sm_scale=None, rotate_k=True, rotate_v=True,
-                      rows=None):
+                      rows=None, sign_seed=0):
     """Reference output [B][n_q][Hq][d] (float64) of chunked prefill attention.
 
     q: float values [B][n_q][Hq][d], the queries of the last n_q positions of
     each sequence (R20); lens[b] >= n_q is the length after the chunk.
-    rows: optional iterable of (b, i, h) triples to evaluate; others stay NaN."""
+    rows: optional iterable of (b, i, h) triples to evaluate; others stay NaN.
+    sign_seed: as for decode_reference."""
     q = np.asarray(q, dtype=np.float64)
     B, n_q, Hq, _ = q.shape
     G = Hq // n_kv_heads
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(d)
-    H = hadamard(d)
+    H = rotation_matrix(d, sign_seed)
     out = np.full((B, n_q, Hq, d), np.nan)
     want = set(rows) if rows is not None else None
     cache = {}
@@ -127,17 +130,18 @@ def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
                 K, V = cache[(b, g)]
                 qr = H @ q[b, i, h] if rotate_k else q[b, i, h]
                 o = softmax_attention(qr, K[:p + 1], V[:p + 1], sm_scale)
-                out[b, i, h] = H @ o if rotate_v else o
+                out[b, i, h] = H.T @ o if rotate_v else o
     return out
 
 
 def dequantize_reference(planes, which, b, t0, t1, n, n_kv_heads, d, bits,
-                         tail_len, space, rotate=True):
+                         tail_len, space, rotate=True, sign_seed=0):
     """Dequantized positions [t0, t1) of sequence b (length n), all KV heads.
 
     space 0: rotated space (exact float32).  space 1: original space, i.e. the
     rotated value multiplied by H again in float32 with the fixed stage order
-    (H is its own inverse), so the GPU must match bit for bit."""
+    (H is its own inverse) and then by the signs of R21, so the GPU must match
+    bit for bit."""
     p = "k" if which == 0 else "v"
     T = int(tail_len)
     nt = min(n, T) if T > 0 else 0
@@ -153,5 +157,5 @@ def dequantize_reference(planes, which, b, t0, t1, n, n_kv_heads, d, bits,
             else:
                 out[pos - t0, g] = bf16_bits_to_f32(planes[p + "_tail"][b, g, pos % T])
     if space == 1:
-        out = rotate_f32(out, rotate)
+        out = unrotate_f32(out, rotate, hadamard_signs(d, sign_seed))
     return out

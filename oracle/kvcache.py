@@ -20,7 +20,7 @@ Readings (the pages do not fix these):
 
 import numpy as np
 
-from .rotation import rotate_f32
+from .rotation import rotate_f32, hadamard_signs
 from .blockquant import (
     BLOCK, TILE, quantize_blocks, dequantize_blocks, pack_rows, unpack_rows,
     row_bytes, padded_row_bytes, rows_to_tiled, tiled_to_rows,
@@ -45,8 +45,9 @@ class OracleCache:
     """
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits,
-                 tail_len, max_ctx, rotate_k=True, rotate_v=True):
+                 tail_len, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0):
         self.B, self.H, self.d = batch, n_kv_heads, head_dim
+        self.signs = hadamard_signs(head_dim, sign_seed)      # reading R21
         self.bits = {"k": k_bits, "v": v_bits}
         self.rot = {"k": bool(rotate_k), "v": bool(rotate_v)}
         self.T = int(tail_len)
@@ -73,7 +74,7 @@ class OracleCache:
             raise ValueError("append exceeds max_ctx")
         for p, new in (("k", k_new), ("v", v_new)):
             x = _widen(new, dtype)
-            y = rotate_f32(x, self.rot[p])                  # [B][n][H][d]
+            y = rotate_f32(x, self.rot[p], self.signs)      # [B][n][H][d]
             for b in range(self.B):
                 self._append_one(p, b, y[b], int(lens[b]))
         return lens + n_new

@@ -15,6 +15,14 @@ Readings (the page does not fix these):
 * R4  The float32 fast Walsh-Hadamard transform runs its stages in the order
       h = 1, 2, 4, ..., d/2 with butterflies (a + b, a - b); the order changes
       rounding, so it is fixed here and the GPU follows it.
+* R21 Randomized-sign variant (a direction the velog.io post names in section
+      "application and background", with no algorithm): R = H diag(s) with
+      s_e = +-1 taken from SplitMix64 (Steele, Lea and Flood, "Fast splittable
+      pseudorandom number generators", OOPSLA 2014) of the 64-bit counter
+      seed * 2^32 + e: s_e = -1 iff the top bit of the output is set.  Seed 0
+      is the plain matrix of R1.  A vector is rotated as H (s * x) and rotated
+      back as s * (H y); sign flips are exact, so the float32 transform and
+      its stage order are unchanged.
 """
 
 import numpy as np
@@ -36,6 +44,35 @@ def hadamard(d):
         parity ^= x & 1
         x >>= 1
     return np.where(parity == 1, -1.0, 1.0) / np.sqrt(float(d))
+
+
+_M64 = (1 << 64) - 1
+
+
+def splitmix64(x):
+    """One SplitMix64 output for the 64-bit counter x (published mixing
+    function: add the golden-gamma increment, then two xor-shift-multiply
+    rounds and a final xor-shift)."""
+    z = (x + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def hadamard_signs(d, seed):
+    """The sign vector s (float64 +-1, length d) of reading R21, or None for
+    seed 0 (no signs)."""
+    if seed == 0:
+        return None
+    seed &= 0xFFFFFFFF
+    return np.array([-1.0 if splitmix64((seed << 32) | e) >> 63 else 1.0 for e in range(d)])
+
+
+def rotation_matrix(d, seed=0):
+    """Dense R = H diag(s) in float64 (H alone for seed 0)."""
+    H = hadamard(d)
+    s = hadamard_signs(d, seed)
+    return H if s is None else H * s[None, :]
 
 
 def rot_scale_f32(d):
@@ -68,14 +105,29 @@ def fwht_f32(x):
     return x
 
 
-def rotate_f32(x, enabled=True):
-    """y = fp32(1/sqrt(d)) * FWHT(x) in float32, or x unchanged if disabled.
+def rotate_f32(x, enabled=True, signs=None):
+    """y = fp32(1/sqrt(d)) * FWHT(s * x) in float32, or x unchanged if disabled.
 
     velog.io post, section "Hadamard rotation" (rotate before storing);
-    readings R1, R3, R4.  The per-plane switch follows the separate K and V
-    disable variables named in section "application and background".
+    readings R1, R3, R4, R21 (signs: a +-1 vector or None).  The per-plane
+    switch follows the separate K and V disable variables named in section
+    "application and background".
     """
     x = np.asarray(x, dtype=np.float32)
     if not enabled:
         return x.copy()
+    if signs is not None:
+        x = x * np.asarray(signs, dtype=np.float32)
     return fwht_f32(x) * rot_scale_f32(x.shape[-1])
+
+
+def unrotate_f32(y, enabled=True, signs=None):
+    """The inverse rotation in float32: s * (fp32(1/sqrt(d)) * FWHT(y)), or y
+    unchanged if disabled (H is symmetric and orthogonal; R21)."""
+    y = np.asarray(y, dtype=np.float32)
+    if not enabled:
+        return y.copy()
+    out = fwht_f32(y) * rot_scale_f32(y.shape[-1])
+    if signs is not None:
+        out = out * np.asarray(signs, dtype=np.float32)
+    return out
