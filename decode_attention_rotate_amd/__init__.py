@@ -40,7 +40,7 @@ def kvq_config_default(batch, n_kv_heads, head_dim, max_ctx):
 
 
 def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
-               tail_len=0, rotate_k=None, rotate_v=None):
+               tail_len=0, rotate_k=None, rotate_v=None, sign_seed=0):
     """kvq_config_default with fields overridden; validated by the library."""
     c = kvq_config_default(batch, n_kv_heads, head_dim, max_ctx)
     c.k_bits, c.v_bits, c.tail_len = k_bits, v_bits, tail_len
@@ -48,6 +48,7 @@ def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
         c.rotate_k = int(rotate_k)
     if rotate_v is not None:
         c.rotate_v = int(rotate_v)
+    c.sign_seed = int(sign_seed) & 0xFFFFFFFF
     _capi.check(_capi.lib().kvq_config_check(ctypes.byref(c)), "kvq_config")
     return c
 

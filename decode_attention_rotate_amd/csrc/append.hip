@@ -212,7 +212,10 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
     for (int e = 0; e < 32; ++e) x[e] = 0.f;
   }
   // every lane takes part in the cross-lane stages
-  if (a.rotate[pl]) rotate_row<D>(x, lane, a.cd);
+  if (a.rotate[pl]) {
+    if (a.has_signs) apply_signs(x, a.signs[j]);
+    rotate_row<D>(x, lane, a.cd);
+  }
   if (T > 0) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = bf16_round(x[e]);
@@ -284,7 +287,10 @@ __device__ void tail_part(const AppendArgs& a, int bx, int g, int b, int pl) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.f;
   }
-  if (a.rotate[pl]) rotate_row<D>(x, lane, a.cd);
+  if (a.rotate[pl]) {
+    if (a.has_signs) apply_signs(x, a.signs[j]);
+    rotate_row<D>(x, lane, a.cd);
+  }
   if (!active) return;
   const size_t unit = (size_t)b * Hkv + g;
   uint4* dst = reinterpret_cast<uint4*>(a.tail[pl] + (unit * T + p % T) * D + kBlock * j);
@@ -370,7 +376,10 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
     }
   }
 
-  if (a.rotate[pl]) rotate_row<D>(x, lane, a.cd);   // every lane takes part
+  if (a.rotate[pl]) {                            // every lane takes part
+    if (a.has_signs) apply_signs(x, a.signs[j]);
+    rotate_row<D>(x, lane, a.cd);
+  }
   if (q_lane) {
     float z[32];
 #pragma unroll

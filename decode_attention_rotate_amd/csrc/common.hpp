@@ -3,7 +3,8 @@
 // The rotation is the normalized Sylvester Hadamard transform (velog.io post
 // "fix KV cache quantization outliers", section "Hadamard rotation"), applied
 // as a float32 fast Walsh-Hadamard transform whose butterfly stages run in the
-// order h = 1, 2, 4, ..., d/2.  The quantizer and the transform must match the
+// order h = 1, 2, 4, ..., d/2 (optionally preceded, or on the way back followed,
+// by the sign flips of a random-sign variant).  The quantizer and the transform must match the
 // CPU reference bit for bit, so everything in this file is compiled with
 // -ffp-contract=off and uses IEEE float32 with denormals preserved.
 #pragma once
@@ -106,6 +107,13 @@ __device__ inline void rotate_row(float (&x)[32], int lane, float cd) {
   if constexpr (D >= 256) fwht_cross_stage<4>(x, lane);
 #pragma unroll
   for (int i = 0; i < 32; ++i) x[i] = x[i] * cd;
+}
+
+// Flip the sign of element i of a 32-element block where bit i of mask is
+// set (the diagonal of the random-sign rotation H diag(s); exact).
+__device__ inline void apply_signs(float (&x)[32], uint32_t mask) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = __uint_as_float(__float_as_uint(x[i]) ^ ((mask << (31 - i)) & 0x80000000u));
 }
 
 // Bit of the 5-bit high-bit word owned by element w (0..31) of a block.

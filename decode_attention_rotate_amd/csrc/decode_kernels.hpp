@@ -298,6 +298,15 @@ void decode_split_kernel(DecodeArgs a) {
       }
     }
     if (!a.rotate_k) return;
+    if (a.has_signs) {   // H diag(s): element 32j + 8r + i flips with bit 8r + i of word j
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t m = a.signs[j] >> (8 * r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          f[j][i] = __uint_as_float(__float_as_uint(f[j][i]) ^ ((m << (31 - i)) & 0x80000000u));
+      }
+    }
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll

@@ -118,7 +118,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
   }
   const float scale = (a.rotate ? a.cd : 1.0f) / L;
-  if (t < D) a.out[(size_t)bh * D + t] = o[t] * scale;
+  if (t < D) {
+    float r = o[t] * scale;
+    if (a.rotate && a.has_signs)   // back by diag(s) H
+      r = __uint_as_float(__float_as_uint(r) ^ (((a.signs[t / 32] >> (t % 32)) & 1u) << 31));
+    a.out[(size_t)bh * D + t] = r;
+  }
 }
 
 }  // namespace

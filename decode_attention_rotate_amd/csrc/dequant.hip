@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       for (int e = 0; e < 32; ++e) x[e] = bf16_to_f32(row[e]);
     }
   }
-  if (a.space == 1 && a.rotate) rotate_row<D>(x, lane, a.cd);
+  if (a.space == 1 && a.rotate) {
+    rotate_row<D>(x, lane, a.cd);
+    if (a.has_signs) apply_signs(x, a.signs[j]);   // back by diag(s) H
+  }
   if (!active) return;
   float4* dst = reinterpret_cast<float4*>(a.out + ((size_t)(p - a.t0) * a.Hkv + g) * D + kBlock * j);
 #pragma unroll

@@ -19,6 +19,8 @@ struct AppendArgs {
   int32_t rotate[2];
   int32_t Hkv, n_new, T, cap, dtype;
   float cd;                  // fp32(1/sqrt(D))
+  int32_t has_signs;         // rotate by H diag(s): flip element e's sign by bit e of signs
+  uint32_t signs[8];
   int32_t len[KVQ_MAX_BATCH];  // lengths before the append
 };
 hipError_t launch_append(int D, const AppendArgs& a, int B, hipStream_t s);
@@ -32,6 +34,8 @@ struct DequantArgs {
   int32_t which;              // 0 = K (row layout), 1 = V (element-major tiles)
   int32_t bits, rotate, space, Hkv, T, cap, b, t0, t1, nq;
   float cd;
+  int32_t has_signs;         // space 1 rotates back by diag(s) H
+  uint32_t signs[8];
 };
 hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
 
@@ -62,6 +66,8 @@ struct DecodeArgs {
   int32_t n_q, n_rb;         // prefill: queries per sequence, 64-row blocks per KV head
   int32_t q_dtype, rotate_k;
   float cd, sm_scale;        // fp32(1/sqrt(D)); softmax scale
+  int32_t has_signs;         // q is rotated by H diag(s) (signs as in AppendArgs)
+  uint32_t signs[8];
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
@@ -79,6 +85,8 @@ struct CombineArgs {
   float* out;                // [B][Hq][D]
   int32_t Hq, S, rotate;
   float cd;
+  int32_t has_signs;         // rotate back by diag(s) H
+  uint32_t signs[8];
 };
 hipError_t launch_combine(int D, const CombineArgs& a, int B, hipStream_t s);
 

@@ -141,6 +141,26 @@ WsLayout ws_layout(const kvq_config& c, int n_q_heads, int S) {
 
 kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
+// SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): the golden-gamma
+// increment, two xor-shift-multiply rounds and a final xor-shift.
+uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Sign mask of the random-sign rotation H diag(s): bit e (word e / 32) is set
+// where s_e = -1, i.e. where the top bit of SplitMix64(seed * 2^32 + e) is.
+// Returns 0 (no signs) for seed 0.
+int sign_mask(const kvq_config& c, uint32_t (&w)[8]) {
+  for (int i = 0; i < 8; ++i) w[i] = 0;
+  if (c.sign_seed == 0) return 0;
+  for (int e = 0; e < c.head_dim; ++e)
+    if (splitmix64(((uint64_t)c.sign_seed << 32) | (uint64_t)e) >> 63) w[e / 32] |= 1u << (e % 32);
+  return 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -157,6 +177,7 @@ kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads, int32_t head_di
   const int on = (head_dim >= 64 && head_dim % 64 == 0) ? 1 : 0;
   c.rotate_k = on;
   c.rotate_v = on;
+  c.sign_seed = 0;
   return c;
 }
 
@@ -221,6 +242,7 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* ca
   a.cap = (int32_t)cap_tokens(c);
   a.dtype = dtype;
   a.cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.has_signs = sign_mask(c, a.signs);
   for (int b = 0; b < c.batch; ++b) a.len[b] = seq_len[b];
   return hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)));
 }
@@ -267,6 +289,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.q_dtype = dtype;
   da.rotate_k = c.rotate_k;
   da.cd = cd;
+  da.has_signs = sign_mask(c, da.signs);
   da.sm_scale = sm_scale;
   da.part_ml = reinterpret_cast<float*>(ws + wl.ml);
   da.part_acc = reinterpret_cast<float*>(ws + wl.acc);
@@ -291,6 +314,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   ca.S = sc.S;
   ca.rotate = c.rotate_v;
   ca.cd = cd;
+  ca.has_signs = da.has_signs;
+  for (int i = 0; i < 8; ++i) ca.signs[i] = da.signs[i];
   return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
 }
 
@@ -345,6 +370,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   da.q_dtype = dtype;
   da.rotate_k = c.rotate_k;
   da.cd = cd;
+  da.has_signs = sign_mask(c, da.signs);
   da.sm_scale = sm_scale;
   da.part_ml = reinterpret_cast<float*>(ws + wl.ml);
   da.part_acc = reinterpret_cast<float*>(ws + wl.acc);
@@ -371,6 +397,8 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   ca.S = ps.S;
   ca.rotate = c.rotate_v;
   ca.cd = cd;
+  ca.has_signs = da.has_signs;
+  for (int i = 0; i < 8; ++i) ca.signs[i] = da.signs[i];
   return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
 }
 
@@ -408,6 +436,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t
   a.t1 = t1;
   a.nq = n - (c.tail_len > 0 ? std::min(n, (int)c.tail_len) : 0);
   a.cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.has_signs = sign_mask(c, a.signs);
   return hip_status(launch_dequant(c.head_dim, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -102,6 +102,11 @@ typedef struct kvq_config {
   int32_t max_ctx;     /* capacity per sequence in tokens, >= 1 */
   int32_t rotate_k;    /* 1: rotate K (and q); 0: store K as is */
   int32_t rotate_v;    /* 1: rotate V and rotate the output back; 0: neither */
+  uint32_t sign_seed;  /* 0: rotate by the Sylvester-Hadamard matrix H; else by
+                        * H diag(s), s_e = -1 iff the top bit of SplitMix64 of
+                        * the counter sign_seed * 2^32 + e is set (a random-sign
+                        * variant, which the velog.io post names in section
+                        * "application and background") */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -114,7 +119,8 @@ typedef struct kvq_cache {
 } kvq_cache;
 
 /* Defaults: 4-bit K and V, no tail, rotation on iff head_dim >= 64 and
- * head_dim % 64 == 0 (velog.io post, section "application and background"). */
+ * head_dim % 64 == 0 (velog.io post, section "application and background"),
+ * sign_seed 0. */
 kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads,
                               int32_t head_dim, int32_t max_ctx);
 

@@ -50,10 +50,10 @@ def gpu_planes(cache, cfg):
 class Pair:
     """A device cache and the oracle cache fed the same appends."""
 
-    def __init__(self, B, H, d, kb, vb, T, max_ctx, rotate_k=True, rotate_v=True):
-        self.cfg = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T, rotate_k, rotate_v)
+    def __init__(self, B, H, d, kb, vb, T, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0):
+        self.cfg = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T, rotate_k, rotate_v, sign_seed)
         self.cache = kvq.KVCache(self.cfg, DEV)
-        self.orc = OracleCache(B, H, d, kb, vb, T, max_ctx, rotate_k, rotate_v)
+        self.orc = OracleCache(B, H, d, kb, vb, T, max_ctx, rotate_k, rotate_v, sign_seed)
         self.lens = np.zeros(B, dtype=np.int64)
 
     def append(self, k, v, dtype, lens=None):
@@ -92,12 +92,22 @@ def attention_errors(got, planes, qv, lens, cfg, sm_scale=None, heads=None):
     ref = decode_reference(planes, qv, lens, cfg.n_kv_heads, cfg.head_dim, cfg.k_bits,
                            cfg.v_bits, cfg.tail_len, sm_scale=sm_scale,
                            rotate_k=bool(cfg.rotate_k), rotate_v=bool(cfg.rotate_v),
-                           heads=heads)
+                           heads=heads, sign_seed=cfg.sign_seed)
     errs = {}
     B, Hq, _ = qv.shape
     for b in range(B):
         for h in range(Hq):
             if heads is not None and (b, h) not in set(heads):
                 continue
-            errs[(b, h)] = np.linalg.norm(got[b, h] - ref[b, h]) / np.linalg.norm(ref[b, h])
+            errs[(b, h)] = rel_l2(got[b, h], ref[b, h])
     return errs
+
+
+def rel_l2(got, ref):
+    """Relative L2 error of one output vector; infinite when the output is not
+    finite, the absolute error when the exact output is the zero vector."""
+    got = np.asarray(got, dtype=np.float64)
+    if not np.all(np.isfinite(got)):
+        return np.inf
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)

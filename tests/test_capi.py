@@ -178,3 +178,12 @@ def test_prefill_validation():
     assert _prefill(c, 8, 4, _lens(5, 5), ws_bytes=100) == _capi.KVQ_ERR_WORKSPACE
     assert _prefill(c, 8, 4, _lens(5, 5), q=FAKE_MISALIGNED) == _capi.KVQ_ERR_ALIGN
     assert _prefill(c, 8, 4, _lens(5, 5), out=0) == _capi.KVQ_ERR_INVALID
+
+
+def test_config_layout_and_sign_seed():
+    # ten 32-bit fields; sign_seed last, 0 by default (plain Sylvester matrix)
+    assert ctypes.sizeof(_capi.KvqConfig) == 40
+    c = kvq.kvq_config_default(1, 1, 128, 64)
+    assert c.sign_seed == 0
+    c2 = kvq.kvq_config(1, 1, 128, 64, sign_seed=0xFFFFFFFF)
+    assert c2.sign_seed == 0xFFFFFFFF
