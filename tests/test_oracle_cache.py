@@ -25,7 +25,7 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("T", (0, 8, 64))
-@pytest.mark.parametrize("bits", ((4, 4), (8, 4), (5, 8)))
+@pytest.mark.parametrize("bits", ((4, 4), (8, 4), (5, 8), (6, 6)))
 def test_chunk_invariance(T, bits):
     B, H, d, n = 2, 2, 64, 150
     k, v = _data(B, n, H, d, seed=T)
@@ -109,7 +109,7 @@ def test_dequantize_reference_spaces():
 
 # ---------------------------------------------------------------- V tile layout
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("bits", [4, 5, 8])
+@pytest.mark.parametrize("bits", [4, 5, 6, 8])
 def test_v_tiles_round_trip_and_size(d, bits):
     qmax = (1 << (bits - 1)) - 1
     rng = np.random.default_rng(d * 10 + bits)
@@ -148,3 +148,11 @@ def test_v_tile_positions_by_hand():
     plane, base = _one_code_plane(64, 4, 45, 3, -7)
     diff = np.nonzero(plane != base)[0]
     assert list(diff) == [1331] and plane[1331] & 15 == 1
+    # 6-bit, token 9 element 20 (item 81, slot 1, nibble 4): u = 32 + 21 = 53
+    # = 0b110101 -> low nibble 5 in byte 326; bits 4-5 (0b11, where a zero
+    # code has 0b10) at bits 2*4 = 8..9 of the 16-bit field 32*64 + 2*81 =
+    # 2210, i.e. bits 0..1 of byte 2211
+    plane, base = _one_code_plane(64, 6, 9, 20, 21)
+    diff = np.nonzero(plane != base)[0]
+    assert list(diff) == [326, 2211]
+    assert plane[326] & 15 == 5 and base[2211] & 3 == 2 and plane[2211] & 3 == 3

@@ -14,10 +14,10 @@ import pytest
 from oracle import (QMAX, quantize_blocks, dequantize_blocks, pack_rows,
                     unpack_rows, row_bytes, rows_to_tiled, tiled_to_rows,
                     padded_row_bytes)
-from oracle.blockquant import _hibit_position
+from oracle.blockquant import _hibit_position, _hi2_position
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-BITS = (4, 5, 8)
+BITS = (4, 5, 6, 8)
 
 
 def _blocks(seed, nblk=400):
@@ -140,6 +140,25 @@ def test_packing_byte_conventions():
     c5[:] = 15
     r5 = pack_rows(c5, 5)
     assert np.all(r5[:32] == 0xFF) and np.all(r5[32:] == 0xFF)
+    # 6-bit: each high word holds the 2-bit fields of 16 elements, covering
+    # its 32 bits once; extreme codes give 0x01/0x00 and 0xFF/0xFF bytes
+    for word in (0, 1):
+        bits_used = sorted(b for w in range(32) if w // 16 == word
+                           for b in (_hi2_position(w), _hi2_position(w) + 1))
+        assert bits_used == list(range(32))
+    c6 = np.full(64, -31, np.int8)
+    r6 = pack_rows(c6, 6)
+    assert np.all(r6[:32] == 0x11) and np.all(r6[32:] == 0)
+    c6[:] = 31
+    r6 = pack_rows(c6, 6)
+    assert np.all(r6[:32] == 0xFF) and np.all(r6[32:] == 0xFF)
+    # element 17 of block 1 (code 31 - 32 + 48 = u 47 = 0b101111): nibble 15,
+    # bits 4-5 = 0b10 at bits 8*0 + 4*0 + 2*1 = 2..3 of word 1 of block 1
+    c6[:] = 0
+    c6[32 + 17] = 15
+    r6 = pack_rows(c6, 6)
+    w = r6[32:].view("<u4")
+    assert (w[2 * 1 + 1] >> 2) & 3 == ((15 + 32) >> 4) & 3
 
 
 def test_tiled_layout_positions():
@@ -165,7 +184,7 @@ def _golden_percent():
 
 
 def test_block_bytes_match_page3_cache_sizes():
-    bits_of = {"q4_0": 4, "q5_0": 5, "q8_0": 8}
+    bits_of = {"q4_0": 4, "q5_0": 5, "q6_0": 6, "q8_0": 8}
     table = _golden_percent()
     assert table.pop("bf16") == 100.0
     for name, pct in table.items():
