@@ -35,7 +35,7 @@ def units():
     for name in ("append.hip", "dequant.hip", "decode_main.hip"):
         out.append((os.path.join(CSRC, name), name.replace(".hip", ".o"), DEVICE))
     for d in (64, 128, 256):
-        for kb in (4, 5, 8):
+        for kb in (4, 5, 6, 8):
             out.append((os.path.join(CSRC, "decode_inst.hip"), "decode_d%d_k%d.o" % (d, kb),
                         DEVICE + ["-DKVQ_INST_D=%d" % d, "-DKVQ_INST_KB=%d" % kb]))
     out.append((os.path.join(CSRC, "kvq_host.cpp"), "kvq_host.o", DEVICE + ["-x", "hip"]))

@@ -101,6 +101,13 @@ __device__ inline void store_k_row(const int (&c)[32], uint8_t* plane, int p, in
       const int byte = D / 2 + 4 * j;
       *reinterpret_cast<uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk) = hw;
     }
+    if constexpr (BITS == 6) {
+      uint32_t hw[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) hw[e / 16] |= (uint32_t)(((c[e] + OFF) >> 4) & 3) << hi2_pos(e);
+      const int byte = D / 2 + 8 * j;
+      *reinterpret_cast<uint2*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk) = make_uint2(hw[0], hw[1]);
+    }
   }
 }
 
@@ -114,6 +121,9 @@ __device__ inline uint32_t quantize_k(int bits, const float (&x)[32], int (&c)[3
   } else if (bits == 5) {
     s = quantize_block<5>(x, c);
     if (active) store_k_row<D, 5>(c, plane, p, j);
+  } else if (bits == 6) {
+    s = quantize_block<6>(x, c);
+    if (active) store_k_row<D, 6>(c, plane, p, j);
   } else {
     s = quantize_block<8>(x, c);
     if (active) store_k_row<D, 8>(c, plane, p, j);
@@ -125,6 +135,7 @@ template <int D>
 __device__ inline uint32_t quantize_any(int bits, const float (&x)[32], int (&c)[32]) {
   if (bits == 4) return quantize_block<4>(x, c);
   if (bits == 5) return quantize_block<5>(x, c);
+  if (bits == 6) return quantize_block<6>(x, c);
   return quantize_block<8>(x, c);
 }
 
@@ -144,14 +155,16 @@ __device__ inline void store_v_item(uint8_t* tile, int item, uint64_t u, uint32_
     *dst = u;
   } else {
     uint32_t w = 0, hi = 0, keep = 0, keep_hi = 0;
+    constexpr int HB = BITS == 6 ? 2 : 1;          // high bits per slot
+    constexpr uint32_t HM = BITS == 6 ? 3u : 1u;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t v = (uint32_t)(u >> (8 * k)) & 0xFFu;
       w |= (v & 15u) << (4 * v_nibble(k));
-      hi |= ((v >> 4) & 1u) << v_nibble(k);
+      hi |= ((v >> 4) & HM) << (HB * v_nibble(k));
       if (!(mask & (1u << k))) {
         keep |= 15u << (4 * v_nibble(k));
-        keep_hi |= 1u << v_nibble(k);
+        keep_hi |= HM << (HB * v_nibble(k));
       }
     }
     uint32_t* dst = reinterpret_cast<uint32_t*>(tile) + item;
@@ -161,6 +174,11 @@ __device__ inline void store_v_item(uint8_t* tile, int item, uint64_t u, uint32_
       uint8_t* dh = tile + 32 * D + item;
       if (keep_hi) hi = (hi & ~keep_hi) | (*dh & keep_hi);
       *dh = (uint8_t)hi;
+    }
+    if constexpr (BITS == 6) {
+      uint16_t* dh = reinterpret_cast<uint16_t*>(tile + 32 * D) + item;
+      if (keep_hi) hi = (hi & ~keep_hi) | (*dh & keep_hi);
+      *dh = (uint16_t)hi;
     }
   }
 }
@@ -259,6 +277,7 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
     const int item = v_item(D, p0 % kTile, e);
     if (bits == 4) store_v_item<D, 4>(tile, item, u, mask);
     else if (bits == 5) store_v_item<D, 5>(tile, item, u, mask);
+    else if (bits == 6) store_v_item<D, 6>(tile, item, u, mask);
     else store_v_item<D, 8>(tile, item, u, mask);
   }
 }
@@ -334,7 +353,7 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
 // items the quantized codes merge into) is issued before any arithmetic, so
 // the wave waits for memory once; the new row overwrites the ring slot the
 // leaving row was read from only after a barrier.
-template <int D>
+template <int D, int VB>
 __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   constexpr int LPR = D / kBlock;
   const int lane = threadIdx.x;
@@ -347,35 +366,75 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   const bool q_lane = rg.q1 > rg.q0 && (T > 0 ? ring_lane : new_lane);
   const int pq = rg.q0;                          // the quantized position
   const size_t unit = (size_t)b * a.Hkv + g;
-  const int bits = a.bits[pl];
+  const int bits = pl == 0 ? a.bits[0] : VB;   // V's width is the template's
 
-  float x[32], y[32];
-  if (new_lane) {
-    load_row_block(a.src[pl], a.dtype, ((size_t)b * a.Hkv + g) * D + (size_t)kBlock * j, x);
-  } else {
+  // raw loads first (converted below, so no load waits for another)
+  uint4 rin[8], rring[4];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = 0.f;
+  for (int q = 0; q < 8; ++q) rin[q] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rring[q] = make_uint4(0u, 0u, 0u, 0u);
+  if (new_lane) {
+    const size_t off = ((size_t)b * a.Hkv + g) * D + (size_t)kBlock * j;
+    if (a.dtype == KVQ_BF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src[pl]) + off);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rin[q] = src[q];
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.src[pl]) + off);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rin[q] = src[q];
+    }
   }
   if (ring_lane) {
-    load_bf16_block(a.tail[pl] + (unit * T + pq % T) * D + kBlock * j, y);
-  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(a.tail[pl] + (unit * T + pq % T) * D + kBlock * j);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) y[e] = 0.f;
+    for (int q = 0; q < 4; ++q) rring[q] = src[q];
   }
   // V items of this lane's 32 elements at the quantized position
-  uint8_t* vtile = a.codes[1] + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, bits) +
-                   (size_t)(pq / kTile) * v_tile_bytes(D, bits);
-  uint32_t oldw[32];
-  uint8_t oldh[32];
-  if (pl == 1 && q_lane && bits != 8) {
+  uint8_t* vtile = a.codes[1] + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, VB) +
+                   (size_t)(pq / kTile) * v_tile_bytes(D, VB);
+  uint32_t oldw[VB == 8 ? 1 : 32];
+  uint32_t oldh[VB == 5 || VB == 6 ? 32 : 1];
+  if constexpr (VB != 8) {
+    if (pl == 1 && q_lane) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int item = v_item(D, pq % kTile, kBlock * j + i);
-      oldw[i] = reinterpret_cast<const uint32_t*>(vtile)[item];
-      oldh[i] = bits == 5 ? vtile[32 * D + item] : 0;
+      for (int i = 0; i < 32; ++i) {
+        const int item = v_item(D, pq % kTile, kBlock * j + i);
+        oldw[i] = reinterpret_cast<const uint32_t*>(vtile)[item];
+        if constexpr (VB == 5) oldh[i] = vtile[32 * D + item];
+        if constexpr (VB == 6) oldh[i] = reinterpret_cast<const uint16_t*>(vtile + 32 * D)[item];
+      }
     }
   }
 
+  float x[32], y[32];
+  auto widen_bf16 = [](const uint4 (&r)[8], float (&f)[32]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[q * 8 + 2 * k] = __uint_as_float(w[k] << 16);
+        f[q * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  };
+  if (a.dtype == KVQ_BF16) {
+    widen_bf16(rin, x);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      x[4 * q] = __uint_as_float(rin[q].x); x[4 * q + 1] = __uint_as_float(rin[q].y);
+      x[4 * q + 2] = __uint_as_float(rin[q].z); x[4 * q + 3] = __uint_as_float(rin[q].w);
+    }
+  }
+  {
+    uint4 r8[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { r8[q] = rring[q]; r8[q + 4] = make_uint4(0u, 0u, 0u, 0u); }
+    widen_bf16(r8, y);
+  }
   if (a.rotate[pl]) {                            // every lane takes part
     if (a.has_signs) apply_signs(x, a.signs[j]);
     rotate_row<D>(x, lane, a.cd);
@@ -390,19 +449,23 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
       uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
       scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_k<D>(bits, z, c, true, plane, pq, j);
     } else {
-      scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_any<D>(bits, z, c);
-      const int k = pq % 8, off = 1 << (bits - 1);
+      scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_block<VB>(z, c);
+      const int k = pq % 8;
+      constexpr int off = 1 << (VB - 1);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int item = v_item(D, pq % kTile, kBlock * j + i);
         const uint32_t u = (uint32_t)(c[i] + off);
-        if (bits == 8) {
+        if constexpr (VB == 8) {
           vtile[8 * item + k] = (uint8_t)u;
         } else {
           const int nb = v_nibble(k);
           reinterpret_cast<uint32_t*>(vtile)[item] = (oldw[i] & ~(15u << (4 * nb))) | ((u & 15u) << (4 * nb));
-          if (bits == 5)
+          if constexpr (VB == 5)
             vtile[32 * D + item] = (uint8_t)((oldh[i] & ~(1u << nb)) | (((u >> 4) & 1u) << nb));
+          if constexpr (VB == 6)
+            reinterpret_cast<uint16_t*>(vtile + 32 * D)[item] =
+                (uint16_t)((oldh[i] & ~(3u << (2 * nb))) | (((u >> 4) & 3u) << (2 * nb)));
         }
       }
     }
@@ -426,7 +489,13 @@ template <int D>
 hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
   constexpr int RPB = 256 / (D / kBlock);
   if (a.n_new == 1) {
-    hipLaunchKernelGGL(append_one_kernel<D>, dim3(a.Hkv, B, 2), dim3(64), 0, s, a);
+    const dim3 grid(a.Hkv, B, 2), block(64);
+    switch (a.bits[1]) {
+      case 4: hipLaunchKernelGGL((append_one_kernel<D, 4>), grid, block, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((append_one_kernel<D, 5>), grid, block, 0, s, a); break;
+      case 6: hipLaunchKernelGGL((append_one_kernel<D, 6>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((append_one_kernel<D, 8>), grid, block, 0, s, a); break;
+    }
     return hipGetLastError();
   }
   if (a.n_new <= RPB - 7) {

@@ -39,6 +39,8 @@ __host__ __device__ inline size_t chunk_offset(int p, int c, int rpad) {
 //   8-bit: eight bytes per item, u = c + 128 of slot k in byte k
 //   5-bit: the 4-bit words of u & 15 for every item (32*d bytes), then one
 //          byte per item whose bit v_nibble(k) is bit 4 of u.
+//   6-bit: the 4-bit words of u & 15, then one 16-bit field per item whose
+//          bits 2*v_nibble(k), +1 are bits 4, 5 of u.
 __host__ __device__ constexpr int v_tile_bytes(int d, int bits) { return kTile * d * bits / 8; }
 __host__ __device__ constexpr int v_item(int d, int t, int e) {
   return ((t / 32) * 64 + 16 * ((t % 32) / 8) + e % 16) * (d / 16) + e / 16;
@@ -119,6 +121,12 @@ __device__ inline void apply_signs(float (&x)[32], uint32_t mask) {
 // Bit of the 5-bit high-bit word owned by element w (0..31) of a block.
 __host__ __device__ constexpr int hibit_pos(int w) {
   return 8 * ((w % 8) / 2) + 2 * (w / 8) + (w % 2);
+}
+// First bit of element w's 2-bit field (bits 4, 5 of a 6-bit code) inside
+// high word w / 16 of its block: the four fields of a group of 8 elements
+// (w / 8) sit 8 bits apart, so one rotate aligns them with code bytes.
+__host__ __device__ constexpr int hi2_pos(int w) {
+  return 8 * ((w % 8) / 2) + 4 * ((w / 8) % 2) + 2 * (w % 2);
 }
 
 // Quantize one 32-element block: fp16 scale bits and int codes.

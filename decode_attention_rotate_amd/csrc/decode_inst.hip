@@ -28,11 +28,12 @@ namespace kvq {
    launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 7>,                            \
    launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8>}
 
-DecodeLauncher KVQ_TABLE[3][8] = {KVQ_ROW(4), KVQ_ROW(5), KVQ_ROW(8)};
+DecodeLauncher KVQ_TABLE[4][8] = {KVQ_ROW(4), KVQ_ROW(5), KVQ_ROW(6), KVQ_ROW(8)};
 
-// chunked prefill, indexed by v_bits 4/5/8
-DecodeLauncher KVQ_PF_TABLE[3] = {launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 4, 8, true>,
+// chunked prefill, indexed by v_bits 4/5/6/8
+DecodeLauncher KVQ_PF_TABLE[4] = {launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 4, 8, true>,
                                   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 5, 8, true>,
+                                  launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 6, 8, true>,
                                   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 8, 8, true>};
 
 }  // namespace kvq

@@ -100,15 +100,16 @@ struct StepRegs {
   static constexpr int NSW = (NB + 1) / 2;   // 32-bit words of fp16 scales per token
   u32x2 k8[KB == 8 ? 2 * NB : 1];            // [m][blk] 8 code bytes
   uint32_t k4[KB == 8 ? 1 : 2 * NB];         // [m][blk] 8 code nibbles
-  uint32_t kh[KB == 5 ? 2 * NB : 1];         // [m][blk] 5-bit high-bit word
+  uint32_t kh[KB == 5 || KB == 6 ? 2 * NB : 1];   // [m][blk] 5/6-bit high-bit word
   uint32_t ks[2][NSW], vs[2][NSW];           // [m] fp16 scales of this lane's token
   u32x4 v[VB == 8 ? NN / 2 : NN / 4];        // V items (4 or 8 bytes each)
-  uint32_t vh[VB == 5 ? NN / 4 : 1];         // 5-bit high-bit bytes
+  uint32_t vh[VB == 5 ? NN / 4 : VB == 6 ? NN / 2 : 1];   // 5-bit bytes / 6-bit fields
 };
 
 // B operand of Q.K for 16 tokens and one block: 8 int8 codes of this lane's
-// token in the k-slot order of the query bytes (4/5-bit: elements
-// 0,2,4,6,1,3,5,7 of the lane's group of 8, widened to bytes).
+// token in the k-slot order of the query bytes (4/5/6-bit: elements
+// 0,2,4,6,1,3,5,7 of the lane's group of 8, widened to bytes; the high bits
+// come from one rotate of the block's high word).
 template <int D, int KB, int VB>
 __device__ inline long k_operand(const StepRegs<D, KB, VB>& R, int i, uint32_t rot_lo, uint32_t rot_hi) {
   if constexpr (KB == 8) {
@@ -120,6 +121,10 @@ __device__ inline long k_operand(const StepRegs<D, KB, VB>& R, int i, uint32_t r
     if constexpr (KB == 5) {
       lo |= rotr(R.kh[i], rot_lo) & 0x10101010u;
       hi |= rotr(R.kh[i], rot_hi) & 0x10101010u;
+    }
+    if constexpr (KB == 6) {
+      lo |= rotr(R.kh[i], rot_lo) & 0x30303030u;
+      hi |= rotr(R.kh[i], rot_hi) & 0x30303030u;
     }
     return (long)(((uint64_t)hi << 32) | lo);
   }
@@ -149,7 +154,18 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t 
     uint32_t w2 = and_or(x8, 0x000F000Fu, magic);
     uint32_t w3 = and_or(x8, 0x00F000F0u, magic);
     _Float16 b_lo, b_hi;
-    if constexpr (VB == 5) {
+    if constexpr (VB == 6) {
+      // slot fields 2n, 2n+1 of nibble position n go to bits 4-5 (low-nibble
+      // halves, value 16 h) or 8-9 (high-nibble halves, value 256 h)
+      const uint32_t h = (R.vh[nb / 2] >> (16 * (nb % 2))) & 0xFFFFu;
+      const uint32_t y = (h << 4) | (h << 12);
+      w0 |= y & 0x00300030u;
+      w1 |= (y << 2) & 0x03000300u;
+      w2 |= (y >> 4) & 0x00300030u;
+      w3 |= (y >> 2) & 0x03000300u;
+      b_lo = (_Float16)-1056.0f;
+      b_hi = (_Float16)-96.0f;
+    } else if constexpr (VB == 5) {
       const uint32_t hb = (R.vh[nb / 4] >> (8 * (nb % 4))) & 0xFFu;
       const uint32_t y = (hb << 4) | (hb << 16);
       w0 |= y & 0x00100010u;
@@ -189,9 +205,10 @@ void decode_split_kernel(DecodeArgs a) {
   // tiles whose bytes a wave keeps in registers ahead of the one computing:
   // at one wave per SIMD (d = 256) the wave alone must cover the latency, so
   // it keeps two where four step buffers fit the 512 registers with at most
-  // a few spilled (4-bit K or 4-bit V; decode only, a prefill wave holds
-  // more state)
-  constexpr int kAhead = split_waves_per_simd(D) == 1 && !PF && (KB == 4 || VB == 4) ? 2 : 1;
+  // a few spilled (4-bit K, or 4-bit V with 5- or 8-bit K; decode only, a
+  // prefill wave holds more state)
+  constexpr int kAhead =
+      split_waves_per_simd(D) == 1 && !PF && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
   constexpr int NSW = (NB + 1) / 2;
@@ -499,9 +516,13 @@ void decode_split_kernel(DecodeArgs a) {
     i4_t cq[KB == 8 ? 1 : NB];
     i4_t cq2[kQX && KB != 8 ? NB : 1];
     // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
-    // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word
-    const uint32_t rot_lo = (uint32_t)(2 * r + 28) & 31u;   // rotate left by 4 - 2r
-    const uint32_t rot_hi = (uint32_t)(2 * r + 29) & 31u;   // rotate left by 3 - 2r
+    // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word;
+    // 6-bit K: bits 4-5 sit at 8i + 4(r%2) (even) and 8i + 4(r%2) + 2 (odd)
+    // of the block's high word r/2; both rotate into bits 4(-5) of byte i
+    const uint32_t rot_lo = KB == 6 ? (uint32_t)(4 * (r & 1) + 28) & 31u
+                                    : (uint32_t)(2 * r + 28) & 31u;
+    const uint32_t rot_hi = KB == 6 ? (uint32_t)(4 * (r & 1) + 30) & 31u
+                                    : (uint32_t)(2 * r + 29) & 31u;
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));
 
@@ -526,6 +547,11 @@ void decode_split_kernel(DecodeArgs a) {
               const int cb = D / 32 + j / 4;
               R.kh[m * NB + j] = *reinterpret_cast<const uint32_t*>(
                   kt + (cb * kTile + 16 * m + col) * kChunk + 4 * (j % 4));
+            }
+            if constexpr (KB == 6) {
+              const int cb = D / 32 + j / 2;
+              R.kh[m * NB + j] = *reinterpret_cast<const uint32_t*>(
+                  kt + (cb * kTile + 16 * m + col) * kChunk + 8 * (j % 2) + 4 * (r >> 1));
             }
           }
         }
@@ -555,6 +581,11 @@ void decode_split_kernel(DecodeArgs a) {
         const uint8_t* hj = vt + (size_t)j2 * 64 * NN + vh_off;
 #pragma unroll
         for (int q = 0; q < NN / 4; ++q) R.vh[q] = reinterpret_cast<const uint32_t*>(hj)[q];
+      }
+      if constexpr (VB == 6) {
+        const uint8_t* hj = vt + 32 * D + (size_t)j2 * 64 * NN * 2 + (size_t)lane * NN * 2;
+#pragma unroll
+        for (int q = 0; q < NN / 2; ++q) R.vh[q] = reinterpret_cast<const uint32_t*>(hj)[q];
       }
     };
 

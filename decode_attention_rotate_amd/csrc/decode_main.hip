@@ -10,35 +10,35 @@
 
 namespace kvq {
 
-// Tables defined by the instantiation units, indexed [v_bits 4/5/8][G-1].
-#define KVQ_DECLARE_TABLE(D, KB) extern DecodeLauncher kvq_decode_table_##D##_##KB[3][8]; \
-  extern DecodeLauncher kvq_prefill_table_##D##_##KB[3];
-KVQ_DECLARE_TABLE(64, 4) KVQ_DECLARE_TABLE(64, 5) KVQ_DECLARE_TABLE(64, 8)
-KVQ_DECLARE_TABLE(128, 4) KVQ_DECLARE_TABLE(128, 5) KVQ_DECLARE_TABLE(128, 8)
-KVQ_DECLARE_TABLE(256, 4) KVQ_DECLARE_TABLE(256, 5) KVQ_DECLARE_TABLE(256, 8)
+// Tables defined by the instantiation units, indexed [v_bits 4/5/6/8][G-1].
+#define KVQ_DECLARE_TABLE(D, KB) extern DecodeLauncher kvq_decode_table_##D##_##KB[4][8]; \
+  extern DecodeLauncher kvq_prefill_table_##D##_##KB[4];
+#define KVQ_ALL_KB(X, D) X(D, 4) X(D, 5) X(D, 6) X(D, 8)
+KVQ_ALL_KB(KVQ_DECLARE_TABLE, 64) KVQ_ALL_KB(KVQ_DECLARE_TABLE, 128) KVQ_ALL_KB(KVQ_DECLARE_TABLE, 256)
 #undef KVQ_DECLARE_TABLE
 
+namespace {
+int v_index(int vb) { return vb == 4 ? 0 : vb == 5 ? 1 : vb == 6 ? 2 : vb == 8 ? 3 : -1; }
+}  // namespace
+
 DecodeLauncher decode_launcher(int D, int kb, int vb, int gc) {
-  const int vi = vb == 4 ? 0 : vb == 5 ? 1 : vb == 8 ? 2 : -1;
+  const int vi = v_index(vb);
   if (vi < 0 || gc < 1 || gc > 8) return nullptr;
 #define KVQ_PICK(DD, KK) if (D == DD && kb == KK) return kvq_decode_table_##DD##_##KK[vi][gc - 1];
-  KVQ_PICK(64, 4) KVQ_PICK(64, 5) KVQ_PICK(64, 8)
-  KVQ_PICK(128, 4) KVQ_PICK(128, 5) KVQ_PICK(128, 8)
-  KVQ_PICK(256, 4) KVQ_PICK(256, 5) KVQ_PICK(256, 8)
+  KVQ_ALL_KB(KVQ_PICK, 64) KVQ_ALL_KB(KVQ_PICK, 128) KVQ_ALL_KB(KVQ_PICK, 256)
 #undef KVQ_PICK
   return nullptr;
 }
 
 DecodeLauncher prefill_launcher(int D, int kb, int vb) {
-  const int vi = vb == 4 ? 0 : vb == 5 ? 1 : vb == 8 ? 2 : -1;
+  const int vi = v_index(vb);
   if (vi < 0) return nullptr;
 #define KVQ_PICK(DD, KK) if (D == DD && kb == KK) return kvq_prefill_table_##DD##_##KK[vi];
-  KVQ_PICK(64, 4) KVQ_PICK(64, 5) KVQ_PICK(64, 8)
-  KVQ_PICK(128, 4) KVQ_PICK(128, 5) KVQ_PICK(128, 8)
-  KVQ_PICK(256, 4) KVQ_PICK(256, 5) KVQ_PICK(256, 8)
+  KVQ_ALL_KB(KVQ_PICK, 64) KVQ_ALL_KB(KVQ_PICK, 128) KVQ_ALL_KB(KVQ_PICK, 256)
 #undef KVQ_PICK
   return nullptr;
 }
+#undef KVQ_ALL_KB
 
 namespace {
 

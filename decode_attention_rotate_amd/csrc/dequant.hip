@@ -25,15 +25,22 @@ __device__ inline void load_codes(const uint8_t* plane, int p, int j, int (&c)[3
     constexpr int OFF = 1 << (BITS - 1);
     const uint4 v = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, j, RP));
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t hw = 0;
+    uint32_t hw = 0, hw2[2] = {0u, 0u};
     if constexpr (BITS == 5) {
       const int byte = D / 2 + 4 * j;
       hw = *reinterpret_cast<const uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
+    }
+    if constexpr (BITS == 6) {
+      const int byte = D / 2 + 8 * j;
+      const uint2 h = *reinterpret_cast<const uint2*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
+      hw2[0] = h.x;
+      hw2[1] = h.y;
     }
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       int u = (int)((w[e / 8] >> (4 * (e % 8))) & 15);
       if constexpr (BITS == 5) u |= (int)((hw >> hibit_pos(e)) & 1) << 4;
+      if constexpr (BITS == 6) u |= (int)((hw2[e / 16] >> hi2_pos(e)) & 3) << 4;
       c[e] = u - OFF;
     }
   }
@@ -55,6 +62,8 @@ __device__ inline void load_v_codes(const uint8_t* plane, int p, int j, int (&c)
       const uint32_t w = reinterpret_cast<const uint32_t*>(tile)[item];
       u = (int)((w >> (4 * v_nibble(k))) & 15u);
       if constexpr (BITS == 5) u |= (int)((tile[32 * D + item] >> v_nibble(k)) & 1u) << 4;
+      if constexpr (BITS == 6)
+        u |= (int)((reinterpret_cast<const uint16_t*>(tile + 32 * D)[item] >> (2 * v_nibble(k))) & 3u) << 4;
     }
     c[i] = u - OFF;
   }
@@ -82,11 +91,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         const uint8_t* plane = a.codes + unit * (size_t)a.cap * padded_row_bytes(D, a.bits);
         if (a.bits == 4) load_codes<D, 4>(plane, p, j, c);
         else if (a.bits == 5) load_codes<D, 5>(plane, p, j, c);
+        else if (a.bits == 6) load_codes<D, 6>(plane, p, j, c);
         else load_codes<D, 8>(plane, p, j, c);
       } else {
         const uint8_t* plane = a.codes + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, a.bits);
         if (a.bits == 4) load_v_codes<D, 4>(plane, p, j, c);
         else if (a.bits == 5) load_v_codes<D, 5>(plane, p, j, c);
+        else if (a.bits == 6) load_v_codes<D, 6>(plane, p, j, c);
         else load_v_codes<D, 8>(plane, p, j, c);
       }
 #pragma unroll

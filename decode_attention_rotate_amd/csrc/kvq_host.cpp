@@ -30,7 +30,7 @@ constexpr int kMaxSplits = kMaxSplitsDevice;
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
 
-bool bits_ok(int b) { return b == 4 || b == 5 || b == 8; }
+bool bits_ok(int b) { return b == 4 || b == 5 || b == 6 || b == 8; }
 bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -11,10 +11,10 @@
  *    head_dim >= 64 and a multiple of 64, and can be switched off separately
  *    for K and V (same post, section "application and background").
  *  - Rotated vectors are stored as 32-element blocks: one fp16 absmax scale
- *    plus 4-, 5- or 8-bit codes, i.e. 4.5 / 5.5 / 8.5 bits per value, the
- *    q4_0 / q5_0 / q8_0 cache sizes (28.1 / 34.4 / 53.1 % of bf16) in the
- *    table "Qwen 3.6 27B Q5_K_S + 64k context KLD results" of aiwitness.kr
- *    post 1txlhxu.  K and V pick their widths independently
+ *    plus 4-, 5-, 6- or 8-bit codes, i.e. 4.5 / 5.5 / 6.5 / 8.5 bits per
+ *    value, the q4_0 / q5_0 / q6_0 / q8_0 cache sizes (28.1 / 34.4 / 40.6 /
+ *    53.1 % of bf16) in the table "Qwen 3.6 27B Q5_K_S + 64k context KLD
+ *    results" of aiwitness.kr post 1txlhxu.  K and V pick their widths independently
  *    (--cache-type-k / --cache-type-v in the velog.io post).
  *  - An optional bf16 precision tail keeps the newest tokens unquantized
  *    (aitrends.kr article 92204, glossary entry "Precision Tail").
@@ -35,18 +35,33 @@
  *
  * Cache memory layout (all planes indexed by sequence b and KV head g,
  * cap = max_ctx rounded up to a multiple of 64 tokens):
- *  - code planes (k_codes, v_codes): per (b, g) a block of cap * R bytes,
- *    where R = head_dim * bits / 8 rounded up to a multiple of 16.  Tokens
- *    are grouped in tiles of 64; inside a tile, bytes [16c, 16c+16) of the
- *    row of token l live at byte (c * 64 + l) * 16.  Row encoding:
+ *  - K code plane (k_codes): per (b, g) a block of cap * R bytes, where
+ *    R = head_dim * bits / 8 rounded up to a multiple of 16.  Tokens are
+ *    grouped in tiles of 64; inside a tile, bytes [16c, 16c+16) of the row
+ *    of token l live at byte (c * 64 + l) * 16.  Row encoding:
  *      8-bit  two's-complement code per element;
  *      4-bit  u = code + 8, element 2i in the low nibble of byte i,
  *             element 2i+1 in the high nibble;
  *      5-bit  u = code + 16: low nibbles packed as 4-bit (head_dim/2 bytes),
  *             then one little-endian 32-bit word per block holding bit 4 of
  *             each code; element w of the block owns bit
- *             8*((w%8)/2) + 2*(w/8) + (w%2).
+ *             8*((w%8)/2) + 2*(w/8) + (w%2);
+ *      6-bit  u = code + 32: low nibbles as 4-bit, then two little-endian
+ *             32-bit words per block holding bits 4-5 of each code; element
+ *             w owns bits 8*((w%8)/2) + 4*((w/8)%2) + 2*(w%2) and the next
+ *             one of word w/16.
  *    Row padding bytes are never read or written.
+ *  - V code plane (v_codes): per (b, g) cap/64 tiles of 64*head_dim*bits/8
+ *    bytes, element-major: token t (0..63 in its tile) and element e belong
+ *    to item ((t/32)*64 + 16*((t%32)/8) + e%16)*(head_dim/16) + e/16, slot
+ *    k = t%8, with offset codes u = code + 2^(bits-1):
+ *      4-bit  one little-endian 32-bit word per item, slot k in nibble
+ *             n(k) = 4*(k%2) + k/2;
+ *      8-bit  eight bytes per item, slot k in byte k;
+ *      5-bit  the 4-bit words of u & 15 for all items (32*head_dim bytes),
+ *             then one byte per item whose bit n(k) is bit 4 of u;
+ *      6-bit  the 4-bit words, then one little-endian 16-bit field per item
+ *             whose bits 2n(k), 2n(k)+1 are bits 4, 5 of u.
  *  - scale planes (k_scales, v_scales): [b][g][cap][head_dim/32] fp16.
  *  - tail planes (k_tail, v_tail): [b][g][tail_len][head_dim] bf16; position
  *    p of the newest tail_len positions lives in slot p % tail_len.  NULL is
@@ -57,7 +72,7 @@
  * through the tail):
  *    a = max|x|;  s = fp16_rne(min(a / qmax, 65504));  r = 1 / float(s);
  *    code = clamp(rint(x * r), -qmax, qmax)   (all codes 0 if s == 0)
- * with qmax = 7 / 15 / 127, IEEE float32 arithmetic, no fused operations.
+ * with qmax = 7 / 15 / 31 / 127, IEEE float32 arithmetic, no fused operations.
  * The rotation is y = fp32(1/sqrt(d)) * FWHT(x) with the float32 butterfly
  * stages applied in the order h = 1, 2, 4, ..., d/2.
  */
@@ -96,8 +111,8 @@ typedef struct kvq_config {
   int32_t batch;       /* sequences, 1..KVQ_MAX_BATCH */
   int32_t n_kv_heads;  /* KV heads per sequence, >= 1 */
   int32_t head_dim;    /* 64, 128 or 256 */
-  int32_t k_bits;      /* 4, 5 or 8 */
-  int32_t v_bits;      /* 4, 5 or 8 */
+  int32_t k_bits;      /* 4, 5, 6 or 8 (q4_0, q5_0, q6_0, q8_0 blocks) */
+  int32_t v_bits;      /* 4, 5, 6 or 8 */
   int32_t tail_len;    /* newest tokens kept in bf16, >= 0 */
   int32_t max_ctx;     /* capacity per sequence in tokens, >= 1 */
   int32_t rotate_k;    /* 1: rotate K (and q); 0: store K as is */

@@ -55,7 +55,9 @@ def test_default_rotation_rule(d, rot):
 def test_config_check():
     c = kvq.kvq_config_default(2, 4, 128, 1000)
     assert kvq.kvq_config_check(c) == 0
-    for field, val, want in (("head_dim", 192, -2), ("head_dim", 32, -2), ("k_bits", 6, -2),
+    c.k_bits, c.v_bits = 6, 6                       # q6_0
+    assert kvq.kvq_config_check(c) == 0
+    for field, val, want in (("head_dim", 192, -2), ("head_dim", 32, -2), ("k_bits", 7, -2),
                              ("v_bits", 3, -2), ("batch", 0, -1), ("batch", 257, -1),
                              ("tail_len", -1, -1), ("max_ctx", 0, -1), ("rotate_k", 2, -1)):
         bad = kvq.kvq_config_default(2, 4, 128, 1000)
@@ -64,7 +66,7 @@ def test_config_check():
 
 
 @pytest.mark.parametrize("d", (64, 128, 256))
-@pytest.mark.parametrize("kb,vb", ((4, 4), (8, 4), (5, 4), (8, 8), (5, 5)))
+@pytest.mark.parametrize("kb,vb", ((4, 4), (8, 4), (5, 4), (8, 8), (5, 5), (6, 6)))
 def test_plane_bytes(d, kb, vb):
     B, H, max_ctx, T = 3, 2, 1000, 16
     c = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T)

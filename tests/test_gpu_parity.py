@@ -35,6 +35,10 @@ APPEND_CASES = [
     (128, 5, 5, 0, "f32", 1, 2, [65], True),
     (128, 4, 8, 0, "bf16", 1, 2, [80], False),
     (256, 4, 4, 32, "bf16", 1, 2, [40, 40], False),
+    # q6_0
+    (128, 6, 6, 0, "bf16", 2, 4, [130, 1, 61], True),
+    (64, 6, 4, 8, "f32", 1, 2, [70, 1, 1], True),
+    (256, 8, 6, 16, "bf16", 1, 2, [40, 1, 30], True),
 ]
 
 
@@ -65,6 +69,7 @@ ONE_TOKEN_CASES = [
     (128, 4, 5, 0, "bf16", 1, 2, False),
     (128, 8, 4, 64, "bf16", 3, 1, True),
     (256, 4, 4, 1, "bf16", 1, 1, True),
+    (128, 6, 6, 8, "bf16", 2, 2, True),
 ]
 
 
@@ -93,7 +98,10 @@ def test_one_token_appends_bit_exact(case):
     pair.compare_planes()
 
 
-@pytest.mark.parametrize("case", APPEND_CASES[:8], ids=[_case_id(c) for c in APPEND_CASES[:8]])
+DEQUANT_CASES = APPEND_CASES[:8] + APPEND_CASES[-3:]
+
+
+@pytest.mark.parametrize("case", DEQUANT_CASES, ids=[_case_id(c) for c in DEQUANT_CASES])
 def test_dequantize_bit_exact(case):
     import torch
     import decode_attention_rotate_amd as kvq
@@ -153,6 +161,9 @@ ATTN_CASES = [
     ("small", dict(Hq=8), [1]),               # G = 1, one token
     ("tiny", dict(B=2, k_bits=8, v_bits=5), [64, 63]),
     ("huge", dict(B=1, Hq=8, k_bits=4, v_bits=8, tail=100), [300]),
+    ("mid", dict(B=2, k_bits=6, v_bits=6), [700, 129]),          # q6_0
+    ("huge", dict(B=1, Hq=8, k_bits=6, v_bits=4), [300]),
+    ("long", dict(B=1, k_bits=8, v_bits=6, tail=64), [500]),
 ]
 
 
@@ -255,6 +266,7 @@ PREFILL_CASES = [
     ("small", dict(Hq=24), [0], 129),                   # G = 3, several row blocks
     ("small", dict(Hq=56, dtype="f32"), [100], 10),     # G = 7, float32 queries
     ("tiny", dict(B=2, k_bits=8, v_bits=5, tail=8), [64, 1], 3),
+    ("small", dict(k_bits=6, v_bits=6), [200], 30),
 ]
 
 
