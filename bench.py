@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--no-rotation-off", action="store_true",
                     help="skip the secondary run with rotation disabled")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--k-bits", type=int, default=0, help="override the workload's K code width")
+    ap.add_argument("--v-bits", type=int, default=0, help="override the workload's V code width")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the chunked-prefill measurement (for profiling) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -179,6 +181,10 @@ def main():
         print(json.dumps(prefill_bench(torch, kvq, dev)), flush=True)
         return 0
     w = workloads.workload(args.workload)
+    if args.k_bits:
+        w["k_bits"] = args.k_bits
+    if args.v_bits:
+        w["v_bits"] = args.v_bits
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     log("workload", describe(w))
 
