@@ -108,8 +108,11 @@ int max_splits(const kvq_config& c, int n_q_heads) {
 
 // Chunked prefill: the n_q * G rows of a KV head go in blocks of 8 rows per
 // wave of a workgroup; each row block is split along the cache into S
-// ranges, enough workgroups for one per compute unit (256), at most one per
-// 64-token tile of the longest sequence.  Non-decreasing in max_len.
+// ranges.  One workgroup fills a compute unit, so a launch of W workgroups
+// runs ceil(W / 256) rounds of 1/S of the work each: S minimises
+// ceil(blocks * S / 256) / S (the first S within 2% of the best) up to
+// max(16, twice what fills the chip), at most one split per 64-token tile of
+// the longest sequence.  Non-decreasing in max_len.
 struct PrefillSchedule {
   int n_rb, S;
 };
@@ -120,8 +123,13 @@ PrefillSchedule prefill_schedule(const kvq_config& c, int n_q_heads, int n_q, in
   p.n_rb = (int)(((int64_t)n_q * G + rows_per_block - 1) / rows_per_block);
   const int64_t blocks = (int64_t)c.batch * c.n_kv_heads * p.n_rb;
   const int64_t tiles = std::max(1, (max_len + kTile - 1) / kTile);
-  const int64_t want = std::max<int64_t>(1, (256 + blocks - 1) / blocks);
-  p.S = (int)std::min<int64_t>(std::min<int64_t>(want, tiles), kMaxSplits);
+  const int64_t smax = std::min<int64_t>(std::min<int64_t>(kMaxSplits, tiles),
+                                         std::max<int64_t>(16, 2 * ((256 + blocks - 1) / blocks)));
+  auto cost = [&](int64_t S) { return (double)((blocks * S + 255) / 256) / (double)S; };
+  double best = cost(1);
+  for (int64_t S = 2; S <= smax; ++S) best = std::min(best, cost(S));
+  p.S = 1;
+  while (p.S < smax && cost(p.S) > best * 1.02) ++p.S;
   return p;
 }
 
