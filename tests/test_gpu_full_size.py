@@ -20,7 +20,7 @@ import torch
 import workloads
 import decode_attention_rotate_amd as kvq
 from gpu_common import say
-from oracle import rotate_f32, quantize_blocks, decode_reference
+from oracle import rotate_f32, quantize_blocks, decode_reference, prefill_reference
 from oracle.blockquant import (bf16_round, bf16_bits_to_f32, f32_to_bf16_bits, padded_row_bytes,
                                v_tile_bytes)
 from oracle.kvcache import plane_codes
@@ -148,3 +148,42 @@ def test_full_size_sampled(name, units):
         torch.cuda.synchronize()
     for b, g in units:
         check_unit_attention(w, cache, cfg, out, q, b, g, n + steps)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_full_size_sampled():
+    # the prefill measurement's shape: batch 1, 40 query / 8 KV heads, K8 V4,
+    # tail 1024, a 512-token chunk appended after 65024 cached tokens; sampled
+    # rows (first, middle, last query of the chunk; two heads each of two KV
+    # heads) against the oracle on the device cache
+    w = workloads.workload("long", B=1)
+    Hkv, Hq, d, n, n_q = w["Hkv"], w["Hq"], w["d"], w["n"], 512
+    n0 = n - n_q
+    cfg = kvq.kvq_config(1, Hkv, d, n, w["k_bits"], w["v_bits"], w["tail"])
+    cache = kvq.KVCache(cfg, DEV)
+    for t0 in range(0, n0, FILL):
+        t1 = min(n0, t0 + FILL)
+        say("prefill full size fill", t0, t1)
+        kvq.kvq_rotate_quantize_append(cfg, cache, workloads.kv_torch(w, 1, t0, t1, DEV, torch),
+                                       workloads.kv_torch(w, 2, t0, t1, DEV, torch), [t0])
+    kvq.kvq_rotate_quantize_append(cfg, cache, workloads.kv_torch(w, 1, n0, n, DEV, torch),
+                                   workloads.kv_torch(w, 2, n0, n, DEV, torch), [n0])
+    q = workloads.prefill_q_torch(w, n_q, 0, DEV, torch)
+    say("prefill full size attention")
+    out = kvq.kvq_prefill_attention(cfg, cache, q, [n])
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    qv = host_values(q)
+    G = Hq // Hkv
+    for g in (2, 7):
+        planes = unit_planes(cache, cfg, 0, g)
+        heads = (g * G, g * G + G - 1)
+        rows = [(0, i, h - g * G) for i in (0, 255, 511) for h in heads]
+        ref = prefill_reference(planes, qv[:, :, g * G:(g + 1) * G], [n], 1, d, w["k_bits"],
+                                w["v_bits"], w["tail"], rows=rows)
+        for b, i, hl in rows:
+            got = out[0, i, g * G + hl]
+            err = np.linalg.norm(got - ref[0, i, hl]) / np.linalg.norm(ref[0, i, hl])
+            say("prefill full size row", (i, g * G + hl), "rel L2 %.3e" % err)
+            assert err <= TOL, (i, g, hl, err)
