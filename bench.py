@@ -152,6 +152,8 @@ def main():
     ap.add_argument("--v-bits", type=int, default=0, help="override the workload's V code width")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the chunked-prefill measurement (for profiling) and exit")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only run the bulk append measurement (for profiling) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -179,6 +181,9 @@ def main():
     torch.cuda.set_device(0)
     if args.prefill_only:
         print(json.dumps(prefill_bench(torch, kvq, dev)), flush=True)
+        return 0
+    if args.append_only:
+        print(json.dumps(bulk_append(torch, kvq, dev)), flush=True)
         return 0
     w = workloads.workload(args.workload)
     if args.k_bits:

@@ -71,40 +71,40 @@ __device__ inline void load_bf16_block(const uint16_t* row, float (&x)[32]) {
   }
 }
 
-// K codes of block j of position p, row layout (tiled 16-byte chunks).
+// K codes of block j of position p, row layout (tiled 16-byte chunks), from
+// the quantizer's words m (low byte: offset code u = c + 2^(BITS-1)).
 template <int D, int BITS>
-__device__ inline void store_k_row(const int (&c)[32], uint8_t* plane, int p, int j) {
+__device__ inline void store_k_row(const uint32_t (&m)[32], uint8_t* plane, int p, int j) {
   constexpr int RP = padded_row_bytes(D, BITS);
   if constexpr (BITS == 8) {
+    // two's-complement bytes: u ^ 0x80 = c
     uint32_t w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      w[k] = (uint32_t)(c[4 * k] & 0xFF) | ((uint32_t)(c[4 * k + 1] & 0xFF) << 8) |
-             ((uint32_t)(c[4 * k + 2] & 0xFF) << 16) | ((uint32_t)(c[4 * k + 3] & 0xFF) << 24);
+      w[k] = gather_low_bytes(m[4 * k], m[4 * k + 1], m[4 * k + 2], m[4 * k + 3]) ^ 0x80808080u;
     *reinterpret_cast<uint4*>(plane + chunk_offset(p, 2 * j, RP)) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint4*>(plane + chunk_offset(p, 2 * j + 1, RP)) = make_uint4(w[4], w[5], w[6], w[7]);
   } else {
-    constexpr int OFF = 1 << (BITS - 1);
+    // nibble pairs: element 2i low, 2i+1 high (u < 16 needs no mask)
+    uint32_t pr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      pr[i] = BITS == 4 ? (m[2 * i + 1] << 4) | m[2 * i] : (m[2 * i + 1] << 4) | (m[2 * i] & 15u);
     uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v |= (uint32_t)((c[8 * k + e] + OFF) & 15) << (4 * e);
-      w[k] = v;
-    }
+    for (int k = 0; k < 4; ++k) w[k] = gather_low_bytes(pr[4 * k], pr[4 * k + 1], pr[4 * k + 2], pr[4 * k + 3]);
     *reinterpret_cast<uint4*>(plane + chunk_offset(p, j, RP)) = make_uint4(w[0], w[1], w[2], w[3]);
     if constexpr (BITS == 5) {
       uint32_t hw = 0;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) hw |= (uint32_t)(((c[e] + OFF) >> 4) & 1) << hibit_pos(e);
+      for (int e = 0; e < 32; ++e) hw |= ((m[e] >> 4) & 1u) << hibit_pos(e);
       const int byte = D / 2 + 4 * j;
       *reinterpret_cast<uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk) = hw;
     }
     if constexpr (BITS == 6) {
       uint32_t hw[2] = {0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 32; ++e) hw[e / 16] |= (uint32_t)(((c[e] + OFF) >> 4) & 3) << hi2_pos(e);
+      for (int e = 0; e < 32; ++e) hw[e / 16] |= ((m[e] >> 4) & 3u) << hi2_pos(e);
       const int byte = D / 2 + 8 * j;
       *reinterpret_cast<uint2*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk) = make_uint2(hw[0], hw[1]);
     }
@@ -112,7 +112,7 @@ __device__ inline void store_k_row(const int (&c)[32], uint8_t* plane, int p, in
 }
 
 template <int D>
-__device__ inline uint32_t quantize_k(int bits, const float (&x)[32], int (&c)[32], bool active,
+__device__ inline uint32_t quantize_k(int bits, const float (&x)[32], uint32_t (&c)[32], bool active,
                                       uint8_t* plane, int p, int j) {
   uint32_t s;
   if (bits == 4) {
@@ -132,7 +132,7 @@ __device__ inline uint32_t quantize_k(int bits, const float (&x)[32], int (&c)[3
 }
 
 template <int D>
-__device__ inline uint32_t quantize_any(int bits, const float (&x)[32], int (&c)[32]) {
+__device__ inline uint32_t quantize_any(int bits, const float (&x)[32], uint32_t (&c)[32]) {
   if (bits == 4) return quantize_block<4>(x, c);
   if (bits == 5) return quantize_block<5>(x, c);
   if (bits == 6) return quantize_block<6>(x, c);
@@ -242,7 +242,7 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
 
   const int bits = a.bits[pl];
   uint16_t* scales = a.scales[pl] + unit * (size_t)a.cap * (D / kBlock);
-  int c[32];
+  uint32_t c[32];
   if (pl == 0) {
     uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
     const uint32_t s = quantize_k<D>(bits, x, c, active, plane, p, j);
@@ -254,10 +254,9 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
   const uint32_t s = quantize_any<D>(bits, x, c);
   if (active) {
     scales[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
-    const int off = 1 << (bits - 1);
     uint8_t* dst = vlds + ((rho / 8) * D + kBlock * j) * 8 + rho % 8;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) dst[8 * e] = (uint8_t)(c[e] + off);
+    for (int e = 0; e < 32; ++e) dst[8 * e] = (uint8_t)c[e];   // offset code
   }
   __syncthreads();
 
@@ -444,18 +443,17 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) z[e] = T > 0 ? y[e] : x[e];
     uint16_t* scales = a.scales[pl] + unit * (size_t)a.cap * (D / kBlock);
-    int c[32];
+    uint32_t c[32];
     if (pl == 0) {
       uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
       scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_k<D>(bits, z, c, true, plane, pq, j);
     } else {
       scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_block<VB>(z, c);
       const int k = pq % 8;
-      constexpr int off = 1 << (VB - 1);
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int item = v_item(D, pq % kTile, kBlock * j + i);
-        const uint32_t u = (uint32_t)(c[i] + off);
+        const uint32_t u = c[i] & 0xFFu;   // offset code
         if constexpr (VB == 8) {
           vtile[8 * item + k] = (uint8_t)u;
         } else {

@@ -129,10 +129,16 @@ __host__ __device__ constexpr int hi2_pos(int w) {
   return 8 * ((w % 8) / 2) + 4 * ((w / 8) % 2) + 2 * (w % 2);
 }
 
-// Quantize one 32-element block: fp16 scale bits and int codes.
+// Quantize one 32-element block: returns the fp16 scale bits; m[i] & 0xFF is
+// the offset code c + 2^(BITS-1) of element i (higher bits are not zero).
+// The code is clamp(x * r) rounded to nearest even: clamping to the integer
+// bound first and then rounding equals rounding then clamping, and adding
+// 1.5 * 2^23 + offset rounds |t| <= 127 to an integer in float32's last
+// place (ties to even), leaving it in the low mantissa bits.
 template <int BITS>
-__device__ inline uint32_t quantize_block(const float (&x)[32], int (&c)[32]) {
+__device__ inline uint32_t quantize_block(const float (&x)[32], uint32_t (&m)[32]) {
   constexpr float qmax = (float)qmax_of(BITS);
+  constexpr float kMagic = 12582912.0f + (float)(1 << (BITS - 1));
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(x[i]));
@@ -143,10 +149,17 @@ __device__ inline uint32_t quantize_block(const float (&x)[32], int (&c)[32]) {
   const float r = sf != 0.f ? 1.0f / sf : 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float t = rintf(x[i] * r);
-    c[i] = (int)fminf(fmaxf(t, -qmax), qmax);
+    const float t = __builtin_amdgcn_fmed3f(x[i] * r, -qmax, qmax);
+    m[i] = __float_as_uint(t + kMagic);
   }
   return (uint32_t)__builtin_bit_cast(uint16_t, s16);
+}
+
+// Low bytes of a, b, c, d as one little-endian word.
+__device__ inline uint32_t gather_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 }  // namespace kvq
