@@ -41,7 +41,8 @@ from .rotation import (hadamard, rot_scale_f32, fwht_f32, rotate_f32, unrotate_f
                        hadamard_signs, rotation_matrix, splitmix64)
 from .blockquant import (
     QMAX, BLOCK, bf16_round, bf16_bits_to_f32, f32_to_bf16_bits,
-    quantize_blocks, dequantize_blocks, pack_rows, unpack_rows,
+    quantize_blocks, dequantize_blocks, quantize_blocks_min, dequantize_blocks_min,
+    pack_rows, unpack_rows,
     row_bytes, padded_row_bytes, rows_to_tiled, tiled_to_rows,
 )
 from .kvcache import OracleCache
@@ -52,7 +53,8 @@ __all__ = [
     "hadamard", "rot_scale_f32", "fwht_f32", "rotate_f32", "unrotate_f32",
     "hadamard_signs", "rotation_matrix", "splitmix64",
     "QMAX", "BLOCK", "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits",
-    "quantize_blocks", "dequantize_blocks", "pack_rows", "unpack_rows",
+    "quantize_blocks", "dequantize_blocks", "quantize_blocks_min", "dequantize_blocks_min",
+    "pack_rows", "unpack_rows",
     "row_bytes", "padded_row_bytes", "rows_to_tiled", "tiled_to_rows",
     "OracleCache", "softmax_attention", "decode_reference", "prefill_reference", "dequantize_unit",
     "dequantize_reference",

@@ -45,20 +45,21 @@ def softmax_attention(q, K, V, sm_scale):
     return w @ V
 
 
-def dequantize_unit(planes, b, g, n, d, k_bits, v_bits, tail_len):
+def dequantize_unit(planes, b, g, n, d, k_bits, v_bits, tail_len, k_min=False, v_min=False):
     """Rotated-space K_hat, V_hat (float64, [n][d]) of sequence b, KV head g.
 
     Positions below n - min(n, T) come from the code planes; the newest
-    min(n, T) positions come from tail slot p mod T."""
+    min(n, T) positions come from tail slot p mod T.  k_min / v_min select
+    the scale-and-min blocks of reading R22."""
     T = int(tail_len)
     nt = min(n, T) if T > 0 else 0
     nq = n - nt
     out = []
-    for p, bits in (("k", k_bits), ("v", v_bits)):
+    for p, bits, mf in (("k", k_bits, k_min), ("v", v_bits, v_min)):
         x = np.zeros((n, d), dtype=np.float64)
         if nq > 0:
             x[:nq] = dequantize_rows(planes[p + "_codes"][b, g],
-                                     planes[p + "_scales"][b, g], d, bits, nq, p)
+                                     planes[p + "_scales"][b, g], d, bits, nq, p, mf)
         for pos in range(nq, n):
             x[pos] = bf16_bits_to_f32(planes[p + "_tail"][b, g, pos % T])
         out.append(x)
@@ -67,7 +68,7 @@ def dequantize_unit(planes, b, g, n, d, k_bits, v_bits, tail_len):
 
 def decode_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
                      tail_len, sm_scale=None, rotate_k=True, rotate_v=True,
-                     heads=None, sign_seed=0):
+                     heads=None, sign_seed=0, k_min=False, v_min=False):
     """Reference output [B][Hq][d] (float64) of decode attention.
 
     q: float values [B][Hq][d] (already widened from bf16 if needed).
@@ -90,7 +91,7 @@ def decode_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
             g = h // G
             if (b, g) not in cache:
                 cache[(b, g)] = dequantize_unit(planes, b, g, int(lens[b]), d,
-                                                k_bits, v_bits, tail_len)
+                                                k_bits, v_bits, tail_len, k_min, v_min)
             K, V = cache[(b, g)]
             qr = H @ q[b, h] if rotate_k else q[b, h]
             o = softmax_attention(qr, K, V, sm_scale)
@@ -100,7 +101,7 @@ def decode_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
 
 def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
                       tail_len, sm_scale=None, rotate_k=True, rotate_v=True,
-                      rows=None, sign_seed=0):
+                      rows=None, sign_seed=0, k_min=False, v_min=False):
     """Reference output [B][n_q][Hq][d] (float64) of chunked prefill attention.
 
     q: float values [B][n_q][Hq][d], the queries of the last n_q positions of
@@ -126,7 +127,7 @@ def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
                 g = h // G
                 if (b, g) not in cache:
                     cache[(b, g)] = dequantize_unit(planes, b, g, n, d, k_bits, v_bits,
-                                                    tail_len)
+                                                    tail_len, k_min, v_min)
                 K, V = cache[(b, g)]
                 qr = H @ q[b, i, h] if rotate_k else q[b, i, h]
                 o = softmax_attention(qr, K[:p + 1], V[:p + 1], sm_scale)
@@ -135,7 +136,7 @@ def prefill_reference(planes, q, lens, n_kv_heads, d, k_bits, v_bits,
 
 
 def dequantize_reference(planes, which, b, t0, t1, n, n_kv_heads, d, bits,
-                         tail_len, space, rotate=True, sign_seed=0):
+                         tail_len, space, rotate=True, sign_seed=0, minf=False):
     """Dequantized positions [t0, t1) of sequence b (length n), all KV heads.
 
     space 0: rotated space (exact float32).  space 1: original space, i.e. the
@@ -150,7 +151,7 @@ def dequantize_reference(planes, which, b, t0, t1, n, n_kv_heads, d, bits,
     for g in range(n_kv_heads):
         if nq > 0:
             rows = dequantize_rows(planes[p + "_codes"][b, g],
-                                   planes[p + "_scales"][b, g], d, bits, nq, p)
+                                   planes[p + "_scales"][b, g], d, bits, nq, p, minf)
         for pos in range(t0, t1):
             if pos < nq:
                 out[pos - t0, g] = rows[pos]

@@ -47,6 +47,15 @@ the GPU reproduces it bit for bit.  Readings (the pages do not fix these):
       4*(k%2) + k//2 is bit 4 of u.  6-bit: the 4-bit words of u & 15, then
       one little-endian 16-bit field per item whose bits 2n and 2n+1, with
       n = 4*(k%2) + k//2, are bits 4 and 5 of u.
+* R22 Scale-and-min blocks q4_1 / q5_1 (the aiwitness.kr table's q5_1 rows, 37.5 %
+      of bf16 = 5 bits plus two 2-byte values per 32; the aitrends.kr article
+      names a q5_0-q4_1 pair): per block lo = min x, hi = max x, s =
+      fp16_rne(min(fp32(hi - lo) / (2^b - 1), 65504)), m = fp16_rne(lo clamped
+      to +-65504), r = 1 / fp32(s), u = clip(rint(fp32(fp32(x - m) * r)), 0,
+      2^b - 1) (all 0 if s == 0); x_hat = fp32(u * s + m).  The scale plane
+      holds the (s, m) pair of each block; the code planes hold u exactly
+      where the symmetric formats hold c + 2^(b-1), so they are laid out by
+      the same rules with c = u - 2^(b-1).
 """
 
 import numpy as np
@@ -110,6 +119,49 @@ def quantize_blocks(xq, bits):
     c = np.where(nz[..., None], c, np.float32(0.0))
     codes = c.astype(np.int8).reshape(x.shape)
     return codes, s16.view(np.uint16)
+
+
+def quantize_blocks_min(xq, bits):
+    """Scale-and-min quantization of float32 rows (reading R22).
+
+    Returns (codes, pairs): codes int8 [..., d] holding u - 2^(bits-1) (the
+    storage convention of the symmetric formats); pairs uint16 [..., d/32, 2]
+    holding the fp16 bits of (s, m)."""
+    if bits not in (4, 5):
+        raise ValueError("scale-and-min blocks are 4 or 5 bits")
+    umax = np.float32((1 << bits) - 1)
+    x = np.asarray(xq, dtype=np.float32)
+    d = x.shape[-1]
+    blocks = x.reshape(x.shape[:-1] + (d // BLOCK, BLOCK))
+    lo = np.min(blocks, axis=-1)
+    hi = np.max(blocks, axis=-1)
+    s32 = (hi - lo).astype(np.float32) / umax
+    s16 = np.minimum(s32, np.float32(65504.0)).astype(np.float16)
+    m16 = np.clip(lo, np.float32(-65504.0), np.float32(65504.0)).astype(np.float16)
+    sf = s16.astype(np.float32)
+    mf = m16.astype(np.float32)
+    nz = sf != 0
+    r = np.where(nz, np.float32(1.0) / np.where(nz, sf, np.float32(1.0)),
+                 np.float32(0.0)).astype(np.float32)
+    t = ((blocks - mf[..., None]).astype(np.float32) * r[..., None]).astype(np.float32)
+    u = np.clip(np.rint(t), np.float32(0), umax)
+    u = np.where(nz[..., None], u, np.float32(0.0))
+    codes = (u.astype(np.int16) - (1 << (bits - 1))).astype(np.int8).reshape(x.shape)
+    pairs = np.stack([s16.view(np.uint16), m16.view(np.uint16)], axis=-1)
+    return codes, pairs
+
+
+def dequantize_blocks_min(codes, pairs, bits):
+    """x_hat = fp32(u * s + m) with u = code + 2^(bits-1): u * s is exact
+    (at most 5 + 11 significant bits), so the single rounding of the sum
+    leaves one right answer (reading R22)."""
+    u = np.asarray(codes, dtype=np.int16).astype(np.float32) + np.float32(1 << (bits - 1))
+    d = u.shape[-1]
+    pr = np.asarray(pairs, dtype=np.uint16).view(np.float16).astype(np.float32)
+    s = pr[..., 0]
+    m = pr[..., 1]
+    out = u.reshape(u.shape[:-1] + (d // BLOCK, BLOCK)) * s[..., None] + m[..., None]
+    return out.reshape(u.shape).astype(np.float32)
 
 
 def dequantize_blocks(codes, scales_bits):

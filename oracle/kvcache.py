@@ -22,7 +22,8 @@ import numpy as np
 
 from .rotation import rotate_f32, hadamard_signs
 from .blockquant import (
-    BLOCK, TILE, quantize_blocks, dequantize_blocks, pack_rows, unpack_rows,
+    BLOCK, TILE, quantize_blocks, dequantize_blocks, quantize_blocks_min,
+    dequantize_blocks_min, pack_rows, unpack_rows,
     row_bytes, padded_row_bytes, rows_to_tiled, tiled_to_rows,
     offset_codes_to_vtiles, vtiles_to_codes, v_tile_bytes,
     f32_to_bf16_bits, bf16_bits_to_f32,
@@ -45,9 +46,11 @@ class OracleCache:
     """
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits,
-                 tail_len, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0):
+                 tail_len, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0,
+                 k_min=False, v_min=False):
         self.B, self.H, self.d = batch, n_kv_heads, head_dim
         self.signs = hadamard_signs(head_dim, sign_seed)      # reading R21
+        self.minf = {"k": bool(k_min), "v": bool(v_min)}      # reading R22
         self.bits = {"k": k_bits, "v": v_bits}
         self.rot = {"k": bool(rotate_k), "v": bool(rotate_v)}
         self.T = int(tail_len)
@@ -61,7 +64,9 @@ class OracleCache:
         # V codes as offset codes u = c + 2^(bits-1) (u = 0: never written)
         self.v_u = np.zeros((batch, n_kv_heads, self.cap, head_dim), np.uint8)
         for p in ("k", "v"):
-            self.scales[p] = np.zeros((batch, n_kv_heads, self.cap, nb), np.uint16)
+            # symmetric: one fp16 scale per block; scale-and-min: (s, m) pairs
+            per = 2 if self.minf[p] else 1
+            self.scales[p] = np.zeros((batch, n_kv_heads, self.cap, nb * per), np.uint16)
             self.tail[p] = np.zeros((batch, n_kv_heads, max(self.T, 0), head_dim), np.uint16)
 
     def append(self, k_new, v_new, lens, dtype="bf16"):
@@ -100,7 +105,11 @@ class OracleCache:
                 self.tail[p][b, :, pos % T, :] = f32_to_bf16_bits(y[i])
 
     def _store_quantized(self, p, b, pos, xq, bits):
-        codes, scales = quantize_blocks(xq, bits)   # [H][d], [H][d/32]
+        if self.minf[p]:
+            codes, pairs = quantize_blocks_min(xq, bits)      # [H][d], [H][d/32][2]
+            scales = pairs.reshape(pairs.shape[0], -1)
+        else:
+            codes, scales = quantize_blocks(xq, bits)         # [H][d], [H][d/32]
         self.rows[p][b, :, pos, :] = pack_rows(codes, bits)
         self.scales[p][b, :, pos, :] = scales
         if p == "v":
@@ -146,6 +155,11 @@ def plane_codes(codes_plane, d, bits, n, which):
     return vtiles_to_codes(codes_plane, n_t, d, bits)[:n]
 
 
-def dequantize_rows(codes_plane, scales_plane, d, bits, n, which):
-    """Dequantized values (rotated space, float32) of quantized rows [0, n)."""
-    return dequantize_blocks(plane_codes(codes_plane, d, bits, n, which), scales_plane[:n])
+def dequantize_rows(codes_plane, scales_plane, d, bits, n, which, minf=False):
+    """Dequantized values (rotated space, float32) of quantized rows [0, n);
+    minf selects the scale-and-min blocks of reading R22."""
+    codes = plane_codes(codes_plane, d, bits, n, which)
+    if minf:
+        pairs = np.asarray(scales_plane[:n]).reshape(n, d // BLOCK, 2)
+        return dequantize_blocks_min(codes, pairs, bits)
+    return dequantize_blocks(codes, scales_plane[:n])

@@ -184,14 +184,16 @@ def _golden_percent():
 
 
 def test_block_bytes_match_page3_cache_sizes():
-    bits_of = {"q4_0": 4, "q5_0": 5, "q6_0": 6, "q8_0": 8}
+    bits_of = {"q4_0": 4, "q5_0": 5, "q6_0": 6, "q8_0": 8, "q5_1": 5}
     table = _golden_percent()
     assert table.pop("bf16") == 100.0
     for name, pct in table.items():
         parts = name.split("-")
         k, v = parts[0], parts[-1]
-        # one 32-element block: packed codes plus a 2-byte scale, vs 64 bytes of bf16
-        per = [Fraction(row_bytes(32, bits_of[p]) + 2, 64) * 100 for p in (k, v)]
+        # one 32-element block: packed codes plus a 2-byte scale (and a 2-byte
+        # minimum for the _1 formats), vs 64 bytes of bf16
+        per = [Fraction(row_bytes(32, bits_of[p]) + (4 if p.endswith("_1") else 2), 64) * 100
+               for p in (k, v)]
         mean = sum(per) / 2
         # the table prints one decimal, rounding halves up (q5_0-q4_0: 31.25 -> 31.3)
         assert int(mean * 10 + Fraction(1, 2)) == round(pct * 10), name
