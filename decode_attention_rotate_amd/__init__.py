@@ -40,8 +40,10 @@ def kvq_config_default(batch, n_kv_heads, head_dim, max_ctx):
 
 
 def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
-               tail_len=0, rotate_k=None, rotate_v=None, sign_seed=0):
-    """kvq_config_default with fields overridden; validated by the library."""
+               tail_len=0, rotate_k=None, rotate_v=None, sign_seed=0, k_min=False,
+               v_min=False):
+    """kvq_config_default with fields overridden; validated by the library.
+    k_min / v_min select scale-and-min blocks (q4_1 / q5_1 at 4 / 5 bits)."""
     c = kvq_config_default(batch, n_kv_heads, head_dim, max_ctx)
     c.k_bits, c.v_bits, c.tail_len = k_bits, v_bits, tail_len
     if rotate_k is not None:
@@ -49,6 +51,7 @@ def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
     if rotate_v is not None:
         c.rotate_v = int(rotate_v)
     c.sign_seed = int(sign_seed) & 0xFFFFFFFF
+    c.k_min, c.v_min = int(k_min), int(v_min)
     _capi.check(_capi.lib().kvq_config_check(ctypes.byref(c)), "kvq_config")
     return c
 

@@ -35,7 +35,8 @@ EXPORTS = (
 class KvqConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "n_kv_heads", "head_dim", "k_bits", "v_bits", "tail_len",
-        "max_ctx", "rotate_k", "rotate_v")] + [("sign_seed", ctypes.c_uint32)]
+        "max_ctx", "rotate_k", "rotate_v")] + [("sign_seed", ctypes.c_uint32),
+                                               ("k_min", ctypes.c_int32), ("v_min", ctypes.c_int32)]
 
     def __repr__(self):
         return "KvqConfig(%s)" % ", ".join(

@@ -3,8 +3,8 @@
 // Each new K/V head vector is rotated by the normalized Hadamard matrix
 // (velog.io post "fix KV cache quantization outliers", section "Hadamard
 // rotation") and either quantized into 32-element blocks with one fp16 absmax
-// scale (byte cost per the aiwitness.kr table "Qwen 3.6 27B Q5_K_S + 64k
-// context KLD results") or, for the newest tail_len positions, stored in the
+// scale, or a scale and a minimum (byte cost per the aiwitness.kr table "Qwen
+// 3.6 27B Q5_K_S + 64k context KLD results"), or, for the newest tail_len positions, stored in the
 // bf16 precision tail (aitrends.kr article 92204, glossary "Precision Tail").
 //
 // An append of n_new tokens to a sequence of length len runs in two steps
@@ -111,15 +111,26 @@ __device__ inline void store_k_row(const uint32_t (&m)[32], uint8_t* plane, int 
   }
 }
 
+// Quantize one block with the symmetric rule, or with the scale-and-min
+// rule when minf (4/5-bit only); the codes' low bytes are what the planes
+// store (c + 2^(bits-1), or the level u), the result the scale (pair) bits.
+template <int BITS>
+__device__ inline uint32_t quantize_fmt(bool minf, const float (&x)[32], uint32_t (&c)[32]) {
+  if constexpr (BITS == 4 || BITS == 5) {
+    if (minf) return quantize_block_min<BITS>(x, c);
+  }
+  return quantize_block<BITS>(x, c);
+}
+
 template <int D>
-__device__ inline uint32_t quantize_k(int bits, const float (&x)[32], uint32_t (&c)[32], bool active,
-                                      uint8_t* plane, int p, int j) {
+__device__ inline uint32_t quantize_k(int bits, bool minf, const float (&x)[32], uint32_t (&c)[32],
+                                      bool active, uint8_t* plane, int p, int j) {
   uint32_t s;
   if (bits == 4) {
-    s = quantize_block<4>(x, c);
+    s = quantize_fmt<4>(minf, x, c);
     if (active) store_k_row<D, 4>(c, plane, p, j);
   } else if (bits == 5) {
-    s = quantize_block<5>(x, c);
+    s = quantize_fmt<5>(minf, x, c);
     if (active) store_k_row<D, 5>(c, plane, p, j);
   } else if (bits == 6) {
     s = quantize_block<6>(x, c);
@@ -132,11 +143,23 @@ __device__ inline uint32_t quantize_k(int bits, const float (&x)[32], uint32_t (
 }
 
 template <int D>
-__device__ inline uint32_t quantize_any(int bits, const float (&x)[32], uint32_t (&c)[32]) {
-  if (bits == 4) return quantize_block<4>(x, c);
-  if (bits == 5) return quantize_block<5>(x, c);
+__device__ inline uint32_t quantize_any(int bits, bool minf, const float (&x)[32], uint32_t (&c)[32]) {
+  if (bits == 4) return quantize_fmt<4>(minf, x, c);
+  if (bits == 5) return quantize_fmt<5>(minf, x, c);
   if (bits == 6) return quantize_block<6>(x, c);
   return quantize_block<8>(x, c);
+}
+
+// Scale entry of block j of position p: one fp16, or an (s, m) pair of fp16
+// (one 32-bit word) for scale-and-min blocks.  sc is the (b, g) plane.
+template <int D>
+__device__ inline void store_scale(uint16_t* sc, bool minf, int p, int j, uint32_t s) {
+  if (minf) reinterpret_cast<uint32_t*>(sc)[(size_t)p * (D / kBlock) + j] = s;
+  else sc[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
+}
+template <int D>
+__device__ inline uint16_t* scale_plane(const AppendArgs& a, int pl, size_t unit) {
+  return a.scales[pl] + unit * (size_t)a.cap * (D / kBlock) * (a.minf[pl] ? 2 : 1);
 }
 
 // Merge the slots of one V item whose bit is set in `mask` into memory.
@@ -241,19 +264,20 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
   if (from_ring) load_bf16_block(a.tail[pl] + (unit * T + p % T) * D + kBlock * j, x);
 
   const int bits = a.bits[pl];
-  uint16_t* scales = a.scales[pl] + unit * (size_t)a.cap * (D / kBlock);
+  const bool minf = a.minf[pl] != 0;
+  uint16_t* scales = scale_plane<D>(a, pl, unit);
   uint32_t c[32];
   if (pl == 0) {
     uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
-    const uint32_t s = quantize_k<D>(bits, x, c, active, plane, p, j);
-    if (active) scales[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
+    const uint32_t s = quantize_k<D>(bits, minf, x, c, active, plane, p, j);
+    if (active) store_scale<D>(scales, minf, p, j, s);
     return;
   }
 
   // V: codes of the block's positions meet in LDS as bytes [group][e][slot]
-  const uint32_t s = quantize_any<D>(bits, x, c);
+  const uint32_t s = quantize_any<D>(bits, minf, x, c);
   if (active) {
-    scales[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
+    store_scale<D>(scales, minf, p, j, s);
     uint8_t* dst = vlds + ((rho / 8) * D + kBlock * j) * 8 + rho % 8;
 #pragma unroll
     for (int e = 0; e < 32; ++e) dst[8 * e] = (uint8_t)c[e];   // offset code
@@ -442,13 +466,14 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
     float z[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) z[e] = T > 0 ? y[e] : x[e];
-    uint16_t* scales = a.scales[pl] + unit * (size_t)a.cap * (D / kBlock);
+    const bool minf = a.minf[pl] != 0;
+    uint16_t* scales = scale_plane<D>(a, pl, unit);
     uint32_t c[32];
     if (pl == 0) {
       uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
-      scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_k<D>(bits, z, c, true, plane, pq, j);
+      store_scale<D>(scales, minf, pq, j, quantize_k<D>(bits, minf, z, c, true, plane, pq, j));
     } else {
-      scales[(size_t)pq * (D / kBlock) + j] = (uint16_t)quantize_block<VB>(z, c);
+      store_scale<D>(scales, minf, pq, j, quantize_fmt<VB>(minf, z, c));
       const int k = pq % 8;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {

@@ -155,6 +155,37 @@ __device__ inline uint32_t quantize_block(const float (&x)[32], uint32_t (&m)[32
   return (uint32_t)__builtin_bit_cast(uint16_t, s16);
 }
 
+// Scale-and-min quantization of one 32-element block (q4_1 / q5_1): returns
+// the fp16 bits of the scale s (low half) and the minimum m (high half);
+// m[i] & 0xFF is the level u in [0, 2^BITS - 1] of element i, which the code
+// planes store where the symmetric formats store c + 2^(BITS-1).
+//   s = fp16(min((hi - lo) / (2^BITS - 1), 65504)), m = fp16(lo clamped),
+//   u = rint(clamp((x - m) * (1 / s), 0, 2^BITS - 1))   (0 when s == 0)
+// rounded to nearest even by the same magic add as quantize_block.
+template <int BITS>
+__device__ inline uint32_t quantize_block_min(const float (&x)[32], uint32_t (&m)[32]) {
+  constexpr float umax = (float)((1 << BITS) - 1);
+  constexpr float kMagic = 12582912.0f;
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+  float s32 = (hi - lo) / umax;          // correctly rounded subtract and divide
+  s32 = fminf(s32, 65504.0f);
+  const _Float16 s16 = (_Float16)s32;
+  const _Float16 m16 = (_Float16)fminf(fmaxf(lo, -65504.0f), 65504.0f);
+  const float sf = (float)s16, mf = (float)m16;
+  const float r = sf != 0.f ? 1.0f / sf : 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float t = __builtin_amdgcn_fmed3f((x[i] - mf) * r, 0.f, umax);
+    m[i] = __float_as_uint(t + kMagic);
+  }
+  return (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, m16) << 16);
+}
+
 // Low bytes of a, b, c, d as one little-endian word.
 __device__ inline uint32_t gather_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);

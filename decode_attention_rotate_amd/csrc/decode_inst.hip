@@ -1,7 +1,8 @@
-// One instantiation unit of the split-K decode kernel: head_dim KVQ_INST_D and
-// K width KVQ_INST_KB (set by the build), every V width and 1..8 query heads
-// per KV-head chunk, plus the chunked-prefill variant per V width.  Split
-// across units so the build compiles in parallel.
+// One instantiation unit of the split-K decode kernel: head_dim KVQ_INST_D,
+// K width KVQ_INST_KB and K block kind KVQ_INST_KM (1: scale-and-min), set by
+// the build; every V format and 1..8 query heads per KV-head chunk, plus the
+// chunked-prefill variant per V format.  Split across units so the build
+// compiles in parallel.
 #include "decode_kernels.hpp"
 
 #ifndef KVQ_INST_D
@@ -10,30 +11,31 @@
 #ifndef KVQ_INST_KB
 #error "KVQ_INST_KB must be defined"
 #endif
+#ifndef KVQ_INST_KM
+#error "KVQ_INST_KM must be defined"
+#endif
 
-#define KVQ_CAT2(a, b, c) a##_##b##_##c
-#define KVQ_CAT(a, b, c) KVQ_CAT2(a, b, c)
-#define KVQ_TABLE KVQ_CAT(kvq_decode_table, KVQ_INST_D, KVQ_INST_KB)
-#define KVQ_PF_TABLE KVQ_CAT(kvq_prefill_table, KVQ_INST_D, KVQ_INST_KB)
+#define KVQ_CAT2(a, b, c, d) a##_##b##_##c##_##d
+#define KVQ_CAT(a, b, c, d) KVQ_CAT2(a, b, c, d)
+#define KVQ_TABLE KVQ_CAT(kvq_decode_table, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
+#define KVQ_PF_TABLE KVQ_CAT(kvq_prefill_table, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
 
 namespace kvq {
 
-#define KVQ_ROW(VB)                                                                \
-  {launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 1>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 2>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 3>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 4>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 5>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 6>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 7>,                            \
-   launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8>}
+constexpr bool kKM = KVQ_INST_KM != 0;
 
-DecodeLauncher KVQ_TABLE[4][8] = {KVQ_ROW(4), KVQ_ROW(5), KVQ_ROW(6), KVQ_ROW(8)};
+#define KVQ_L(VB, VM, G) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, G, false, kKM, VM>
+#define KVQ_ROW(VB, VM) \
+  {KVQ_L(VB, VM, 1), KVQ_L(VB, VM, 2), KVQ_L(VB, VM, 3), KVQ_L(VB, VM, 4), \
+   KVQ_L(VB, VM, 5), KVQ_L(VB, VM, 6), KVQ_L(VB, VM, 7), KVQ_L(VB, VM, 8)}
 
-// chunked prefill, indexed by v_bits 4/5/6/8
-DecodeLauncher KVQ_PF_TABLE[4] = {launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 4, 8, true>,
-                                  launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 5, 8, true>,
-                                  launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 6, 8, true>,
-                                  launch_decode_split<KVQ_INST_D, KVQ_INST_KB, 8, 8, true>};
+// V formats in the order q4_0, q5_0, q6_0, q8_0, q4_1, q5_1
+DecodeLauncher KVQ_TABLE[6][8] = {KVQ_ROW(4, false), KVQ_ROW(5, false), KVQ_ROW(6, false),
+                                  KVQ_ROW(8, false), KVQ_ROW(4, true), KVQ_ROW(5, true)};
+
+// chunked prefill, same V order
+#define KVQ_P(VB, VM) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8, true, kKM, VM>
+DecodeLauncher KVQ_PF_TABLE[6] = {KVQ_P(4, false), KVQ_P(5, false), KVQ_P(6, false),
+                                  KVQ_P(8, false), KVQ_P(4, true), KVQ_P(5, true)};
 
 }  // namespace kvq

@@ -36,6 +36,11 @@
 // bf16 tail tokens run the same steps on bf16 matrix products, with the
 // float32 query and weights split into high and low bf16 parts, and share
 // the online-softmax state of the quantized tokens.
+// Scale-and-min blocks (x = u * s + m, levels u >= 0): Q.K takes the levels
+// without an offset and adds m * sum(q) of the block, from per-block query
+// sums made once; P.V takes the levels and each lane keeps sum(p * m) per
+// (head, block) beside the accumulators, rescaled with them, added to the
+// output elements of that block at the end.
 #pragma once
 
 #include "common.hpp"
@@ -92,26 +97,53 @@ __device__ inline float half_of(uint32_t w, int hi) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(hi ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-// Cache bytes of one 32-token step held in registers.
-template <int D, int KB, int VB>
+// Cache bytes of one 32-token step held in registers.  KM / VM: K / V use
+// scale-and-min blocks, whose scale planes hold an (s, m) fp16 pair per block.
+template <int D, int KB, int VB, bool KM, bool VM>
 struct StepRegs {
   static constexpr int NB = D / kBlock;
   static constexpr int NN = D / 16;
   static constexpr int NSW = (NB + 1) / 2;   // 32-bit words of fp16 scales per token
+  static constexpr int KSW = KM ? NB : NSW;  // ... of K scales (pairs: one word a block)
+  static constexpr int VSW = VM ? NB : NSW;
   u32x2 k8[KB == 8 ? 2 * NB : 1];            // [m][blk] 8 code bytes
   uint32_t k4[KB == 8 ? 1 : 2 * NB];         // [m][blk] 8 code nibbles
   uint32_t kh[KB == 5 || KB == 6 ? 2 * NB : 1];   // [m][blk] 5/6-bit high-bit word
-  uint32_t ks[2][NSW], vs[2][NSW];           // [m] fp16 scales of this lane's token
+  uint32_t ks[2][KSW], vs[2][VSW];           // [m] fp16 scales (pairs) of this lane's token
   u32x4 v[VB == 8 ? NN / 2 : NN / 4];        // V items (4 or 8 bytes each)
   uint32_t vh[VB == 5 ? NN / 4 : VB == 6 ? NN / 2 : 1];   // 5-bit bytes / 6-bit fields
+
+  // scale of block j of token-row half m, and the minimum of a pair block
+  __device__ float k_scale(int m, int j) const { return KM ? half_of(ks[m][j], 0) : half_of(ks[m][j / 2], j % 2); }
+  __device__ float v_scale(int m, int j) const { return VM ? half_of(vs[m][j], 0) : half_of(vs[m][j / 2], j % 2); }
+  __device__ float k_min(int m, int j) const { return half_of(ks[m][j], 1); }
+  __device__ float v_min(int m, int j) const { return half_of(vs[m][j], 1); }
 };
+
+// Load NW consecutive 32-bit words (NW = 1, 2, 4 or 8) with the widest loads.
+template <int NW>
+__device__ inline void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
+  if constexpr (NW == 1) {
+    w[0] = p[0];
+  } else if constexpr (NW == 2) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(p)[q];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[4 * q + k] = x[k];
+    }
+  }
+}
 
 // B operand of Q.K for 16 tokens and one block: 8 int8 codes of this lane's
 // token in the k-slot order of the query bytes (4/5/6-bit: elements
 // 0,2,4,6,1,3,5,7 of the lane's group of 8, widened to bytes; the high bits
 // come from one rotate of the block's high word).
-template <int D, int KB, int VB>
-__device__ inline long k_operand(const StepRegs<D, KB, VB>& R, int i, uint32_t rot_lo, uint32_t rot_hi) {
+template <int D, int KB, int VB, bool KM, bool VM>
+__device__ inline long k_operand(const StepRegs<D, KB, VB, KM, VM>& R, int i, uint32_t rot_lo, uint32_t rot_hi) {
   if constexpr (KB == 8) {
     return __builtin_bit_cast(long, R.k8[i]);
   } else {
@@ -131,9 +163,10 @@ __device__ inline long k_operand(const StepRegs<D, KB, VB>& R, int i, uint32_t r
 }
 
 // B operand of P.V for output elements 16*nb..+15: this lane's element for
-// the 8 tokens of its k-slots, as exact fp16 codes.
-template <int D, int KB, int VB>
-__device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t magic) {
+// the 8 tokens of its k-slots, as exact fp16 codes (levels u for
+// scale-and-min blocks).
+template <int D, int KB, int VB, bool KM, bool VM>
+__device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, uint32_t magic) {
   const h2_t one16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   if constexpr (VB == 8) {
     const u32x4 q = R.v[nb / 2];
@@ -178,6 +211,10 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t 
       b_lo = (_Float16)-1032.0f;
       b_hi = (_Float16)-72.0f;
     }
+    if constexpr (VM) {   // levels u, no offset
+      b_lo = (_Float16)-1024.0f;
+      b_hi = (_Float16)-64.0f;
+    }
     const h2_t bl = {b_lo, b_lo}, bh = {b_hi, b_hi};
     const h2_t d0 = as_h2(w0) + bl;
     const h2_t d1 = __builtin_elementwise_fma(as_h2(w1), one16, bh);   // exact
@@ -195,7 +232,7 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB>& R, int nb, uint32_t 
 // n - n_q + i and sees positions up to there.  All waves of a workgroup walk
 // the same tiles, so each cache byte comes from HBM once per workgroup (the
 // other waves find it in L1 / L2).
-template <int D, int KB, int VB, int G, bool PF>
+template <int D, int KB, int VB, int G, bool PF, bool KM, bool VM>
 __global__ __launch_bounds__(64 * split_group_waves(D))
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D), split_waves_per_simd(D))))
 void decode_split_kernel(DecodeArgs a) {
@@ -208,7 +245,7 @@ void decode_split_kernel(DecodeArgs a) {
   // a few spilled (4-bit K, or 4-bit V with 5- or 8-bit K; decode only, a
   // prefill wave holds more state)
   constexpr int kAhead =
-      split_waves_per_simd(D) == 1 && !PF && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
+      split_waves_per_simd(D) == 1 && !PF && !KM && !VM && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
   constexpr int NSW = (NB + 1) / 2;
@@ -220,7 +257,7 @@ void decode_split_kernel(DecodeArgs a) {
   constexpr int WROW = 48;
   constexpr int LOROW = 8 * NB;
   constexpr int ZROW = 8 * NB + 8;
-  using Regs = StepRegs<D, KB, VB>;
+  using Regs = StepRegs<D, KB, VB, KM, VM>;
 
   __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9) * WROW];
   __shared__ __align__(16) float alds_all[kGroupWaves][16];
@@ -288,6 +325,10 @@ void decode_split_kernel(DecodeArgs a) {
   f4_t acc[NN];
 #pragma unroll
   for (int i = 0; i < NN; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+  // V minima: this lane's share of sum(p * m) of heads hA, hB per V block
+  float mvA[VM ? NB : 1], mvB[VM ? NB : 1];
+#pragma unroll
+  for (int j = 0; j < (VM ? NB : 1); ++j) mvA[j] = mvB[j] = 0.f;
 
   // Query of this lane's A row in registers: row col < 2G is the wave's row
   // col/2; the lane holds elements 32j + 8r + i (j < NB, i < 8), rotated in
@@ -397,6 +438,13 @@ void decode_split_kernel(DecodeArgs a) {
       const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]);
 #pragma unroll
       for (int i = 0; i < NN; ++i) acc[i] *= al;
+      if constexpr (VM) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          mvA[j] *= aA;
+          mvB[j] *= aB;
+        }
+      }
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -495,10 +543,12 @@ void decode_split_kernel(DecodeArgs a) {
 
   // ------------------------------------------------ quantized positions
   if (wq0 < wq1) {
+    constexpr int KSE = KM ? 2 * NB : NB;   // 16-bit scale entries per token
+    constexpr int VSE = VM ? 2 * NB : NB;
     const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
-    const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * NB;
+    const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * KSE;
     const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
-    const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * NB;
+    const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * VSE;
     // A operand of Q.K: the rotated query in 16-bit fixed point (step
     // amax / 32639 per head), high bytes in even rows, low bytes in odd rows;
     // 4/5-bit codes widen to bytes in the order 0,2,4,6,1,3,5,7 of each group
@@ -510,11 +560,14 @@ void decode_split_kernel(DecodeArgs a) {
     // sums land in the same lanes), with its own offset correction.  Rows
     // whose output nearly cancels need those bits on heavy-tailed data.
     constexpr bool kQX = PF;
+    constexpr bool kOffset = KB != 8 && !KM;   // offset-binary codes
     long qop[NB];
     long qres[kQX ? NB : 1];
     float ckA, ckB;
-    i4_t cq[KB == 8 ? 1 : NB];
-    i4_t cq2[kQX && KB != 8 ? NB : 1];
+    i4_t cq[kOffset ? NB : 1];
+    i4_t cq2[kQX && kOffset ? NB : 1];
+    // K minima: sum of the fixed-point query over each block, heads hA, hB
+    float bsA[KM ? NB : 1], bsB[KM ? NB : 1];
     // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
     // 8i + 2r (even elements) and 8i + 2r + 1 (odd) of the block's word;
     // 6-bit K: bits 4-5 sit at 8i + 4(r%2) (even) and 8i + 4(r%2) + 2 (odd)
@@ -556,22 +609,8 @@ void decode_split_kernel(DecodeArgs a) {
           }
         }
         const size_t tok = (size_t)s0 + 16 * m + col;
-        const uint32_t* ksp = reinterpret_cast<const uint32_t*>(ksc + tok * NB);
-        const uint32_t* vsp = reinterpret_cast<const uint32_t*>(vsc + tok * NB);
-        if constexpr (NSW == 1) {
-          R.ks[m][0] = ksp[0];
-          R.vs[m][0] = vsp[0];
-        } else if constexpr (NSW == 2) {
-          const u32x2 k2 = *reinterpret_cast<const u32x2*>(ksp);
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(vsp);
-          R.ks[m][0] = k2[0]; R.ks[m][1] = k2[1];
-          R.vs[m][0] = v2[0]; R.vs[m][1] = v2[1];
-        } else {
-          const u32x4 k4 = *reinterpret_cast<const u32x4*>(ksp);
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(vsp);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { R.ks[m][q] = k4[q]; R.vs[m][q] = v4[q]; }
-        }
+        load_words(reinterpret_cast<const uint32_t*>(ksc + tok * KSE), R.ks[m]);
+        load_words(reinterpret_cast<const uint32_t*>(vsc + tok * VSE), R.vs[m]);
       }
       const uint8_t* vt = vpl + (size_t)(s0 / kTile) * VTB;
       const uint8_t* vj = vt + (size_t)j2 * 64 * NN * (VB == 8 ? 8 : 4) + v_off;
@@ -596,21 +635,26 @@ void decode_split_kernel(DecodeArgs a) {
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const long kop = k_operand<D, KB, VB>(R, m * NB + j, rot_lo, rot_hi);
+          const long kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
           const i4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-              qop[j], kop, KB == 8 ? i4_t{0, 0, 0, 0} : cq[KB == 8 ? 0 : j], 0, 0, 0);
+              qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
           const int vA = (d[0] << 8) + d[1];
           const int vB = (d[2] << 8) + d[3];
-          const float ks = half_of(R.ks[m][j / 2], j % 2);
+          const float ks = R.k_scale(m, j);
           float fA = (float)vA, fB = (float)vB;
           if constexpr (kQX) {
             const i4_t e = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                qres[j], kop, KB == 8 ? i4_t{0, 0, 0, 0} : cq2[KB == 8 ? 0 : j], 0, 0, 0);
+                qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
             fA = __builtin_fmaf((float)e[1], 0.00390625f, fA);
             fB = __builtin_fmaf((float)e[3], 0.00390625f, fB);
           }
           sA[m] = __builtin_fmaf(ks, fA, sA[m]);
           sB[m] = __builtin_fmaf(ks, fB, sB[m]);
+          if constexpr (KM) {
+            const float km = R.k_min(m, j);
+            sA[m] = __builtin_fmaf(km, bsA[j], sA[m]);
+            sB[m] = __builtin_fmaf(km, bsB[j], sB[m]);
+          }
         }
       }
       float xA[2], xB[2], pA[2], pB[2];
@@ -632,12 +676,20 @@ void decode_split_kernel(DecodeArgs a) {
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const float vs = half_of(R.vs[m][j / 2], j % 2);
+          const float vs = R.v_scale(m, j);
           const int t = 16 * m + col;
           const _Float16 wA = (_Float16)(pA[m] * vs);
           const _Float16 wB = (_Float16)(pB[m] * vs);
           wl[(8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, wA);
           wl[(8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, wB);
+        }
+      }
+      if constexpr (VM) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const float v0 = R.v_min(0, j), v1 = R.v_min(1, j);
+          mvA[j] = __builtin_fmaf(pA[1], v1, __builtin_fmaf(pA[0], v0, mvA[j]));
+          mvB[j] = __builtin_fmaf(pB[1], v1, __builtin_fmaf(pB[0], v0, mvB[j]));
         }
       }
       wave_sync();
@@ -648,7 +700,7 @@ void decode_split_kernel(DecodeArgs a) {
         const h8_t wa = *reinterpret_cast<const h8_t*>(&wl[row * WROW + 8 * r]);
 #pragma unroll
         for (int i = 2 * j; i < 2 * j + 2; ++i)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, v_operand<D, KB, VB>(R, i, magic), acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, v_operand<D, KB, VB, KM, VM>(R, i, magic), acc[i], 0, 0, 0);
       }
     };
 
@@ -718,16 +770,28 @@ void decode_split_kernel(DecodeArgs a) {
         const bool row_here = col < 2 * G && row_ok(col / 2);
         qop[j] = row_here ? (long)w : 0;
         if constexpr (kQX) qres[j] = row_here && (col & 1) ? (long)wr : 0;
-        if constexpr (KB != 8) {
+        if constexpr (KM) {
+          bsum += __shfl_xor(bsum, 16);
+          bsum += __shfl_xor(bsum, 32);
+          float bf = (float)bsum;
+          if constexpr (kQX) {
+            rsum += __shfl_xor(rsum, 16);
+            rsum += __shfl_xor(rsum, 32);
+            bf = __builtin_fmaf((float)rsum, 0.00390625f, bf);
+          }
+          bsA[j] = okA ? __shfl(bf, 4 * r) : 0.f;
+          bsB[j] = okB ? __shfl(bf, 4 * r + 2) : 0.f;
+        }
+        if constexpr (kOffset) {
           bsum += __shfl_xor(bsum, 16);
           bsum += __shfl_xor(bsum, 32);
           const int corr = -(1 << (KB - 1)) * bsum;
-          cq[KB == 8 ? 0 : j] = i4_t{0, okA ? __shfl(corr, 4 * r) : 0, 0, okB ? __shfl(corr, 4 * r + 2) : 0};
+          cq[j] = i4_t{0, okA ? __shfl(corr, 4 * r) : 0, 0, okB ? __shfl(corr, 4 * r + 2) : 0};
           if constexpr (kQX) {
             rsum += __shfl_xor(rsum, 16);
             rsum += __shfl_xor(rsum, 32);
             const int corr2 = -(1 << (KB - 1)) * rsum;
-            cq2[KB == 8 ? 0 : j] = i4_t{0, okA ? __shfl(corr2, 4 * r) : 0, 0, okB ? __shfl(corr2, 4 * r + 2) : 0};
+            cq2[j] = i4_t{0, okA ? __shfl(corr2, 4 * r) : 0, 0, okB ? __shfl(corr2, 4 * r + 2) : 0};
           }
         }
       }
@@ -794,6 +858,28 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc[i][k] += __shfl_xor(acc[i][k], 32);
   }
+  if constexpr (VM) {
+    // head h's sum(p * m) of V block j (reduced over the row's 16 lanes) goes
+    // to output elements 32j..32j+31 through this wave's LDS rows
+    float* mvl = reinterpret_cast<float*>(wl);
+    wave_sync();
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float sa = row16_sum(mvA[j]), sb = row16_sum(mvB[j]);
+      if (col == 0) {
+        mvl[hA * NB + j] = sa;
+        mvl[hB * NB + j] = sb;
+      }
+    }
+    wave_sync();
+    if (r < 2) {
+#pragma unroll
+      for (int i = 0; i < NN; ++i) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] += mvl[(4 * r + k) * NB + i / 2];
+      }
+    }
+  }
   if (r < 2) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -817,10 +903,10 @@ void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int KB, int VB, int G, bool PF = false>
+template <int D, int KB, int VB, int G, bool PF = false, bool KM = false, bool VM = false>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF>), grid, dim3(64 * split_group_waves(D)), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM>), grid, dim3(64 * split_group_waves(D)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -10,35 +10,42 @@
 
 namespace kvq {
 
-// Tables defined by the instantiation units, indexed [v_bits 4/5/6/8][G-1].
-#define KVQ_DECLARE_TABLE(D, KB) extern DecodeLauncher kvq_decode_table_##D##_##KB[4][8]; \
-  extern DecodeLauncher kvq_prefill_table_##D##_##KB[4];
-#define KVQ_ALL_KB(X, D) X(D, 4) X(D, 5) X(D, 6) X(D, 8)
-KVQ_ALL_KB(KVQ_DECLARE_TABLE, 64) KVQ_ALL_KB(KVQ_DECLARE_TABLE, 128) KVQ_ALL_KB(KVQ_DECLARE_TABLE, 256)
+// Tables defined by the instantiation units, indexed [V format][G-1] with V
+// formats q4_0, q5_0, q6_0, q8_0, q4_1, q5_1; one pair of tables per (D, K
+// width, K block kind).
+#define KVQ_DECLARE_TABLE(D, KB, KM) extern DecodeLauncher kvq_decode_table_##D##_##KB##_##KM[6][8]; \
+  extern DecodeLauncher kvq_prefill_table_##D##_##KB##_##KM[6];
+#define KVQ_ALL_K(X, D) X(D, 4, 0) X(D, 5, 0) X(D, 6, 0) X(D, 8, 0) X(D, 4, 1) X(D, 5, 1)
+KVQ_ALL_K(KVQ_DECLARE_TABLE, 64) KVQ_ALL_K(KVQ_DECLARE_TABLE, 128) KVQ_ALL_K(KVQ_DECLARE_TABLE, 256)
 #undef KVQ_DECLARE_TABLE
 
 namespace {
-int v_index(int vb) { return vb == 4 ? 0 : vb == 5 ? 1 : vb == 6 ? 2 : vb == 8 ? 3 : -1; }
+int v_index(int vb, bool vm) {
+  if (vm) return vb == 4 ? 4 : vb == 5 ? 5 : -1;
+  return vb == 4 ? 0 : vb == 5 ? 1 : vb == 6 ? 2 : vb == 8 ? 3 : -1;
+}
 }  // namespace
 
-DecodeLauncher decode_launcher(int D, int kb, int vb, int gc) {
-  const int vi = v_index(vb);
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm) {
+  const int vi = v_index(vb, vm);
   if (vi < 0 || gc < 1 || gc > 8) return nullptr;
-#define KVQ_PICK(DD, KK) if (D == DD && kb == KK) return kvq_decode_table_##DD##_##KK[vi][gc - 1];
-  KVQ_ALL_KB(KVQ_PICK, 64) KVQ_ALL_KB(KVQ_PICK, 128) KVQ_ALL_KB(KVQ_PICK, 256)
+#define KVQ_PICK(DD, KK, MM) \
+  if (D == DD && kb == KK && (int)km == MM) return kvq_decode_table_##DD##_##KK##_##MM[vi][gc - 1];
+  KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 256)
 #undef KVQ_PICK
   return nullptr;
 }
 
-DecodeLauncher prefill_launcher(int D, int kb, int vb) {
-  const int vi = v_index(vb);
+DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm) {
+  const int vi = v_index(vb, vm);
   if (vi < 0) return nullptr;
-#define KVQ_PICK(DD, KK) if (D == DD && kb == KK) return kvq_prefill_table_##DD##_##KK[vi];
-  KVQ_ALL_KB(KVQ_PICK, 64) KVQ_ALL_KB(KVQ_PICK, 128) KVQ_ALL_KB(KVQ_PICK, 256)
+#define KVQ_PICK(DD, KK, MM) \
+  if (D == DD && kb == KK && (int)km == MM) return kvq_prefill_table_##DD##_##KK##_##MM[vi];
+  KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 256)
 #undef KVQ_PICK
   return nullptr;
 }
-#undef KVQ_ALL_KB
+#undef KVQ_ALL_K
 
 namespace {
 

@@ -1,5 +1,5 @@
-// Dequantize (read-back) kernel: code * fp16 scale for quantized positions,
-// the stored bf16 value for tail positions, optionally rotated back to the
+// Dequantize (read-back) kernel: code * fp16 scale for quantized positions
+// (level * scale + minimum for scale-and-min blocks), the stored bf16 value for tail positions, optionally rotated back to the
 // original space with the same float32 transform as the append (the
 // normalized Sylvester matrix is its own inverse; velog.io post "fix KV cache
 // quantization outliers", section "Hadamard rotation").
@@ -85,7 +85,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int e = 0; e < 32; ++e) x[e] = 0.f;
   if (active) {
     if (p < a.nq) {
-      const float s = (float)__builtin_bit_cast(_Float16, a.scales[(unit * a.cap + p) * (D / kBlock) + j]);
+      float s, mn = 0.f;
+      if (a.minf) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(a.scales)[(unit * a.cap + p) * (D / kBlock) + j];
+        s = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+        mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+      } else {
+        s = (float)__builtin_bit_cast(_Float16, a.scales[(unit * a.cap + p) * (D / kBlock) + j]);
+      }
       int c[32];
       if (a.which == 0) {
         const uint8_t* plane = a.codes + unit * (size_t)a.cap * padded_row_bytes(D, a.bits);
@@ -100,8 +107,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         else if (a.bits == 6) load_v_codes<D, 6>(plane, p, j, c);
         else load_v_codes<D, 8>(plane, p, j, c);
       }
+      if (a.minf) {
+        // level u = c + 2^(bits-1); u * s is exact, one rounding in the add
+        const int off = 1 << (a.bits - 1);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = (float)c[e] * s;
+        for (int e = 0; e < 32; ++e) x[e] = (float)(c[e] + off) * s + mn;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[e] = (float)c[e] * s;
+      }
     } else {
       const uint16_t* row = a.tail + (unit * a.T + p % a.T) * D + kBlock * j;
 #pragma unroll

@@ -13,9 +13,10 @@ namespace kvq {
 struct AppendArgs {
   const void* src[2];        // k_new, v_new: [B][n_new][Hkv][D]
   uint8_t* codes[2];         // tiled code planes
-  uint16_t* scales[2];       // [B][Hkv][cap][D/32] fp16 bits
+  uint16_t* scales[2];       // [B][Hkv][cap][D/32] fp16 bits ([..][D/32][2] (s, m) with minf)
   uint16_t* tail[2];         // [B][Hkv][T][D] bf16 bits (unused when T == 0)
   int32_t bits[2];
+  int32_t minf[2];           // 1: scale-and-min blocks (4/5-bit only)
   int32_t rotate[2];
   int32_t Hkv, n_new, T, cap, dtype;
   float cd;                  // fp32(1/sqrt(D))
@@ -33,6 +34,7 @@ struct DequantArgs {
   float* out;                // [t1-t0][Hkv][D]
   int32_t which;              // 0 = K (row layout), 1 = V (element-major tiles)
   int32_t bits, rotate, space, Hkv, T, cap, b, t0, t1, nq;
+  int32_t minf;              // scale-and-min blocks: (s, m) pairs, x = u * s + m
   float cd;
   int32_t has_signs;         // space 1 rotates back by diag(s) H
   uint32_t signs[8];
@@ -71,10 +73,11 @@ struct DecodeArgs {
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
-// Table lookup for (D, k_bits, v_bits, heads per chunk); nullptr if absent.
-DecodeLauncher decode_launcher(int D, int kb, int vb, int gc);
-// The prefill variant of the split kernel for (D, k_bits, v_bits).
-DecodeLauncher prefill_launcher(int D, int kb, int vb);
+// Table lookup for (D, k_bits, v_bits, heads per chunk, K / V scale-and-min
+// blocks); nullptr if absent.
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm);
+// The prefill variant of the split kernel for (D, k_bits, v_bits, km, vm).
+DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm);
 
 // Largest split count the host schedules (bounds the combine kernel's LDS).
 constexpr int kMaxSplitsDevice = 1024;

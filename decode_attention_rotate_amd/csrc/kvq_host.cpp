@@ -40,9 +40,12 @@ kvq_status check_cfg(const kvq_config* c) {
   if (!c) return KVQ_ERR_INVALID;
   if (c->batch < 1 || c->batch > KVQ_MAX_BATCH || c->n_kv_heads < 1 || c->max_ctx < 1 ||
       c->tail_len < 0 || (c->rotate_k != 0 && c->rotate_k != 1) ||
-      (c->rotate_v != 0 && c->rotate_v != 1))
+      (c->rotate_v != 0 && c->rotate_v != 1) || (c->k_min != 0 && c->k_min != 1) ||
+      (c->v_min != 0 && c->v_min != 1))
     return KVQ_ERR_INVALID;
   if (!dim_ok(c->head_dim) || !bits_ok(c->k_bits) || !bits_ok(c->v_bits)) return KVQ_ERR_UNSUPPORTED;
+  // scale-and-min blocks come in the 4- and 5-bit widths (q4_1, q5_1)
+  if ((c->k_min && c->k_bits > 5) || (c->v_min && c->v_bits > 5)) return KVQ_ERR_UNSUPPORTED;
   if (c->n_kv_heads > 65535 / 2) return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
@@ -186,6 +189,8 @@ kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads, int32_t head_di
   c.rotate_k = on;
   c.rotate_v = on;
   c.sign_seed = 0;
+  c.k_min = 0;
+  c.v_min = 0;
   return c;
 }
 
@@ -199,8 +204,8 @@ size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane) {
   switch (plane) {
     case KVQ_K_CODES: return units * cap * padded_row_bytes(c.head_dim, c.k_bits);
     case KVQ_V_CODES: return units * (cap / kTile) * v_tile_bytes(c.head_dim, c.v_bits);
-    case KVQ_K_SCALES:
-    case KVQ_V_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t);
+    case KVQ_K_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t) * (c.k_min ? 2 : 1);
+    case KVQ_V_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t) * (c.v_min ? 2 : 1);
     case KVQ_K_TAIL:
     case KVQ_V_TAIL: return units * (size_t)c.tail_len * c.head_dim * sizeof(uint16_t);
   }
@@ -242,6 +247,8 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* ca
   a.tail[1] = static_cast<uint16_t*>(cache->v_tail);
   a.bits[0] = c.k_bits;
   a.bits[1] = c.v_bits;
+  a.minf[0] = c.k_min;
+  a.minf[1] = c.v_min;
   a.rotate[0] = c.rotate_k;
   a.rotate[1] = c.rotate_v;
   a.Hkv = c.n_kv_heads;
@@ -278,7 +285,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   const Schedule sc = schedule(c, n_q_heads, max_len);
   const WsLayout wl = ws_layout(c, n_q_heads, sc.S);
   if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
-  const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc);
+  const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc, c.k_min != 0, c.v_min != 0);
   if (!fn) return KVQ_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -359,7 +366,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   if ((int64_t)c.n_kv_heads * ps.n_rb > 65535) return KVQ_ERR_INVALID;
   const WsLayout wl = ws_layout(c, n_q * n_q_heads, ps.S);
   if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
-  const DecodeLauncher fn = prefill_launcher(c.head_dim, c.k_bits, c.v_bits);
+  const DecodeLauncher fn = prefill_launcher(c.head_dim, c.k_bits, c.v_bits, c.k_min != 0, c.v_min != 0);
   if (!fn) return KVQ_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -434,6 +441,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t
   a.out = out;
   a.which = which;
   a.bits = which == 0 ? c.k_bits : c.v_bits;
+  a.minf = which == 0 ? c.k_min : c.v_min;
   a.rotate = which == 0 ? c.rotate_k : c.rotate_v;
   a.space = space;
   a.Hkv = c.n_kv_heads;

@@ -14,7 +14,9 @@
  *    plus 4-, 5-, 6- or 8-bit codes, i.e. 4.5 / 5.5 / 6.5 / 8.5 bits per
  *    value, the q4_0 / q5_0 / q6_0 / q8_0 cache sizes (28.1 / 34.4 / 40.6 /
  *    53.1 % of bf16) in the table "Qwen 3.6 27B Q5_K_S + 64k context KLD
- *    results" of aiwitness.kr post 1txlhxu.  K and V pick their widths independently
+ *    results" of aiwitness.kr post 1txlhxu.  4- and 5-bit blocks may instead
+ *    carry an fp16 scale and an fp16 minimum (q4_1 / q5_1; q5_1 is 37.5 % in
+ *    the same table).  K and V pick their widths independently
  *    (--cache-type-k / --cache-type-v in the velog.io post).
  *  - An optional bf16 precision tail keeps the newest tokens unquantized
  *    (aitrends.kr article 92204, glossary entry "Precision Tail").
@@ -62,7 +64,11 @@
  *             then one byte per item whose bit n(k) is bit 4 of u;
  *      6-bit  the 4-bit words, then one little-endian 16-bit field per item
  *             whose bits 2n(k), 2n(k)+1 are bits 4, 5 of u.
- *  - scale planes (k_scales, v_scales): [b][g][cap][head_dim/32] fp16.
+ *  - scale planes (k_scales, v_scales): [b][g][cap][head_dim/32] fp16, or
+ *    [b][g][cap][head_dim/32][2] fp16 (s, m) pairs for scale-and-min blocks.
+ *    Attention reads the entries of positions past seq_len up to the end of
+ *    their 64-token tile (weighting them by zero), so the scale planes must
+ *    hold finite values there: zero them once when the cache is allocated.
  *  - tail planes (k_tail, v_tail): [b][g][tail_len][head_dim] bf16; position
  *    p of the newest tail_len positions lives in slot p % tail_len.  NULL is
  *    allowed when tail_len == 0.
@@ -73,6 +79,15 @@
  *    a = max|x|;  s = fp16_rne(min(a / qmax, 65504));  r = 1 / float(s);
  *    code = clamp(rint(x * r), -qmax, qmax)   (all codes 0 if s == 0)
  * with qmax = 7 / 15 / 31 / 127, IEEE float32 arithmetic, no fused operations.
+ *
+ * Scale-and-min blocks (k_min / v_min; 4 or 5 bits, the q4_1 / q5_1 formats,
+ * whose size the aiwitness.kr table prints: two fp16 values per 32 elements):
+ *    lo = min x, hi = max x;  s = fp16_rne(min((hi - lo) / (2^bits - 1), 65504));
+ *    m = fp16_rne(lo clamped to +-65504);  r = 1 / float(s);
+ *    u = clamp(rint((x - m) * r), 0, 2^bits - 1)   (all u 0 if s == 0)
+ *    x_hat = u * s + m
+ * The code planes store u where the absmax formats store code + 2^(bits-1),
+ * so their layouts are the same.
  * The rotation is y = fp32(1/sqrt(d)) * FWHT(x) with the float32 butterfly
  * stages applied in the order h = 1, 2, 4, ..., d/2.
  */
@@ -122,6 +137,11 @@ typedef struct kvq_config {
                         * the counter sign_seed * 2^32 + e is set (a random-sign
                         * variant, which the velog.io post names in section
                         * "application and background") */
+  int32_t k_min;       /* 1: K uses scale-and-min blocks (q4_1 / q5_1; k_bits
+                        * 4 or 5), 0: absmax blocks.  Byte cost per the
+                        * aiwitness.kr table's q5_1 rows; see "Scale-and-min
+                        * blocks" above */
+  int32_t v_min;       /* the same for V */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -135,7 +155,7 @@ typedef struct kvq_cache {
 
 /* Defaults: 4-bit K and V, no tail, rotation on iff head_dim >= 64 and
  * head_dim % 64 == 0 (velog.io post, section "application and background"),
- * sign_seed 0. */
+ * sign_seed 0, absmax blocks (k_min = v_min = 0). */
 kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads,
                               int32_t head_dim, int32_t max_ctx);
 

@@ -39,7 +39,8 @@ def gpu_planes(cache, cfg):
     for p in ("k", "v"):
         codes = cache[p + "_codes"].cpu().numpy()
         out[p + "_codes"] = codes.reshape(B, H, -1)
-        out[p + "_scales"] = cache[p + "_scales"].cpu().numpy().view(np.uint16).reshape(B, H, cap, d // 32)
+        # one fp16 per block, or an (s, m) pair for scale-and-min blocks
+        out[p + "_scales"] = cache[p + "_scales"].cpu().numpy().view(np.uint16).reshape(B, H, cap, -1)
         if T > 0:
             out[p + "_tail"] = cache[p + "_tail"].cpu().numpy().view(np.uint16).reshape(B, H, T, d)
         else:
@@ -50,10 +51,13 @@ def gpu_planes(cache, cfg):
 class Pair:
     """A device cache and the oracle cache fed the same appends."""
 
-    def __init__(self, B, H, d, kb, vb, T, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0):
-        self.cfg = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T, rotate_k, rotate_v, sign_seed)
+    def __init__(self, B, H, d, kb, vb, T, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0,
+                 k_min=False, v_min=False):
+        self.cfg = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T, rotate_k, rotate_v, sign_seed,
+                                  k_min, v_min)
         self.cache = kvq.KVCache(self.cfg, DEV)
-        self.orc = OracleCache(B, H, d, kb, vb, T, max_ctx, rotate_k, rotate_v, sign_seed)
+        self.orc = OracleCache(B, H, d, kb, vb, T, max_ctx, rotate_k, rotate_v, sign_seed,
+                               k_min, v_min)
         self.lens = np.zeros(B, dtype=np.int64)
 
     def append(self, k, v, dtype, lens=None):
@@ -92,7 +96,8 @@ def attention_errors(got, planes, qv, lens, cfg, sm_scale=None, heads=None):
     ref = decode_reference(planes, qv, lens, cfg.n_kv_heads, cfg.head_dim, cfg.k_bits,
                            cfg.v_bits, cfg.tail_len, sm_scale=sm_scale,
                            rotate_k=bool(cfg.rotate_k), rotate_v=bool(cfg.rotate_v),
-                           heads=heads, sign_seed=cfg.sign_seed)
+                           heads=heads, sign_seed=cfg.sign_seed, k_min=bool(cfg.k_min),
+                           v_min=bool(cfg.v_min))
     errs = {}
     B, Hq, _ = qv.shape
     for b in range(B):

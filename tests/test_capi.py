@@ -59,10 +59,17 @@ def test_config_check():
     assert kvq.kvq_config_check(c) == 0
     for field, val, want in (("head_dim", 192, -2), ("head_dim", 32, -2), ("k_bits", 7, -2),
                              ("v_bits", 3, -2), ("batch", 0, -1), ("batch", 257, -1),
-                             ("tail_len", -1, -1), ("max_ctx", 0, -1), ("rotate_k", 2, -1)):
+                             ("tail_len", -1, -1), ("max_ctx", 0, -1), ("rotate_k", 2, -1),
+                             ("k_min", 2, -1), ("v_min", -1, -1)):
         bad = kvq.kvq_config_default(2, 4, 128, 1000)
         setattr(bad, field, val)
         assert kvq.kvq_config_check(bad) == want, field
+    # scale-and-min blocks exist at 4 and 5 bits only (q4_1, q5_1)
+    for kb, vb, km, vm, want in ((4, 5, 1, 1, 0), (5, 8, 1, 0, 0), (8, 4, 0, 1, 0),
+                                 (6, 4, 1, 0, -2), (4, 8, 0, 1, -2)):
+        m = kvq.kvq_config_default(2, 4, 128, 1000)
+        m.k_bits, m.v_bits, m.k_min, m.v_min = kb, vb, km, vm
+        assert kvq.kvq_config_check(m) == want, (kb, vb, km, vm)
 
 
 @pytest.mark.parametrize("d", (64, 128, 256))
@@ -182,10 +189,25 @@ def test_prefill_validation():
     assert _prefill(c, 8, 4, _lens(5, 5), out=0) == _capi.KVQ_ERR_INVALID
 
 
+@pytest.mark.parametrize("d", (64, 128, 256))
+def test_plane_bytes_scale_and_min(d):
+    # an (s, m) fp16 pair per block: q5_1 costs 32*5/8 + 4 = 24 bytes per 32
+    # elements, 37.5 % of bf16 (the aiwitness.kr table's q5_1 row)
+    B, H, cap = 2, 3, 1024
+    c = kvq.kvq_config(B, H, d, 1000, 5, 4, 0, k_min=True, v_min=False)
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_K_SCALES) == B * H * cap * (d // 32) * 4
+    assert kvq.kvq_plane_bytes(c, kvq.KVQ_V_SCALES) == B * H * cap * (d // 32) * 2
+    c = kvq.kvq_config(B, H, d, 1000, 5, 5, 0, k_min=True, v_min=True)
+    per_tok = (kvq.kvq_plane_bytes(c, kvq.KVQ_V_CODES) + kvq.kvq_plane_bytes(c, kvq.KVQ_V_SCALES)) / (B * H * cap)
+    assert per_tok / (2 * d) == 0.375
+
+
 def test_config_layout_and_sign_seed():
-    # ten 32-bit fields; sign_seed last, 0 by default (plain Sylvester matrix)
-    assert ctypes.sizeof(_capi.KvqConfig) == 40
+    # twelve 32-bit fields: sign_seed, then k_min, v_min last; all 0 by
+    # default (plain Sylvester matrix, absmax blocks)
+    assert ctypes.sizeof(_capi.KvqConfig) == 48
+    assert _capi.KvqConfig.sign_seed.offset == 36 and _capi.KvqConfig.v_min.offset == 44
     c = kvq.kvq_config_default(1, 1, 128, 64)
-    assert c.sign_seed == 0
+    assert c.sign_seed == 0 and c.k_min == 0 and c.v_min == 0
     c2 = kvq.kvq_config(1, 1, 128, 64, sign_seed=0xFFFFFFFF)
     assert c2.sign_seed == 0xFFFFFFFF

@@ -21,7 +21,10 @@ value distributions of the cases below):
 
 Outlier channels are one fixed (head, channel) set per workload, the same for
 every token and sequence, drawn independently for K and V.  q carries no
-outliers.  Random streams are keyed by (workload, role, chunk) so any token
+outliers.  An optional field bias = b adds a fixed per-(head, channel) offset
+b * N(0, 1) to every K and V token (stream role 6; absent in the workloads
+above), which makes blocks asymmetric about zero, the case scale-and-min
+blocks are for.  Random streams are keyed by (workload, role, chunk) so any token
 range can be regenerated on its own: role 0 = outlier choice, 1 = K, 2 = V,
 3 = Q, 4 = new decode tokens.
 """
@@ -77,6 +80,17 @@ def outlier_scale(w, role):
     return s
 
 
+def channel_bias(w, role):
+    """[Hkv][d] float32 per-channel offsets of K (role 1) or V (role 2):
+    zero unless the workload sets bias."""
+    Hkv, d = w["Hkv"], w["d"]
+    b = w.get("bias", 0.0)
+    if not b:
+        return np.zeros((Hkv, d), dtype=np.float32)
+    rng = np.random.default_rng((w["idx"], 6, role))
+    return (rng.standard_normal((Hkv, d)) * b).astype(np.float32)
+
+
 def to_bf16_bits(x):
     """float32 -> bf16 bit patterns, round to nearest even (input preparation)."""
     b = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
@@ -109,6 +123,8 @@ def kv_numpy(w, role, t0, t1, batch=None):
             lo, hi = max(t0, c * CHUNK_TOKENS), min(t1, (c + 1) * CHUNK_TOKENS)
             parts.append(x[lo - c * CHUNK_TOKENS: hi - c * CHUNK_TOKENS])
         x = np.concatenate(parts, axis=0) * scale[None]
+        if w.get("bias"):
+            x = x + channel_bias(w, role)[None]
         out.append(x)
     x = np.stack(out).astype(np.float32)
     return to_bf16_bits(x) if w["dtype"] == "bf16" else x
@@ -133,6 +149,8 @@ def new_tokens_numpy(w, role, step, n_new=1):
     rng = np.random.default_rng((w["idx"], 4, role, step))
     x = _draw(rng, w["dist"], (w["B"], n_new, w["Hkv"], w["d"]))
     x = x * outlier_scale(w, role)[None, None]
+    if w.get("bias"):
+        x = x + channel_bias(w, role)[None, None]
     return to_bf16_bits(x) if w["dtype"] == "bf16" else x.astype(np.float32)
 
 
@@ -166,6 +184,8 @@ def kv_torch(w, role, t0, t1, device, torch):
         lo, hi = max(t0, c * CHUNK_TOKENS), min(t1, (c + 1) * CHUNK_TOKENS)
         parts.append(x[:, lo - c * CHUNK_TOKENS: hi - c * CHUNK_TOKENS])
     x = torch.cat(parts, dim=1) * scale
+    if w.get("bias"):
+        x = x + torch.from_numpy(channel_bias(w, role)).to(device)
     dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     return x.to(dt).contiguous()
 
@@ -194,6 +214,8 @@ def new_tokens_torch(w, role, step, device, torch, n_new=1):
     gen.manual_seed(((w["idx"] * 8 + 4) << 32) + (role << 24) + step)
     x = _torch_draw(torch, gen, w["dist"], (w["B"], n_new, w["Hkv"], w["d"]), device)
     x = x * torch.from_numpy(outlier_scale(w, role)).to(device)
+    if w.get("bias"):
+        x = x + torch.from_numpy(channel_bias(w, role)).to(device)
     dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     return x.to(dt).contiguous()
 
@@ -214,5 +236,20 @@ def adversarial_numpy(seed, shape, dtype="bf16"):
     flat[kinds == 4] *= np.float32(3e5)
     ints = rng.integers(-15, 16, size=flat.shape).astype(np.float32) * np.float32(0.5)
     flat[kinds == 5] = ints[kinds == 5]
+    x = flat.reshape(shape)
+    return to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def shifted_numpy(seed, shape, dtype="bf16"):
+    """adversarial_numpy rows moved off zero: each row gets an offset of up to
+    four times its largest magnitude, and one row in eight is constant (a
+    block whose range is zero).  shape = (B, n, H, d)."""
+    rng = np.random.default_rng((97, seed))
+    x = adversarial_numpy(seed, shape, "f32").copy()
+    flat = x.reshape(-1, shape[-1])
+    spread = np.abs(flat).max(axis=1, keepdims=True)
+    flat += rng.uniform(-4, 4, (flat.shape[0], 1)).astype(np.float32) * spread
+    const = rng.integers(0, 8, size=flat.shape[0]) == 7
+    flat[const] = flat[const, :1]
     x = flat.reshape(shape)
     return to_bf16_bits(x) if dtype == "bf16" else x
