@@ -69,22 +69,27 @@ def log(*a):
 
 def cache_bytes_per_step(w, lens):
     """Algorithmic bytes one attention call reads: packed codes + fp16 scales
-    of quantized tokens, bf16 K and V rows of tail tokens."""
+    (scale-and-min blocks: fp16 pairs) of quantized tokens, bf16 K and V rows
+    of tail tokens."""
     d, T = w["d"], w["tail"]
     nb = d // 32
+    scale_bytes = 2 * nb * ((2 if w.get("km") else 1) + (2 if w.get("vm") else 1))
     tot = 0
     for n in lens:
         nt = min(n, T) if T > 0 else 0
         nq = n - nt
-        q_bytes = nq * (d * w["k_bits"] // 8 + d * w["v_bits"] // 8 + 2 * 2 * nb)
+        q_bytes = nq * (d * w["k_bits"] // 8 + d * w["v_bits"] // 8 + scale_bytes)
         tot += (q_bytes + nt * 2 * d * 2) * w["Hkv"]
     return tot
 
 
 def describe(w):
-    return ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %d, K%d V%d, "
+    # K8 V4: absmax blocks of those widths; "_1" marks scale-and-min blocks
+    fk = "%d%s" % (w["k_bits"], "_1" if w.get("km") else "")
+    fv = "%d%s" % (w["v_bits"], "_1" if w.get("vm") else "")
+    return ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %d, K%s V%s, "
             "bf16 tail %d, %s inputs" % (w["name"], w["B"], w["Hq"], w["Hkv"], w["d"], w["n"],
-                                        w["k_bits"], w["v_bits"], w["tail"], w["dist"]))
+                                        fk, fv, w["tail"], w["dist"]))
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -97,12 +102,13 @@ def _oracle_unit(args):
     from oracle.blockquant import bf16_bits_to_f32
     n, d = k.shape[0], w["d"]
     G = q.shape[0]
-    c = OracleCache(1, 1, d, w["k_bits"], w["v_bits"], w["tail"], n)
+    km, vm = bool(w.get("km")), bool(w.get("vm"))
+    c = OracleCache(1, 1, d, w["k_bits"], w["v_bits"], w["tail"], n, k_min=km, v_min=vm)
     c.append(k[None, :, None], v[None, :, None], [0], dtype="bf16")
     planes = c.physical()
     t0 = time.perf_counter()
     decode_reference(planes, bf16_bits_to_f32(q)[None], [n], 1, d, w["k_bits"], w["v_bits"],
-                     w["tail"])
+                     w["tail"], k_min=km, v_min=vm)
     return time.perf_counter() - t0, G
 
 
@@ -150,6 +156,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--k-bits", type=int, default=0, help="override the workload's K code width")
     ap.add_argument("--v-bits", type=int, default=0, help="override the workload's V code width")
+    ap.add_argument("--k-min", action="store_true",
+                    help="K in scale-and-min blocks (q4_1 / q5_1; with a 4- or 5-bit K width)")
+    ap.add_argument("--v-min", action="store_true", help="V in scale-and-min blocks")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the chunked-prefill measurement (for profiling) and exit")
     ap.add_argument("--append-only", action="store_true",
@@ -190,6 +199,7 @@ def main():
         w["k_bits"] = args.k_bits
     if args.v_bits:
         w["v_bits"] = args.v_bits
+    w["km"], w["vm"] = args.k_min, args.v_min
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     log("workload", describe(w))
 
@@ -280,7 +290,8 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep):
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     total_steps = warmup + 2 * steps
     cfg = kvq.kvq_config(B, Hkv, d, n + total_steps + 64, w["k_bits"], w["v_bits"], w["tail"],
-                         rotate_k=rotate, rotate_v=rotate)
+                         rotate_k=rotate, rotate_v=rotate, k_min=w.get("km", False),
+                         v_min=w.get("vm", False))
     cache = kvq.KVCache(cfg, dev)
     if keep is not None:
         keep["k"] = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev)
