@@ -38,7 +38,8 @@ example or test vector (parity unpinned against any external implementation).
 """
 
 from .rotation import (hadamard, rot_scale_f32, fwht_f32, rotate_f32, unrotate_f32,
-                       hadamard_signs, rotation_matrix, splitmix64)
+                       hadamard_signs, rotation_matrix, splitmix64, rotation_block,
+                       block_hadamard)
 from .blockquant import (
     QMAX, BLOCK, bf16_round, bf16_bits_to_f32, f32_to_bf16_bits,
     quantize_blocks, dequantize_blocks, quantize_blocks_min, dequantize_blocks_min,
@@ -51,7 +52,7 @@ from .attention import (softmax_attention, decode_reference, dequantize_unit,
 
 __all__ = [
     "hadamard", "rot_scale_f32", "fwht_f32", "rotate_f32", "unrotate_f32",
-    "hadamard_signs", "rotation_matrix", "splitmix64",
+    "hadamard_signs", "rotation_matrix", "splitmix64", "rotation_block", "block_hadamard",
     "QMAX", "BLOCK", "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "quantize_blocks", "dequantize_blocks", "quantize_blocks_min", "dequantize_blocks_min",
     "pack_rows", "unpack_rows",

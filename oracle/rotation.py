@@ -23,6 +23,11 @@ Readings (the page does not fix these):
       is the plain matrix of R1.  A vector is rotated as H (s * x) and rotated
       back as s * (H y); sign flips are exact, so the float32 transform and
       its stage order are unchanged.
+* R23 head_dim a multiple of 64 but not a power of two (the rule of section
+      "application and background" admits it; no Sylvester matrix of that
+      size exists): the rotation is block-diagonal, one normalized H_64 per
+      consecutive group of 64 elements, each group transformed as in R3/R4
+      with stages h = 1..32 and the factor fp32(1/8).
 """
 
 import numpy as np
@@ -68,9 +73,27 @@ def hadamard_signs(d, seed):
     return np.array([-1.0 if splitmix64((seed << 32) | e) >> 63 else 1.0 for e in range(d)])
 
 
+def rotation_block(d):
+    """Size of the Hadamard blocks the rotation of a d-vector uses: d itself
+    for a power of two, 64 for other multiples of 64 (reading R23)."""
+    if d >= 1 and d & (d - 1) == 0:
+        return d
+    if d % 64 == 0:
+        return 64
+    raise ValueError("the rotation needs a power of two or a multiple of 64")
+
+
+def block_hadamard(d):
+    """Dense float64 rotation matrix of reading R23: block-diagonal with
+    normalized H_b blocks, b = rotation_block(d) (H_d itself when b = d)."""
+    b = rotation_block(d)
+    return np.kron(np.eye(d // b), hadamard(b))
+
+
 def rotation_matrix(d, seed=0):
-    """Dense R = H diag(s) in float64 (H alone for seed 0)."""
-    H = hadamard(d)
+    """Dense R = H diag(s) in float64 (H alone for seed 0; H block-diagonal
+    for a d that is not a power of two, reading R23)."""
+    H = block_hadamard(d)
     s = hadamard_signs(d, seed)
     return H if s is None else H * s[None, :]
 
@@ -80,21 +103,24 @@ def rot_scale_f32(d):
     return np.float32(1.0 / np.sqrt(np.float64(d)))
 
 
-def fwht_f32(x):
+def fwht_f32(x, block=None):
     """Unnormalized fast Walsh-Hadamard transform along the last axis, float32.
 
     Stage order h = 1, 2, ..., d/2 (reading R4); in each stage every index i
     with (i & h) == 0 pairs with i + h and becomes (x[i] + x[i+h],
     x[i] - x[i+h]), each rounded to float32.  No fused operations.
-    The result equals sqrt(d) * H @ x up to float32 rounding.
+    The result equals sqrt(d) * H @ x up to float32 rounding.  With block,
+    each consecutive group of block elements is transformed on its own
+    (stages h < block; reading R23).
     """
     x = np.array(x, dtype=np.float32, copy=True)
     d = x.shape[-1]
-    if d < 1 or d & (d - 1):
+    n = d if block is None else block
+    if n < 1 or n & (n - 1) or d % n:
         raise ValueError("FWHT needs a power-of-two length")
     lead = x.shape[:-1]
     h = 1
-    while h < d:
+    while h < n:
         v = x.reshape(lead + (d // (2 * h), 2, h))
         a = v[..., 0, :].copy()
         b = v[..., 1, :].copy()
@@ -118,7 +144,8 @@ def rotate_f32(x, enabled=True, signs=None):
         return x.copy()
     if signs is not None:
         x = x * np.asarray(signs, dtype=np.float32)
-    return fwht_f32(x) * rot_scale_f32(x.shape[-1])
+    b = rotation_block(x.shape[-1])
+    return fwht_f32(x, b) * rot_scale_f32(b)
 
 
 def unrotate_f32(y, enabled=True, signs=None):
@@ -127,7 +154,8 @@ def unrotate_f32(y, enabled=True, signs=None):
     y = np.asarray(y, dtype=np.float32)
     if not enabled:
         return y.copy()
-    out = fwht_f32(y) * rot_scale_f32(y.shape[-1])
+    b = rotation_block(y.shape[-1])
+    out = fwht_f32(y, b) * rot_scale_f32(b)
     if signs is not None:
         out = out * np.asarray(signs, dtype=np.float32)
     return out
