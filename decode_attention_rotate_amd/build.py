@@ -35,7 +35,7 @@ def units():
     for name in ("append.hip", "dequant.hip", "decode_main.hip"):
         out.append((os.path.join(CSRC, name), name.replace(".hip", ".o"), DEVICE))
     # K formats: (bits, scale-and-min) for q4_0 q5_0 q6_0 q8_0 q4_1 q5_1
-    for d in (256, 128, 64):          # the slowest units first
+    for d in (256, 192, 128, 64):     # the slowest units first
         for kb, km in ((4, 0), (5, 0), (6, 0), (8, 0), (4, 1), (5, 1)):
             out.append((os.path.join(CSRC, "decode_inst.hip"), "decode_d%d_k%d_m%d.o" % (d, kb, km),
                         DEVICE + ["-DKVQ_INST_D=%d" % d, "-DKVQ_INST_KB=%d" % kb,

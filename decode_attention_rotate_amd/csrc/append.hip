@@ -227,7 +227,7 @@ __device__ inline AppendRange append_range(const AppendArgs& a, int b) {
 template <int D>
 __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, uint8_t* vlds) {
   constexpr int LPR = D / kBlock;
-  constexpr int RPB = 256 / LPR;   // positions per block, a multiple of 8
+  constexpr int RPB = rows_per_block(D);   // positions per block, a multiple of 8
   constexpr int NGRP = RPB / 8;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,7 +239,7 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
   if (blk0 >= q1) return;                       // uniform over the block
   const int rho = tid / LPR;
   const int p = blk0 + rho;
-  const bool active = p >= q0 && p < q1;
+  const bool active = rho < RPB && p >= q0 && p < q1;
   const bool from_ring = active && p < len;     // leaving the tail (T > 0)
   const int Hkv = a.Hkv;
   const size_t unit = (size_t)b * Hkv + g;
@@ -310,7 +310,7 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
 template <int D>
 __device__ void tail_part(const AppendArgs& a, int bx, int g, int b, int pl) {
   constexpr int LPR = D / kBlock;
-  constexpr int RPB = 256 / LPR;
+  constexpr int RPB = rows_per_block(D);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = tid % LPR;
@@ -318,7 +318,7 @@ __device__ void tail_part(const AppendArgs& a, int bx, int g, int b, int pl) {
   const int len = rg.len, n1 = rg.n1;
   const int T = a.T;
   const int p = rg.t0 + bx * RPB + tid / LPR;
-  const bool active = p < n1;
+  const bool active = tid / LPR < RPB && p < n1;
   const int Hkv = a.Hkv;
 
   float x[32];
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   constexpr int LPR = D / kBlock;
   const int lane = threadIdx.x;
   const int g = blockIdx.x, b = blockIdx.y, pl = blockIdx.z;
-  const int j = lane % LPR;
+  const int j = (lane & 31) % LPR;   // block of lane l and of lane 32 + l
   const AppendRange rg = append_range(a, b);
   const int len = rg.len, T = a.T;
   const bool new_lane = lane < LPR;
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
 
 template <int D>
 hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
-  constexpr int RPB = 256 / (D / kBlock);
+  constexpr int RPB = rows_per_block(D);
   if (a.n_new == 1) {
     const dim3 grid(a.Hkv, B, 2), block(64);
     switch (a.bits[1]) {
@@ -549,6 +549,7 @@ hipError_t launch_append(int D, const AppendArgs& a, int B, hipStream_t s) {
   switch (D) {
     case 64: return launch_append_d<64>(a, B, s);
     case 128: return launch_append_d<128>(a, B, s);
+    case 192: return launch_append_d<192>(a, B, s);
     case 256: return launch_append_d<256>(a, B, s);
     default: return hipErrorInvalidValue;
   }

@@ -26,6 +26,15 @@ __host__ __device__ constexpr int padded_row_bytes(int d, int bits) {
 }
 __host__ __device__ constexpr int qmax_of(int bits) { return (1 << (bits - 1)) - 1; }
 
+// Size of the Hadamard blocks of the rotation: d for a power of two, else 64
+// (head_dim 192: block-diagonal, one H_64 per group of 64 elements).
+__host__ __device__ constexpr int rot_block(int d) { return (d & (d - 1)) == 0 ? d : 64; }
+
+// Positions one 256-thread block covers at one lane per 32-element block: a
+// multiple of 8 (V groups), so at head_dim 192 (6 lanes a row) 40 positions
+// use 240 threads and the last 16 only join the cross-lane stages.
+__host__ __device__ constexpr int rows_per_block(int d) { return 256 / (d / kBlock) / 8 * 8; }
+
 // Byte offset of 16-byte chunk c of token p's row inside one (b, g) plane.
 __host__ __device__ inline size_t chunk_offset(int p, int c, int rpad) {
   return (size_t)(p / kTile) * kTile * rpad + (size_t)(c * kTile + (p % kTile)) * kChunk;
@@ -100,13 +109,15 @@ __device__ inline void fwht_cross_stage(float (&x)[32], int lane) {
 }
 
 // Full transform of a d-element row spread over d/32 consecutive lanes, each
-// holding one 32-element block, followed by the normalization multiply.
+// holding one 32-element block, followed by the normalization multiply.  At
+// head_dim 192 each pair of lanes (one H_64 block) is transformed on its own.
 template <int D>
 __device__ inline void rotate_row(float (&x)[32], int lane, float cd) {
+  constexpr int RB = rot_block(D);
   fwht32_in_lane(x);
-  if constexpr (D >= 64) fwht_cross_stage<1>(x, lane);
-  if constexpr (D >= 128) fwht_cross_stage<2>(x, lane);
-  if constexpr (D >= 256) fwht_cross_stage<4>(x, lane);
+  if constexpr (RB >= 64) fwht_cross_stage<1>(x, lane);
+  if constexpr (RB >= 128) fwht_cross_stage<2>(x, lane);
+  if constexpr (RB >= 256) fwht_cross_stage<4>(x, lane);
 #pragma unroll
   for (int i = 0; i < 32; ++i) x[i] = x[i] * cd;
 }

@@ -120,14 +120,20 @@ struct StepRegs {
   __device__ float v_min(int m, int j) const { return half_of(vs[m][j], 1); }
 };
 
-// Load NW consecutive 32-bit words (NW = 1, 2, 4 or 8) with the widest loads.
+// Load NW consecutive 32-bit words with the widest loads their alignment
+// allows: NW * 4 bytes per token, so 8-byte loads for even NW, 16-byte ones
+// for multiples of 4 (head_dim 192 has NW = 3 or 6).
 template <int NW>
 __device__ inline void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
-  if constexpr (NW == 1) {
-    w[0] = p[0];
-  } else if constexpr (NW == 2) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
-    w[0] = x[0]; w[1] = x[1];
+  if constexpr (NW % 4 != 0 && NW % 2 != 0) {
+#pragma unroll
+    for (int q = 0; q < NW; ++q) w[q] = p[q];
+  } else if constexpr (NW % 4 != 0) {
+#pragma unroll
+    for (int q = 0; q < NW / 2; ++q) {
+      const u32x2 x = reinterpret_cast<const u32x2*>(p)[q];
+      w[2 * q] = x[0]; w[2 * q + 1] = x[1];
+    }
   } else {
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
@@ -391,8 +397,10 @@ void decode_split_kernel(DecodeArgs a) {
         }
       }
     }
+    // stages across blocks, up to the rotation's block size (head_dim 192:
+    // H_64 blocks, only the pairs j, j + 1)
 #pragma unroll
-    for (int h = 1; h < NB; h <<= 1) {
+    for (int h = 1; h < rot_block(D) / kBlock; h <<= 1) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if ((j & h) == 0) {

@@ -16,7 +16,8 @@ namespace kvq {
 #define KVQ_DECLARE_TABLE(D, KB, KM) extern DecodeLauncher kvq_decode_table_##D##_##KB##_##KM[6][8]; \
   extern DecodeLauncher kvq_prefill_table_##D##_##KB##_##KM[6];
 #define KVQ_ALL_K(X, D) X(D, 4, 0) X(D, 5, 0) X(D, 6, 0) X(D, 8, 0) X(D, 4, 1) X(D, 5, 1)
-KVQ_ALL_K(KVQ_DECLARE_TABLE, 64) KVQ_ALL_K(KVQ_DECLARE_TABLE, 128) KVQ_ALL_K(KVQ_DECLARE_TABLE, 256)
+KVQ_ALL_K(KVQ_DECLARE_TABLE, 64) KVQ_ALL_K(KVQ_DECLARE_TABLE, 128)
+KVQ_ALL_K(KVQ_DECLARE_TABLE, 192) KVQ_ALL_K(KVQ_DECLARE_TABLE, 256)
 #undef KVQ_DECLARE_TABLE
 
 namespace {
@@ -31,7 +32,7 @@ DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm) 
   if (vi < 0 || gc < 1 || gc > 8) return nullptr;
 #define KVQ_PICK(DD, KK, MM) \
   if (D == DD && kb == KK && (int)km == MM) return kvq_decode_table_##DD##_##KK##_##MM[vi][gc - 1];
-  KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 256)
+  KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 192) KVQ_ALL_K(KVQ_PICK, 256)
 #undef KVQ_PICK
   return nullptr;
 }
@@ -41,7 +42,7 @@ DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm) {
   if (vi < 0) return nullptr;
 #define KVQ_PICK(DD, KK, MM) \
   if (D == DD && kb == KK && (int)km == MM) return kvq_prefill_table_##DD##_##KK##_##MM[vi];
-  KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 256)
+  KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 192) KVQ_ALL_K(KVQ_PICK, 256)
 #undef KVQ_PICK
   return nullptr;
 }
@@ -70,8 +71,9 @@ __device__ inline float block_sum(float v, float* red) {
 // One 256-thread block per (sequence, query head), log-sum-exp merge of the
 // S split partials: M = max m_s, w_s = 2^(m_s - M), out = sum w_s acc_s /
 // sum w_s l_s, then the inverse rotation.  The weights go to LDS once;
-// thread t then sums element t % D over the splits s = t / D (mod 256 / D)
-// with several loads in flight.
+// thread t < P * D then sums element t % D over the splits s = t / D (mod
+// P = 256 / D; at head_dim 192 the last 64 threads sum nothing) with several
+// loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int P = 256 / D;       // split phases handled in parallel
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const float L = block_sum(lsum, red);   // its barriers also publish wgt
   const int e = t % D, ph = t / D;
   float v[U] = {};
-  int s = ph;
+  int s = t < P * D ? ph : S;
   for (; s + (U - 1) * P < S; s += U * P) {
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] += wgt[s + u * P] * acc[(size_t)(s + u * P) * D + e];
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
   __syncthreads();
   if (a.rotate) {
-    for (int h = 1; h < D; h <<= 1) {
+    for (int h = 1; h < rot_block(D); h <<= 1) {   // head_dim 192: within each H_64 block
       if (t < D / 2) {
         const int i = (t / h) * 2 * h + (t % h);
         const float u = o[i], w = o[i + h];
@@ -141,6 +143,7 @@ hipError_t launch_combine(int D, const CombineArgs& a, int B, hipStream_t s) {
   switch (D) {
     case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 192: hipLaunchKernelGGL(combine_kernel<192>, grid, dim3(256), 0, s, a); break;
     case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }

@@ -72,13 +72,13 @@ __device__ inline void load_v_codes(const uint8_t* plane, int p, int j, int (&c)
 template <int D>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   constexpr int LPR = D / kBlock;
-  constexpr int RPB = 256 / LPR;
+  constexpr int RPB = rows_per_block(D);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int j = tid % LPR;
   const int g = blockIdx.y;
   const int p = a.t0 + blockIdx.x * RPB + tid / LPR;
-  const bool active = p < a.t1;
+  const bool active = tid / LPR < RPB && p < a.t1;
   const size_t unit = (size_t)a.b * a.Hkv + g;
   float x[32];
 #pragma unroll
@@ -136,13 +136,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 
 hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  const int rpb = 256 / (D / kBlock);
+  const int rpb = rows_per_block(D);
   const int n = a.t1 - a.t0;
   if (n <= 0) return hipSuccess;
   const dim3 grid((n + rpb - 1) / rpb, a.Hkv, 1);
   switch (D) {
     case 64: hipLaunchKernelGGL(dequant_kernel<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(dequant_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 192: hipLaunchKernelGGL(dequant_kernel<192>, grid, dim3(256), 0, s, a); break;
     case 256: hipLaunchKernelGGL(dequant_kernel<256>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }

@@ -31,7 +31,7 @@ thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
 
 bool bits_ok(int b) { return b == 4 || b == 5 || b == 6 || b == 8; }
-bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool dim_ok(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t cap_tokens(const kvq_config& c) { return ((int64_t)c.max_ctx + kTile - 1) / kTile * kTile; }
@@ -256,7 +256,7 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* ca
   a.T = c.tail_len;
   a.cap = (int32_t)cap_tokens(c);
   a.dtype = dtype;
-  a.cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
   a.has_signs = sign_mask(c, a.signs);
   for (int b = 0; b < c.batch; ++b) a.len[b] = seq_len[b];
   return hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)));
@@ -290,7 +290,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const float cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  const float cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
 
   DecodeArgs da;
   std::memset(&da, 0, sizeof(da));
@@ -371,7 +371,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const float cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  const float cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
 
   DecodeArgs da;
   std::memset(&da, 0, sizeof(da));
@@ -451,7 +451,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t
   a.t0 = t0;
   a.t1 = t1;
   a.nq = n - (c.tail_len > 0 ? std::min(n, (int)c.tail_len) : 0);
-  a.cd = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
   a.has_signs = sign_mask(c, a.signs);
   return hip_status(launch_dequant(c.head_dim, a, static_cast<hipStream_t>(stream)));
 }

@@ -89,7 +89,11 @@
  * The code planes store u where the absmax formats store code + 2^(bits-1),
  * so their layouts are the same.
  * The rotation is y = fp32(1/sqrt(d)) * FWHT(x) with the float32 butterfly
- * stages applied in the order h = 1, 2, 4, ..., d/2.
+ * stages applied in the order h = 1, 2, 4, ..., d/2.  head_dim 192, a
+ * multiple of 64 that is not a power of two (the velog.io post's rule turns
+ * the rotation on for it; no Sylvester matrix of that size exists), is
+ * rotated block-diagonally: each group of 64 elements by itself, stages
+ * h = 1..32, factor fp32(1/8).
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -125,7 +129,7 @@ typedef enum kvq_plane {
 typedef struct kvq_config {
   int32_t batch;       /* sequences, 1..KVQ_MAX_BATCH */
   int32_t n_kv_heads;  /* KV heads per sequence, >= 1 */
-  int32_t head_dim;    /* 64, 128 or 256 */
+  int32_t head_dim;    /* 64, 128, 192 or 256 */
   int32_t k_bits;      /* 4, 5, 6 or 8 (q4_0, q5_0, q6_0, q8_0 blocks) */
   int32_t v_bits;      /* 4, 5, 6 or 8 */
   int32_t tail_len;    /* newest tokens kept in bf16, >= 0 */

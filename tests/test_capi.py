@@ -57,7 +57,7 @@ def test_config_check():
     assert kvq.kvq_config_check(c) == 0
     c.k_bits, c.v_bits = 6, 6                       # q6_0
     assert kvq.kvq_config_check(c) == 0
-    for field, val, want in (("head_dim", 192, -2), ("head_dim", 32, -2), ("k_bits", 7, -2),
+    for field, val, want in (("head_dim", 320, -2), ("head_dim", 32, -2), ("k_bits", 7, -2),
                              ("v_bits", 3, -2), ("batch", 0, -1), ("batch", 257, -1),
                              ("tail_len", -1, -1), ("max_ctx", 0, -1), ("rotate_k", 2, -1),
                              ("k_min", 2, -1), ("v_min", -1, -1)):
@@ -72,7 +72,7 @@ def test_config_check():
         assert kvq.kvq_config_check(m) == want, (kb, vb, km, vm)
 
 
-@pytest.mark.parametrize("d", (64, 128, 256))
+@pytest.mark.parametrize("d", (64, 128, 192, 256))
 @pytest.mark.parametrize("kb,vb", ((4, 4), (8, 4), (5, 4), (8, 8), (5, 5), (6, 6)))
 def test_plane_bytes(d, kb, vb):
     B, H, max_ctx, T = 3, 2, 1000, 16
@@ -189,7 +189,7 @@ def test_prefill_validation():
     assert _prefill(c, 8, 4, _lens(5, 5), out=0) == _capi.KVQ_ERR_INVALID
 
 
-@pytest.mark.parametrize("d", (64, 128, 256))
+@pytest.mark.parametrize("d", (64, 128, 192, 256))
 def test_plane_bytes_scale_and_min(d):
     # an (s, m) fp16 pair per block: q5_1 costs 32*5/8 + 4 = 24 bytes per 32
     # elements, 37.5 % of bf16 (the aiwitness.kr table's q5_1 row)
