@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--k-bits", type=int, default=0, help="override the workload's K code width")
     ap.add_argument("--v-bits", type=int, default=0, help="override the workload's V code width")
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="override the workload's head_dim (64, 128, 192 or 256)")
     ap.add_argument("--k-min", action="store_true",
                     help="K in scale-and-min blocks (q4_1 / q5_1; with a 4- or 5-bit K width)")
     ap.add_argument("--v-min", action="store_true", help="V in scale-and-min blocks")
@@ -200,6 +202,8 @@ def main():
     if args.v_bits:
         w["v_bits"] = args.v_bits
     w["km"], w["vm"] = args.k_min, args.v_min
+    if args.head_dim:
+        w["d"] = args.head_dim
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     log("workload", describe(w))
 

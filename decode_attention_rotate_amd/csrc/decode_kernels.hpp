@@ -239,19 +239,22 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, u
 // the same tiles, so each cache byte comes from HBM once per workgroup (the
 // other waves find it in L1 / L2).
 template <int D, int KB, int VB, int G, bool PF, bool KM, bool VM>
-__global__ __launch_bounds__(64 * split_group_waves(D))
-__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D), split_waves_per_simd(D))))
+__global__ __launch_bounds__(64 * split_group_waves(D, KM || VM || PF))
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D, KM || VM || PF),
+                                   split_waves_per_simd(D, KM || VM || PF))))
 void decode_split_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
   static_assert(!PF || G == 8, "prefill waves own 8 rows");
-  constexpr int kGroupWaves = split_group_waves(D);
+  constexpr int kGroupWaves = split_group_waves(D, KM || VM || PF);
   // tiles whose bytes a wave keeps in registers ahead of the one computing:
   // at one wave per SIMD (d = 256) the wave alone must cover the latency, so
   // it keeps two where four step buffers fit the 512 registers with at most
   // a few spilled (4-bit K, or 4-bit V with 5- or 8-bit K; decode only, a
-  // prefill wave holds more state)
+  // prefill wave holds more state).  The one-wave d = 192 variants measured
+  // no faster with two.
   constexpr int kAhead =
-      split_waves_per_simd(D) == 1 && !PF && !KM && !VM && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
+      split_waves_per_simd(D, KM || VM || PF) == 1 && D == 256 && !PF && !KM && !VM &&
+              (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
   constexpr int NSW = (NB + 1) / 2;
@@ -914,7 +917,8 @@ void decode_split_kernel(DecodeArgs a) {
 template <int D, int KB, int VB, int G, bool PF = false, bool KM = false, bool VM = false>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM>), grid, dim3(64 * split_group_waves(D)), 0, s, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM>), grid,
+                     dim3(64 * split_group_waves(D, KM || VM || PF)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -47,12 +47,17 @@ hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
 // in registers: at d <= 128 that fits the 256 registers of two waves per
 // SIMD; at d = 256 it needs about 300, which one wave per SIMD (512
 // registers, half of them AGPRs) allows.
-constexpr int split_waves_per_simd(int D) { return D >= 256 ? 1 : 2; }
+// At d = 192 two waves per SIMD fit the absmax decode variants (about 250
+// registers); variants with scale-and-min blocks or prefill rows ("wide")
+// need more and run at one wave per SIMD too.
+constexpr int split_waves_per_simd(int D, bool wide = false) {
+  return D >= 256 || (D == 192 && wide) ? 1 : 2;
+}
 // Waves per workgroup: one workgroup fills a compute unit's four SIMDs at
 // that occupancy.  The waves of a workgroup share one contiguous range of a
 // unit's quantized tiles and take them from an LDS counter; the split count
 // S is a multiple of this.
-constexpr int split_group_waves(int D) { return 4 * split_waves_per_simd(D); }
+constexpr int split_group_waves(int D, bool wide = false) { return 4 * split_waves_per_simd(D, wide); }
 
 struct DecodeArgs {
   const uint8_t* k_codes;

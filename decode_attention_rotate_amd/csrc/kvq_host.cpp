@@ -24,7 +24,7 @@ using namespace kvq;
 
 // Split-K waves per decode launch: one resident round on 256 compute units
 // of 4 SIMDs at the kernel's occupancy.
-int target_waves(int D) { return 256 * 4 * split_waves_per_simd(D); }
+int target_waves(int D, bool wide) { return 256 * 4 * split_waves_per_simd(D, wide); }
 constexpr int kMaxSplits = kMaxSplitsDevice;
 
 thread_local hipEvent_t g_ev_before = nullptr;
@@ -74,10 +74,10 @@ int head_chunk(int G) {
 // Splits per unit: enough waves for one resident round, at most one per
 // 64-token tile of the longest sequence, a multiple of the workgroup size and
 // at most kMaxSplits.  Non-decreasing in max_len.
-int split_count(int D, int64_t units, int max_len) {
+int split_count(int D, bool wide, int64_t units, int max_len) {
   const int64_t tiles = std::max(1, (max_len + kTile - 1) / kTile);
-  const int64_t gw = split_group_waves(D);
-  const int64_t want = std::max<int64_t>(1, (target_waves(D) + units - 1) / units);
+  const int64_t gw = split_group_waves(D, wide);
+  const int64_t want = std::max<int64_t>(1, (target_waves(D, wide) + units - 1) / units);
   int64_t S = (std::min(want, tiles) + gw - 1) / gw * gw;
   if (S > kMaxSplits) S = kMaxSplits / gw * gw;
   return (int)S;
@@ -96,7 +96,7 @@ Schedule schedule(const kvq_config& c, int n_q_heads, int max_len) {
   s.gc = head_chunk(G);
   s.nchunk = G / s.gc;
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * s.nchunk;
-  s.S = split_count(c.head_dim, units, max_len);
+  s.S = split_count(c.head_dim, c.k_min || c.v_min, units, max_len);
   return s;
 }
 
@@ -106,7 +106,7 @@ int max_splits(const kvq_config& c, int n_q_heads) {
   const int G = n_q_heads / c.n_kv_heads;
   const int nchunk = G / head_chunk(G);
   const int64_t units = (int64_t)c.batch * c.n_kv_heads * nchunk;
-  return split_count(c.head_dim, units, c.max_ctx);
+  return split_count(c.head_dim, c.k_min || c.v_min, units, c.max_ctx);
 }
 
 // Chunked prefill: the n_q * G rows of a KV head go in blocks of 8 rows per
@@ -122,7 +122,7 @@ struct PrefillSchedule {
 PrefillSchedule prefill_schedule(const kvq_config& c, int n_q_heads, int n_q, int max_len) {
   PrefillSchedule p;
   const int64_t G = n_q_heads / c.n_kv_heads;
-  const int64_t rows_per_block = 8 * split_group_waves(c.head_dim);
+  const int64_t rows_per_block = 8 * split_group_waves(c.head_dim, true);
   p.n_rb = (int)(((int64_t)n_q * G + rows_per_block - 1) / rows_per_block);
   const int64_t blocks = (int64_t)c.batch * c.n_kv_heads * p.n_rb;
   const int64_t tiles = std::max(1, (max_len + kTile - 1) / kTile);
@@ -316,7 +316,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.cap = (int32_t)cap_tokens(c);
   da.S = sc.S;
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
-  const dim3 grid(sc.S / split_group_waves(c.head_dim), c.n_kv_heads * sc.nchunk, c.batch);
+  const dim3 grid(sc.S / split_group_waves(c.head_dim, c.k_min || c.v_min), c.n_kv_heads * sc.nchunk,
+                  c.batch);
   if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
   if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
   if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
