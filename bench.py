@@ -154,6 +154,11 @@ def main():
     ap.add_argument("--no-rotation-off", action="store_true",
                     help="skip the secondary run with rotation disabled")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--paged", action="store_true",
+                    help="run the main measurement on a paged cache (64-position pages in a "
+                         "shuffled order) instead of the contiguous layout")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the secondary run on a paged cache")
     ap.add_argument("--k-bits", type=int, default=0, help="override the workload's K code width")
     ap.add_argument("--v-bits", type=int, default=0, help="override the workload's V code width")
     ap.add_argument("--head-dim", type=int, default=0,
@@ -216,7 +221,7 @@ def main():
         units = [all_units[i] for i in sorted(pick)]
     keep = None if args.no_cpu_baseline else {}
 
-    run = decode_run(torch, kvq, w, dev, args.warmup, args.steps, True, keep)
+    run = decode_run(torch, kvq, w, dev, args.warmup, args.steps, True, keep, paged=args.paged)
     ms_step = run["ms_step"]
     value = run["bytes_step"] / (ms_step * 1e-3) / 1e9
     kern_ms = run["kern_ms"]
@@ -238,14 +243,15 @@ def main():
         "vs_baseline": None,
         "dtype": "int8/u4 codes, fp16 scales, f32 accumulation",
         "data": "synthetic",
-        "config": {"workload": describe(w), "cache_bytes_per_step": int(run["bytes_step"]),
+        "config": {"workload": describe(w) + (", paged cache" if args.paged else ""),
+                   "cache_bytes_per_step": int(run["bytes_step"]),
                    "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
                    "us_per_step": round(ms_step * 1e3, 2),
                    "attention_kernel_us": round(kern_avg_ms * 1e3, 2),
                    "fill_append_mtok_s": round(run["fill_mtok_s"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload)},
+                     "traffic": None if args.paged else measured_traffic(args.workload)},
         "secondary": {"attention_kernel_us": percentiles(kern_ms),
                       "single_token_append_us": percentiles(run["app_ms"])},
     }
@@ -263,6 +269,19 @@ def main():
             "step_slowdown_of_rotation_pct": round(100 * (ms_step / off["ms_step"] - 1), 2)}
         log("rotation off: step %.1f us" % (off["ms_step"] * 1e3))
         del off
+
+    if not args.no_paged and not args.paged:
+        # the same step on a paged cache: 64-position pages of a shared pool,
+        # assigned in a shuffled order through the page table
+        pg = decode_run(torch, kvq, w, dev, args.warmup, args.steps, True, None, paged=True)
+        pg_kern = float(np.mean(pg["kern_ms"]))
+        result["secondary"]["paged"] = {
+            "us_per_step": round(pg["ms_step"] * 1e3, 2),
+            "attention_kernel_us": percentiles(pg["kern_ms"]),
+            "attention_kernel_gbs": round(pg["bytes_kern"] / (pg_kern * 1e-3) / 1e9, 1),
+            "single_token_append_us": percentiles(pg["app_ms"])}
+        log("paged: step %.1f us, kernel %.1f us" % (pg["ms_step"] * 1e3, pg_kern * 1e3))
+        del pg
 
 
     if not args.no_append:
@@ -285,18 +304,28 @@ def percentiles(ms):
             "p90": round(float(p[2]), 2)}
 
 
-def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep):
+def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False):
     """Fill a cache for workload w, then run warm-up steps, `steps` timed
     steps, and as many steps again with HIP events around the split kernel
     (recorded by the library on the call's stream) and around the append
     (kept out of the timed loop: event records sit between kernels).  When
-    `keep` is a dict it receives the bf16 K and V inputs for the oracle."""
+    `keep` is a dict it receives the bf16 K and V inputs for the oracle.
+    paged: the cache is a pool of 64-position pages, every tile of every
+    sequence on a page drawn from a seeded shuffle of the pool."""
     B, Hq, Hkv, d, n = w["B"], w["Hq"], w["Hkv"], w["d"], w["n"]
     total_steps = warmup + 2 * steps
-    cfg = kvq.kvq_config(B, Hkv, d, n + total_steps + 64, w["k_bits"], w["v_bits"], w["tail"],
+    max_ctx = n + total_steps + 64
+    table = None
+    pool = 0
+    if paged:
+        tiles = (max_ctx + kvq.KVQ_PAGE_TOKENS - 1) // kvq.KVQ_PAGE_TOKENS
+        pool = B * tiles
+        perm = np.random.default_rng(12345).permutation(pool).astype(np.int32)
+        table = torch.from_numpy(perm.reshape(B, tiles)).to(dev)
+    cfg = kvq.kvq_config(B, Hkv, d, max_ctx, w["k_bits"], w["v_bits"], w["tail"],
                          rotate_k=rotate, rotate_v=rotate, k_min=w.get("km", False),
-                         v_min=w.get("vm", False))
-    cache = kvq.KVCache(cfg, dev)
+                         v_min=w.get("vm", False), page_pool=pool)
+    cache = kvq.KVCache(cfg, dev, page_table=table)
     if keep is not None:
         keep["k"] = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev)
         keep["v"] = torch.empty_like(keep["k"])

@@ -18,7 +18,7 @@ import math
 from . import _capi
 from ._capi import (KvqConfig, KvqCache, KvqError, KVQ_BF16, KVQ_F32,
                     KVQ_K_CODES, KVQ_K_SCALES, KVQ_V_CODES, KVQ_V_SCALES,
-                    KVQ_K_TAIL, KVQ_V_TAIL, KVQ_MAX_BATCH, LIB_PATH)
+                    KVQ_K_TAIL, KVQ_V_TAIL, KVQ_MAX_BATCH, KVQ_PAGE_TOKENS, LIB_PATH)
 
 __all__ = [
     "KvqConfig", "KvqCache", "KvqError", "KVCache", "kvq_config",
@@ -26,7 +26,7 @@ __all__ = [
     "kvq_decode_workspace_bytes", "kvq_rotate_quantize_append",
     "kvq_decode_attention", "kvq_dequantize", "kvq_status_str",
     "kvq_profile_decode_events", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
-    "LIB_PATH",
+    "KVQ_PAGE_TOKENS", "LIB_PATH",
 ]
 
 
@@ -41,9 +41,10 @@ def kvq_config_default(batch, n_kv_heads, head_dim, max_ctx):
 
 def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
                tail_len=0, rotate_k=None, rotate_v=None, sign_seed=0, k_min=False,
-               v_min=False):
+               v_min=False, page_pool=0):
     """kvq_config_default with fields overridden; validated by the library.
-    k_min / v_min select scale-and-min blocks (q4_1 / q5_1 at 4 / 5 bits)."""
+    k_min / v_min select scale-and-min blocks (q4_1 / q5_1 at 4 / 5 bits);
+    page_pool > 0 makes a paged cache of that many 64-position pages."""
     c = kvq_config_default(batch, n_kv_heads, head_dim, max_ctx)
     c.k_bits, c.v_bits, c.tail_len = k_bits, v_bits, tail_len
     if rotate_k is not None:
@@ -52,6 +53,7 @@ def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
         c.rotate_v = int(rotate_v)
     c.sign_seed = int(sign_seed) & 0xFFFFFFFF
     c.k_min, c.v_min = int(k_min), int(v_min)
+    c.page_pool = int(page_pool)
     _capi.check(_capi.lib().kvq_config_check(ctypes.byref(c)), "kvq_config")
     return c
 
@@ -96,18 +98,42 @@ def kvq_profile_decode_events(before, after):
                                           ctypes.c_void_p(after.cuda_event))
 
 
+def page_table_tiles(cfg):
+    """Row length of a paged cache's page table: ceil(max_ctx / 64)."""
+    return (cfg.max_ctx + KVQ_PAGE_TOKENS - 1) // KVQ_PAGE_TOKENS
+
+
+__all__ += ["page_table_tiles"]
+
+
 class KVCache:
-    """Device planes of one cache, allocated zeroed with torch (uint8)."""
+    """Device planes of one cache, allocated zeroed with torch (uint8).
+
+    For a paged configuration (cfg.page_pool > 0) the code and scale planes
+    are the page pool and `page_table` is the int32 device tensor
+    [batch][ceil(max_ctx/64)] mapping each sequence's 64-position tiles to
+    pages; the caller fills it (the planes keep a reference to it)."""
 
     PLANES = (("k_codes", KVQ_K_CODES), ("k_scales", KVQ_K_SCALES),
               ("v_codes", KVQ_V_CODES), ("v_scales", KVQ_V_SCALES),
               ("k_tail", KVQ_K_TAIL), ("v_tail", KVQ_V_TAIL))
 
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", page_table=None):
         torch = _torch()
         self.cfg = cfg
         self.planes = {}
         ptrs = {}
+        self.page_table = None
+        if cfg.page_pool > 0:
+            if page_table is None:
+                raise ValueError("a paged cache needs a page_table")
+            want = (cfg.batch, page_table_tiles(cfg))
+            if (page_table.dtype != torch.int32 or tuple(page_table.shape) != want
+                    or not page_table.is_cuda or not page_table.is_contiguous()):
+                raise ValueError("page_table must be a contiguous int32 device tensor of shape %s"
+                                 % (want,))
+            self.page_table = page_table
+            ptrs["page_table"] = page_table.data_ptr()
         for name, pid in self.PLANES:
             nbytes = kvq_plane_bytes(cfg, pid)
             if nbytes == 0 and name.endswith("tail") and cfg.tail_len == 0:
@@ -123,6 +149,37 @@ class KVCache:
 
     def __getitem__(self, name):
         return self.planes[name]
+
+    def sequence(self, b):
+        """(config, cache) of sequence b alone over the same device memory:
+        batch 1, the same page pool, row b of the page table and sequence b's
+        tail slots, so calls can run on one sequence of a paged cache (for
+        instance appends of a length the others do not share).  Paged caches
+        only."""
+        cfg = self.cfg
+        if cfg.page_pool <= 0:
+            raise ValueError("sequence views need a paged cache")
+        if not 0 <= b < cfg.batch:
+            raise IndexError("sequence %d of %d" % (b, cfg.batch))
+        one = KvqConfig.from_buffer_copy(cfg)
+        one.batch = 1
+        view = KVCache.__new__(KVCache)
+        view.cfg = one
+        view.page_table = self.page_table[b:b + 1]
+        view.planes = dict(self.planes)
+        tail_bytes = cfg.n_kv_heads * cfg.tail_len * cfg.head_dim * 2
+        ptrs = {"page_table": view.page_table.data_ptr()}
+        for name, _ in self.PLANES:
+            t = self.planes[name]
+            if t is None:
+                ptrs[name] = None
+            elif name.endswith("tail"):
+                view.planes[name] = t[b * tail_bytes:(b + 1) * tail_bytes]
+                ptrs[name] = view.planes[name].data_ptr()
+            else:
+                ptrs[name] = t.data_ptr()
+        view.struct = KvqCache(**ptrs)
+        return one, view
 
 
 def _stream(stream):

@@ -150,16 +150,26 @@ __device__ inline uint32_t quantize_any(int bits, bool minf, const float (&x)[32
   return quantize_block<8>(x, c);
 }
 
-// Scale entry of block j of position p: one fp16, or an (s, m) pair of fp16
-// (one 32-bit word) for scale-and-min blocks.  sc is the (b, g) plane.
+// Scale entry of block j of position l (0..63) of a tile: one fp16, or an
+// (s, m) pair of fp16 (one 32-bit word) for scale-and-min blocks.  sc is the
+// tile's first entry.
 template <int D>
-__device__ inline void store_scale(uint16_t* sc, bool minf, int p, int j, uint32_t s) {
-  if (minf) reinterpret_cast<uint32_t*>(sc)[(size_t)p * (D / kBlock) + j] = s;
-  else sc[(size_t)p * (D / kBlock) + j] = (uint16_t)s;
+__device__ inline void store_scale(uint16_t* sc, bool minf, int l, int j, uint32_t s) {
+  if (minf) reinterpret_cast<uint32_t*>(sc)[l * (D / kBlock) + j] = s;
+  else sc[l * (D / kBlock) + j] = (uint16_t)s;
+}
+// First scale entry, K row tile and V tile of tile slot `slot` in plane pl.
+template <int D>
+__device__ inline uint16_t* scale_tile(const AppendArgs& a, int pl, size_t slot) {
+  return a.scales[pl] + slot * (size_t)kTile * (D / kBlock) * (a.minf[pl] ? 2 : 1);
 }
 template <int D>
-__device__ inline uint16_t* scale_plane(const AppendArgs& a, int pl, size_t unit) {
-  return a.scales[pl] + unit * (size_t)a.cap * (D / kBlock) * (a.minf[pl] ? 2 : 1);
+__device__ inline uint8_t* k_tile(const AppendArgs& a, size_t slot, int bits) {
+  return a.codes[0] + slot * (size_t)kTile * padded_row_bytes(D, bits);
+}
+template <int D>
+__device__ inline uint8_t* v_tile(const AppendArgs& a, size_t slot, int bits) {
+  return a.codes[1] + slot * (size_t)v_tile_bytes(D, bits);
 }
 
 // Merge the slots of one V item whose bit is set in `mask` into memory.
@@ -243,6 +253,9 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
   const bool from_ring = active && p < len;     // leaving the tail (T > 0)
   const int Hkv = a.Hkv;
   const size_t unit = (size_t)b * Hkv + g;
+  // slot of p's tile; positions on a page outside the pool are not stored
+  const long long slot = active ? tile_slot(a.map, b, g, p / kTile) : -1LL;
+  const bool store = slot >= 0;
 
   float x[32];
   if (active && !from_ring) {
@@ -265,19 +278,19 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
 
   const int bits = a.bits[pl];
   const bool minf = a.minf[pl] != 0;
-  uint16_t* scales = scale_plane<D>(a, pl, unit);
+  const size_t st = store ? (size_t)slot : 0;
+  uint16_t* scales = scale_tile<D>(a, pl, st);
   uint32_t c[32];
   if (pl == 0) {
-    uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
-    const uint32_t s = quantize_k<D>(bits, minf, x, c, active, plane, p, j);
-    if (active) store_scale<D>(scales, minf, p, j, s);
+    const uint32_t s = quantize_k<D>(bits, minf, x, c, store, k_tile<D>(a, st, bits), p % kTile, j);
+    if (store) store_scale<D>(scales, minf, p % kTile, j, s);
     return;
   }
 
   // V: codes of the block's positions meet in LDS as bytes [group][e][slot]
   const uint32_t s = quantize_any<D>(bits, minf, x, c);
+  if (store) store_scale<D>(scales, minf, p % kTile, j, s);
   if (active) {
-    store_scale<D>(scales, minf, p, j, s);
     uint8_t* dst = vlds + ((rho / 8) * D + kBlock * j) * 8 + rho % 8;
 #pragma unroll
     for (int e = 0; e < 32; ++e) dst[8 * e] = (uint8_t)c[e];   // offset code
@@ -285,7 +298,6 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
   __syncthreads();
 
   constexpr int NN = D / 16;
-  uint8_t* vplane = a.codes[1] + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, bits);
   for (int it = tid; it < NGRP * D; it += 256) {
     const int grp = it / D, idx = it % D;
     const int e = 16 * (idx % NN) + idx / NN;   // consecutive threads: consecutive items
@@ -295,8 +307,10 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
     for (int k = 0; k < 8; ++k)
       if (p0 + k >= q0 && p0 + k < q1) mask |= 1u << k;
     if (!mask) continue;
+    const long long vslot = tile_slot(a.map, b, g, p0 / kTile);
+    if (vslot < 0) continue;
     const uint64_t u = *reinterpret_cast<const uint64_t*>(vlds + (grp * D + e) * 8);
-    uint8_t* tile = vplane + (size_t)(p0 / kTile) * v_tile_bytes(D, bits);
+    uint8_t* tile = v_tile<D>(a, (size_t)vslot, bits);
     const int item = v_item(D, p0 % kTile, e);
     if (bits == 4) store_v_item<D, 4>(tile, item, u, mask);
     else if (bits == 5) store_v_item<D, 5>(tile, item, u, mask);
@@ -386,8 +400,11 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   const int len = rg.len, T = a.T;
   const bool new_lane = lane < LPR;
   const bool ring_lane = T > 0 && rg.q1 > rg.q0 && lane >= 32 && lane < 32 + LPR;
-  const bool q_lane = rg.q1 > rg.q0 && (T > 0 ? ring_lane : new_lane);
   const int pq = rg.q0;                          // the quantized position
+  // slot of pq's tile (-1: no quantized position, or a page outside the pool)
+  const long long qslot = rg.q1 > rg.q0 ? tile_slot(a.map, b, g, pq / kTile) : -1LL;
+  const bool q_lane = qslot >= 0 && (T > 0 ? ring_lane : new_lane);
+  const size_t qs = qslot >= 0 ? (size_t)qslot : 0;
   const size_t unit = (size_t)b * a.Hkv + g;
   const int bits = pl == 0 ? a.bits[0] : VB;   // V's width is the template's
 
@@ -415,8 +432,7 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
     for (int q = 0; q < 4; ++q) rring[q] = src[q];
   }
   // V items of this lane's 32 elements at the quantized position
-  uint8_t* vtile = a.codes[1] + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, VB) +
-                   (size_t)(pq / kTile) * v_tile_bytes(D, VB);
+  uint8_t* vtile = v_tile<D>(a, qs, VB);
   uint32_t oldw[VB == 8 ? 1 : 32];
   uint32_t oldh[VB == 5 || VB == 6 ? 32 : 1];
   if constexpr (VB != 8) {
@@ -467,13 +483,13 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) z[e] = T > 0 ? y[e] : x[e];
     const bool minf = a.minf[pl] != 0;
-    uint16_t* scales = scale_plane<D>(a, pl, unit);
+    uint16_t* scales = scale_tile<D>(a, pl, qs);
     uint32_t c[32];
     if (pl == 0) {
-      uint8_t* plane = a.codes[0] + unit * (size_t)a.cap * padded_row_bytes(D, bits);
-      store_scale<D>(scales, minf, pq, j, quantize_k<D>(bits, minf, z, c, true, plane, pq, j));
+      store_scale<D>(scales, minf, pq % kTile, j,
+                     quantize_k<D>(bits, minf, z, c, true, k_tile<D>(a, qs, bits), pq % kTile, j));
     } else {
-      store_scale<D>(scales, minf, pq, j, quantize_fmt<VB>(minf, z, c));
+      store_scale<D>(scales, minf, pq % kTile, j, quantize_fmt<VB>(minf, z, c));
       const int k = pq % 8;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {

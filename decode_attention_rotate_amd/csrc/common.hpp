@@ -40,6 +40,32 @@ __host__ __device__ inline size_t chunk_offset(int p, int c, int rpad) {
   return (size_t)(p / kTile) * kTile * rpad + (size_t)(c * kTile + (p % kTile)) * kChunk;
 }
 
+// Where the 64-token tiles of the tiled planes (K codes, V codes, scales)
+// live.  Contiguous caches keep the cap/64 tiles of each (sequence, KV head)
+// together: tile t of (b, g) is slot (b*Hkv + g)*tiles + t.  Paged caches
+// draw pages of 64 tokens from a pool shared by all sequences: tile t of
+// sequence b is page ptab[b*tiles + t], whose slot for KV head g is
+// page*Hkv + g.  A plane's tile of (b, g, t) starts at slot * (its tile bytes).
+struct TileMap {
+  const int32_t* ptab;   // [B][tiles] device page table; nullptr: contiguous
+  int32_t n_pages;       // pool size in pages (paged caches)
+  int32_t tiles;         // cap / 64: tiles per sequence, the table's row length
+  int32_t Hkv;
+};
+// Slot of tile t of (b, g); -1 when the table entry lies outside
+// [0, n_pages), which the kernels never follow.
+__device__ inline long long tile_slot(const TileMap& m, int b, int g, int t) {
+  if (!m.ptab) return ((long long)b * m.Hkv + g) * m.tiles + t;
+  const int page = m.ptab[(size_t)b * m.tiles + t];
+  return (unsigned)page < (unsigned)m.n_pages ? (long long)page * m.Hkv + g : -1LL;
+}
+// For reads: a bad entry reads page 0 instead, which stays inside the pool
+// (results for those positions are then unspecified).
+__device__ inline size_t tile_slot_read(const TileMap& m, int b, int g, int t) {
+  const long long s = tile_slot(m, b, g, t);
+  return s < 0 ? (size_t)g : (size_t)s;
+}
+
 // V code planes are stored element-major per 64-token tile, so that the
 // codes of one element for eight consecutive tokens sit in one item (the
 // shape of one lane's P.V matrix-core operand).  Token t (0..63) and element

@@ -556,10 +556,6 @@ void decode_split_kernel(DecodeArgs a) {
   if (wq0 < wq1) {
     constexpr int KSE = KM ? 2 * NB : NB;   // 16-bit scale entries per token
     constexpr int VSE = VM ? 2 * NB : NB;
-    const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
-    const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * KSE;
-    const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
-    const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * VSE;
     // A operand of Q.K: the rotated query in 16-bit fixed point (step
     // amax / 32639 per head), high bytes in even rows, low bytes in odd rows;
     // 4/5-bit codes widen to bytes in the order 0,2,4,6,1,3,5,7 of each group
@@ -596,9 +592,11 @@ void decode_split_kernel(DecodeArgs a) {
     const uint32_t v_off = (uint32_t)(lane * NN * (VB == 8 ? 8 : 4));
     const uint32_t vh_off = (uint32_t)(32 * D + lane * NN);
 
+    // tile of position s0: its slot in the (contiguous or paged) planes
     auto load_step = [&](Regs& R, int s0) {
       const int j2 = (s0 / kStep) & 1;
-      const uint8_t* kt = kpl + (size_t)(s0 / kTile) * kTile * RKP + j2 * kStep * kChunk;
+      const size_t slot = tile_slot_read(a.map, b, g, s0 / kTile);
+      const uint8_t* kt = a.k_codes + slot * (kTile * RKP) + j2 * kStep * kChunk;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -619,11 +617,11 @@ void decode_split_kernel(DecodeArgs a) {
             }
           }
         }
-        const size_t tok = (size_t)s0 + 16 * m + col;
-        load_words(reinterpret_cast<const uint32_t*>(ksc + tok * KSE), R.ks[m]);
-        load_words(reinterpret_cast<const uint32_t*>(vsc + tok * VSE), R.vs[m]);
+        const size_t tok = slot * kTile + (s0 % kTile) + 16 * m + col;
+        load_words(reinterpret_cast<const uint32_t*>(a.k_scales + tok * KSE), R.ks[m]);
+        load_words(reinterpret_cast<const uint32_t*>(a.v_scales + tok * VSE), R.vs[m]);
       }
-      const uint8_t* vt = vpl + (size_t)(s0 / kTile) * VTB;
+      const uint8_t* vt = a.v_codes + slot * VTB;
       const uint8_t* vj = vt + (size_t)j2 * 64 * NN * (VB == 8 ? 8 : 4) + v_off;
 #pragma unroll
       for (int q = 0; q < (VB == 8 ? NN / 2 : NN / 4); ++q) R.v[q] = reinterpret_cast<const u32x4*>(vj)[q];

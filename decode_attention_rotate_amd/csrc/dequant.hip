@@ -85,27 +85,31 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int e = 0; e < 32; ++e) x[e] = 0.f;
   if (active) {
     if (p < a.nq) {
+      // p's tile in the contiguous or paged planes; l is p's place in it
+      const size_t slot = tile_slot_read(a.map, a.b, g, p / kTile);
+      const int l = p % kTile;
+      const size_t srow = slot * kTile + l;
       float s, mn = 0.f;
       if (a.minf) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(a.scales)[(unit * a.cap + p) * (D / kBlock) + j];
+        const uint32_t w = reinterpret_cast<const uint32_t*>(a.scales)[srow * (D / kBlock) + j];
         s = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
         mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
       } else {
-        s = (float)__builtin_bit_cast(_Float16, a.scales[(unit * a.cap + p) * (D / kBlock) + j]);
+        s = (float)__builtin_bit_cast(_Float16, a.scales[srow * (D / kBlock) + j]);
       }
       int c[32];
       if (a.which == 0) {
-        const uint8_t* plane = a.codes + unit * (size_t)a.cap * padded_row_bytes(D, a.bits);
-        if (a.bits == 4) load_codes<D, 4>(plane, p, j, c);
-        else if (a.bits == 5) load_codes<D, 5>(plane, p, j, c);
-        else if (a.bits == 6) load_codes<D, 6>(plane, p, j, c);
-        else load_codes<D, 8>(plane, p, j, c);
+        const uint8_t* tile = a.codes + slot * kTile * padded_row_bytes(D, a.bits);
+        if (a.bits == 4) load_codes<D, 4>(tile, l, j, c);
+        else if (a.bits == 5) load_codes<D, 5>(tile, l, j, c);
+        else if (a.bits == 6) load_codes<D, 6>(tile, l, j, c);
+        else load_codes<D, 8>(tile, l, j, c);
       } else {
-        const uint8_t* plane = a.codes + unit * (size_t)(a.cap / kTile) * v_tile_bytes(D, a.bits);
-        if (a.bits == 4) load_v_codes<D, 4>(plane, p, j, c);
-        else if (a.bits == 5) load_v_codes<D, 5>(plane, p, j, c);
-        else if (a.bits == 6) load_v_codes<D, 6>(plane, p, j, c);
-        else load_v_codes<D, 8>(plane, p, j, c);
+        const uint8_t* tile = a.codes + slot * v_tile_bytes(D, a.bits);
+        if (a.bits == 4) load_v_codes<D, 4>(tile, l, j, c);
+        else if (a.bits == 5) load_v_codes<D, 5>(tile, l, j, c);
+        else if (a.bits == 6) load_v_codes<D, 6>(tile, l, j, c);
+        else load_v_codes<D, 8>(tile, l, j, c);
       }
       if (a.minf) {
         // level u = c + 2^(bits-1); u * s is exact, one rounding in the add

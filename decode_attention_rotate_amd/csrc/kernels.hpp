@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
 #include "kvq.h"
 
 namespace kvq {
@@ -19,6 +20,7 @@ struct AppendArgs {
   int32_t minf[2];           // 1: scale-and-min blocks (4/5-bit only)
   int32_t rotate[2];
   int32_t Hkv, n_new, T, cap, dtype;
+  TileMap map;               // tile slots of the code and scale planes
   float cd;                  // fp32(1/sqrt(D))
   int32_t has_signs;         // rotate by H diag(s): flip element e's sign by bit e of signs
   uint32_t signs[8];
@@ -35,6 +37,7 @@ struct DequantArgs {
   int32_t which;              // 0 = K (row layout), 1 = V (element-major tiles)
   int32_t bits, rotate, space, Hkv, T, cap, b, t0, t1, nq;
   int32_t minf;              // scale-and-min blocks: (s, m) pairs, x = u * s + m
+  TileMap map;
   float cd;
   int32_t has_signs;         // space 1 rotates back by diag(s) H
   uint32_t signs[8];
@@ -70,6 +73,7 @@ struct DecodeArgs {
   float* part_ml;            // [B][Hq][S][2]  running max (log2 units), sum
   float* part_acc;           // [B][Hq][S][D]  unnormalised output, rotated space
   int32_t Hkv, Hq, G, n_gchunks, T, cap, S;
+  TileMap map;               // tile slots of the code and scale planes
   int32_t n_q, n_rb;         // prefill: queries per sequence, 64-row blocks per KV head
   int32_t q_dtype, rotate_k;
   float cd, sm_scale;        // fp32(1/sqrt(D)); softmax scale

@@ -41,7 +41,7 @@ kvq_status check_cfg(const kvq_config* c) {
   if (c->batch < 1 || c->batch > KVQ_MAX_BATCH || c->n_kv_heads < 1 || c->max_ctx < 1 ||
       c->tail_len < 0 || (c->rotate_k != 0 && c->rotate_k != 1) ||
       (c->rotate_v != 0 && c->rotate_v != 1) || (c->k_min != 0 && c->k_min != 1) ||
-      (c->v_min != 0 && c->v_min != 1))
+      (c->v_min != 0 && c->v_min != 1) || c->page_pool < 0)
     return KVQ_ERR_INVALID;
   if (!dim_ok(c->head_dim) || !bits_ok(c->k_bits) || !bits_ok(c->v_bits)) return KVQ_ERR_UNSUPPORTED;
   // scale-and-min blocks come in the 4- and 5-bit widths (q4_1, q5_1)
@@ -61,7 +61,21 @@ kvq_status check_cache(const kvq_config& c, const kvq_cache* k) {
     if (!k->k_tail || !k->v_tail) return KVQ_ERR_INVALID;
     if (!aligned16(k->k_tail) || !aligned16(k->v_tail)) return KVQ_ERR_ALIGN;
   }
+  if (c.page_pool > 0) {
+    if (!k->page_table) return KVQ_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(k->page_table) & 3u) != 0) return KVQ_ERR_ALIGN;
+  }
   return KVQ_OK;
+}
+
+// Where the kernels find the 64-token tiles of the code and scale planes.
+TileMap tile_map(const kvq_config& c, const kvq_cache* k) {
+  TileMap m;
+  m.ptab = c.page_pool > 0 ? k->page_table : nullptr;
+  m.n_pages = c.page_pool;
+  m.tiles = (int32_t)(cap_tokens(c) / kTile);
+  m.Hkv = c.n_kv_heads;
+  return m;
 }
 
 // Largest divisor of G that is at most 8 (query heads per kernel instance).
@@ -191,6 +205,7 @@ kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads, int32_t head_di
   c.sign_seed = 0;
   c.k_min = 0;
   c.v_min = 0;
+  c.page_pool = 0;
   return c;
 }
 
@@ -200,12 +215,16 @@ size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane) {
   if (check_cfg(cfg) != KVQ_OK) return 0;
   const kvq_config& c = *cfg;
   const size_t units = (size_t)c.batch * c.n_kv_heads;
-  const size_t cap = (size_t)cap_tokens(c);
+  // 64-token tiles of the code and scale planes: cap/64 per (b, g), or
+  // page_pool per KV head for a paged cache
+  const size_t tiles = c.page_pool > 0 ? (size_t)c.page_pool * c.n_kv_heads
+                                       : units * (size_t)(cap_tokens(c) / kTile);
+  const size_t nb = (size_t)(c.head_dim / kBlock);
   switch (plane) {
-    case KVQ_K_CODES: return units * cap * padded_row_bytes(c.head_dim, c.k_bits);
-    case KVQ_V_CODES: return units * (cap / kTile) * v_tile_bytes(c.head_dim, c.v_bits);
-    case KVQ_K_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t) * (c.k_min ? 2 : 1);
-    case KVQ_V_SCALES: return units * cap * (c.head_dim / kBlock) * sizeof(uint16_t) * (c.v_min ? 2 : 1);
+    case KVQ_K_CODES: return tiles * kTile * padded_row_bytes(c.head_dim, c.k_bits);
+    case KVQ_V_CODES: return tiles * v_tile_bytes(c.head_dim, c.v_bits);
+    case KVQ_K_SCALES: return tiles * kTile * nb * sizeof(uint16_t) * (c.k_min ? 2 : 1);
+    case KVQ_V_SCALES: return tiles * kTile * nb * sizeof(uint16_t) * (c.v_min ? 2 : 1);
     case KVQ_K_TAIL:
     case KVQ_V_TAIL: return units * (size_t)c.tail_len * c.head_dim * sizeof(uint16_t);
   }
@@ -255,6 +274,7 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* ca
   a.n_new = n_new;
   a.T = c.tail_len;
   a.cap = (int32_t)cap_tokens(c);
+  a.map = tile_map(c, cache);
   a.dtype = dtype;
   a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
   a.has_signs = sign_mask(c, a.signs);
@@ -314,6 +334,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   da.n_gchunks = sc.nchunk;
   da.T = c.tail_len;
   da.cap = (int32_t)cap_tokens(c);
+  da.map = tile_map(c, cache);
   da.S = sc.S;
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
   const dim3 grid(sc.S / split_group_waves(c.head_dim, c.k_min || c.v_min), c.n_kv_heads * sc.nchunk,
@@ -396,6 +417,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   da.n_gchunks = 1;
   da.T = c.tail_len;
   da.cap = (int32_t)cap_tokens(c);
+  da.map = tile_map(c, cache);
   da.S = ps.S;
   da.n_q = n_q;
   da.n_rb = ps.n_rb;
@@ -448,6 +470,7 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t
   a.Hkv = c.n_kv_heads;
   a.T = c.tail_len;
   a.cap = (int32_t)cap_tokens(c);
+  a.map = tile_map(c, cache);
   a.b = b;
   a.t0 = t0;
   a.t1 = t1;

@@ -33,7 +33,9 @@
  *    nothing.  A failed kernel launch returns KVQ_ERR_HIP.  Errors raised by
  *    the device later surface from the HIP runtime on the caller's next
  *    synchronisation.
- *  - Device pointers must be 16-byte aligned (KVQ_ERR_ALIGN otherwise).
+ *  - Device pointers must be 16-byte aligned (KVQ_ERR_ALIGN otherwise; the
+ *    page table of a paged cache 4-byte aligned).  A paged cache without a
+ *    page table is KVQ_ERR_INVALID, and so is a negative page_pool.
  *
  * Cache memory layout (all planes indexed by sequence b and KV head g,
  * cap = max_ctx rounded up to a multiple of 64 tokens):
@@ -72,6 +74,16 @@
  *  - tail planes (k_tail, v_tail): [b][g][tail_len][head_dim] bf16; position
  *    p of the newest tail_len positions lives in slot p % tail_len.  NULL is
  *    allowed when tail_len == 0.
+ *  - paged caches (page_pool > 0): the K code, V code and scale planes are
+ *    a pool of page_pool pages of KVQ_PAGE_TOKENS (64) positions shared by
+ *    all sequences, each page holding one 64-token tile per KV head:
+ *    [page][g][tile], with the tile formats above (K rows tiled in 16-byte
+ *    chunks, V element-major, scales [64][head_dim/32]).  Positions
+ *    64t .. 64t+63 of sequence b live in page page_table[b][t].  The
+ *    contiguous layout is the same tile sequence ordered [b][g][t].  Tail
+ *    planes are not paged.  The pages name no cache layout; paging lets
+ *    sequences of very different lengths share one pool, as serving stacks
+ *    do.
  *
  * Quantization of one block of 32 rotated values x (bf16-rounded first when
  * tail_len > 0, so that a token gets the same codes whether or not it passed
@@ -126,6 +138,9 @@ typedef enum kvq_plane {
  * kernel arguments). */
 #define KVQ_MAX_BATCH 256
 
+/* Positions per page of a paged cache (one tile of every tiled plane). */
+#define KVQ_PAGE_TOKENS 64
+
 typedef struct kvq_config {
   int32_t batch;       /* sequences, 1..KVQ_MAX_BATCH */
   int32_t n_kv_heads;  /* KV heads per sequence, >= 1 */
@@ -146,6 +161,10 @@ typedef struct kvq_config {
                         * aiwitness.kr table's q5_1 rows; see "Scale-and-min
                         * blocks" above */
   int32_t v_min;       /* the same for V */
+  int32_t page_pool;   /* 0: contiguous planes, each (sequence, KV head)
+                        * owns max_ctx rounded up to 64 positions; > 0: the
+                        * code and scale planes are a pool of this many pages
+                        * of 64 positions, mapped by kvq_cache.page_table */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -155,11 +174,22 @@ typedef struct kvq_cache {
   void* v_scales;
   void* k_tail;  /* may be NULL when tail_len == 0 */
   void* v_tail;  /* may be NULL when tail_len == 0 */
+  /* Paged caches only (ignored when page_pool == 0): device int32
+   * [batch][ceil(max_ctx / 64)], the page of each 64-position tile of each
+   * sequence, 4-byte aligned, owned and filled by the caller.  Entries for
+   * tiles a call writes or reads must name pages in [0, page_pool); a page
+   * must not be written for two sequences.  The kernels never follow an
+   * entry outside [0, page_pool): the append skips positions on such a page
+   * and attention and read-back read page 0 in its place (results for those
+   * positions are unspecified).  Entries past a sequence's last tile are
+   * never read. */
+  const int32_t* page_table;
 } kvq_cache;
 
 /* Defaults: 4-bit K and V, no tail, rotation on iff head_dim >= 64 and
  * head_dim % 64 == 0 (velog.io post, section "application and background"),
- * sign_seed 0, absmax blocks (k_min = v_min = 0). */
+ * sign_seed 0, absmax blocks (k_min = v_min = 0), contiguous planes
+ * (page_pool = 0). */
 kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads,
                               int32_t head_dim, int32_t max_ctx);
 
@@ -167,7 +197,8 @@ kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads,
 kvq_status kvq_config_check(const kvq_config* cfg);
 
 /* Bytes the caller must allocate for one cache plane; 0 for an invalid
- * configuration or plane (and for tail planes when tail_len == 0). */
+ * configuration or plane (and for tail planes when tail_len == 0).  For a
+ * paged cache the code and scale planes hold page_pool pages. */
 size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane);
 
 /* Device workspace kvq_decode_attention needs for n_q_heads query heads per

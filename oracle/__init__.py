@@ -19,6 +19,8 @@ What the oracle computes, and where each step comes from:
 * Precision tail: the newest tokens stay in bf16, the rest are quantized.
   Source: aitrends.kr article 92204, glossary entry "Precision Tail" and the
   detail section on tail length.
+* Paged planes (pages_to_contiguous): a storage layout the pages do not
+  describe (reading R24); the functions only move whole 64-position tiles.
 
 Everything the pages leave open (Hadamard ordering, fp32 association of the
 transform, rounding of the scale, code encoding, memory layout) is a stated
@@ -46,7 +48,7 @@ from .blockquant import (
     pack_rows, unpack_rows,
     row_bytes, padded_row_bytes, rows_to_tiled, tiled_to_rows,
 )
-from .kvcache import OracleCache
+from .kvcache import OracleCache, pages_to_contiguous, contiguous_to_pages
 from .attention import (softmax_attention, decode_reference, dequantize_unit,
                         dequantize_reference, prefill_reference)
 
@@ -58,5 +60,5 @@ __all__ = [
     "pack_rows", "unpack_rows",
     "row_bytes", "padded_row_bytes", "rows_to_tiled", "tiled_to_rows",
     "OracleCache", "softmax_attention", "decode_reference", "prefill_reference", "dequantize_unit",
-    "dequantize_reference",
+    "dequantize_reference", "pages_to_contiguous", "contiguous_to_pages",
 ]

@@ -163,3 +163,50 @@ def dequantize_rows(codes_plane, scales_plane, d, bits, n, which, minf=False):
         pairs = np.asarray(scales_plane[:n]).reshape(n, d // BLOCK, 2)
         return dequantize_blocks_min(codes, pairs, bits)
     return dequantize_blocks(codes, scales_plane[:n])
+
+
+def pages_to_contiguous(pool, table, n_kv_heads, tile_size):
+    """Gather one paged plane into the contiguous layout (reading R24).
+
+    The pages fix no memory layout.  A paged cache keeps the 64-position
+    tiles of its code and scale planes in a pool of pages shared by all
+    sequences, one tile per KV head in each page, [page][g][tile]; the page
+    table names the page of tile t of sequence b.  The contiguous layout
+    orders the same tiles [b][g][t].
+
+    pool:      array whose leading axis runs over pages * n_kv_heads tiles of
+               tile_size elements each (any dtype; flattened).
+    table:     int array [B][tiles]; an entry < 0 marks a tile that holds no
+               positions, which comes back zero.
+    Returns [B][n_kv_heads][tiles * tile_size] of pool's dtype.
+    """
+    table = np.asarray(table)
+    B, tiles = table.shape
+    flat = np.asarray(pool).reshape(-1)
+    n_pages = flat.size // (n_kv_heads * tile_size)
+    pages = flat[: n_pages * n_kv_heads * tile_size].reshape(n_pages, n_kv_heads, tile_size)
+    out = np.zeros((B, n_kv_heads, tiles, tile_size), flat.dtype)
+    for b in range(B):
+        for t in range(tiles):
+            page = int(table[b, t])
+            if page >= 0:
+                out[b, :, t, :] = pages[page]
+    return out.reshape(B, n_kv_heads, tiles * tile_size)
+
+
+def contiguous_to_pages(planes, table, n_pages, tile_size):
+    """Scatter a contiguous plane [B][Hkv][tiles * tile_size] into a pool of
+    n_pages pages (the inverse of pages_to_contiguous); pages no entry names
+    stay zero.  Returns [n_pages][Hkv][tile_size]."""
+    planes = np.asarray(planes)
+    table = np.asarray(table)
+    B, H = planes.shape[:2]
+    tiles = table.shape[1]
+    src = planes.reshape(B, H, tiles, tile_size)
+    pool = np.zeros((n_pages, H, tile_size), planes.dtype)
+    for b in range(B):
+        for t in range(tiles):
+            page = int(table[b, t])
+            if page >= 0:
+                pool[page] = src[b, :, t, :]
+    return pool

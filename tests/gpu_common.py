@@ -7,8 +7,8 @@ import numpy as np
 import torch
 
 import decode_attention_rotate_amd as kvq
-from oracle import OracleCache, decode_reference
-from oracle.blockquant import bf16_bits_to_f32
+from oracle import OracleCache, decode_reference, pages_to_contiguous, padded_row_bytes
+from oracle.blockquant import bf16_bits_to_f32, v_tile_bytes
 
 DEV = "cuda"
 
@@ -31,16 +31,25 @@ def to_values(x, dtype):
     return bf16_bits_to_f32(x) if dtype == "bf16" else np.asarray(x, np.float32)
 
 
-def gpu_planes(cache, cfg):
-    """Device planes as numpy arrays shaped like OracleCache.physical()."""
+def gpu_planes(cache, cfg, table=None):
+    """Device planes as numpy arrays shaped like OracleCache.physical(); a
+    paged cache's pool is gathered into that layout through `table` (numpy
+    [B][tiles], -1 for tiles that hold no positions)."""
     B, H, d, T = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.tail_len
     cap = (cfg.max_ctx + 63) // 64 * 64
     out = {}
     for p in ("k", "v"):
+        bits = cfg.k_bits if p == "k" else cfg.v_bits
+        minf = cfg.k_min if p == "k" else cfg.v_min
         codes = cache[p + "_codes"].cpu().numpy()
+        scales = cache[p + "_scales"].cpu().numpy().view(np.uint16)
+        if cfg.page_pool > 0:
+            ct = 64 * padded_row_bytes(d, bits) if p == "k" else v_tile_bytes(d, bits)
+            codes = pages_to_contiguous(codes, table, H, ct)
+            scales = pages_to_contiguous(scales, table, H, 64 * (d // 32) * (2 if minf else 1))
         out[p + "_codes"] = codes.reshape(B, H, -1)
         # one fp16 per block, or an (s, m) pair for scale-and-min blocks
-        out[p + "_scales"] = cache[p + "_scales"].cpu().numpy().view(np.uint16).reshape(B, H, cap, -1)
+        out[p + "_scales"] = scales.reshape(B, H, cap, -1)
         if T > 0:
             out[p + "_tail"] = cache[p + "_tail"].cpu().numpy().view(np.uint16).reshape(B, H, T, d)
         else:
@@ -52,10 +61,15 @@ class Pair:
     """A device cache and the oracle cache fed the same appends."""
 
     def __init__(self, B, H, d, kb, vb, T, max_ctx, rotate_k=True, rotate_v=True, sign_seed=0,
-                 k_min=False, v_min=False):
+                 k_min=False, v_min=False, page_pool=0, table=None):
         self.cfg = kvq.kvq_config(B, H, d, max_ctx, kb, vb, T, rotate_k, rotate_v, sign_seed,
-                                  k_min, v_min)
-        self.cache = kvq.KVCache(self.cfg, DEV)
+                                  k_min, v_min, page_pool)
+        self.table = None
+        dev_table = None
+        if page_pool > 0:
+            self.table = np.asarray(table, dtype=np.int32)
+            dev_table = torch.from_numpy(self.table).to(DEV)
+        self.cache = kvq.KVCache(self.cfg, DEV, page_table=dev_table)
         self.orc = OracleCache(B, H, d, kb, vb, T, max_ctx, rotate_k, rotate_v, sign_seed,
                                k_min, v_min)
         self.lens = np.zeros(B, dtype=np.int64)
@@ -70,7 +84,7 @@ class Pair:
         self.lens = lens + k.shape[1]
 
     def compare_planes(self):
-        got = gpu_planes(self.cache, self.cfg)
+        got = gpu_planes(self.cache, self.cfg, self.table)
         want = self.orc.physical()
         for key in want:
             a, b = got[key], want[key]

@@ -203,11 +203,64 @@ def test_plane_bytes_scale_and_min(d):
 
 
 def test_config_layout_and_sign_seed():
-    # twelve 32-bit fields: sign_seed, then k_min, v_min last; all 0 by
-    # default (plain Sylvester matrix, absmax blocks)
-    assert ctypes.sizeof(_capi.KvqConfig) == 48
+    # thirteen 32-bit fields: sign_seed, then k_min, v_min, page_pool last;
+    # all 0 by default (plain Sylvester matrix, absmax blocks, contiguous)
+    assert ctypes.sizeof(_capi.KvqConfig) == 52
     assert _capi.KvqConfig.sign_seed.offset == 36 and _capi.KvqConfig.v_min.offset == 44
+    assert _capi.KvqConfig.page_pool.offset == 48
     c = kvq.kvq_config_default(1, 1, 128, 64)
-    assert c.sign_seed == 0 and c.k_min == 0 and c.v_min == 0
+    assert c.sign_seed == 0 and c.k_min == 0 and c.v_min == 0 and c.page_pool == 0
     c2 = kvq.kvq_config(1, 1, 128, 64, sign_seed=0xFFFFFFFF)
     assert c2.sign_seed == 0xFFFFFFFF
+
+
+def test_cache_struct_layout():
+    # six plane pointers, then the page table
+    assert ctypes.sizeof(_capi.KvqCache) == 7 * 8
+    assert _capi.KvqCache.page_table.offset == 48
+
+
+@pytest.mark.parametrize("d,kb,vb,km", [(64, 4, 4, 0), (128, 8, 4, 0), (192, 5, 6, 0),
+                                        (256, 5, 4, 1)])
+def test_plane_bytes_paged(d, kb, vb, km):
+    # a pool of P pages holds P tiles of 64 positions per KV head; the tail
+    # planes keep their per-sequence size
+    B, H, T, P = 3, 2, 16, 37
+    flat = kvq.kvq_config(B, H, d, 1000, kb, vb, T, k_min=km)
+    paged = kvq.kvq_config(B, H, d, 1000, kb, vb, T, k_min=km, page_pool=P)
+    tiles = (1000 + 63) // 64
+    for plane in (kvq.KVQ_K_CODES, kvq.KVQ_V_CODES, kvq.KVQ_K_SCALES, kvq.KVQ_V_SCALES):
+        per_tile = kvq.kvq_plane_bytes(flat, plane) // (B * H * tiles)
+        assert kvq.kvq_plane_bytes(flat, plane) == B * H * tiles * per_tile
+        assert kvq.kvq_plane_bytes(paged, plane) == P * H * per_tile
+    for plane in (kvq.KVQ_K_TAIL, kvq.KVQ_V_TAIL):
+        assert kvq.kvq_plane_bytes(paged, plane) == kvq.kvq_plane_bytes(flat, plane) == B * H * T * d * 2
+    assert kvq.page_table_tiles(paged) == tiles
+
+
+def _paged_cache(table):
+    c = _cache()
+    c.page_table = table
+    return c
+
+
+def test_paged_validation():
+    c = kvq.kvq_config(2, 2, 128, 100, 4, 4, 0, page_pool=8)
+    bad = kvq.kvq_config_default(2, 2, 128, 100)
+    bad.page_pool = -1
+    assert kvq.kvq_config_check(bad) == _capi.KVQ_ERR_INVALID
+    assert kvq.kvq_plane_bytes(bad, kvq.KVQ_K_CODES) == 0
+    # no page table, or one not 4-byte aligned: rejected before any launch
+    assert _append(c, _paged_cache(0), 1, _lens(0, 0)) == _capi.KVQ_ERR_INVALID
+    assert _append(c, _paged_cache(FAKE + 2), 1, _lens(0, 0)) == _capi.KVQ_ERR_ALIGN
+    assert _decode(c, 4, _lens(1, 1), cache=_paged_cache(0)) == _capi.KVQ_ERR_INVALID
+    assert _decode(c, 4, _lens(1, 1), cache=_paged_cache(FAKE + 1)) == _capi.KVQ_ERR_ALIGN
+    out = FAKE
+    assert L.kvq_dequantize(ctypes.byref(c), ctypes.byref(_paged_cache(0)), 0, 0, 0, 1,
+                            _lens(1, 1), 0, out, None) == _capi.KVQ_ERR_INVALID
+    # a table 4-byte aligned but not 16 is accepted (validation passes; n_new = 0
+    # queues nothing)
+    assert _append(c, _paged_cache(FAKE + 4), 0, _lens(0, 0)) == _capi.KVQ_OK
+    # the table is ignored by contiguous caches
+    flat = kvq.kvq_config(2, 2, 128, 100, 4, 4, 0)
+    assert _append(flat, _paged_cache(0), 0, _lens(0, 0)) == _capi.KVQ_OK
