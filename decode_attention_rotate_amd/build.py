@@ -35,11 +35,13 @@ def units():
     for name in ("append.hip", "dequant.hip", "decode_main.hip"):
         out.append((os.path.join(CSRC, name), name.replace(".hip", ".o"), DEVICE))
     # K formats: (bits, scale-and-min) for q4_0 q5_0 q6_0 q8_0 q4_1 q5_1
-    for d in (256, 192, 128, 64):     # the slowest units first
+    # (head_dim 256 also builds its paged-layout kernels as units of their own)
+    for d, paged in ((256, 0), (256, 1), (192, 0), (128, 0), (64, 0)):   # the slowest first
         for kb, km in ((4, 0), (5, 0), (6, 0), (8, 0), (4, 1), (5, 1)):
-            out.append((os.path.join(CSRC, "decode_inst.hip"), "decode_d%d_k%d_m%d.o" % (d, kb, km),
+            out.append((os.path.join(CSRC, "decode_inst.hip"),
+                        "decode_d%d_k%d_m%d%s.o" % (d, kb, km, "_paged" if paged else ""),
                         DEVICE + ["-DKVQ_INST_D=%d" % d, "-DKVQ_INST_KB=%d" % kb,
-                                  "-DKVQ_INST_KM=%d" % km]))
+                                  "-DKVQ_INST_KM=%d" % km] + (["-DKVQ_INST_PAGED=1"] if paged else [])))
     out.append((os.path.join(CSRC, "kvq_host.cpp"), "kvq_host.o", DEVICE + ["-x", "hip"]))
     return out
 

@@ -17,14 +17,31 @@
 
 #define KVQ_CAT2(a, b, c, d) a##_##b##_##c##_##d
 #define KVQ_CAT(a, b, c, d) KVQ_CAT2(a, b, c, d)
-#define KVQ_TABLE KVQ_CAT(kvq_decode_table, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
-#define KVQ_PF_TABLE KVQ_CAT(kvq_prefill_table, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
 
 namespace kvq {
 
 constexpr bool kKM = KVQ_INST_KM != 0;
 
-#define KVQ_L(VB, VM, G) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, G, false, kKM, VM>
+// head_dim 256 builds the contiguous and the paged layouts as separate
+// kernels (KVQ_INST_PAGED selects the paged tables); other sizes decide the
+// layout at run time.
+#if KVQ_INST_D == 256
+#ifdef KVQ_INST_PAGED
+constexpr int kPGM = kPagePaged;
+#define KVQ_TABLE KVQ_CAT(kvq_decode_ptable, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
+#define KVQ_PF_TABLE KVQ_CAT(kvq_prefill_ptable, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
+#else
+constexpr int kPGM = kPageFlat;
+#endif
+#else
+constexpr int kPGM = kPageAny;
+#endif
+#ifndef KVQ_TABLE
+#define KVQ_TABLE KVQ_CAT(kvq_decode_table, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
+#define KVQ_PF_TABLE KVQ_CAT(kvq_prefill_table, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
+#endif
+
+#define KVQ_L(VB, VM, G) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, G, false, kKM, VM, kPGM>
 #define KVQ_ROW(VB, VM) \
   {KVQ_L(VB, VM, 1), KVQ_L(VB, VM, 2), KVQ_L(VB, VM, 3), KVQ_L(VB, VM, 4), \
    KVQ_L(VB, VM, 5), KVQ_L(VB, VM, 6), KVQ_L(VB, VM, 7), KVQ_L(VB, VM, 8)}
@@ -34,7 +51,7 @@ DecodeLauncher KVQ_TABLE[6][8] = {KVQ_ROW(4, false), KVQ_ROW(5, false), KVQ_ROW(
                                   KVQ_ROW(8, false), KVQ_ROW(4, true), KVQ_ROW(5, true)};
 
 // chunked prefill, same V order
-#define KVQ_P(VB, VM) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8, true, kKM, VM>
+#define KVQ_P(VB, VM) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8, true, kKM, VM, kPGM>
 DecodeLauncher KVQ_PF_TABLE[6] = {KVQ_P(4, false), KVQ_P(5, false), KVQ_P(6, false),
                                   KVQ_P(8, false), KVQ_P(4, true), KVQ_P(5, true)};
 

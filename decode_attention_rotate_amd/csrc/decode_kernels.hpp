@@ -238,7 +238,10 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, u
 // n - n_q + i and sees positions up to there.  All waves of a workgroup walk
 // the same tiles, so each cache byte comes from HBM once per workgroup (the
 // other waves find it in L1 / L2).
-template <int D, int KB, int VB, int G, bool PF, bool KM, bool VM>
+// PGM: where tiles live.  kPageAny decides at run time between contiguous
+// and paged planes; kPageFlat and kPagePaged fix it at compile time, for the
+// variants whose register budget is too tight to carry both.
+template <int D, int KB, int VB, int G, bool PF, bool KM, bool VM, int PGM>
 __global__ __launch_bounds__(64 * split_group_waves(D, KM || VM || PF))
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D, KM || VM || PF),
                                    split_waves_per_simd(D, KM || VM || PF))))
@@ -250,11 +253,12 @@ void decode_split_kernel(DecodeArgs a) {
   // at one wave per SIMD (d = 256) the wave alone must cover the latency, so
   // it keeps two where four step buffers fit the 512 registers with at most
   // a few spilled (4-bit K, or 4-bit V with 5- or 8-bit K; decode only, a
-  // prefill wave holds more state).  The one-wave d = 192 variants measured
-  // no faster with two.
+  // prefill wave holds more state; contiguous planes only, a paged wave also
+  // carries its page lookups and then spilled inside the loop).  The
+  // one-wave d = 192 variants measured no faster with two.
   constexpr int kAhead =
       split_waves_per_simd(D, KM || VM || PF) == 1 && D == 256 && !PF && !KM && !VM &&
-              (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
+              PGM != kPagePaged && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
   constexpr int NSW = (NB + 1) / 2;
@@ -592,11 +596,36 @@ void decode_split_kernel(DecodeArgs a) {
     const uint32_t v_off = (uint32_t)(lane * NN * (VB == 8 ? 8 : 4));
     const uint32_t vh_off = (uint32_t)(32 * D + lane * NN);
 
-    // tile of position s0: its slot in the (contiguous or paged) planes
+    // Slot of position s0's tile in the contiguous or paged planes (see
+    // tile_slot).  A paged cache's entry is read through the scalar cache
+    // (the table is read-only while the kernel runs), so the lookup holds no
+    // vector register and waits for no tile load; consecutive tiles share
+    // its cache line.
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    // contiguous planes of this (b, g)
+    const uint8_t* kpl = a.k_codes + unit * (size_t)a.cap * RKP;
+    const uint16_t* ksc = a.k_scales + unit * (size_t)a.cap * KSE;
+    const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
+    const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * VSE;
     auto load_step = [&](Regs& R, int s0) {
       const int j2 = (s0 / kStep) & 1;
-      const size_t slot = tile_slot_read(a.map, b, g, s0 / kTile);
-      const uint8_t* kt = a.k_codes + slot * (kTile * RKP) + j2 * kStep * kChunk;
+      // s0's K and V tiles and its row of each scale plane
+      const uint8_t* ktile = kpl + (size_t)(s0 / kTile) * kTile * RKP;
+      const uint8_t* vt = vpl + (size_t)(s0 / kTile) * VTB;
+      const uint16_t* ksrow = ksc;
+      const uint16_t* vsrow = vsc;
+      int srow = s0;   // scale row of s0 from ksrow / vsrow
+      if (PGM == kPagePaged || (PGM == kPageAny && a.map.ptab != nullptr)) {
+        const int page = ((const_i32*)a.map.ptab)[(size_t)b * a.map.tiles + s0 / kTile];
+        const size_t slot =
+            (unsigned)page < (unsigned)a.map.n_pages ? (size_t)page * a.map.Hkv + g : (size_t)g;
+        ktile = a.k_codes + slot * (kTile * RKP);
+        vt = a.v_codes + slot * VTB;
+        ksrow = a.k_scales + slot * kTile * KSE;
+        vsrow = a.v_scales + slot * kTile * VSE;
+        srow = s0 % kTile;
+      }
+      const uint8_t* kt = ktile + j2 * kStep * kChunk;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
@@ -617,11 +646,10 @@ void decode_split_kernel(DecodeArgs a) {
             }
           }
         }
-        const size_t tok = slot * kTile + (s0 % kTile) + 16 * m + col;
-        load_words(reinterpret_cast<const uint32_t*>(a.k_scales + tok * KSE), R.ks[m]);
-        load_words(reinterpret_cast<const uint32_t*>(a.v_scales + tok * VSE), R.vs[m]);
+        const size_t tok = (size_t)srow + 16 * m + col;
+        load_words(reinterpret_cast<const uint32_t*>(ksrow + tok * KSE), R.ks[m]);
+        load_words(reinterpret_cast<const uint32_t*>(vsrow + tok * VSE), R.vs[m]);
       }
-      const uint8_t* vt = a.v_codes + slot * VTB;
       const uint8_t* vj = vt + (size_t)j2 * 64 * NN * (VB == 8 ? 8 : 4) + v_off;
 #pragma unroll
       for (int q = 0; q < (VB == 8 ? NN / 2 : NN / 4); ++q) R.v[q] = reinterpret_cast<const u32x4*>(vj)[q];
@@ -912,10 +940,11 @@ void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int KB, int VB, int G, bool PF = false, bool KM = false, bool VM = false>
+template <int D, int KB, int VB, int G, bool PF = false, bool KM = false, bool VM = false,
+          int PGM = kPageAny>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM>), grid,
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM, PGM>), grid,
                      dim3(64 * split_group_waves(D, KM || VM || PF)), 0, s, a);
   return hipGetLastError();
 }

@@ -18,6 +18,9 @@ namespace kvq {
 #define KVQ_ALL_K(X, D) X(D, 4, 0) X(D, 5, 0) X(D, 6, 0) X(D, 8, 0) X(D, 4, 1) X(D, 5, 1)
 KVQ_ALL_K(KVQ_DECLARE_TABLE, 64) KVQ_ALL_K(KVQ_DECLARE_TABLE, 128)
 KVQ_ALL_K(KVQ_DECLARE_TABLE, 192) KVQ_ALL_K(KVQ_DECLARE_TABLE, 256)
+#define KVQ_DECLARE_PTABLE(D, KB, KM) extern DecodeLauncher kvq_decode_ptable_##D##_##KB##_##KM[6][8]; \
+  extern DecodeLauncher kvq_prefill_ptable_##D##_##KB##_##KM[6];
+KVQ_ALL_K(KVQ_DECLARE_PTABLE, 256)
 #undef KVQ_DECLARE_TABLE
 
 namespace {
@@ -27,9 +30,16 @@ int v_index(int vb, bool vm) {
 }
 }  // namespace
 
-DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm) {
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, bool paged) {
   const int vi = v_index(vb, vm);
   if (vi < 0 || gc < 1 || gc > 8) return nullptr;
+  if (paged && split_fixed_layout(D)) {
+#define KVQ_PICK(DD, KK, MM) \
+  if (D == DD && kb == KK && (int)km == MM) return kvq_decode_ptable_##DD##_##KK##_##MM[vi][gc - 1];
+    KVQ_ALL_K(KVQ_PICK, 256)
+#undef KVQ_PICK
+    return nullptr;
+  }
 #define KVQ_PICK(DD, KK, MM) \
   if (D == DD && kb == KK && (int)km == MM) return kvq_decode_table_##DD##_##KK##_##MM[vi][gc - 1];
   KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 192) KVQ_ALL_K(KVQ_PICK, 256)
@@ -37,9 +47,16 @@ DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm) 
   return nullptr;
 }
 
-DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm) {
+DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm, bool paged) {
   const int vi = v_index(vb, vm);
   if (vi < 0) return nullptr;
+  if (paged && split_fixed_layout(D)) {
+#define KVQ_PICK(DD, KK, MM) \
+  if (D == DD && kb == KK && (int)km == MM) return kvq_prefill_ptable_##DD##_##KK##_##MM[vi];
+    KVQ_ALL_K(KVQ_PICK, 256)
+#undef KVQ_PICK
+    return nullptr;
+  }
 #define KVQ_PICK(DD, KK, MM) \
   if (D == DD && kb == KK && (int)km == MM) return kvq_prefill_table_##DD##_##KK##_##MM[vi];
   KVQ_ALL_K(KVQ_PICK, 64) KVQ_ALL_K(KVQ_PICK, 128) KVQ_ALL_K(KVQ_PICK, 192) KVQ_ALL_K(KVQ_PICK, 256)

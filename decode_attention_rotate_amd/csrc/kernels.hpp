@@ -82,11 +82,17 @@ struct DecodeArgs {
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
+// Page modes of the split kernel: tiles found at run time in contiguous or
+// paged planes (kPageAny), or fixed at compile time.  head_dim 256 builds
+// kPageFlat and kPagePaged: its two-tile pipeline fills the register file,
+// and carrying both layouts spilled a tile address into the loop.
+constexpr int kPageAny = 0, kPageFlat = 1, kPagePaged = 2;
+constexpr bool split_fixed_layout(int D) { return D == 256; }
 // Table lookup for (D, k_bits, v_bits, heads per chunk, K / V scale-and-min
-// blocks); nullptr if absent.
-DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm);
-// The prefill variant of the split kernel for (D, k_bits, v_bits, km, vm).
-DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm);
+// blocks, paged planes); nullptr if absent.
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, bool paged);
+// The prefill variant of the split kernel for (D, k_bits, v_bits, km, vm, paged).
+DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm, bool paged);
 
 // Largest split count the host schedules (bounds the combine kernel's LDS).
 constexpr int kMaxSplitsDevice = 1024;

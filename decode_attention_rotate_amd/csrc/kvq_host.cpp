@@ -305,7 +305,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   const Schedule sc = schedule(c, n_q_heads, max_len);
   const WsLayout wl = ws_layout(c, n_q_heads, sc.S);
   if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
-  const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc, c.k_min != 0, c.v_min != 0);
+  const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc, c.k_min != 0,
+                                            c.v_min != 0, c.page_pool > 0);
   if (!fn) return KVQ_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -388,7 +389,8 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   if ((int64_t)c.n_kv_heads * ps.n_rb > 65535) return KVQ_ERR_INVALID;
   const WsLayout wl = ws_layout(c, n_q * n_q_heads, ps.S);
   if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
-  const DecodeLauncher fn = prefill_launcher(c.head_dim, c.k_bits, c.v_bits, c.k_min != 0, c.v_min != 0);
+  const DecodeLauncher fn = prefill_launcher(c.head_dim, c.k_bits, c.v_bits, c.k_min != 0,
+                                             c.v_min != 0, c.page_pool > 0);
   if (!fn) return KVQ_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -118,7 +118,9 @@ def test_paged_decode_attention(case):
     assert worst <= TOL
 
 
-def test_paged_ragged_lengths_share_a_pool():
+@pytest.mark.parametrize("name,over", [("long", dict(Hq=10, tail=32)),
+                                       ("huge", dict(Hq=8, tail=0))], ids=["d128-k8v4-T32", "d256-k5v4"])
+def test_paged_ragged_lengths_share_a_pool(name, over):
     """Sequences of very different lengths in a pool smaller than the
     contiguous layout would need (the point of paging), each appended on its
     own through a one-sequence view; decode and prefill over the whole
@@ -126,7 +128,7 @@ def test_paged_ragged_lengths_share_a_pool():
     import torch
     import decode_attention_rotate_amd as kvq
     from oracle import OracleCache
-    w = workloads.workload("long", B=3, Hq=10, Hkv=2, tail=32)
+    w = workloads.workload(name, B=3, Hkv=2, **over)
     B, H, d, T, kb, vb = 3, 2, w["d"], w["tail"], w["k_bits"], w["v_bits"]
     lens = [700, 64, 230]
     max_ctx = 1000
@@ -169,6 +171,7 @@ def test_paged_ragged_lengths_share_a_pool():
     say("paged prefill n_q=%d lens=%s" % (n_q, lens))
     pre = kvq.kvq_prefill_attention(cfg, cache, to_device(qp, w["dtype"]), lens).cpu().numpy()
     ref = prefill_reference(planes, to_values(qp, w["dtype"]), lens, H, d, kb, vb, T)
+    torch.cuda.synchronize()
     err = np.linalg.norm(pre - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
     say("paged prefill worst rel L2 %.3e" % err.max())
     assert err.max() <= TOL
