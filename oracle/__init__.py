@@ -21,6 +21,9 @@ What the oracle computes, and where each step comes from:
   detail section on tail length.
 * Paged planes (pages_to_contiguous): a storage layout the pages do not
   describe (reading R24); the functions only move whole 64-position tiles.
+* Outlier channels at 8 bits (oracle.outliers, reading R25): the mixed
+  precision the velog.io post names in section "application and
+  background".  The GPU path does not build it yet.
 
 Everything the pages leave open (Hadamard ordering, fp32 association of the
 transform, rounding of the scale, code encoding, memory layout) is a stated
