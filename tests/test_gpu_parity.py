@@ -324,3 +324,23 @@ def test_prefill_one_query_and_rotation_off():
                             list(pair2.lens), 8, 128, 8, 8, 0, rotate_k=False, rotate_v=False)
     err = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
     assert err.max() <= TOL, err.max()
+
+
+def test_decode_at_the_largest_batch():
+    """KVQ_MAX_BATCH sequences of ragged lengths (1 .. 300) in one call: the
+    length array and the grid at their largest; without a tail, positions
+    past a sequence's length are never read."""
+    import decode_attention_rotate_amd as kvq
+    B = kvq.KVQ_MAX_BATCH
+    w = workloads.workload("tiny", B=B, Hq=2, Hkv=1, dtype="bf16")
+    lens = [1 + (37 * b) % 300 for b in range(B)]
+    pair = Pair(B, 1, 64, 4, 4, 0, 320)
+    pair.append(workloads.kv_numpy(w, 1, 0, max(lens)), workloads.kv_numpy(w, 2, 0, max(lens)),
+                "bf16")
+    q = workloads.q_numpy(w)
+    got = pair.decode(q, "bf16", lens=lens)
+    planes = gpu_planes(pair.cache, pair.cfg)
+    errs = attention_errors(got, planes, to_values(q, "bf16"), lens, pair.cfg)
+    worst = max(errs.values())
+    say("largest batch worst rel L2 %.3e" % worst)
+    assert worst <= TOL
