@@ -234,7 +234,11 @@ __device__ inline AppendRange append_range(const AppendArgs& a, int b) {
 
 // Quantize the positions of block bx of [q0 & ~7, q1) (RPB per block) for
 // plane pl of (b, g).  Called by all 256 threads; contains barriers.
-template <int D>
+// FAST: both planes use absmax blocks, whose codes and scales do not see the
+// sign of a zero, so the rotation may take its one-instruction cross-lane
+// stages (rotate_row_for_absmax); scale-and-min blocks see it in their
+// minimum.
+template <int D, bool FAST>
 __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, uint8_t* vlds) {
   constexpr int LPR = D / kBlock;
   constexpr int RPB = rows_per_block(D);   // positions per block, a multiple of 8
@@ -268,7 +272,8 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
   // every lane takes part in the cross-lane stages
   if (a.rotate[pl]) {
     if (a.has_signs) apply_signs(x, a.signs[j]);
-    rotate_row<D>(x, lane, a.cd);
+    if constexpr (FAST) rotate_row_for_absmax<D>(x, lane, a.cd);
+    else rotate_row<D>(x, lane, a.cd);
   }
   if (T > 0) {
 #pragma unroll
@@ -360,10 +365,10 @@ __device__ void tail_part(const AppendArgs& a, int bx, int g, int b, int pl) {
   }
 }
 
-template <int D>
+template <int D, bool FAST>
 __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a) {
   __shared__ __align__(16) uint8_t vlds[256 * kBlock];
-  quant_part<D>(a, blockIdx.x, blockIdx.y, blockIdx.z >> 1, blockIdx.z & 1, vlds);
+  quant_part<D, FAST>(a, blockIdx.x, blockIdx.y, blockIdx.z >> 1, blockIdx.z & 1, vlds);
 }
 
 template <int D>
@@ -373,11 +378,11 @@ __global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
 
 // Appends small enough for one block per (b, g, plane): quantize, then (after
 // a barrier, so every displaced slot has been read) write the tail.
-template <int D>
+template <int D, bool FAST>
 __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   __shared__ __align__(16) uint8_t vlds[256 * kBlock];
   const int g = blockIdx.y, b = blockIdx.z >> 1, pl = blockIdx.z & 1;
-  quant_part<D>(a, 0, g, b, pl, vlds);
+  quant_part<D, FAST>(a, 0, g, b, pl, vlds);
   __syncthreads();
   if (a.T > 0) tail_part<D>(a, 0, g, b, pl);
 }
@@ -390,7 +395,8 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
 // items the quantized codes merge into) is issued before any arithmetic, so
 // the wave waits for memory once; the new row overwrites the ring slot the
 // leaving row was read from only after a barrier.
-template <int D, int VB>
+// FAST: no tail and absmax blocks in both planes (see quant_part).
+template <int D, int VB, bool FAST>
 __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   constexpr int LPR = D / kBlock;
   const int lane = threadIdx.x;
@@ -476,7 +482,8 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   }
   if (a.rotate[pl]) {                            // every lane takes part
     if (a.has_signs) apply_signs(x, a.signs[j]);
-    rotate_row<D>(x, lane, a.cd);
+    if constexpr (FAST) rotate_row_for_absmax<D>(x, lane, a.cd);
+    else rotate_row<D>(x, lane, a.cd);
   }
   if (q_lane) {
     float z[32];
@@ -527,19 +534,30 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
 template <int D>
 hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
   constexpr int RPB = rows_per_block(D);
+  const bool absmax = !a.minf[0] && !a.minf[1];
   if (a.n_new == 1) {
     const dim3 grid(a.Hkv, B, 2), block(64);
-    switch (a.bits[1]) {
-      case 4: hipLaunchKernelGGL((append_one_kernel<D, 4>), grid, block, 0, s, a); break;
-      case 5: hipLaunchKernelGGL((append_one_kernel<D, 5>), grid, block, 0, s, a); break;
-      case 6: hipLaunchKernelGGL((append_one_kernel<D, 6>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((append_one_kernel<D, 8>), grid, block, 0, s, a); break;
+    if (absmax && a.T == 0) {
+      switch (a.bits[1]) {
+        case 4: hipLaunchKernelGGL((append_one_kernel<D, 4, true>), grid, block, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((append_one_kernel<D, 5, true>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((append_one_kernel<D, 6, true>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((append_one_kernel<D, 8, true>), grid, block, 0, s, a); break;
+      }
+    } else {
+      switch (a.bits[1]) {
+        case 4: hipLaunchKernelGGL((append_one_kernel<D, 4, false>), grid, block, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((append_one_kernel<D, 5, false>), grid, block, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((append_one_kernel<D, 6, false>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((append_one_kernel<D, 8, false>), grid, block, 0, s, a); break;
+      }
     }
     return hipGetLastError();
   }
   if (a.n_new <= RPB - 7) {
     // [q0 & ~7, q1) spans at most n_new + 7 positions and the tail at most n_new
-    hipLaunchKernelGGL(append_small_kernel<D>, dim3(1, a.Hkv, 2 * B), dim3(256), 0, s, a);
+    if (absmax) hipLaunchKernelGGL((append_small_kernel<D, true>), dim3(1, a.Hkv, 2 * B), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((append_small_kernel<D, false>), dim3(1, a.Hkv, 2 * B), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   int quant_blocks = 0;
@@ -549,8 +567,11 @@ hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
     const int q1 = a.T > 0 ? max(0, n1 - a.T) : n1;
     if (q1 > q0) quant_blocks = max(quant_blocks, (q1 - (q0 & ~7) + RPB - 1) / RPB);
   }
-  if (quant_blocks > 0)
-    hipLaunchKernelGGL(append_quant_kernel<D>, dim3(quant_blocks, a.Hkv, 2 * B), dim3(256), 0, s, a);
+  if (quant_blocks > 0) {
+    const dim3 grid(quant_blocks, a.Hkv, 2 * B);
+    if (absmax) hipLaunchKernelGGL((append_quant_kernel<D, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((append_quant_kernel<D, false>), grid, dim3(256), 0, s, a);
+  }
   const int n_tail = a.T > 0 ? min(a.n_new, a.T) : 0;
   if (n_tail > 0)
     hipLaunchKernelGGL(append_tail_kernel<D>, dim3((n_tail + RPB - 1) / RPB, a.Hkv, 2 * B),

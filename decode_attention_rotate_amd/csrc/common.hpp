@@ -134,6 +134,51 @@ __device__ inline void fwht_cross_stage(float (&x)[32], int lane) {
   }
 }
 
+// The same stage in one instruction per element (lane distances 1 and 2):
+// v_fmac_f32 with a DPP operand computes own + s * partner, s = +1 on the
+// lower lane and -1 on the upper one, rounding once like the add.  The upper
+// lane gets a_high - b_low, the negation of the butterfly's value, so the
+// stored values carry a per-lane sign (the product of the stages' flips,
+// shared by the partners of later stages), which the final multiply removes.
+// Nonzero results are bit for bit those of the plain stage; an exact zero
+// may come out with the other sign.  Only for values that go straight into
+// an absmax quantizer, whose codes and scales do not see the sign of a zero.
+// The compiler does not form this instruction from the intrinsics, so it is
+// written out; a DPP operand must not be read within two wait states of the
+// VALU write that produced it, hence the s_nop ahead of each group (inside a
+// group every instruction reads a register written before the group).
+#define KVQ_FMAC_DPP(PERM, I) "v_fmac_f32_dpp %" #I ", %" #I ", %16 " PERM " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+#define KVQ_FMAC_DPP16(PERM)                                                             \
+  "s_nop 1\n" KVQ_FMAC_DPP(PERM, 0) KVQ_FMAC_DPP(PERM, 1) KVQ_FMAC_DPP(PERM, 2)          \
+  KVQ_FMAC_DPP(PERM, 3) KVQ_FMAC_DPP(PERM, 4) KVQ_FMAC_DPP(PERM, 5) KVQ_FMAC_DPP(PERM, 6) \
+  KVQ_FMAC_DPP(PERM, 7) KVQ_FMAC_DPP(PERM, 8) KVQ_FMAC_DPP(PERM, 9)                      \
+  KVQ_FMAC_DPP(PERM, 10) KVQ_FMAC_DPP(PERM, 11) KVQ_FMAC_DPP(PERM, 12)                   \
+  KVQ_FMAC_DPP(PERM, 13) KVQ_FMAC_DPP(PERM, 14) KVQ_FMAC_DPP(PERM, 15)
+template <int M>
+__device__ inline void fwht_cross_stage_fma(float (&x)[32], int lane) {
+  static_assert(M == 1 || M == 2, "DPP quad permutations");
+  const float s = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int g = 0; g < 32; g += 16) {
+    float* y = x + g;
+    if constexpr (M == 1) {
+      asm(KVQ_FMAC_DPP16("quad_perm:[1,0,3,2]")
+          : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]),
+            "+v"(y[6]), "+v"(y[7]), "+v"(y[8]), "+v"(y[9]), "+v"(y[10]), "+v"(y[11]),
+            "+v"(y[12]), "+v"(y[13]), "+v"(y[14]), "+v"(y[15])
+          : "v"(s));
+    } else {
+      asm(KVQ_FMAC_DPP16("quad_perm:[2,3,0,1]")
+          : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]),
+            "+v"(y[6]), "+v"(y[7]), "+v"(y[8]), "+v"(y[9]), "+v"(y[10]), "+v"(y[11]),
+            "+v"(y[12]), "+v"(y[13]), "+v"(y[14]), "+v"(y[15])
+          : "v"(s));
+    }
+  }
+}
+#undef KVQ_FMAC_DPP16
+#undef KVQ_FMAC_DPP
+
 // Full transform of a d-element row spread over d/32 consecutive lanes, each
 // holding one 32-element block, followed by the normalization multiply.  At
 // head_dim 192 each pair of lanes (one H_64 block) is transformed on its own.
@@ -146,6 +191,22 @@ __device__ inline void rotate_row(float (&x)[32], int lane, float cd) {
   if constexpr (RB >= 256) fwht_cross_stage<4>(x, lane);
 #pragma unroll
   for (int i = 0; i < 32; ++i) x[i] = x[i] * cd;
+}
+
+// rotate_row for values that only feed an absmax quantizer: the cross-lane
+// stages at lane distances 1 and 2 take one instruction per element, and the
+// normalization multiply by +-fp32(1/sqrt(d)) removes their sign.  Equal to
+// rotate_row except possibly for the sign of exact zeros.
+template <int D>
+__device__ inline void rotate_row_for_absmax(float (&x)[32], int lane, float cd) {
+  constexpr int RB = rot_block(D);
+  fwht32_in_lane(x);
+  if constexpr (RB >= 64) fwht_cross_stage_fma<1>(x, lane);
+  if constexpr (RB >= 128) fwht_cross_stage_fma<2>(x, lane);
+  if constexpr (RB >= 256) fwht_cross_stage<4>(x, lane);
+  const float c = (__builtin_popcount(lane & (RB >= 128 ? 3 : 1)) & 1) ? -cd : cd;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = x[i] * c;
 }
 
 // Flip the sign of element i of a 32-element block where bit i of mask is
