@@ -666,15 +666,37 @@ void decode_split_kernel(DecodeArgs a) {
     };
 
     auto compute_step = [&](const Regs& R, int s0) {
-      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements
+      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements.
+      // Up to head_dim 128 (decode) all of them are issued before the first
+      // result is read, so their latencies overlap instead of each product
+      // waiting out the last one's (the registers allow it there).
       float sA[2] = {0.f, 0.f}, sB[2] = {0.f, 0.f};
+      constexpr bool kIssueAll = !kQX && NB <= 4;
+      i4_t dq[kIssueAll ? NB : 1][2];
+      if constexpr (kIssueAll) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const long kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
+            dq[j][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const long kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
-          const i4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-              qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+          i4_t d;
+          long kop = 0;
+          if constexpr (kIssueAll) {
+            d = dq[j][m];
+          } else {
+            kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
+            d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+          }
           const int vA = (d[0] << 8) + d[1];
           const int vB = (d[2] << 8) + d[3];
           const float ks = R.k_scale(m, j);
