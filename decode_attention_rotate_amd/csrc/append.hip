@@ -186,6 +186,17 @@ __device__ inline void store_v_item(uint8_t* tile, int item, uint64_t u, uint32_
       u = (u & ~keep) | (*dst & keep);
     }
     *dst = u;
+  } else if (BITS == 4 && mask == 0xFFu) {
+    // a whole group: gather the even slots' and the odd slots' bytes, fold
+    // each byte pair into one byte (slot codes < 16), and take bytes 0 and 2
+    // of both: nibbles 0-3 = slots 0, 2, 4, 6 and nibbles 4-7 = slots 1, 3,
+    // 5, 7, the order v_nibble gives
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const uint32_t ev = __builtin_amdgcn_perm(hi, lo, 0x06040200u);   // b0 b2 b4 b6
+    const uint32_t od = __builtin_amdgcn_perm(hi, lo, 0x07050301u);   // b1 b3 b5 b7
+    const uint32_t fe = ev | __builtin_amdgcn_alignbit(ev, ev, 4);
+    const uint32_t fo = od | __builtin_amdgcn_alignbit(od, od, 4);
+    reinterpret_cast<uint32_t*>(tile)[item] = __builtin_amdgcn_perm(fo, fe, 0x06040200u);
   } else {
     uint32_t w = 0, hi = 0, keep = 0, keep_hi = 0;
     constexpr int HB = BITS == 6 ? 2 : 1;          // high bits per slot
