@@ -666,13 +666,16 @@ void decode_split_kernel(DecodeArgs a) {
     };
 
     auto compute_step = [&](const Regs& R, int s0) {
-      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements.
-      // Up to head_dim 128 (decode) all of them are issued before the first
-      // result is read, so their latencies overlap instead of each product
-      // waiting out the last one's (the registers allow it there).
+      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements
+      // (twice that for prefill's 24-bit queries).  Up to head_dim 128 all of
+      // them are issued before the first result is read, so their latencies
+      // overlap instead of each product waiting out the last one's; the
+      // registers allow it there except for prefill with scale-and-min blocks
+      // or 5- and 6-bit K (their high-bit words), which then spilled.
       float sA[2] = {0.f, 0.f}, sB[2] = {0.f, 0.f};
-      constexpr bool kIssueAll = !kQX && NB <= 4;
+      constexpr bool kIssueAll = NB <= 4 && !(kQX && (KM || VM || KB == 5 || KB == 6));
       i4_t dq[kIssueAll ? NB : 1][2];
+      i4_t dr[kIssueAll && kQX ? NB : 1][2];
       if constexpr (kIssueAll) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -681,6 +684,9 @@ void decode_split_kernel(DecodeArgs a) {
             const long kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
             dq[j][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
                 qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+            if constexpr (kQX)
+              dr[j][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                  qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
           }
         }
       }
@@ -702,8 +708,13 @@ void decode_split_kernel(DecodeArgs a) {
           const float ks = R.k_scale(m, j);
           float fA = (float)vA, fB = (float)vB;
           if constexpr (kQX) {
-            const i4_t e = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+            i4_t e;
+            if constexpr (kIssueAll) {
+              e = dr[j][m];
+            } else {
+              e = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                  qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+            }
             fA = __builtin_fmaf((float)e[1], 0.00390625f, fA);
             fB = __builtin_fmaf((float)e[3], 0.00390625f, fB);
           }
