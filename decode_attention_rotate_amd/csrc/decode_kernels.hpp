@@ -575,7 +575,12 @@ void decode_split_kernel(DecodeArgs a) {
     long qop[NB];
     long qres[kQX ? NB : 1];
     float ckA, ckB;
-    i4_t cq[kOffset ? NB : 1];
+    // head_dim 256 keeps the correction as two integers per block, added to
+    // the combined sums (exact), to free registers for issuing the two token
+    // halves' products together
+    constexpr bool kCorrInt = kOffset && D == 256 && !kQX;
+    i4_t cq[kOffset && !kCorrInt ? NB : 1];
+    int ciA[kCorrInt ? NB : 1], ciB[kCorrInt ? NB : 1];
     i4_t cq2[kQX && kOffset ? NB : 1];
     // K minima: sum of the fixed-point query over each block, heads hA, hB
     float bsA[KM ? NB : 1], bsB[KM ? NB : 1];
@@ -674,6 +679,8 @@ void decode_split_kernel(DecodeArgs a) {
       // or 5- and 6-bit K (their high-bit words), which then spilled.
       float sA[2] = {0.f, 0.f}, sB[2] = {0.f, 0.f};
       constexpr bool kIssueAll = NB <= 4 && !(kQX && (KM || VM || KB == 5 || KB == 6));
+      // head_dim 256: the two token halves of one block together
+      constexpr bool kIssuePair = !kIssueAll && D == 256 && !kQX;
       i4_t dq[kIssueAll ? NB : 1][2];
       i4_t dr[kIssueAll && kQX ? NB : 1][2];
       if constexpr (kIssueAll) {
@@ -683,7 +690,7 @@ void decode_split_kernel(DecodeArgs a) {
           for (int m = 0; m < 2; ++m) {
             const long kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
             dq[j][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+                qop[j], kop, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
             if constexpr (kQX)
               dr[j][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
                   qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
@@ -696,15 +703,30 @@ void decode_split_kernel(DecodeArgs a) {
         for (int m = 0; m < 2; ++m) {
           i4_t d;
           long kop = 0;
-          if constexpr (kIssueAll) {
+          if constexpr (kIssuePair) {
+            if (m == 0) {
+#pragma unroll
+              for (int mm = 0; mm < 2; ++mm) {
+                const long kp = k_operand<D, KB, VB, KM, VM>(R, mm * NB + j, rot_lo, rot_hi);
+                dq[0][mm] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                    qop[j], kp, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0},
+                    0, 0, 0);
+              }
+            }
+            d = dq[0][m];
+          } else if constexpr (kIssueAll) {
             d = dq[j][m];
           } else {
             kop = k_operand<D, KB, VB, KM, VM>(R, m * NB + j, rot_lo, rot_hi);
             d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                qop[j], kop, kOffset ? cq[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+                qop[j], kop, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
           }
-          const int vA = (d[0] << 8) + d[1];
-          const int vB = (d[2] << 8) + d[3];
+          int vA = (d[0] << 8) + d[1];
+          int vB = (d[2] << 8) + d[3];
+          if constexpr (kCorrInt) {
+            vA += ciA[j];
+            vB += ciB[j];
+          }
           const float ks = R.k_scale(m, j);
           float fA = (float)vA, fB = (float)vB;
           if constexpr (kQX) {
@@ -856,7 +878,13 @@ void decode_split_kernel(DecodeArgs a) {
           bsum += __shfl_xor(bsum, 16);
           bsum += __shfl_xor(bsum, 32);
           const int corr = -(1 << (KB - 1)) * bsum;
-          cq[j] = i4_t{0, okA ? __shfl(corr, 4 * r) : 0, 0, okB ? __shfl(corr, 4 * r + 2) : 0};
+          const int cA = okA ? __shfl(corr, 4 * r) : 0, cB = okB ? __shfl(corr, 4 * r + 2) : 0;
+          if constexpr (kCorrInt) {
+            ciA[j] = cA;
+            ciB[j] = cB;
+          } else {
+            cq[j] = i4_t{0, cA, 0, cB};
+          }
           if constexpr (kQX) {
             rsum += __shfl_xor(rsum, 16);
             rsum += __shfl_xor(rsum, 32);
