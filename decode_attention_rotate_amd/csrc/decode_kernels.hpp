@@ -578,7 +578,7 @@ void decode_split_kernel(DecodeArgs a) {
     // head_dim 256 keeps the correction as two integers per block, added to
     // the combined sums (exact), to free registers for issuing the two token
     // halves' products together
-    constexpr bool kCorrInt = kOffset && D == 256 && !kQX;
+    constexpr bool kCorrInt = kOffset && D >= 192 && !kQX;
     i4_t cq[kOffset && !kCorrInt ? NB : 1];
     int ciA[kCorrInt ? NB : 1], ciB[kCorrInt ? NB : 1];
     i4_t cq2[kQX && kOffset ? NB : 1];
@@ -680,7 +680,7 @@ void decode_split_kernel(DecodeArgs a) {
       float sA[2] = {0.f, 0.f}, sB[2] = {0.f, 0.f};
       constexpr bool kIssueAll = NB <= 4 && !(kQX && (KM || VM || KB == 5 || KB == 6));
       // head_dim 256: the two token halves of one block together
-      constexpr bool kIssuePair = !kIssueAll && D == 256 && !kQX;
+      constexpr bool kIssuePair = !kIssueAll && D >= 192 && !kQX;
       i4_t dq[kIssueAll ? NB : 1][2];
       i4_t dr[kIssueAll && kQX ? NB : 1][2];
       if constexpr (kIssueAll) {
