@@ -681,7 +681,11 @@ void decode_split_kernel(DecodeArgs a) {
       constexpr bool kIssueAll = NB <= 4 && !(kQX && (KM || VM || KB == 5 || KB == 6));
       // head_dim 256: the two token halves of one block together
       constexpr bool kIssuePair = !kIssueAll && D >= 192 && !kQX;
-      i4_t dq[kIssueAll ? NB : 1][2];
+      // blocks per issued group above head_dim 128: two at 256 (one wave per
+      // SIMD, registers for it once the correction is two integers), one at
+      // 192 (two waves per SIMD)
+      constexpr int kPairBlocks = D == 256 ? 2 : 1;
+      i4_t dq[kIssueAll ? NB : kPairBlocks][2];
       i4_t dr[kIssueAll && kQX ? NB : 1][2];
       if constexpr (kIssueAll) {
 #pragma unroll
@@ -704,16 +708,18 @@ void decode_split_kernel(DecodeArgs a) {
           i4_t d;
           long kop = 0;
           if constexpr (kIssuePair) {
-            if (m == 0) {
+            if (m == 0 && j % kPairBlocks == 0) {
+#pragma unroll
+              for (int jj = j; jj < j + kPairBlocks; ++jj)
 #pragma unroll
               for (int mm = 0; mm < 2; ++mm) {
-                const long kp = k_operand<D, KB, VB, KM, VM>(R, mm * NB + j, rot_lo, rot_hi);
-                dq[0][mm] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                    qop[j], kp, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0},
+                const long kp = k_operand<D, KB, VB, KM, VM>(R, mm * NB + jj, rot_lo, rot_hi);
+                dq[jj % kPairBlocks][mm] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                    qop[jj], kp, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? jj : 0] : i4_t{0, 0, 0, 0},
                     0, 0, 0);
               }
             }
-            d = dq[0][m];
+            d = dq[j % kPairBlocks][m];
           } else if constexpr (kIssueAll) {
             d = dq[j][m];
           } else {
