@@ -51,6 +51,8 @@ CASES = [
     (256, 5, 4, False, False, 0, "bf16", 2, 2, [130, 1, 1], 4),
     (192, 6, 5, False, False, 4, "bf16", 1, 2, [100, 1, 29], 3),
     (128, 4, 5, True, True, 12, "bf16", 2, 2, [77, 1, 60], 1),
+    (256, 5, 4, True, True, 0, "bf16", 1, 2, [70, 1, 30], 2),
+    (192, 8, 5, False, True, 6, "f32", 2, 1, [65, 1, 40], 3),
 ]
 
 
