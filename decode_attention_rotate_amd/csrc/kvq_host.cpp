@@ -26,6 +26,7 @@ using namespace kvq;
 // of 4 SIMDs at the kernel's occupancy.
 int target_waves(int D, bool wide) { return 256 * 4 * split_waves_per_simd(D, wide); }
 constexpr int kMaxSplits = kMaxSplitsDevice;
+constexpr int32_t kMaxCtx = 2147483647 - 2 * kTile;
 
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
@@ -47,6 +48,9 @@ kvq_status check_cfg(const kvq_config* c) {
   // scale-and-min blocks come in the 4- and 5-bit widths (q4_1, q5_1)
   if ((c->k_min && c->k_bits > 5) || (c->v_min && c->v_bits > 5)) return KVQ_ERR_UNSUPPORTED;
   if (c->n_kv_heads > 65535 / 2) return KVQ_ERR_INVALID;
+  // lengths, capacities and plane offsets are int32 in the kernels: the
+  // capacity rounded up to a whole tile, plus a tile of slack, must fit
+  if (c->max_ctx > kMaxCtx) return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
 
@@ -303,6 +307,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
     max_len = std::max(max_len, (int)seq_len[b]);
   }
   const Schedule sc = schedule(c, n_q_heads, max_len);
+  // grid y is (KV head, head chunk); the hardware limit of a grid dimension
+  if ((int64_t)c.n_kv_heads * sc.nchunk > 65535) return KVQ_ERR_INVALID;
   const WsLayout wl = ws_layout(c, n_q_heads, sc.S);
   if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
   const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc, c.k_min != 0,

@@ -60,7 +60,10 @@ def test_config_check():
     for field, val, want in (("head_dim", 320, -2), ("head_dim", 32, -2), ("k_bits", 7, -2),
                              ("v_bits", 3, -2), ("batch", 0, -1), ("batch", 257, -1),
                              ("tail_len", -1, -1), ("max_ctx", 0, -1), ("rotate_k", 2, -1),
-                             ("k_min", 2, -1), ("v_min", -1, -1)):
+                             ("k_min", 2, -1), ("v_min", -1, -1),
+                             # int32 positions: the capacity rounded up to a
+                             # tile, plus slack, must stay below 2^31
+                             ("max_ctx", 2147483647, -1), ("max_ctx", 2147483647 - 64, -1)):
         bad = kvq.kvq_config_default(2, 4, 128, 1000)
         setattr(bad, field, val)
         assert kvq.kvq_config_check(bad) == want, field
@@ -134,6 +137,16 @@ def _decode(c, hq, lens, ws_bytes=1 << 40, sm=0.1, q=FAKE, out=FAKE, cache=None)
     cache = cache or _cache()
     return L.kvq_decode_attention(ctypes.byref(c), ctypes.byref(cache), q, 0, hq, sm, lens,
                                   out, FAKE, ws_bytes, None)
+
+
+def test_decode_grid_limit():
+    # 11 query heads per KV head run as 11 chunks of one head: with 10000 KV
+    # heads the grid's y size (KV head x chunk) would exceed 65535
+    c = kvq.kvq_config(1, 10000, 128, 100, 8, 4, 0)
+    assert kvq.kvq_config_check(c) == 0
+    assert _decode(c, 110000, _lens(50)) == _capi.KVQ_ERR_INVALID
+    big = kvq.kvq_config(1, 8, 128, 2147483647 - 128, 8, 4, 0)
+    assert kvq.kvq_config_check(big) == 0
 
 
 def test_decode_validation():
