@@ -170,6 +170,9 @@ def main():
                     help="only run the chunked-prefill measurement (for profiling) and exit")
     ap.add_argument("--append-only", action="store_true",
                     help="only run the bulk append measurement (for profiling) and exit")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the part's read bandwidth (a linear stream, and the "
+                         "split kernel's tile pattern without its arithmetic) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -195,6 +198,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.read_ceiling:
+        print(json.dumps(read_ceiling(torch, kvq, dev)), flush=True)
+        return 0
     if args.prefill_only:
         print(json.dumps(prefill_bench(torch, kvq, dev)), flush=True)
         return 0
@@ -399,6 +405,84 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False):
            "app_ms": [ev_app[s][0].elapsed_time(ev_app[s][1]) for s in timed],
            "fill_mtok_s": fill_mtok_s, "q0": qs[0]}
     del cache, qs, ks, vs
+    return res
+
+
+def read_ceiling(torch, kvq, dev, reps=10):
+    """Read bandwidth the part reaches without the decode arithmetic:
+    * a linear read of a buffer the size of the 64k workload's cache, over
+      workgroup counts, loads in flight per lane and non-temporal loads;
+    * the split kernel's access pattern on planes of the 64k workload's
+      geometry (64 units of 1024 tiles: 8 KiB of K codes, 4 KiB of V codes
+      and 512 B per scale plane per tile), over splits per unit and tiles of
+      loads in flight per wave.
+    Each configuration runs `reps` times after one warm-up; medians by HIP
+    events on the call's stream."""
+    from decode_attention_rotate_amd import _capi
+    import ctypes
+    C = _capi.ceiling_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    w = workloads.workload("long")
+    cache_bytes = cache_bytes_per_step(w, [w["n"]] * w["B"])
+    nbytes = cache_bytes // 4096 * 4096
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    stream_rows = []
+    for blocks in (512, 1024, 2048, 4096, 8192):
+        sink = torch.empty(C.kvq_ceiling_sink_words(blocks, 1), dtype=torch.int32, device=dev)
+        for unroll in (4, 8, 16):
+            for nt in (0, 1):
+                def run():
+                    st = C.kvq_ceiling_stream(buf.data_ptr(), nbytes, blocks, unroll, nt,
+                                              sink.data_ptr(), stream)
+                    assert st == 0, st
+                ms = timed(run)
+                stream_rows.append({"blocks": blocks, "unroll": unroll, "nontemporal": nt,
+                                    "us": round(ms * 1e3, 1),
+                                    "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        del sink
+    del buf
+    units, tiles = w["B"] * w["Hkv"], w["n"] // 64
+    kt, vt, st_b = 64 * 128, 64 * 64, 64 * 4 * 2
+    planes = [torch.ones(units * tiles * b // 4, dtype=torch.int32, device=dev) for b in (kt, vt, st_b, st_b)]
+    args = _capi.KvqCeilingTilesArgs(planes[0].data_ptr(), planes[1].data_ptr(), planes[2].data_ptr(),
+                                     planes[3].data_ptr(), units, tiles, kt, vt, st_b)
+    tile_bytes = units * tiles * (kt + vt + 2 * st_b)
+    tile_rows = []
+    for splits in (2, 4, 8, 16):
+        sink = torch.empty(C.kvq_ceiling_sink_words(splits, units), dtype=torch.int32, device=dev)
+        for ahead in (1, 2):
+            def run():
+                st = C.kvq_ceiling_tiles(ctypes.byref(args), splits, ahead, sink.data_ptr(), stream)
+                assert st == 0, st
+            ms = timed(run)
+            tile_rows.append({"workgroups_per_unit": splits, "waves": splits * 8 * units,
+                              "tiles_ahead": ahead, "us": round(ms * 1e3, 1),
+                              "gbs": round(tile_bytes / (ms * 1e-3) / 1e9, 1)})
+        del sink
+    del planes
+    best_s = max(stream_rows, key=lambda r: r["gbs"])
+    best_t = max(tile_rows, key=lambda r: r["gbs"])
+    res = {"read_ceiling": {
+        "stream_bytes": nbytes, "tile_pattern_bytes": tile_bytes,
+        "best_stream_gbs": best_s["gbs"], "best_stream": best_s,
+        "best_tile_pattern_gbs": best_t["gbs"], "best_tile_pattern": best_t,
+        "pct_of_8000": {"stream": round(100 * best_s["gbs"] / HBM_PEAK_GBS, 1),
+                        "tile_pattern": round(100 * best_t["gbs"] / HBM_PEAK_GBS, 1)},
+        "stream": stream_rows, "tile_pattern": tile_rows}}
+    log("read ceiling: stream %.0f GB/s (%s), tile pattern %.0f GB/s (%s)"
+        % (best_s["gbs"], best_s, best_t["gbs"], best_t))
     return res
 
 

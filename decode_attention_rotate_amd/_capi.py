@@ -8,6 +8,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
+CEILING_PATH = os.path.join(_HERE, "libkvq_ceiling.so")
 
 KVQ_OK = 0
 KVQ_ERR_INVALID = -1
@@ -33,6 +34,9 @@ EXPORTS = (
 )
 
 
+CEILING_EXPORTS = ("kvq_ceiling_stream", "kvq_ceiling_tiles", "kvq_ceiling_sink_words")
+
+
 class KvqConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "n_kv_heads", "head_dim", "k_bits", "v_bits", "tail_len",
@@ -48,6 +52,12 @@ class KvqConfig(ctypes.Structure):
 class KvqCache(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
         "k_codes", "k_scales", "v_codes", "v_scales", "k_tail", "v_tail", "page_table")]
+
+
+class KvqCeilingTilesArgs(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in ("k_codes", "v_codes", "k_scales", "v_scales")] + [
+        (name, ctypes.c_int32) for name in ("units", "tiles", "k_tile_bytes", "v_tile_bytes",
+                                            "s_tile_bytes")]
 
 
 class KvqError(RuntimeError):
@@ -97,6 +107,32 @@ def lib():
             fn.argtypes = args
         _lib = L
     return _lib
+
+
+_ceiling = None
+
+
+def ceiling_lib():
+    """The read-bandwidth probe library (include/kvq_ceiling.h); measurement
+    only, loaded by the benchmark."""
+    global _ceiling
+    if _ceiling is None:
+        import torch  # noqa: F401  (same HIP runtime as torch, see lib())
+        if not os.path.exists(CEILING_PATH):
+            raise ImportError("libkvq_ceiling.so is not built (%s)" % CEILING_PATH)
+        L = ctypes.CDLL(CEILING_PATH)
+        P, I32, SZ, vp = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+        sig = {
+            "kvq_ceiling_stream": (I32, [vp, SZ, I32, I32, I32, vp, vp]),
+            "kvq_ceiling_tiles": (I32, [P(KvqCeilingTilesArgs), I32, I32, vp, vp]),
+            "kvq_ceiling_sink_words": (SZ, [I32, I32]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _ceiling = L
+    return _ceiling
 
 
 def event_elapsed_ms(before, after):

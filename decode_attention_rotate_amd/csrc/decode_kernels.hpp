@@ -28,8 +28,11 @@
 //      score += scale_k * float(256 * sum(q_hi * c) + sum(q_lo * c))
 //  * Online softmax in log2 units, rescaling only when a running max grows.
 //  * P.V, v_mfma_f32_16x16x32_f16 per 32 tokens and 16 output elements.  A
-//    rows are the weights p * scale_v of each head (rounded once to fp16,
-//    moved from score layout to operand layout through LDS); B columns are
+//    rows are the weights p * scale_v * 2^e of each head (rounded once to
+//    fp16, moved from score layout to operand layout through LDS; 2^e keeps
+//    the largest V scale near 2^11, so weights stay in fp16's normal range
+//    for V of any size, and the accumulators are divided by it at the end);
+//    B columns are
 //    V codes of one element for 8 consecutive tokens, which the element-major
 //    V tiles store together: nibbles / bytes become exact fp16 integers with
 //    one v_and_or (or v_perm) per pair plus one packed fp16 add.
@@ -38,9 +41,10 @@
 // the online-softmax state of the quantized tokens.
 // Scale-and-min blocks (x = u * s + m, levels u >= 0): Q.K takes the levels
 // without an offset and adds m * sum(q) of the block, from per-block query
-// sums made once; P.V takes the levels and each lane keeps sum(p * m) per
-// (head, block) beside the accumulators, rescaled with them, added to the
-// output elements of that block at the end.
+// sums made once; P.V takes the centred levels u - 2^(b-1) and each lane
+// keeps sum(p * (m + 2^(b-1) * s)) per (head, block) beside the
+// accumulators, rescaled with them, added to the output elements of that
+// block at the end.
 #pragma once
 
 #include "common.hpp"
@@ -120,6 +124,19 @@ struct StepRegs {
   __device__ float v_min(int m, int j) const { return half_of(vs[m][j], 1); }
 };
 
+// Largest fp16 V scale (as its bit pattern; scales are >= 0, so bit patterns
+// order like the values) of token-row half m of this lane.  Scale-and-min
+// words hold (s, m) pairs with s in the low half.
+template <int D, int KB, int VB, bool KM, bool VM>
+__device__ inline uint32_t v_scale_max_bits(const StepRegs<D, KB, VB, KM, VM>& R, int m) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  constexpr int VSW = StepRegs<D, KB, VB, KM, VM>::VSW;
+  u16x2 x = __builtin_bit_cast(u16x2, R.vs[m][0]);
+#pragma unroll
+  for (int w = 1; w < VSW; ++w) x = __builtin_elementwise_max(x, __builtin_bit_cast(u16x2, R.vs[m][w]));
+  return VM ? (uint32_t)x[0] : (uint32_t)(x[0] > x[1] ? x[0] : x[1]);
+}
+
 // Load NW consecutive 32-bit words with the widest loads their alignment
 // allows: NW * 4 bytes per token, so 8-byte loads for even NW, 16-byte ones
 // for multiples of 4 (head_dim 192 has NW = 3 or 6).
@@ -169,8 +186,8 @@ __device__ inline long k_operand(const StepRegs<D, KB, VB, KM, VM>& R, int i, ui
 }
 
 // B operand of P.V for output elements 16*nb..+15: this lane's element for
-// the 8 tokens of its k-slots, as exact fp16 codes (levels u for
-// scale-and-min blocks).
+// the 8 tokens of its k-slots, as exact fp16 codes (centred levels
+// u - 2^(VB-1) for scale-and-min blocks).
 template <int D, int KB, int VB, bool KM, bool VM>
 __device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, uint32_t magic) {
   const h2_t one16 = {(_Float16)0.0625f, (_Float16)0.0625f};
@@ -217,10 +234,6 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, u
       b_lo = (_Float16)-1032.0f;
       b_hi = (_Float16)-72.0f;
     }
-    if constexpr (VM) {   // levels u, no offset
-      b_lo = (_Float16)-1024.0f;
-      b_hi = (_Float16)-64.0f;
-    }
     const h2_t bl = {b_lo, b_lo}, bh = {b_hi, b_hi};
     const h2_t d0 = as_h2(w0) + bl;
     const h2_t d1 = __builtin_elementwise_fma(as_h2(w1), one16, bh);   // exact
@@ -266,13 +279,16 @@ void decode_split_kernel(DecodeArgs a) {
   constexpr int VTB = v_tile_bytes(D, VB);
   // LDS weight rows of 32 tokens (+ pad), 16-bit: row 8*j + h holds head h's
   // weights for V block j; the tail keeps the low bf16 parts of its weights
-  // in rows LOROW + h; row ZROW stays zero (A rows 8..15 of quantized steps).
+  // in rows LOROW + h; row ZROW stays zero (A rows 8..15 of quantized steps
+  // with absmax V).  Scale-and-min V keeps the low fp16 parts of its
+  // weights in rows LOQ + 8*j + h, as A rows 8..15 (see the weights below).
   constexpr int WROW = 48;
   constexpr int LOROW = 8 * NB;
   constexpr int ZROW = 8 * NB + 8;
+  constexpr int LOQ = 8 * NB + 9;
   using Regs = StepRegs<D, KB, VB, KM, VM>;
 
-  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9) * WROW];
+  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9 + (VM ? 8 * NB : 0)) * WROW];
   __shared__ __align__(16) float alds_all[kGroupWaves][16];
   __shared__ uint32_t tile_ctr;
 
@@ -342,6 +358,15 @@ void decode_split_kernel(DecodeArgs a) {
   float mvA[VM ? NB : 1], mvB[VM ? NB : 1];
 #pragma unroll
   for (int j = 0; j < (VM ? NB : 1); ++j) mvA[j] = mvB[j] = 0.f;
+  // Weight factor of the quantized positions: their fp16 weights are
+  // p * scale_v * 2^vfe, with 2^(11 - vfe) <= the largest V scale seen so far
+  // < 2^(12 - vfe), so a weight never drops into fp16's subnormal range
+  // however small V is (the result is the same for V and for V times a power
+  // of two).  The accumulators carry the factor; a scale at or above vthr
+  // (fp16 bits of 2^(15 - vfe)) raises it, and the accumulators are divided
+  // by it at the end.  Powers of two: every rescale is exact.
+  int vfe = 0;
+  uint32_t vthr = 0u;   // the first step with a nonzero scale sets the factor
 
   // Query of this lane's A row in registers: row col < 2G is the wave's row
   // col/2; the lane holds elements 32j + 8r + i (j < NB, i < 8), rotated in
@@ -767,8 +792,30 @@ void decode_split_kernel(DecodeArgs a) {
         xB[m] = validB && okB ? yb : -INFINITY;
       }
       softmax(xA, xB, pA, pB);
-      // weights p * scale_v in fp16 (0 for masked tokens and absent heads),
-      // moved to the A-operand layout via LDS
+      // largest V scale of the step's positions (those past the quantized
+      // range hold no data) against the weight factor's threshold
+      {
+        const uint32_t l0 = s0 + col < nq ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 0) : 0u;
+        const uint32_t l1 = s0 + 16 + col < nq ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 1) : 0u;
+        const uint32_t lm = l0 > l1 ? l0 : l1;
+        if (__builtin_amdgcn_ballot_w64(lm >= vthr) != 0) {
+          const float mx = row16_max((float)__builtin_bit_cast(_Float16, (uint16_t)lm));
+          const uint32_t mb = __builtin_amdgcn_readfirstlane(__float_as_uint(mx));
+          if (mb != 0u) {
+            const int e = (int)((mb >> 23) & 0xFFu) - 127;   // 2^e <= max < 2^(e+1), e >= -24
+            const int nfe = 11 - e;
+            const float ratio = __uint_as_float((uint32_t)(127 + nfe - vfe) << 23);
+#pragma unroll
+            for (int i = 0; i < NN; ++i) acc[i] *= ratio;
+            vfe = nfe;
+            const int k = e + 4;   // threshold 2^(e + 4) in fp16 bits
+            vthr = k > 15 ? 0x7C00u : (k >= -14 ? (uint32_t)(k + 15) << 10 : 1u << (k + 24));
+          }
+        }
+      }
+      const float vf = __uint_as_float((uint32_t)(127 + vfe) << 23);
+      // weights p * scale_v * 2^vfe in fp16 (0 for masked tokens and absent
+      // heads), moved to the A-operand layout via LDS
       wave_sync();
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -776,16 +823,34 @@ void decode_split_kernel(DecodeArgs a) {
         for (int m = 0; m < 2; ++m) {
           const float vs = R.v_scale(m, j);
           const int t = 16 * m + col;
-          const _Float16 wA = (_Float16)(pA[m] * vs);
-          const _Float16 wB = (_Float16)(pB[m] * vs);
+          const float fA = pA[m] * vf * vs, fB = pB[m] * vf * vs;
+          const _Float16 wA = (_Float16)fA;
+          const _Float16 wB = (_Float16)fB;
           wl[(8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, wA);
           wl[(8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, wB);
+          if constexpr (VM) {
+            // Scale-and-min blocks: a block whose range an outlier stretches
+            // puts its ordinary elements far from the block's middle level,
+            // so their centred levels are large against their values, and
+            // the weight's fp16 rounding, common to the whole block, would
+            // not cancel in a sum that nearly does.  The low fp16 part of
+            // each weight goes in A rows 8..15 (otherwise zero), whose
+            // accumulator rows are added to rows 0..7 at the end: about 22
+            // significant bits for no extra matrix products.
+            wl[(LOQ + 8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, (_Float16)(fA - (float)wA));
+            wl[(LOQ + 8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, (_Float16)(fB - (float)wB));
+          }
         }
       }
       if constexpr (VM) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const float v0 = R.v_min(0, j), v1 = R.v_min(1, j);
+          // x = u * s + m = (u - o) * s + (m + o * s): the matrix product
+          // takes the centred levels u - o, so the rounding of its fp16
+          // weights does not act on the block's offset, which goes here
+          constexpr float o = (float)(1 << (VB - 1));
+          const float v0 = __builtin_fmaf(o, R.v_scale(0, j), R.v_min(0, j));
+          const float v1 = __builtin_fmaf(o, R.v_scale(1, j), R.v_min(1, j));
           mvA[j] = __builtin_fmaf(pA[1], v1, __builtin_fmaf(pA[0], v0, mvA[j]));
           mvB[j] = __builtin_fmaf(pB[1], v1, __builtin_fmaf(pB[0], v0, mvB[j]));
         }
@@ -794,7 +859,7 @@ void decode_split_kernel(DecodeArgs a) {
       // P.V on the matrix cores: NN products of 16 rows x 32 tokens x 16 elements
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int row = col < 8 ? 8 * j + col : ZROW;
+        const int row = col < 8 ? 8 * j + col : (VM ? LOQ + 8 * j + col - 8 : ZROW);
         const h8_t wa = *reinterpret_cast<const h8_t*>(&wl[row * WROW + 8 * r]);
 #pragma unroll
         for (int i = 2 * j; i < 2 * j + 2; ++i)
@@ -957,6 +1022,11 @@ void decode_split_kernel(DecodeArgs a) {
   // rows h and 8+h of the accumulators belong to head h
   lA = row16_sum(lA);
   lB = row16_sum(lB);
+  {
+    const float inv = __uint_as_float((uint32_t)(127 - vfe) << 23);   // exact
+#pragma unroll
+    for (int i = 0; i < NN; ++i) acc[i] *= inv;
+  }
 #pragma unroll
   for (int i = 0; i < NN; ++i) {
 #pragma unroll

@@ -25,8 +25,8 @@ FAKE = 0x10000          # aligned, never dereferenced (validation fails first)
 FAKE_MISALIGNED = 0x10008
 
 
-def _header_functions():
-    text = open(HEADER).read()
+def _header_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text))
 
@@ -36,6 +36,24 @@ def test_exports_every_declared_function():
     assert declared == set(_capi.EXPORTS)
     for name in declared:
         assert hasattr(L, name)
+
+
+def test_ceiling_library_exports_its_header():
+    # the benchmark's read-bandwidth probes live in a library of their own
+    if not os.path.exists(_capi.CEILING_PATH):
+        pytest.skip("libkvq_ceiling.so not built")
+    declared = _header_functions(os.path.join(ROOT, "include", "kvq_ceiling.h"))
+    assert declared == set(_capi.CEILING_EXPORTS)
+    C = _capi.ceiling_lib()
+    assert C.kvq_ceiling_sink_words(4, 3) == 4 * 3 * 512
+    # invalid arguments are refused before any launch
+    assert C.kvq_ceiling_stream(None, 1024, 4, 4, 0, FAKE, None) == -1
+    assert C.kvq_ceiling_stream(FAKE, 1000, 4, 4, 0, FAKE, None) == -1
+    assert C.kvq_ceiling_stream(FAKE, 1024, 4, 3, 0, FAKE, None) == -1
+    args = _capi.KvqCeilingTilesArgs(FAKE, FAKE, FAKE, FAKE, 2, 10, 8192, 4096, 512)
+    assert C.kvq_ceiling_tiles(ctypes.byref(args), 4, 3, FAKE, None) == -1
+    bad = _capi.KvqCeilingTilesArgs(FAKE, FAKE, FAKE, FAKE, 2, 10, 8192, 16384, 512)
+    assert C.kvq_ceiling_tiles(ctypes.byref(bad), 4, 1, FAKE, None) == -1
 
 
 def test_status_strings():

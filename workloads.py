@@ -24,7 +24,9 @@ every token and sequence, drawn independently for K and V.  q carries no
 outliers.  An optional field bias = b adds a fixed per-(head, channel) offset
 b * N(0, 1) to every K and V token (stream role 6; absent in the workloads
 above), which makes blocks asymmetric about zero, the case scale-and-min
-blocks are for.  Random streams are keyed by (workload, role, chunk) so any token
+blocks are for.  Optional fields amp_k / amp_v multiply every K / V value
+(outliers and bias included) by a constant, for caches of very small or very
+large magnitude.  Random streams are keyed by (workload, role, chunk) so any token
 range can be regenerated on its own: role 0 = outlier choice, 1 = K, 2 = V,
 3 = Q, 4 = new decode tokens.
 """
@@ -80,6 +82,12 @@ def outlier_scale(w, role):
     return s
 
 
+def amplitude(w, role):
+    """Constant factor of K (role 1) or V (role 2) values: amp_k / amp_v, 1 if
+    absent."""
+    return float(w.get("amp_k" if role == 1 else "amp_v", 1.0))
+
+
 def channel_bias(w, role):
     """[Hkv][d] float32 per-channel offsets of K (role 1) or V (role 2):
     zero unless the workload sets bias."""
@@ -125,7 +133,7 @@ def kv_numpy(w, role, t0, t1, batch=None):
         x = np.concatenate(parts, axis=0) * scale[None]
         if w.get("bias"):
             x = x + channel_bias(w, role)[None]
-        out.append(x)
+        out.append(x * np.float32(amplitude(w, role)))
     x = np.stack(out).astype(np.float32)
     return to_bf16_bits(x) if w["dtype"] == "bf16" else x
 
@@ -151,7 +159,8 @@ def new_tokens_numpy(w, role, step, n_new=1):
     x = x * outlier_scale(w, role)[None, None]
     if w.get("bias"):
         x = x + channel_bias(w, role)[None, None]
-    return to_bf16_bits(x) if w["dtype"] == "bf16" else x.astype(np.float32)
+    x = (x * np.float32(amplitude(w, role))).astype(np.float32)
+    return to_bf16_bits(x) if w["dtype"] == "bf16" else x
 
 
 # ---------------------------------------------------------------- torch side
@@ -186,6 +195,7 @@ def kv_torch(w, role, t0, t1, device, torch):
     x = torch.cat(parts, dim=1) * scale
     if w.get("bias"):
         x = x + torch.from_numpy(channel_bias(w, role)).to(device)
+    x = x * amplitude(w, role)
     dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     return x.to(dt).contiguous()
 
@@ -216,6 +226,7 @@ def new_tokens_torch(w, role, step, device, torch, n_new=1):
     x = x * torch.from_numpy(outlier_scale(w, role)).to(device)
     if w.get("bias"):
         x = x + torch.from_numpy(channel_bias(w, role)).to(device)
+    x = x * amplitude(w, role)
     dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
     return x.to(dt).contiguous()
 
