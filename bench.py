@@ -414,8 +414,9 @@ def read_ceiling(torch, kvq, dev, reps=10):
       workgroup counts, loads in flight per lane and non-temporal loads;
     * the split kernel's access pattern on planes of the 64k workload's
       geometry (64 units of 1024 tiles: 8 KiB of K codes, 4 KiB of V codes
-      and 512 B per scale plane per tile), over splits per unit and tiles of
-      loads in flight per wave.
+      and 512 B per scale plane per tile), over splits per unit, tiles of
+      loads in flight per wave, non-temporal loads, and contiguous ranges
+      per workgroup against chunks of 8 tiles dealt round-robin.
     Each configuration runs `reps` times after one warm-up; medians by HIP
     events on the call's stream."""
     from decode_attention_rotate_amd import _capi
@@ -463,13 +464,16 @@ def read_ceiling(torch, kvq, dev, reps=10):
     for splits in (2, 4, 8, 16):
         sink = torch.empty(C.kvq_ceiling_sink_words(splits, units), dtype=torch.int32, device=dev)
         for ahead in (1, 2):
-            def run():
-                st = C.kvq_ceiling_tiles(ctypes.byref(args), splits, ahead, sink.data_ptr(), stream)
-                assert st == 0, st
-            ms = timed(run)
-            tile_rows.append({"workgroups_per_unit": splits, "waves": splits * 8 * units,
-                              "tiles_ahead": ahead, "us": round(ms * 1e3, 1),
-                              "gbs": round(tile_bytes / (ms * 1e-3) / 1e9, 1)})
+            for mode in (0, 1, 2, 3):
+                def run():
+                    st = C.kvq_ceiling_tiles(ctypes.byref(args), splits, ahead, mode, sink.data_ptr(),
+                                             stream)
+                    assert st == 0, st
+                ms = timed(run)
+                tile_rows.append({"workgroups_per_unit": splits, "waves": splits * 8 * units,
+                                  "tiles_ahead": ahead, "nontemporal": mode & 1,
+                                  "chunked": (mode >> 1) & 1, "us": round(ms * 1e3, 1),
+                                  "gbs": round(tile_bytes / (ms * 1e-3) / 1e9, 1)})
         del sink
     del planes
     best_s = max(stream_rows, key=lambda r: r["gbs"])

@@ -124,7 +124,7 @@ def ceiling_lib():
         P, I32, SZ, vp = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
         sig = {
             "kvq_ceiling_stream": (I32, [vp, SZ, I32, I32, I32, vp, vp]),
-            "kvq_ceiling_tiles": (I32, [P(KvqCeilingTilesArgs), I32, I32, vp, vp]),
+            "kvq_ceiling_tiles": (I32, [P(KvqCeilingTilesArgs), I32, I32, I32, vp, vp]),
             "kvq_ceiling_sink_words": (SZ, [I32, I32]),
         }
         for name, (res, args) in sig.items():

@@ -44,11 +44,13 @@ int kvq_ceiling_stream(const void* buf, size_t bytes, int32_t blocks, int32_t un
 
 /* Read every tile of every unit once in the decode kernel's pattern: grid
  * (splits, units) workgroups of 8 waves; a workgroup takes a contiguous
- * range of its unit's tiles, its waves pull tiles from an LDS counter and
- * keep `ahead` (1 or 2) tiles of loads in flight.  sink: device uint32 of at
- * least kvq_ceiling_sink_words(splits, units) words. */
+ * range of its unit's tiles (mode bit 1 clear) or every splits-th chunk of 8
+ * tiles (mode bit 1 set), its waves pull tiles from an LDS counter and keep
+ * `ahead` (1 or 2) tiles of loads in flight; mode bit 0 makes the loads
+ * non-temporal.  sink: device uint32 of at least
+ * kvq_ceiling_sink_words(splits, units) words. */
 int kvq_ceiling_tiles(const kvq_ceiling_tiles_args* args, int32_t splits, int32_t ahead,
-                      uint32_t* sink, void* stream);
+                      int32_t mode, uint32_t* sink, void* stream);
 
 /* Words of `sink` the two calls above need. */
 size_t kvq_ceiling_sink_words(int32_t blocks_or_splits, int32_t units);

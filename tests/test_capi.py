@@ -51,9 +51,10 @@ def test_ceiling_library_exports_its_header():
     assert C.kvq_ceiling_stream(FAKE, 1000, 4, 4, 0, FAKE, None) == -1
     assert C.kvq_ceiling_stream(FAKE, 1024, 4, 3, 0, FAKE, None) == -1
     args = _capi.KvqCeilingTilesArgs(FAKE, FAKE, FAKE, FAKE, 2, 10, 8192, 4096, 512)
-    assert C.kvq_ceiling_tiles(ctypes.byref(args), 4, 3, FAKE, None) == -1
+    assert C.kvq_ceiling_tiles(ctypes.byref(args), 4, 3, 0, FAKE, None) == -1
+    assert C.kvq_ceiling_tiles(ctypes.byref(args), 4, 1, 4, FAKE, None) == -1
     bad = _capi.KvqCeilingTilesArgs(FAKE, FAKE, FAKE, FAKE, 2, 10, 8192, 16384, 512)
-    assert C.kvq_ceiling_tiles(ctypes.byref(bad), 4, 1, FAKE, None) == -1
+    assert C.kvq_ceiling_tiles(ctypes.byref(bad), 4, 1, 0, FAKE, None) == -1
 
 
 def test_status_strings():
