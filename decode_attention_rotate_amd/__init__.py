@@ -18,7 +18,8 @@ import math
 from . import _capi
 from ._capi import (KvqConfig, KvqCache, KvqError, KVQ_BF16, KVQ_F32,
                     KVQ_K_CODES, KVQ_K_SCALES, KVQ_V_CODES, KVQ_V_SCALES,
-                    KVQ_K_TAIL, KVQ_V_TAIL, KVQ_MAX_BATCH, KVQ_PAGE_TOKENS, LIB_PATH)
+                    KVQ_K_TAIL, KVQ_V_TAIL, KVQ_MAX_BATCH, KVQ_PAGE_TOKENS,
+                    KVQ_STATIC_WORKSPACE_BYTES, LIB_PATH)
 
 __all__ = [
     "KvqConfig", "KvqCache", "KvqError", "KVCache", "kvq_config",
@@ -26,6 +27,7 @@ __all__ = [
     "kvq_decode_workspace_bytes", "kvq_rotate_quantize_append",
     "kvq_decode_attention", "kvq_dequantize", "kvq_status_str",
     "kvq_profile_decode_events", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
+    "kvq_decode_attention_static", "KVQ_STATIC_WORKSPACE_BYTES",
     "KVQ_PAGE_TOKENS", "LIB_PATH",
 ]
 
@@ -246,6 +248,27 @@ def kvq_decode_attention(cfg, cache, q, seq_len, sm_scale=None, out=None,
         float(sm_scale), _lens(seq_len, cfg.batch), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _capi.check(st, "kvq_decode_attention")
+    return out
+
+
+def kvq_decode_attention_static(cfg, cache, q, seq_len, sm_scale=None, out=None, stream=None):
+    """kvq_decode_attention with the library's static device workspace (no
+    workspace argument, nothing allocated by the library); calls on one GPU
+    share that workspace and must not overlap.  Returns float32 [B][Hq][d]."""
+    torch = _torch()
+    _device_tensor(q, "q")
+    B, Hq, d = q.shape
+    if (B, d) != (cfg.batch, cfg.head_dim):
+        raise ValueError("q shape %s does not match the configuration" % (tuple(q.shape),))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _device_tensor(out, "out")
+    st = _capi.lib().kvq_decode_attention_static(
+        ctypes.byref(cfg), ctypes.byref(cache.struct), q.data_ptr(), _dtype_code(q), Hq,
+        float(sm_scale), _lens(seq_len, cfg.batch), out.data_ptr(), _stream(stream))
+    _capi.check(st, "kvq_decode_attention_static")
     return out
 
 

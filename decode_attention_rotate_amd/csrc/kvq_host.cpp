@@ -13,10 +13,17 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
 #include "kvq.h"
+
+// Workspace of kvq_decode_attention_static: one copy of this array on each
+// GPU the library runs on, held until the process ends.  In host code its
+// name only stands in for the symbol; the device address comes from
+// hipGetSymbolAddress, once per device (static_workspace below).
+static __device__ __align__(256) uint8_t scratch[KVQ_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -286,17 +293,27 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* ca
   return hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)));
 }
 
-kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
-                                kvq_dtype dtype, int32_t n_q_heads, float sm_scale,
-                                const int32_t* seq_len, float* out, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks of a decode call (everything but the workspace); on success
+// the schedule, the workspace it needs and the kernel to launch.
+struct DecodePlan {
+  Schedule sc;
+  WsLayout wl;
+  DecodeLauncher fn;
+};
+kvq_status plan_decode(const kvq_config* cfg, const kvq_cache* cache, const void* q, kvq_dtype dtype,
+                       int32_t n_q_heads, float sm_scale, const int32_t* seq_len, const float* out,
+                       DecodePlan* plan) {
   kvq_status st = check_cfg(cfg);
   if (st != KVQ_OK) return st;
   const kvq_config& c = *cfg;
   if ((st = check_cache(c, cache)) != KVQ_OK) return st;
   if (dtype != KVQ_BF16 && dtype != KVQ_F32) return KVQ_ERR_INVALID;
-  if (!q || !out || !workspace || !seq_len) return KVQ_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (!q || !out || !seq_len) return KVQ_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
   if (n_q_heads < c.n_kv_heads || n_q_heads % c.n_kv_heads != 0) return KVQ_ERR_INVALID;
   if ((int64_t)c.batch * n_q_heads > 2147483647 / 8) return KVQ_ERR_INVALID;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
@@ -306,15 +323,24 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
     if (seq_len[b] > c.max_ctx) return KVQ_ERR_CAPACITY;
     max_len = std::max(max_len, (int)seq_len[b]);
   }
-  const Schedule sc = schedule(c, n_q_heads, max_len);
+  plan->sc = schedule(c, n_q_heads, max_len);
   // grid y is (KV head, head chunk); the hardware limit of a grid dimension
-  if ((int64_t)c.n_kv_heads * sc.nchunk > 65535) return KVQ_ERR_INVALID;
-  const WsLayout wl = ws_layout(c, n_q_heads, sc.S);
-  if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
-  const DecodeLauncher fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, sc.gc, c.k_min != 0,
-                                            c.v_min != 0, c.page_pool > 0);
-  if (!fn) return KVQ_ERR_UNSUPPORTED;
+  if ((int64_t)c.n_kv_heads * plan->sc.nchunk > 65535) return KVQ_ERR_INVALID;
+  plan->wl = ws_layout(c, n_q_heads, plan->sc.S);
+  plan->fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, plan->sc.gc, c.k_min != 0, c.v_min != 0,
+                             c.page_pool > 0);
+  if (!plan->fn) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
 
+// Queue the split kernel and the combine of a checked decode call.
+kvq_status run_decode(const kvq_config& c, const kvq_cache* cache, const void* q, kvq_dtype dtype,
+                      int32_t n_q_heads, float sm_scale, const int32_t* seq_len, float* out,
+                      void* workspace, const DecodePlan& plan, void* stream) {
+  kvq_status st;
+  const Schedule& sc = plan.sc;
+  const WsLayout& wl = plan.wl;
+  const DecodeLauncher fn = plan.fn;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const float cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
@@ -361,6 +387,53 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   ca.has_signs = da.has_signs;
   for (int i = 0; i < 8; ++i) ca.signs[i] = da.signs[i];
   return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the
+// first call there; nullptr if the runtime reports an error.
+void* static_workspace() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                kvq_dtype dtype, int32_t n_q_heads, float sm_scale,
+                                const int32_t* seq_len, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  kvq_status st = plan_decode(cfg, cache, q, dtype, n_q_heads, sm_scale, seq_len, out, &plan);
+  if (st != KVQ_OK) return st;
+  if (!workspace) return KVQ_ERR_INVALID;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (workspace_bytes < plan.wl.total) return KVQ_ERR_WORKSPACE;
+  return run_decode(*cfg, cache, q, dtype, n_q_heads, sm_scale, seq_len, out, workspace, plan, stream);
+}
+
+kvq_status kvq_decode_attention_static(const kvq_config* cfg, const kvq_cache* cache, const void* q,
+                                       kvq_dtype dtype, int32_t n_q_heads, float sm_scale,
+                                       const int32_t* seq_len, float* out, void* stream) {
+  DecodePlan plan;
+  kvq_status st = plan_decode(cfg, cache, q, dtype, n_q_heads, sm_scale, seq_len, out, &plan);
+  if (st != KVQ_OK) return st;
+  if (plan.wl.total > KVQ_STATIC_WORKSPACE_BYTES) return KVQ_ERR_WORKSPACE;
+  void* ws = static_workspace();
+  if (!ws) return KVQ_ERR_HIP;
+  return run_decode(*cfg, cache, q, dtype, n_q_heads, sm_scale, seq_len, out, ws, plan, stream);
 }
 
 size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads, int32_t n_q) {

@@ -24,7 +24,9 @@
  * Conventions shared by every call:
  *  - Ownership: the caller allocates and frees every device buffer; the
  *    library never allocates device memory and keeps no global state, so
- *    calls are re-entrant.  Host arrays (seq_len) are read during the call
+ *    calls are re-entrant.  The one exception is the static workspace of
+ *    kvq_decode_attention_static, a fixed device array the library holds on
+ *    each GPU it runs on.  Host arrays (seq_len) are read during the call
  *    only.
  *  - Execution: all device work is queued on `stream` (a hipStream_t passed
  *    as void*; NULL is the default stream) and is asynchronous.
@@ -244,6 +246,28 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const int32_t* seq_len, float* out,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* Size of the device workspace kvq_decode_attention_static uses. */
+#define KVQ_STATIC_WORKSPACE_BYTES 33554432
+
+/* kvq_decode_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and errors are those of
+ * kvq_decode_attention without the workspace: the split partials go to a
+ * static device buffer of KVQ_STATIC_WORKSPACE_BYTES that the library holds
+ * on each GPU it runs on until the process ends.  The call allocates
+ * nothing.  Returns KVQ_ERR_WORKSPACE, queueing nothing, when the call would
+ * need more than that (the need grows with batch x query heads and is at
+ * most kvq_decode_workspace_bytes(cfg, n_q_heads)); KVQ_ERR_HIP if the
+ * buffer's device address cannot be obtained.  Every call on one GPU shares
+ * the buffer, and it keeps the last call's partials: calls that overlap on
+ * one GPU (on other streams or host threads) race and must be ordered by
+ * the caller. */
+kvq_status kvq_decode_attention_static(const kvq_config* cfg, const kvq_cache* cache,
+                                       const void* q, kvq_dtype dtype,
+                                       int32_t n_q_heads, float sm_scale,
+                                       const int32_t* seq_len, float* out,
+                                       void* stream);
 
 /* Workspace bytes kvq_prefill_attention needs for n_q_heads query heads and
  * n_q queries per sequence at any length up to cfg->max_ctx; 0 if the

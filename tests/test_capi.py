@@ -168,6 +168,28 @@ def test_decode_grid_limit():
     assert kvq.kvq_config_check(big) == 0
 
 
+def test_static_workspace_decode_validation():
+    # the entry point for callers that cannot allocate: host checks first,
+    # then a call whose partials would not fit the static workspace is
+    # refused before any device work
+    B = 256
+    c = kvq.kvq_config(B, 8, 256, 70000, 8, 8, 0)
+    assert kvq.kvq_decode_workspace_bytes(c, 64) > _capi.KVQ_STATIC_WORKSPACE_BYTES
+    lens = _lens(*([65536] * B))
+    f = L.kvq_decode_attention_static
+    assert f(ctypes.byref(c), ctypes.byref(_cache()), FAKE, 0, 64, 0.1, lens, FAKE, None) == \
+        _capi.KVQ_ERR_WORKSPACE
+    small = kvq.kvq_config(2, 4, 128, 100, 8, 4, 0)
+    assert f(ctypes.byref(small), ctypes.byref(_cache()), 0, 0, 8, 0.1, _lens(5, 5), FAKE, None) == \
+        _capi.KVQ_ERR_INVALID
+    assert f(ctypes.byref(small), ctypes.byref(_cache()), FAKE, 0, 6, 0.1, _lens(5, 5), FAKE, None) == \
+        _capi.KVQ_ERR_INVALID
+    assert f(ctypes.byref(small), ctypes.byref(_cache()), FAKE, 0, 8, 0.1, _lens(5, 101), FAKE, None) == \
+        _capi.KVQ_ERR_CAPACITY
+    assert f(ctypes.byref(small), ctypes.byref(_cache()), FAKE_MISALIGNED, 0, 8, 0.1, _lens(5, 5), FAKE,
+             None) == _capi.KVQ_ERR_ALIGN
+
+
 def test_decode_validation():
     c = kvq.kvq_config(2, 4, 128, 100, 8, 4, 0)
     assert _decode(c, 6, _lens(5, 5)) == _capi.KVQ_ERR_INVALID      # 6 % 4 != 0
