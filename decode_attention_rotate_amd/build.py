@@ -49,8 +49,19 @@ def units():
     return out
 
 
-def _compile(job):
+def _sources_newer(obj_path):
+    """True when any source or header of the library is newer than obj_path."""
+    if not os.path.exists(obj_path):
+        return True
+    t = os.path.getmtime(obj_path)
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "kvq.h")]
+    return any(os.path.getmtime(f) > t for f in srcs)
+
+
+def _compile(job, incremental=False):
     src, obj, extra = job
+    if incremental and not _sources_newer(os.path.join(BUILD, obj)):
+        return obj, 0, "", []
     cmd = [HIPCC] + COMMON + extra + ["-c", src, "-o", os.path.join(BUILD, obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = ("unknown target feature", "packed-fp32-ops", "warning generated")
@@ -59,15 +70,19 @@ def _compile(job):
     return obj, r.returncode, msgs, cmd
 
 
-def build(jobs=None, verbose=False):
-    """Compile every unit and link libkvq.so; raises on any failure."""
+def build(jobs=None, verbose=False, only=None, incremental=False):
+    """Compile every unit and link libkvq.so; raises on any failure.
+    only: compile just the units whose object name contains this string
+    (the others must already be built); incremental: skip units whose
+    object is newer than every source (development builds)."""
     if not os.path.exists(HIPCC):
         raise RuntimeError("hipcc not found at %s" % HIPCC)
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(16, os.cpu_count() or 4)
     failed = []
+    todo = [u for u in units() if only is None or any(o in u[1] for o in only.split(","))]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        for obj, rc, msgs, cmd in ex.map(_compile, units()):
+        for obj, rc, msgs, cmd in ex.map(lambda u: _compile(u, incremental), todo):
             if rc != 0:
                 failed.append((obj, msgs, cmd))
             elif verbose and msgs:
@@ -94,8 +109,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--only", default=None, help="compile only units whose object name contains one of these (comma-separated)")
     args = ap.parse_args(argv)
-    print(build(args.jobs, args.verbose))
+    print(build(args.jobs, args.verbose, only=args.only))
 
 
 if __name__ == "__main__":

@@ -137,24 +137,36 @@ __device__ inline uint32_t v_scale_max_bits(const StepRegs<D, KB, VB, KM, VM>& R
   return VM ? (uint32_t)x[0] : (uint32_t)(x[0] > x[1] ? x[0] : x[1]);
 }
 
+// Loads of cache bytes.  Each byte is read once per call; with NT the loads
+// are non-temporal (the hint lets the caches stream them past), which the
+// part serves about a tenth faster than ordinary loads for this access
+// pattern at two waves per SIMD (read-ceiling probes and the 64k decode
+// kernel), but which made the one-wave-per-SIMD head_dim 256 kernel 2%
+// slower, so those keep ordinary loads.
+template <bool NT, typename T>
+__device__ inline T ld_cache(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
 // Load NW consecutive 32-bit words with the widest loads their alignment
 // allows: NW * 4 bytes per token, so 8-byte loads for even NW, 16-byte ones
 // for multiples of 4 (head_dim 192 has NW = 3 or 6).
-template <int NW>
+template <bool NT, int NW>
 __device__ inline void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
   if constexpr (NW % 4 != 0 && NW % 2 != 0) {
 #pragma unroll
-    for (int q = 0; q < NW; ++q) w[q] = p[q];
+    for (int q = 0; q < NW; ++q) w[q] = ld_cache<NT, uint32_t>(p + q);
   } else if constexpr (NW % 4 != 0) {
 #pragma unroll
     for (int q = 0; q < NW / 2; ++q) {
-      const u32x2 x = reinterpret_cast<const u32x2*>(p)[q];
+      const u32x2 x = ld_cache<NT, u32x2>(p + 2 * q);
       w[2 * q] = x[0]; w[2 * q + 1] = x[1];
     }
   } else {
 #pragma unroll
     for (int q = 0; q < NW / 4; ++q) {
-      const u32x4 x = reinterpret_cast<const u32x4*>(p)[q];
+      const u32x4 x = ld_cache<NT, u32x4>(p + 4 * q);
 #pragma unroll
       for (int k = 0; k < 4; ++k) w[4 * q + k] = x[k];
     }
@@ -262,6 +274,8 @@ void decode_split_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
   static_assert(!PF || G == 8, "prefill waves own 8 rows");
   constexpr int kGroupWaves = split_group_waves(D, KM || VM || PF);
+  // non-temporal cache loads at two waves per SIMD (see ld_cache)
+  constexpr bool kNT = split_waves_per_simd(D, KM || VM || PF) >= 2;
   // tiles whose bytes a wave keeps in registers ahead of the one computing:
   // at one wave per SIMD (d = 256) the wave alone must cover the latency, so
   // it keeps two where four step buffers fit the 512 registers with at most
@@ -327,17 +341,24 @@ void decode_split_kernel(DecodeArgs a) {
   const int T = a.T;
   const int nt = T > 0 ? min(n, T) : 0;
   const int nq = n - nt;
-  // Quantized tiles: workgroup wg of NG takes the contiguous range
-  // [ctq*wg/NG, ctq*(wg+1)/NG) and its waves pull tiles from it one at a
-  // time, so they finish together however the compute unit schedules them
-  // (prefill: every wave takes every tile of the range, up to its rows' last
-  // position).  bf16 tail tiles (few, each worth several quantized tiles) are
-  // dealt out round-robin: tile k to workgroup k mod NG, wave (k / NG) mod
-  // kGroupWaves (prefill: to every wave of workgroup k mod NG).
+  // Quantized tiles (decode): the unit's tiles are dealt round-robin to its
+  // NG workgroups (tile t to workgroup t mod NG), and a workgroup's waves
+  // pull its tiles, in order, one at a time from an LDS counter, so they
+  // finish together however the compute unit schedules them.  At any time
+  // the workgroups of a unit read neighbouring tiles: a compact window of
+  // addresses, which HBM serves faster than far-apart ranges (read-ceiling
+  // probes; dealing chunks of one tile measured a little faster than chunks
+  // of a workgroup's size, and balances to one tile).  Prefill: workgroup
+  // wg takes the contiguous range [ctq*wg/NG, ctq*(wg+1)/NG) and every wave
+  // takes every tile of it, up to its rows' last position.  bf16 tail tiles
+  // (few, each worth several quantized tiles) are dealt out round-robin:
+  // tile k to workgroup k mod NG, wave (k / NG) mod kGroupWaves (prefill: to
+  // every wave of workgroup k mod NG).
   const int ctq = (nq + kTile - 1) / kTile;
   const int ctt = (nt + kTile - 1) / kTile;
   const int NG = (int)gridDim.x;
   const int wq0 = (int)((int64_t)ctq * blockIdx.x / NG), wq1 = (int)((int64_t)ctq * (blockIdx.x + 1) / NG);
+  const int qend = PF ? wq1 : ctq;   // a grabbed tile at or past this ends the loop
   const size_t unit = (size_t)b * a.Hkv + g;
 
   for (int i = lane; i < WROW; i += 64) wl[ZROW * WROW + i] = 0;
@@ -456,9 +477,12 @@ void decode_split_kernel(DecodeArgs a) {
   // The running maxima only move, and the accumulators are only rescaled,
   // when some score exceeds them (a wave-uniform branch); every weight stays
   // at most 1.
-  auto softmax = [&](const float (&xA)[2], const float (&xB)[2], float (&pA)[2], float (&pB)[2]) {
+  // vtrig (wave-uniform): the accumulators also take the factor vratio, the
+  // change of the V weight factor (one rescaling site for both).
+  auto softmax = [&](const float (&xA)[2], const float (&xB)[2], float (&pA)[2], float (&pB)[2],
+                     bool vtrig, float vratio) {
     const bool up = xA[0] > mA || xA[1] > mA || xB[0] > mB || xB[1] > mB;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    if (vtrig || __builtin_amdgcn_ballot_w64(up) != 0) {
       const float nA = fmax_fast(mA, row16_max(fmax_fast(xA[0], xA[1])));
       const float nB = fmax_fast(mB, row16_max(fmax_fast(xB[0], xB[1])));
       const float aA = nA > mA ? __builtin_amdgcn_exp2f(mA - nA) : 1.f;
@@ -475,7 +499,7 @@ void decode_split_kernel(DecodeArgs a) {
         alds[8 + hB] = aB;
       }
       wave_sync();
-      const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]);
+      const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]) * vratio;
 #pragma unroll
       for (int i = 0; i < NN; ++i) acc[i] *= al;
       if constexpr (VM) {
@@ -533,8 +557,7 @@ void decode_split_kernel(DecodeArgs a) {
         const uint16_t* krow = ktl + (size_t)((tok < tb ? tok : ta) % T) * D + 8 * r;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt[j], *reinterpret_cast<const bf8_t*>(krow + kBlock * j),
-                                                          d[m], 0, 0, 0);
+          d[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt[j], ld_cache<kNT, bf8_t>(krow + kBlock * j), d[m], 0, 0, 0);
       }
       bool vA[2], vB[2];
       float xA[2], xB[2], pA[2], pB[2];
@@ -548,7 +571,7 @@ void decode_split_kernel(DecodeArgs a) {
         xA[m] = vA[m] && okA ? ya : -INFINITY;
         xB[m] = vB[m] && okB ? yb : -INFINITY;
       }
-      softmax(xA, xB, pA, pB);
+      softmax(xA, xB, pA, pB, false, 1.f);
       wave_sync();
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -574,7 +597,7 @@ void decode_split_kernel(DecodeArgs a) {
       for (int i = 0; i < NN; ++i) {
         bf8_t vb;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) vb[k] = __builtin_bit_cast(__bf16, vtl[voff[k] + 16 * i]);
+        for (int k = 0; k < 8; ++k) vb[k] = __builtin_bit_cast(__bf16, ld_cache<kNT, uint16_t>(vtl + voff[k] + 16 * i));
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, vb, acc[i], 0, 0, 0);
       }
     }
@@ -582,7 +605,7 @@ void decode_split_kernel(DecodeArgs a) {
   }
 
   // ------------------------------------------------ quantized positions
-  if (wq0 < wq1) {
+  if (PF ? wq0 < wq1 : (int)blockIdx.x < ctq) {
     constexpr int KSE = KM ? 2 * NB : NB;   // 16-bit scale entries per token
     constexpr int VSE = VM ? 2 * NB : NB;
     // A operand of Q.K: the rotated query in 16-bit fixed point (step
@@ -661,37 +684,36 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if constexpr (KB == 8) {
-            R.k8[m * NB + j] = *reinterpret_cast<const u32x2*>(kt + (2 * j * kTile + 16 * m) * kChunk + k_off);
+            R.k8[m * NB + j] = ld_cache<kNT, u32x2>(kt + (2 * j * kTile + 16 * m) * kChunk + k_off);
           } else {
-            R.k4[m * NB + j] = *reinterpret_cast<const uint32_t*>(kt + (j * kTile + 16 * m) * kChunk + k_off);
+            R.k4[m * NB + j] = ld_cache<kNT, uint32_t>(kt + (j * kTile + 16 * m) * kChunk + k_off);
             if constexpr (KB == 5) {
               const int cb = D / 32 + j / 4;
-              R.kh[m * NB + j] = *reinterpret_cast<const uint32_t*>(
-                  kt + (cb * kTile + 16 * m + col) * kChunk + 4 * (j % 4));
+              R.kh[m * NB + j] = ld_cache<kNT, uint32_t>(kt + (cb * kTile + 16 * m + col) * kChunk + 4 * (j % 4));
             }
             if constexpr (KB == 6) {
               const int cb = D / 32 + j / 2;
-              R.kh[m * NB + j] = *reinterpret_cast<const uint32_t*>(
-                  kt + (cb * kTile + 16 * m + col) * kChunk + 8 * (j % 2) + 4 * (r >> 1));
+              R.kh[m * NB + j] = ld_cache<kNT, uint32_t>(kt + (cb * kTile + 16 * m + col) * kChunk + 8 * (j % 2) +
+                                                     4 * (r >> 1));
             }
           }
         }
         const size_t tok = (size_t)srow + 16 * m + col;
-        load_words(reinterpret_cast<const uint32_t*>(ksrow + tok * KSE), R.ks[m]);
-        load_words(reinterpret_cast<const uint32_t*>(vsrow + tok * VSE), R.vs[m]);
+        load_words<kNT>(reinterpret_cast<const uint32_t*>(ksrow + tok * KSE), R.ks[m]);
+        load_words<kNT>(reinterpret_cast<const uint32_t*>(vsrow + tok * VSE), R.vs[m]);
       }
       const uint8_t* vj = vt + (size_t)j2 * 64 * NN * (VB == 8 ? 8 : 4) + v_off;
 #pragma unroll
-      for (int q = 0; q < (VB == 8 ? NN / 2 : NN / 4); ++q) R.v[q] = reinterpret_cast<const u32x4*>(vj)[q];
+      for (int q = 0; q < (VB == 8 ? NN / 2 : NN / 4); ++q) R.v[q] = ld_cache<kNT, u32x4>(vj + 16 * q);
       if constexpr (VB == 5) {
         const uint8_t* hj = vt + (size_t)j2 * 64 * NN + vh_off;
 #pragma unroll
-        for (int q = 0; q < NN / 4; ++q) R.vh[q] = reinterpret_cast<const uint32_t*>(hj)[q];
+        for (int q = 0; q < NN / 4; ++q) R.vh[q] = ld_cache<kNT, uint32_t>(hj + 4 * q);
       }
       if constexpr (VB == 6) {
         const uint8_t* hj = vt + 32 * D + (size_t)j2 * 64 * NN * 2 + (size_t)lane * NN * 2;
 #pragma unroll
-        for (int q = 0; q < NN / 2; ++q) R.vh[q] = reinterpret_cast<const uint32_t*>(hj)[q];
+        for (int q = 0; q < NN / 2; ++q) R.vh[q] = ld_cache<kNT, uint32_t>(hj + 4 * q);
       }
     };
 
@@ -791,9 +813,11 @@ void decode_split_kernel(DecodeArgs a) {
         xA[m] = validA && okA ? ya : -INFINITY;
         xB[m] = validB && okB ? yb : -INFINITY;
       }
-      softmax(xA, xB, pA, pB);
       // largest V scale of the step's positions (those past the quantized
-      // range hold no data) against the weight factor's threshold
+      // range hold no data) against the weight factor's threshold; a new
+      // factor rescales the accumulators with the softmax's rescaling
+      bool vtrig = false;
+      float vratio = 1.f;
       {
         const uint32_t l0 = s0 + col < nq ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 0) : 0u;
         const uint32_t l1 = s0 + 16 + col < nq ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 1) : 0u;
@@ -804,15 +828,15 @@ void decode_split_kernel(DecodeArgs a) {
           if (mb != 0u) {
             const int e = (int)((mb >> 23) & 0xFFu) - 127;   // 2^e <= max < 2^(e+1), e >= -24
             const int nfe = 11 - e;
-            const float ratio = __uint_as_float((uint32_t)(127 + nfe - vfe) << 23);
-#pragma unroll
-            for (int i = 0; i < NN; ++i) acc[i] *= ratio;
+            vratio = __uint_as_float((uint32_t)(127 + nfe - vfe) << 23);
+            vtrig = true;
             vfe = nfe;
             const int k = e + 4;   // threshold 2^(e + 4) in fp16 bits
             vthr = k > 15 ? 0x7C00u : (k >= -14 ? (uint32_t)(k + 15) << 10 : 1u << (k + 24));
           }
         }
       }
+      softmax(xA, xB, pA, pB, vtrig, vratio);
       const float vf = __uint_as_float((uint32_t)(127 + vfe) << 23);
       // weights p * scale_v * 2^vfe in fp16 (0 for masked tokens and absent
       // heads), moved to the A-operand layout via LDS
@@ -867,9 +891,9 @@ void decode_split_kernel(DecodeArgs a) {
       }
     };
 
-    // Tiles of [wq0, wq1) come from the workgroup's LDS counter, one tile
-    // ahead: the second half of a tile and the first half of the next one
-    // load while the half before computes.
+    // Tiles come from the workgroup's LDS counter, one tile ahead: the
+    // second half of a tile and the first half of the next one load while
+    // the half before computes.
     uint32_t pf_next = 0;
     auto grab_issue = [&]() {
       uint32_t v = 0;
@@ -881,8 +905,13 @@ void decode_split_kernel(DecodeArgs a) {
       return v;
     };
     auto grab_read = [&](uint32_t v) {
-      const int t = wq0 + (int)__builtin_amdgcn_readfirstlane(v);
-      return PF && t * kTile > wlim ? wq1 : t;   // past the rows' last position
+      const int c = (int)__builtin_amdgcn_readfirstlane(v);
+      if constexpr (PF) {
+        const int t = wq0 + c;
+        return t * kTile > wlim ? wq1 : t;   // past the rows' last position
+      } else {
+        return c * NG + (int)blockIdx.x;
+      }
     };
     // query operands, built while the first loads are in flight
     auto prep_query = [&]() {
@@ -967,7 +996,7 @@ void decode_split_kernel(DecodeArgs a) {
     };
     if constexpr (kAhead == 1) {
       int t_cur = grab_read(grab_issue());
-      if (t_cur < wq1) {
+      if (t_cur < qend) {
         int t_nxt = grab_read(grab_issue());
         Regs ra, rb;
         load_step(ra, t_cur * kTile);
@@ -976,10 +1005,10 @@ void decode_split_kernel(DecodeArgs a) {
           const uint32_t t_aft_v = grab_issue();
           load_step(rb, t_cur * kTile + kStep);
           compute_step(ra, t_cur * kTile);
-          if (t_nxt < wq1) load_step(ra, t_nxt * kTile);
+          if (t_nxt < qend) load_step(ra, t_nxt * kTile);
           compute_step(rb, t_cur * kTile + kStep);
           const int t_aft = grab_read(t_aft_v);
-          if (t_nxt >= wq1) break;
+          if (t_nxt >= qend) break;
           t_cur = t_nxt;
           t_nxt = t_aft;
         }
@@ -988,12 +1017,12 @@ void decode_split_kernel(DecodeArgs a) {
       // two tiles (four steps) in registers: while one step computes, the
       // next three are loaded or in flight
       int t0 = grab_read(grab_issue());
-      if (t0 < wq1) {
+      if (t0 < qend) {
         int t1 = grab_read(grab_issue());
         Regs ra0, rb0, ra1, rb1;
         load_step(ra0, t0 * kTile);
         load_step(rb0, t0 * kTile + kStep);
-        if (t1 < wq1) {
+        if (t1 < qend) {
           load_step(ra1, t1 * kTile);
           load_step(rb1, t1 * kTile + kStep);
         }
@@ -1001,16 +1030,16 @@ void decode_split_kernel(DecodeArgs a) {
         while (true) {
           const int t2 = grab_read(grab_issue());
           compute_step(ra0, t0 * kTile);
-          if (t2 < wq1) load_step(ra0, t2 * kTile);
+          if (t2 < qend) load_step(ra0, t2 * kTile);
           compute_step(rb0, t0 * kTile + kStep);
-          if (t2 < wq1) load_step(rb0, t2 * kTile + kStep);
-          if (t1 >= wq1) break;
+          if (t2 < qend) load_step(rb0, t2 * kTile + kStep);
+          if (t1 >= qend) break;
           const int t3 = grab_read(grab_issue());
           compute_step(ra1, t1 * kTile);
-          if (t3 < wq1) load_step(ra1, t3 * kTile);
+          if (t3 < qend) load_step(ra1, t3 * kTile);
           compute_step(rb1, t1 * kTile + kStep);
-          if (t3 < wq1) load_step(rb1, t3 * kTile + kStep);
-          if (t2 >= wq1) break;
+          if (t3 < qend) load_step(rb1, t3 * kTile + kStep);
+          if (t2 >= qend) break;
           t0 = t2;
           t1 = t3;
         }
