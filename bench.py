@@ -2,7 +2,8 @@
 
 One step is the decode hot path for one batch: rotate-quantize-append one new
 token per sequence (with tail graduation), then single-query decode attention
-over the whole cache.  Default workload "long": batch 8, 40 query / 8 KV
+over the whole cache, as one kvq_decode_step call (two launches: the split
+kernel, which also appends the token, and the combine).  Default workload "long": batch 8, 40 query / 8 KV
 heads, head_dim 128, 65536 cached tokens, K 8-bit / V 4-bit 32-element blocks
 with fp16 scales, newest 1024 tokens in a bf16 tail, Hadamard-128 rotation.
 
@@ -151,6 +152,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=64,
                     help="(sequence, KV head) units the CPU oracle times (all when >= batch * KV heads)")
     ap.add_argument("--no-append", action="store_true", help="skip the bulk append measurement")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the secondary run with the append and the attention as two calls")
     ap.add_argument("--no-rotation-off", action="store_true",
                     help="skip the secondary run with rotation disabled")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
@@ -258,11 +261,22 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if args.paged else measured_traffic(args.workload)},
-        "secondary": {"attention_kernel_us": percentiles(kern_ms),
-                      "single_token_append_us": percentiles(run["app_ms"])},
+        "secondary": {"attention_kernel_us": percentiles(kern_ms)},
     }
     q0 = run["q0"]
     del run
+
+    if not args.no_unfused:
+        # the same step as two calls: kvq_rotate_quantize_append, then
+        # kvq_decode_attention (three launches instead of two)
+        uf = decode_run(torch, kvq, w, dev, args.warmup, args.steps, True, None, paged=args.paged,
+                        fused=False)
+        result["secondary"]["unfused_step"] = {
+            "us_per_step": round(uf["ms_step"] * 1e3, 2),
+            "attention_kernel_us": percentiles(uf["kern_ms"]),
+            "single_token_append_us": percentiles(uf["app_ms"])}
+        log("append + attention as two calls: step %.1f us" % (uf["ms_step"] * 1e3))
+        del uf
 
     if not args.no_rotation_off:
         # the same step with rotation disabled for K and V (no query rotation,
@@ -271,7 +285,6 @@ def main():
         result["secondary"]["rotation_off"] = {
             "us_per_step": round(off["ms_step"] * 1e3, 2),
             "attention_kernel_us": percentiles(off["kern_ms"]),
-            "single_token_append_us": percentiles(off["app_ms"]),
             "step_slowdown_of_rotation_pct": round(100 * (ms_step / off["ms_step"] - 1), 2)}
         log("rotation off: step %.1f us" % (off["ms_step"] * 1e3))
         del off
@@ -284,8 +297,7 @@ def main():
         result["secondary"]["paged"] = {
             "us_per_step": round(pg["ms_step"] * 1e3, 2),
             "attention_kernel_us": percentiles(pg["kern_ms"]),
-            "attention_kernel_gbs": round(pg["bytes_kern"] / (pg_kern * 1e-3) / 1e9, 1),
-            "single_token_append_us": percentiles(pg["app_ms"])}
+            "attention_kernel_gbs": round(pg["bytes_kern"] / (pg_kern * 1e-3) / 1e9, 1)}
         log("paged: step %.1f us, kernel %.1f us" % (pg["ms_step"] * 1e3, pg_kern * 1e3))
         del pg
 
@@ -310,7 +322,7 @@ def percentiles(ms):
             "p90": round(float(p[2]), 2)}
 
 
-def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False):
+def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False, fused=True):
     """Fill a cache for workload w, then run warm-up steps, `steps` timed
     steps, and as many steps again with HIP events around the split kernel
     (recorded by the library on the call's stream) and around the append
@@ -370,6 +382,14 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False):
     ev_app = [new_events() for _ in range(total_steps)]
 
     def step(s, events):
+        if fused:
+            # one call: append the token and attend (kvq_decode_step)
+            if events:
+                kvq.kvq_profile_decode_events(ev[s][0], ev[s][1])
+            kvq.kvq_decode_step(cfg, cache, ks[s], vs[s], qs[s], lens, out=out, workspace=ws)
+            for b in range(B):
+                lens[b] += 1
+            return
         if events:
             ev_app[s][0].record()
         kvq.kvq_rotate_quantize_append(cfg, cache, ks[s], vs[s], lens)
@@ -402,7 +422,7 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False):
     res = {"ms_step": elapsed / steps * 1e3, "bytes_step": float(np.mean(step_bytes)),
            "bytes_kern": float(np.mean(kern_bytes)),
            "kern_ms": [kvq.kernel_elapsed_ms(ev[s][0], ev[s][1]) for s in timed],
-           "app_ms": [ev_app[s][0].elapsed_time(ev_app[s][1]) for s in timed],
+           "app_ms": [] if fused else [ev_app[s][0].elapsed_time(ev_app[s][1]) for s in timed],
            "fill_mtok_s": fill_mtok_s, "q0": qs[0]}
     del cache, qs, ks, vs
     return res

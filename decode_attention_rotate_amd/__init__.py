@@ -27,7 +27,7 @@ __all__ = [
     "kvq_decode_workspace_bytes", "kvq_rotate_quantize_append",
     "kvq_decode_attention", "kvq_dequantize", "kvq_status_str",
     "kvq_profile_decode_events", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
-    "kvq_decode_attention_static", "KVQ_STATIC_WORKSPACE_BYTES",
+    "kvq_decode_attention_static", "KVQ_STATIC_WORKSPACE_BYTES", "kvq_decode_step",
     "KVQ_PAGE_TOKENS", "LIB_PATH",
 ]
 
@@ -248,6 +248,37 @@ def kvq_decode_attention(cfg, cache, q, seq_len, sm_scale=None, out=None,
         float(sm_scale), _lens(seq_len, cfg.batch), out.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _capi.check(st, "kvq_decode_attention")
+    return out
+
+
+def kvq_decode_step(cfg, cache, k_new, v_new, q, seq_len, sm_scale=None, out=None,
+                    workspace=None, stream=None):
+    """One decode step: append k_new / v_new [B][1][Hkv][d] at positions
+    seq_len[b] (lengths before the step), then attend q [B][Hq][d] over the
+    seq_len[b] + 1 positions; returns float32 [B][Hq][d].  The caller
+    advances its lengths afterwards."""
+    torch = _torch()
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
+        _device_tensor(t, name)
+    B, Hq, d = q.shape
+    if (B, d) != (cfg.batch, cfg.head_dim) or tuple(k_new.shape) != (B, 1, cfg.n_kv_heads, d) \
+            or tuple(v_new.shape) != tuple(k_new.shape) or v_new.dtype != k_new.dtype:
+        raise ValueError("shapes q %s, k_new %s, v_new %s do not match the configuration"
+                         % (tuple(q.shape), tuple(k_new.shape), tuple(v_new.shape)))
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _device_tensor(out, "out")
+    need = kvq_decode_workspace_bytes(cfg, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = _capi.lib().kvq_decode_step(
+        ctypes.byref(cfg), ctypes.byref(cache.struct), k_new.data_ptr(), v_new.data_ptr(),
+        _dtype_code(k_new), q.data_ptr(), _dtype_code(q), Hq, float(sm_scale),
+        _lens(seq_len, cfg.batch), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _capi.check(st, "kvq_decode_step")
     return out
 
 

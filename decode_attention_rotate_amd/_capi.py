@@ -30,7 +30,7 @@ EXPORTS = (
     "kvq_decode_workspace_bytes", "kvq_rotate_quantize_append",
     "kvq_decode_attention", "kvq_dequantize", "kvq_status_str",
     "kvq_profile_decode_events", "kvq_prefill_workspace_bytes",
-    "kvq_prefill_attention", "kvq_decode_attention_static",
+    "kvq_prefill_attention", "kvq_decode_attention_static", "kvq_decode_step",
 )
 KVQ_STATIC_WORKSPACE_BYTES = 33554432
 
@@ -95,6 +95,8 @@ def lib():
             "kvq_rotate_quantize_append": (I32, [CFG, CACHE, vp, vp, I32, I32, P(I32), vp]),
             "kvq_decode_attention": (I32, [CFG, CACHE, vp, I32, I32, ctypes.c_float, P(I32),
                                            vp, vp, SZ, vp]),
+            "kvq_decode_step": (I32, [CFG, CACHE, vp, vp, I32, vp, I32, I32, ctypes.c_float, P(I32),
+                                      vp, vp, SZ, vp]),
             "kvq_decode_attention_static": (I32, [CFG, CACHE, vp, I32, I32, ctypes.c_float,
                                                   P(I32), vp, vp]),
             "kvq_prefill_workspace_bytes": (SZ, [CFG, I32, I32]),

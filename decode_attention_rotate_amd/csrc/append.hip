@@ -28,8 +28,7 @@
 // one (sequence, KV head, plane).  The in-lane butterfly stages h = 1..16 run
 // in registers, the remaining stages cross lanes with DPP / ds_swizzle, and
 // the block absmax and the codes never leave the lane.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "append_one.hpp"
 
 namespace kvq {
 namespace {
@@ -69,107 +68,6 @@ __device__ inline void load_bf16_block(const uint16_t* row, float (&x)[32]) {
       x[q * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
   }
-}
-
-// K codes of block j of position p, row layout (tiled 16-byte chunks), from
-// the quantizer's words m (low byte: offset code u = c + 2^(BITS-1)).
-template <int D, int BITS>
-__device__ inline void store_k_row(const uint32_t (&m)[32], uint8_t* plane, int p, int j) {
-  constexpr int RP = padded_row_bytes(D, BITS);
-  if constexpr (BITS == 8) {
-    // two's-complement bytes: u ^ 0x80 = c
-    uint32_t w[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      w[k] = gather_low_bytes(m[4 * k], m[4 * k + 1], m[4 * k + 2], m[4 * k + 3]) ^ 0x80808080u;
-    *reinterpret_cast<uint4*>(plane + chunk_offset(p, 2 * j, RP)) = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint4*>(plane + chunk_offset(p, 2 * j + 1, RP)) = make_uint4(w[4], w[5], w[6], w[7]);
-  } else {
-    // nibble pairs: element 2i low, 2i+1 high (u < 16 needs no mask)
-    uint32_t pr[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pr[i] = BITS == 4 ? (m[2 * i + 1] << 4) | m[2 * i] : (m[2 * i + 1] << 4) | (m[2 * i] & 15u);
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = gather_low_bytes(pr[4 * k], pr[4 * k + 1], pr[4 * k + 2], pr[4 * k + 3]);
-    *reinterpret_cast<uint4*>(plane + chunk_offset(p, j, RP)) = make_uint4(w[0], w[1], w[2], w[3]);
-    if constexpr (BITS == 5) {
-      uint32_t hw = 0;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) hw |= ((m[e] >> 4) & 1u) << hibit_pos(e);
-      const int byte = D / 2 + 4 * j;
-      *reinterpret_cast<uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk) = hw;
-    }
-    if constexpr (BITS == 6) {
-      uint32_t hw[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 32; ++e) hw[e / 16] |= ((m[e] >> 4) & 3u) << hi2_pos(e);
-      const int byte = D / 2 + 8 * j;
-      *reinterpret_cast<uint2*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk) = make_uint2(hw[0], hw[1]);
-    }
-  }
-}
-
-// Quantize one block with the symmetric rule, or with the scale-and-min
-// rule when minf (4/5-bit only); the codes' low bytes are what the planes
-// store (c + 2^(bits-1), or the level u), the result the scale (pair) bits.
-template <int BITS>
-__device__ inline uint32_t quantize_fmt(bool minf, const float (&x)[32], uint32_t (&c)[32]) {
-  if constexpr (BITS == 4 || BITS == 5) {
-    if (minf) return quantize_block_min<BITS>(x, c);
-  }
-  return quantize_block<BITS>(x, c);
-}
-
-template <int D>
-__device__ inline uint32_t quantize_k(int bits, bool minf, const float (&x)[32], uint32_t (&c)[32],
-                                      bool active, uint8_t* plane, int p, int j) {
-  uint32_t s;
-  if (bits == 4) {
-    s = quantize_fmt<4>(minf, x, c);
-    if (active) store_k_row<D, 4>(c, plane, p, j);
-  } else if (bits == 5) {
-    s = quantize_fmt<5>(minf, x, c);
-    if (active) store_k_row<D, 5>(c, plane, p, j);
-  } else if (bits == 6) {
-    s = quantize_block<6>(x, c);
-    if (active) store_k_row<D, 6>(c, plane, p, j);
-  } else {
-    s = quantize_block<8>(x, c);
-    if (active) store_k_row<D, 8>(c, plane, p, j);
-  }
-  return s;
-}
-
-template <int D>
-__device__ inline uint32_t quantize_any(int bits, bool minf, const float (&x)[32], uint32_t (&c)[32]) {
-  if (bits == 4) return quantize_fmt<4>(minf, x, c);
-  if (bits == 5) return quantize_fmt<5>(minf, x, c);
-  if (bits == 6) return quantize_block<6>(x, c);
-  return quantize_block<8>(x, c);
-}
-
-// Scale entry of block j of position l (0..63) of a tile: one fp16, or an
-// (s, m) pair of fp16 (one 32-bit word) for scale-and-min blocks.  sc is the
-// tile's first entry.
-template <int D>
-__device__ inline void store_scale(uint16_t* sc, bool minf, int l, int j, uint32_t s) {
-  if (minf) reinterpret_cast<uint32_t*>(sc)[l * (D / kBlock) + j] = s;
-  else sc[l * (D / kBlock) + j] = (uint16_t)s;
-}
-// First scale entry, K row tile and V tile of tile slot `slot` in plane pl.
-template <int D>
-__device__ inline uint16_t* scale_tile(const AppendArgs& a, int pl, size_t slot) {
-  return a.scales[pl] + slot * (size_t)kTile * (D / kBlock) * (a.minf[pl] ? 2 : 1);
-}
-template <int D>
-__device__ inline uint8_t* k_tile(const AppendArgs& a, size_t slot, int bits) {
-  return a.codes[0] + slot * (size_t)kTile * padded_row_bytes(D, bits);
-}
-template <int D>
-__device__ inline uint8_t* v_tile(const AppendArgs& a, size_t slot, int bits) {
-  return a.codes[1] + slot * (size_t)v_tile_bytes(D, bits);
 }
 
 // Merge the slots of one V item whose bit is set in `mask` into memory.
@@ -225,22 +123,6 @@ __device__ inline void store_v_item(uint8_t* tile, int item, uint64_t u, uint32_
       *dh = (uint16_t)hi;
     }
   }
-}
-
-// Positions [q0, q1) that become quantized and the first position of the
-// tail after the append of sequence b.
-struct AppendRange {
-  int len, n1, q0, q1, t0;
-};
-__device__ inline AppendRange append_range(const AppendArgs& a, int b) {
-  AppendRange r;
-  r.len = a.len[b];
-  r.n1 = r.len + a.n_new;
-  const int T = a.T;
-  r.q0 = T > 0 ? max(0, r.len - T) : r.len;
-  r.q1 = T > 0 ? max(0, r.n1 - T) : r.n1;
-  r.t0 = max(r.len, r.n1 - T);
-  return r;
 }
 
 // Quantize the positions of block bx of [q0 & ~7, q1) (RPB per block) for
@@ -398,148 +280,15 @@ __global__ __launch_bounds__(256) void append_small_kernel(AppendArgs a) {
   if (a.T > 0) tail_part<D>(a, 0, g, b, pl);
 }
 
-// One new token per sequence (a decode step), one wave per (b, g, plane).
-// Lanes [0, LPR) hold the new token's blocks and rotate them; lanes
-// [32, 32 + LPR) hold the row leaving the bf16 tail, when there is one.  The
-// position that becomes quantized is the new token itself without a tail,
-// the leaving row with one.  Every global load (input row, ring row, the V
-// items the quantized codes merge into) is issued before any arithmetic, so
-// the wave waits for memory once; the new row overwrites the ring slot the
-// leaving row was read from only after a barrier.
-// FAST: no tail and absmax blocks in both planes (see quant_part).
+// One new token per sequence (a decode step), one wave per (b, g, plane):
+// append_one_load and append_one_finish, shared with the fused decode step.
 template <int D, int VB, bool FAST>
 __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
-  constexpr int LPR = D / kBlock;
-  const int lane = threadIdx.x;
-  const int g = blockIdx.x, b = blockIdx.y, pl = blockIdx.z;
-  const int j = (lane & 31) % LPR;   // block of lane l and of lane 32 + l
-  const AppendRange rg = append_range(a, b);
-  const int len = rg.len, T = a.T;
-  const bool new_lane = lane < LPR;
-  const bool ring_lane = T > 0 && rg.q1 > rg.q0 && lane >= 32 && lane < 32 + LPR;
-  const int pq = rg.q0;                          // the quantized position
-  // slot of pq's tile (-1: no quantized position, or a page outside the pool)
-  const long long qslot = rg.q1 > rg.q0 ? tile_slot(a.map, b, g, pq / kTile) : -1LL;
-  const bool q_lane = qslot >= 0 && (T > 0 ? ring_lane : new_lane);
-  const size_t qs = qslot >= 0 ? (size_t)qslot : 0;
-  const size_t unit = (size_t)b * a.Hkv + g;
-  const int bits = pl == 0 ? a.bits[0] : VB;   // V's width is the template's
-
-  // raw loads first (converted below, so no load waits for another)
-  uint4 rin[8], rring[4];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) rin[q] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) rring[q] = make_uint4(0u, 0u, 0u, 0u);
-  if (new_lane) {
-    const size_t off = ((size_t)b * a.Hkv + g) * D + (size_t)kBlock * j;
-    if (a.dtype == KVQ_BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.src[pl]) + off);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rin[q] = src[q];
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.src[pl]) + off);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) rin[q] = src[q];
-    }
-  }
-  if (ring_lane) {
-    const uint4* src = reinterpret_cast<const uint4*>(a.tail[pl] + (unit * T + pq % T) * D + kBlock * j);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) rring[q] = src[q];
-  }
-  // V items of this lane's 32 elements at the quantized position
-  uint8_t* vtile = v_tile<D>(a, qs, VB);
-  uint32_t oldw[VB == 8 ? 1 : 32];
-  uint32_t oldh[VB == 5 || VB == 6 ? 32 : 1];
-  if constexpr (VB != 8) {
-    if (pl == 1 && q_lane) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int item = v_item(D, pq % kTile, kBlock * j + i);
-        oldw[i] = reinterpret_cast<const uint32_t*>(vtile)[item];
-        if constexpr (VB == 5) oldh[i] = vtile[32 * D + item];
-        if constexpr (VB == 6) oldh[i] = reinterpret_cast<const uint16_t*>(vtile + 32 * D)[item];
-      }
-    }
-  }
-
-  float x[32], y[32];
-  auto widen_bf16 = [](const uint4 (&r)[8], float (&f)[32]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        f[q * 8 + 2 * k] = __uint_as_float(w[k] << 16);
-        f[q * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
-    }
-  };
-  if (a.dtype == KVQ_BF16) {
-    widen_bf16(rin, x);
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      x[4 * q] = __uint_as_float(rin[q].x); x[4 * q + 1] = __uint_as_float(rin[q].y);
-      x[4 * q + 2] = __uint_as_float(rin[q].z); x[4 * q + 3] = __uint_as_float(rin[q].w);
-    }
-  }
-  {
-    uint4 r8[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { r8[q] = rring[q]; r8[q + 4] = make_uint4(0u, 0u, 0u, 0u); }
-    widen_bf16(r8, y);
-  }
-  if (a.rotate[pl]) {                            // every lane takes part
-    if (a.has_signs) apply_signs(x, a.signs[j]);
-    if constexpr (FAST) rotate_row_for_absmax<D>(x, lane, a.cd);
-    else rotate_row<D>(x, lane, a.cd);
-  }
-  if (q_lane) {
-    float z[32];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) z[e] = T > 0 ? y[e] : x[e];
-    const bool minf = a.minf[pl] != 0;
-    uint16_t* scales = scale_tile<D>(a, pl, qs);
-    uint32_t c[32];
-    if (pl == 0) {
-      store_scale<D>(scales, minf, pq % kTile, j,
-                     quantize_k<D>(bits, minf, z, c, true, k_tile<D>(a, qs, bits), pq % kTile, j));
-    } else {
-      store_scale<D>(scales, minf, pq % kTile, j, quantize_fmt<VB>(minf, z, c));
-      const int k = pq % 8;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int item = v_item(D, pq % kTile, kBlock * j + i);
-        const uint32_t u = c[i] & 0xFFu;   // offset code
-        if constexpr (VB == 8) {
-          vtile[8 * item + k] = (uint8_t)u;
-        } else {
-          const int nb = v_nibble(k);
-          reinterpret_cast<uint32_t*>(vtile)[item] = (oldw[i] & ~(15u << (4 * nb))) | ((u & 15u) << (4 * nb));
-          if constexpr (VB == 5)
-            vtile[32 * D + item] = (uint8_t)((oldh[i] & ~(1u << nb)) | (((u >> 4) & 1u) << nb));
-          if constexpr (VB == 6)
-            reinterpret_cast<uint16_t*>(vtile + 32 * D)[item] =
-                (uint16_t)((oldh[i] & ~(3u << (2 * nb))) | (((u >> 4) & 3u) << (2 * nb)));
-        }
-      }
-    }
-  }
-  if (T == 0) return;
-  __syncthreads();   // the ring row has been read
-  if (new_lane) {
-    uint4* dst = reinterpret_cast<uint4*>(a.tail[pl] + (unit * T + len % T) * D + kBlock * j);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = f32_to_bf16_bits(x[q * 8 + 2 * k]) | (f32_to_bf16_bits(x[q * 8 + 2 * k + 1]) << 16);
-      dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
+  const OneArgs o = one_args(a);
+  OneLoads L;
+  append_one_load<D, VB>(o, blockIdx.x, blockIdx.y, blockIdx.z, a.len[blockIdx.y], true, L);
+  append_one_finish<D, VB, FAST>(o, blockIdx.x, blockIdx.y, blockIdx.z, a.len[blockIdx.y], true, L, nullptr,
+                                 nullptr);
 }
 
 template <int D>

@@ -47,6 +47,7 @@
 // block at the end.
 #pragma once
 
+#include "append_one.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -305,6 +306,10 @@ void decode_split_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9 + (VM ? 8 * NB : 0)) * WROW];
   __shared__ __align__(16) float alds_all[kGroupWaves][16];
   __shared__ uint32_t tile_ctr;
+  // fused step: new K, new V, quantized K, quantized V values; the two
+  // positions' weights per head
+  __shared__ __align__(16) float step_vals[PF ? 1 : 4 * D];
+  __shared__ float step_w[2][8];
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -341,6 +346,14 @@ void decode_split_kernel(DecodeArgs a) {
   const int T = a.T;
   const int nt = T > 0 ? min(n, T) : 0;
   const int nq = n - nt;
+  // Fused decode step (decode only): this launch also appends the step's
+  // token, so the positions the append changes, nq - 1 (the one that becomes
+  // quantized, if any) and, with a tail, n - 1 (the new token), are attended
+  // to from the values the append computes (below), not read from the
+  // planes and the ring, which the append is writing meanwhile.
+  const bool stp = !PF && a.step_on != 0;
+  const int nqr = stp ? max(nq - 1, 0) : nq;   // quantized positions read from the planes
+  const int ntr = stp && T > 0 ? n - 1 : n;    // tail positions [nq, ntr) read from the ring
   // Quantized tiles (decode): the unit's tiles are dealt round-robin to its
   // NG workgroups (tile t to workgroup t mod NG), and a workgroup's waves
   // pull its tiles, in order, one at a time from an LDS counter, so they
@@ -354,8 +367,8 @@ void decode_split_kernel(DecodeArgs a) {
   // (few, each worth several quantized tiles) are dealt out round-robin:
   // tile k to workgroup k mod NG, wave (k / NG) mod kGroupWaves (prefill: to
   // every wave of workgroup k mod NG).
-  const int ctq = (nq + kTile - 1) / kTile;
-  const int ctt = (nt + kTile - 1) / kTile;
+  const int ctq = (nqr + kTile - 1) / kTile;
+  const int ctt = (ntr - nq + kTile - 1) / kTile;
   const int NG = (int)gridDim.x;
   const int wq0 = (int)((int64_t)ctq * blockIdx.x / NG), wq1 = (int)((int64_t)ctq * (blockIdx.x + 1) / NG);
   const int qend = PF ? wq1 : ctq;   // a grabbed tile at or past this ends the loop
@@ -519,6 +532,79 @@ void decode_split_kernel(DecodeArgs a) {
     lB += pB[0] + pB[1];
   };
 
+  // ------------------------------------------------ fused step's positions
+  // One wave per (b, g, head chunk) appends the step's token to the cache
+  // (the first chunk stores it; every chunk needs its values) and attends
+  // to the positions the append changes: position 0 below is the one that
+  // becomes quantized (nq >= 1), position 1 the new token in the bf16 tail
+  // (T > 0).  It runs before the wave's tiles (the workgroup's other waves
+  // take more of them meanwhile), and issues every load it needs (both
+  // planes' rows, the V items the new codes merge into, the query) before
+  // it waits once.  The contributions take the V weight factor 2^vfe (1
+  // here).  The ring slot the new token overwrites held the position that
+  // leaves the tail, which no other wave reads in this launch.
+  if constexpr (!PF) {
+    if (stp && blockIdx.x == 0 && wv == 0) {
+      float* sv = step_vals;
+      const bool first = (int)blockIdx.y % a.n_gchunks == 0;
+      OneLoads LK, LV;
+      append_one_load<D, VB>(a.step, g, b, 0, n - 1, first, LK);
+      append_one_load<D, VB>(a.step, g, b, 1, n - 1, first, LV);
+      float f[NB][8];
+      load_query(f);
+      append_one_finish<D, VB, false, KB>(a.step, g, b, 0, n - 1, first, LK, sv, sv + 2 * D);
+      append_one_finish<D, VB, false, KB>(a.step, g, b, 1, n - 1, first, LV, sv + D, sv + 3 * D);
+      wave_sync();
+      const bool has0 = nq >= 1, has1 = T > 0;
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = kBlock * j + 8 * r + i;
+          d0 = __builtin_fmaf(f[j][i], has0 ? sv[2 * D + e] : 0.f, d0);
+          d1 = __builtin_fmaf(f[j][i], has1 ? sv[e] : 0.f, d1);
+        }
+      }
+      d0 += __shfl_xor(d0, 16);
+      d0 += __shfl_xor(d0, 32);
+      d1 += __shfl_xor(d1, 16);
+      d1 += __shfl_xor(d1, 32);
+      // head h's score sits in lane 2h (column 2h, row group 0)
+      const float cs = a.sm_scale * kLog2e;
+      const float a0 = __shfl(d0 * cs, 4 * r), b0 = __shfl(d0 * cs, 4 * r + 2);
+      const float a1 = __shfl(d1 * cs, 4 * r), b1 = __shfl(d1 * cs, 4 * r + 2);
+      float xA[2], xB[2], pA[2], pB[2];
+      xA[0] = col == 0 && has0 && okA ? a0 : -INFINITY;
+      xA[1] = col == 0 && has1 && okA ? a1 : -INFINITY;
+      xB[0] = col == 0 && has0 && okB ? b0 : -INFINITY;
+      xB[1] = col == 0 && has1 && okB ? b1 : -INFINITY;
+      softmax(xA, xB, pA, pB, false, 1.f);
+      const float vfac = __uint_as_float((uint32_t)(127 + vfe) << 23);
+      wave_sync();
+      if (col == 0) {
+        step_w[0][hA] = pA[0];
+        step_w[0][hB] = pB[0];
+        step_w[1][hA] = pA[1];
+        step_w[1][hB] = pB[1];
+      }
+      wave_sync();
+      if (r < 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float w0 = has0 ? step_w[0][4 * r + k] * vfac : 0.f;
+          const float w1 = has1 ? step_w[1][4 * r + k] * vfac : 0.f;
+#pragma unroll
+          for (int i = 0; i < NN; ++i) {
+            const int e = 16 * i + col;
+            const float v0 = has0 ? sv[3 * D + e] : 0.f, v1 = has1 ? sv[D + e] : 0.f;
+            acc[i][k] = __builtin_fmaf(w1, v1, __builtin_fmaf(w0, v0, acc[i][k]));
+          }
+        }
+      }
+    }
+  }
+
   // ------------------------------------------------ bf16 tail positions
   // Same steps on bf16 rows with bf16 matrix products.  The float32 query
   // and the weights are each split into a high and a low bf16 part, so the
@@ -547,7 +633,7 @@ void decode_split_kernel(DecodeArgs a) {
     const float csA = okA ? a.sm_scale * kLog2e : 0.f;
     const float csB = okB ? a.sm_scale * kLog2e : 0.f;
     for (int kt = tk0; kt < ctt; kt += NG * (PF ? 1 : kGroupWaves)) {
-    const int ta = nq + kt * kTile, tb = min(n, ta + kTile);
+    const int ta = nq + kt * kTile, tb = min(ntr, ta + kTile);
     if (PF && ta > wlim) break;
     for (int s0 = ta; s0 < tb && (!PF || s0 <= wlim); s0 += kStep) {
       f4_t d[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
@@ -806,8 +892,8 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int tok = s0 + 16 * m + col;
-        const bool validA = tok < nq && (!PF || tok <= limA);
-        const bool validB = tok < nq && (!PF || tok <= limB);
+        const bool validA = tok < nqr && (!PF || tok <= limA);
+        const bool validB = tok < nqr && (!PF || tok <= limB);
         float ya = sA[m] * ckA, yb = sB[m] * ckB;
         asm volatile("" : "+v"(ya), "+v"(yb));   // selects, not branches
         xA[m] = validA && okA ? ya : -INFINITY;
@@ -819,8 +905,8 @@ void decode_split_kernel(DecodeArgs a) {
       bool vtrig = false;
       float vratio = 1.f;
       {
-        const uint32_t l0 = s0 + col < nq ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 0) : 0u;
-        const uint32_t l1 = s0 + 16 + col < nq ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 1) : 0u;
+        const uint32_t l0 = s0 + col < nqr ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 0) : 0u;
+        const uint32_t l1 = s0 + 16 + col < nqr ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 1) : 0u;
         const uint32_t lm = l0 > l1 ? l0 : l1;
         if (__builtin_amdgcn_ballot_w64(lm >= vthr) != 0) {
           const float mx = row16_max((float)__builtin_bit_cast(_Float16, (uint16_t)lm));

@@ -28,6 +28,44 @@ struct AppendArgs {
 };
 hipError_t launch_append(int D, const AppendArgs& a, int B, hipStream_t s);
 
+// What the one-token append of a decode step reads (AppendArgs without the
+// lengths, which the caller passes): the fused decode step carries it in its
+// own arguments.
+struct OneArgs {
+  const void* src[2];        // k_new, v_new: [B][1][Hkv][D]
+  uint8_t* codes[2];
+  uint16_t* scales[2];
+  uint16_t* tail[2];
+  int32_t bits[2];
+  int32_t minf[2];
+  int32_t rotate[2];
+  int32_t Hkv, T, dtype;
+  TileMap map;
+  float cd;
+  int32_t has_signs;
+  uint32_t signs[8];
+};
+__host__ __device__ inline OneArgs one_args(const AppendArgs& a) {
+  OneArgs o;
+  for (int p = 0; p < 2; ++p) {
+    o.src[p] = a.src[p];
+    o.codes[p] = a.codes[p];
+    o.scales[p] = a.scales[p];
+    o.tail[p] = a.tail[p];
+    o.bits[p] = a.bits[p];
+    o.minf[p] = a.minf[p];
+    o.rotate[p] = a.rotate[p];
+  }
+  o.Hkv = a.Hkv;
+  o.T = a.T;
+  o.dtype = a.dtype;
+  o.map = a.map;
+  o.cd = a.cd;
+  o.has_signs = a.has_signs;
+  for (int i = 0; i < 8; ++i) o.signs[i] = a.signs[i];
+  return o;
+}
+
 // ------------------------------------------------------------- dequantize
 struct DequantArgs {
   const uint8_t* codes;
@@ -79,6 +117,10 @@ struct DecodeArgs {
   float cd, sm_scale;        // fp32(1/sqrt(D)); softmax scale
   int32_t has_signs;         // q is rotated by H diag(s) (signs as in AppendArgs)
   uint32_t signs[8];
+  // fused decode step: the launch also appends one token per sequence (the
+  // lengths below then count it); step_on 0: plain decode over the cache
+  int32_t step_on;
+  OneArgs step;
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);

@@ -197,6 +197,36 @@ int sign_mask(const kvq_config& c, uint32_t (&w)[8]) {
   return 1;
 }
 
+// Append arguments of a checked call (lengths left to the caller).
+AppendArgs append_args(const kvq_config& c, const kvq_cache* cache, const void* k_new, const void* v_new,
+                       kvq_dtype dtype, int32_t n_new) {
+  AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src[0] = k_new;
+  a.src[1] = v_new;
+  a.codes[0] = static_cast<uint8_t*>(cache->k_codes);
+  a.codes[1] = static_cast<uint8_t*>(cache->v_codes);
+  a.scales[0] = static_cast<uint16_t*>(cache->k_scales);
+  a.scales[1] = static_cast<uint16_t*>(cache->v_scales);
+  a.tail[0] = static_cast<uint16_t*>(cache->k_tail);
+  a.tail[1] = static_cast<uint16_t*>(cache->v_tail);
+  a.bits[0] = c.k_bits;
+  a.bits[1] = c.v_bits;
+  a.minf[0] = c.k_min;
+  a.minf[1] = c.v_min;
+  a.rotate[0] = c.rotate_k;
+  a.rotate[1] = c.rotate_v;
+  a.Hkv = c.n_kv_heads;
+  a.n_new = n_new;
+  a.T = c.tail_len;
+  a.cap = (int32_t)cap_tokens(c);
+  a.map = tile_map(c, cache);
+  a.dtype = dtype;
+  a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
+  a.has_signs = sign_mask(c, a.signs);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,30 +295,7 @@ kvq_status kvq_rotate_quantize_append(const kvq_config* cfg, const kvq_cache* ca
   if (!k_new || !v_new) return KVQ_ERR_INVALID;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGN;
 
-  AppendArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.src[0] = k_new;
-  a.src[1] = v_new;
-  a.codes[0] = static_cast<uint8_t*>(cache->k_codes);
-  a.codes[1] = static_cast<uint8_t*>(cache->v_codes);
-  a.scales[0] = static_cast<uint16_t*>(cache->k_scales);
-  a.scales[1] = static_cast<uint16_t*>(cache->v_scales);
-  a.tail[0] = static_cast<uint16_t*>(cache->k_tail);
-  a.tail[1] = static_cast<uint16_t*>(cache->v_tail);
-  a.bits[0] = c.k_bits;
-  a.bits[1] = c.v_bits;
-  a.minf[0] = c.k_min;
-  a.minf[1] = c.v_min;
-  a.rotate[0] = c.rotate_k;
-  a.rotate[1] = c.rotate_v;
-  a.Hkv = c.n_kv_heads;
-  a.n_new = n_new;
-  a.T = c.tail_len;
-  a.cap = (int32_t)cap_tokens(c);
-  a.map = tile_map(c, cache);
-  a.dtype = dtype;
-  a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
-  a.has_signs = sign_mask(c, a.signs);
+  AppendArgs a = append_args(c, cache, k_new, v_new, dtype, n_new);
   for (int b = 0; b < c.batch; ++b) a.len[b] = seq_len[b];
   return hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)));
 }
@@ -334,9 +341,11 @@ kvq_status plan_decode(const kvq_config* cfg, const kvq_cache* cache, const void
 }
 
 // Queue the split kernel and the combine of a checked decode call.
+// step: the fused decode step's one-token append (seq_len then counts the
+// token), or null.
 kvq_status run_decode(const kvq_config& c, const kvq_cache* cache, const void* q, kvq_dtype dtype,
                       int32_t n_q_heads, float sm_scale, const int32_t* seq_len, float* out,
-                      void* workspace, const DecodePlan& plan, void* stream) {
+                      void* workspace, const DecodePlan& plan, void* stream, const OneArgs* step = nullptr) {
   kvq_status st;
   const Schedule& sc = plan.sc;
   const WsLayout& wl = plan.wl;
@@ -369,6 +378,10 @@ kvq_status run_decode(const kvq_config& c, const kvq_cache* cache, const void* q
   da.cap = (int32_t)cap_tokens(c);
   da.map = tile_map(c, cache);
   da.S = sc.S;
+  if (step) {
+    da.step_on = 1;
+    da.step = *step;
+  }
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
   const dim3 grid(sc.S / split_group_waves(c.head_dim, c.k_min || c.v_min), c.n_kv_heads * sc.nchunk,
                   c.batch);
@@ -422,6 +435,42 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
   if (workspace_bytes < plan.wl.total) return KVQ_ERR_WORKSPACE;
   return run_decode(*cfg, cache, q, dtype, n_q_heads, sm_scale, seq_len, out, workspace, plan, stream);
+}
+
+kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, const void* k_new,
+                           const void* v_new, kvq_dtype kv_dtype, const void* q, kvq_dtype q_dtype,
+                           int32_t n_q_heads, float sm_scale, const int32_t* seq_len, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = *cfg;
+  if ((st = check_cache(c, cache)) != KVQ_OK) return st;
+  if (kv_dtype != KVQ_BF16 && kv_dtype != KVQ_F32) return KVQ_ERR_INVALID;
+  if (!seq_len || !k_new || !v_new) return KVQ_ERR_INVALID;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGN;
+  int32_t lens[KVQ_MAX_BATCH];
+  for (int b = 0; b < c.batch; ++b) {
+    if (seq_len[b] < 0) return KVQ_ERR_INVALID;
+    if ((int64_t)seq_len[b] + 1 > c.max_ctx) return KVQ_ERR_CAPACITY;
+    lens[b] = seq_len[b] + 1;
+  }
+  DecodePlan plan;
+  if ((st = plan_decode(cfg, cache, q, q_dtype, n_q_heads, sm_scale, lens, out, &plan)) != KVQ_OK) return st;
+  if (!workspace) return KVQ_ERR_INVALID;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (workspace_bytes < plan.wl.total) return KVQ_ERR_WORKSPACE;
+  AppendArgs a = append_args(c, cache, k_new, v_new, kv_dtype, 1);
+  if (plan.sc.nchunk > 1) {
+    // a KV head's query heads span several chunks, each of which would
+    // need the values of the position leaving the tail while another one
+    // overwrites it: append first, then attend
+    for (int b = 0; b < c.batch; ++b) a.len[b] = seq_len[b];
+    if ((st = hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)))) != KVQ_OK)
+      return st;
+    return run_decode(c, cache, q, q_dtype, n_q_heads, sm_scale, lens, out, workspace, plan, stream);
+  }
+  const OneArgs one = one_args(a);
+  return run_decode(c, cache, q, q_dtype, n_q_heads, sm_scale, lens, out, workspace, plan, stream, &one);
 }
 
 kvq_status kvq_decode_attention_static(const kvq_config* cfg, const kvq_cache* cache, const void* q,

@@ -247,6 +247,31 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* One decode step: kvq_rotate_quantize_append of one token per sequence
+ * followed by kvq_decode_attention over the cache with that token, in fewer
+ * launches.  The token's K/V are appended exactly as the append call would
+ * (the cache afterwards holds the same bytes), and attention sees the cache
+ * as it stands after the append: the positions the append changes (the new
+ * token and the position that becomes quantized) are attended to from the
+ * values the append computes, the rest from the cache (velog.io post "fix
+ * KV cache quantization outliers", section "Hadamard rotation": rotate and
+ * store at append, rotated scores and weighted sum at attention; aitrends.kr
+ * article 92204, glossary "Precision Tail").
+ *  k_new, v_new: device [batch][1][n_kv_heads][head_dim] of kv_dtype.
+ *  q:            device [batch][n_q_heads][head_dim] of q_dtype.
+ *  seq_len:      host [batch], each sequence's length BEFORE the step (>= 0);
+ *                attention covers seq_len[b] + 1 positions.  The caller
+ *                advances its lengths afterwards.
+ *  out, workspace, workspace_bytes, sm_scale: as kvq_decode_attention, with
+ *                kvq_decode_workspace_bytes(cfg, n_q_heads) bytes enough.
+ * Errors: those of the two calls it replaces (KVQ_ERR_CAPACITY if
+ * seq_len[b] + 1 > max_ctx); nothing is queued on an error. */
+kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache,
+                           const void* k_new, const void* v_new, kvq_dtype kv_dtype,
+                           const void* q, kvq_dtype q_dtype, int32_t n_q_heads,
+                           float sm_scale, const int32_t* seq_len, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Size of the device workspace kvq_decode_attention_static uses. */
 #define KVQ_STATIC_WORKSPACE_BYTES 33554432
 

@@ -130,3 +130,23 @@ def rel_l2(got, ref):
         return np.inf
     den = np.linalg.norm(ref)
     return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
+
+
+def fill_lengths(pair, w, n_list, dtype):
+    """Append workload tokens so sequence b ends with length n_list[b] (at
+    most two distinct lengths): one append for everyone, then a second one
+    that restarts the shorter sequences (a sequence given length 0 starts
+    afresh)."""
+    import workloads
+    nmax = max(n_list)
+    k = workloads.kv_numpy(w, 1, 0, nmax)
+    v = workloads.kv_numpy(w, 2, 0, nmax)
+    short = [n for n in n_list if n < nmax]
+    if not short:
+        pair.append(k, v, dtype)
+        return
+    m = min(short)
+    assert all(x in (nmax, m) for x in n_list), "two distinct lengths supported"
+    pair.append(k[:, : nmax - m], v[:, : nmax - m], dtype)
+    lens = [nmax - m if n == nmax else 0 for n in n_list]
+    pair.append(k[:, nmax - m:], v[:, nmax - m:], dtype, lens=lens)

@@ -190,6 +190,30 @@ def test_static_workspace_decode_validation():
              None) == _capi.KVQ_ERR_ALIGN
 
 
+def test_decode_step_validation():
+    # the fused append-and-attend call: the append's and the decode's host
+    # checks, all before any device work
+    c = kvq.kvq_config(2, 4, 128, 100, 8, 4, 16)
+    f = L.kvq_decode_step
+
+    def step(lens, k=FAKE, v=FAKE, q=FAKE, hq=8, kvdt=0, qdt=0, ws=1 << 40, cache=None, cfg=c):
+        return f(ctypes.byref(cfg), ctypes.byref(cache or _cache()), k, v, kvdt, q, qdt, hq, 0.1,
+                 lens, FAKE, FAKE, ws, None)
+    assert step(_lens(100, 0)) == _capi.KVQ_ERR_CAPACITY
+    assert step(_lens(-1, 0)) == _capi.KVQ_ERR_INVALID
+    assert step(_lens(5, 5), k=0) == _capi.KVQ_ERR_INVALID
+    assert step(_lens(5, 5), v=FAKE_MISALIGNED) == _capi.KVQ_ERR_ALIGN
+    assert step(_lens(5, 5), kvdt=3) == _capi.KVQ_ERR_INVALID
+    assert step(_lens(5, 5), qdt=3) == _capi.KVQ_ERR_INVALID
+    assert step(_lens(5, 5), hq=6) == _capi.KVQ_ERR_INVALID
+    assert step(_lens(5, 5), q=0) == _capi.KVQ_ERR_INVALID
+    assert step(_lens(5, 5), ws=16) == _capi.KVQ_ERR_WORKSPACE
+    assert step(_lens(5, 5), cache=_cache(tail=0)) == _capi.KVQ_ERR_INVALID
+    bad = kvq.kvq_config_default(2, 4, 128, 100)
+    bad.v_bits = 7
+    assert step(_lens(5, 5), cfg=bad) == _capi.KVQ_ERR_UNSUPPORTED
+
+
 def test_decode_validation():
     c = kvq.kvq_config(2, 4, 128, 100, 8, 4, 0)
     assert _decode(c, 6, _lens(5, 5)) == _capi.KVQ_ERR_INVALID      # 6 % 4 != 0
