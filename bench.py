@@ -96,49 +96,80 @@ def describe(w):
 # ----------------------------------------------------------- CPU baseline
 def _oracle_unit(args):
     """Time the oracle's decode attention for one (sequence, KV head) unit
-    whose cache the oracle builds itself from the same generator inputs."""
+    whose cache the oracle builds itself from the same generator inputs.
+    Returns the wall-clock start and end of the timed attention."""
     os.environ["OMP_NUM_THREADS"] = "1"
     k, v, q, w = args
     from oracle import OracleCache, decode_reference
     from oracle.blockquant import bf16_bits_to_f32
     n, d = k.shape[0], w["d"]
-    G = q.shape[0]
     km, vm = bool(w.get("km")), bool(w.get("vm"))
     c = OracleCache(1, 1, d, w["k_bits"], w["v_bits"], w["tail"], n, k_min=km, v_min=vm)
     c.append(k[None, :, None], v[None, :, None], [0], dtype="bf16")
     planes = c.physical()
-    t0 = time.perf_counter()
+    t0 = time.time()
     decode_reference(planes, bf16_bits_to_f32(q)[None], [n], 1, d, w["k_bits"], w["v_bits"],
                      w["tail"], k_min=km, v_min=vm)
-    return time.perf_counter() - t0, G
+    return t0, time.time()
 
 
-def cpu_baseline(w, units, k_dev, v_dev, q_host, torch, budget_units):
-    """Oracle decode attention over a sample of units, run in a process pool."""
+def _oracle_append_unit(args):
+    """Time the oracle's rotate-quantize-append of one (sequence, KV head)
+    unit's tokens in one call.  Returns the wall-clock start and end."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    k, v, w = args
+    from oracle import OracleCache
+    n = k.shape[0]
+    c = OracleCache(1, 1, w["d"], w["k_bits"], w["v_bits"], w["tail"], n)
+    t0 = time.time()
+    c.append(k[None, :, None], v[None, :, None], [0], dtype="bf16")
+    return t0, time.time()
+
+
+# Worker processes of the oracle baseline: the host cores a one-GPU share of
+# the box gives (16), or fewer where the affinity set is smaller.
+CPU_WORKERS = 16
+
+
+def cpu_baseline(w, units, k_dev, v_dev, q_host, torch, scaled=False):
+    """Oracle decode attention over `units`, one (sequence, KV head) unit per
+    task in a process pool.  The rate is the units' algorithmic cache bytes
+    over the wall time of the timed attention work (first start to last end
+    across workers; building each unit's oracle cache is not timed).  scaled:
+    the units are a sample of the workload, and the rate stands for it."""
     import multiprocessing as mp
-    cores = min(len(os.sched_getaffinity(0)), 16)
-    sample = units[:budget_units]
+    cores = min(len(os.sched_getaffinity(0)), CPU_WORKERS)
     G = w["Hq"] // w["Hkv"]
     jobs = []
-    for b, g in sample:
+    for b, g in units:
         k = k_dev[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         v = v_dev[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         jobs.append((k, v, q_host[b, g * G:(g + 1) * G], w))
     ctx = mp.get_context("spawn")
-    t0 = time.perf_counter()
-    with ctx.Pool(min(cores, len(jobs))) as pool:
-        res = pool.map(_oracle_unit, jobs)
-    wall = time.perf_counter() - t0
-    busy = sum(r[0] for r in res)
-    unit_bytes = cache_bytes_per_step(dict(w, B=1, Hkv=1), [w["n"]])
-    # throughput of the timed attention work at the pool's parallelism
     par = min(cores, len(jobs))
-    gbs = len(jobs) * unit_bytes / (busy / par) / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": par, "kind": "oracle",
-            "sample": "%d of %d (sequence, KV head) units at full context %d; float64 "
-                      "attention over the oracle-built cache, %.1f s of CPU time "
-                      "(pool wall %.1f s incl. setup)" % (len(jobs), w["B"] * w["Hkv"],
-                                                         w["n"], busy, wall)}
+    with ctx.Pool(par) as pool:
+        res = pool.map(_oracle_unit, jobs)
+    wall = max(r[1] for r in res) - min(r[0] for r in res)
+    busy = sum(r[1] - r[0] for r in res)
+    unit_bytes = cache_bytes_per_step(dict(w, B=1, Hkv=1), [w["n"]])
+    gbs = len(jobs) * unit_bytes / wall / 1e9
+    total = w["B"] * w["Hkv"]
+    what = ("%d of %d (sequence, KV head) units at full context %d%s" %
+            (len(jobs), total, w["n"], ", a seeded sample whose rate stands for the workload"
+             if scaled or len(jobs) < total else ""))
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": par, "kind": "oracle",
+            "sample": "%s; float64 attention over the oracle-built cache, %.1f s wall for the timed "
+                      "attention (%.1f s of CPU time over %d processes)" % (what, wall, busy, par)}
+
+
+def unit_sample(w, count, seed=0):
+    """(sequence, KV head) units the oracle baseline times: all of them, or
+    a seeded sample of `count`."""
+    all_units = [(b, g) for b in range(w["B"]) for g in range(w["Hkv"])]
+    if count >= len(all_units):
+        return all_units
+    pick = np.random.default_rng(seed).choice(len(all_units), count, replace=False)
+    return [all_units[i] for i in sorted(pick)]
 
 
 # ------------------------------------------------------------------ main
@@ -152,6 +183,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=64,
                     help="(sequence, KV head) units the CPU oracle times (all when >= batch * KV heads)")
     ap.add_argument("--no-append", action="store_true", help="skip the bulk append measurement")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the sub-results of the small, mid and huge decode workloads")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the secondary run with the append and the attention as two calls")
     ap.add_argument("--no-rotation-off", action="store_true",
@@ -222,12 +255,7 @@ def main():
     log("workload", describe(w))
 
     # (sequence, KV head) units whose inputs the CPU oracle gets
-    all_units = [(b, g) for b in range(B) for g in range(Hkv)]
-    if args.cpu_units >= len(all_units):
-        units = all_units
-    else:
-        pick = np.random.default_rng(0).choice(len(all_units), args.cpu_units, replace=False)
-        units = [all_units[i] for i in sorted(pick)]
+    units = unit_sample(w, args.cpu_units)
     keep = None if args.no_cpu_baseline else {}
 
     run = decode_run(torch, kvq, w, dev, args.warmup, args.steps, True, keep, paged=args.paged)
@@ -302,17 +330,57 @@ def main():
         del pg
 
 
+    if not args.no_other_configs:
+        # the other decode workloads, each with its own oracle baseline
+        result["configs"] = {}
+        for name, cpu_units in OTHER_CONFIGS:
+            result["configs"][name] = other_config(torch, kvq, dev, name, cpu_units, args.steps,
+                                                   args.warmup, not args.no_cpu_baseline)
+
     if not args.no_append:
-        result["append"] = bulk_append(torch, kvq, dev)
+        result["append"] = bulk_append(torch, kvq, dev, not args.no_cpu_baseline)
     if not args.no_prefill:
         result["prefill"] = prefill_bench(torch, kvq, dev)
 
     if not args.no_cpu_baseline:
         q_host = q0.view(torch.int16).cpu().numpy().view(np.uint16)
         log("cpu baseline on %d units" % len(units))
-        result["cpu_baseline"] = cpu_baseline(w, units, keep["k"], keep["v"], q_host, torch, len(units))
+        result["cpu_baseline"] = cpu_baseline(w, units, keep["k"], keep["v"], q_host, torch)
     print(json.dumps(result), flush=True)
     return 0
+
+
+# Other decode workloads reported beside the main one, with the number of
+# (sequence, KV head) units their oracle baseline times (mid: 32 of 128 and
+# huge: 16 of 128 are seeded samples; small: all 8).
+OTHER_CONFIGS = (("small", 8), ("mid", 32), ("huge", 16))
+
+
+def other_config(torch, kvq, dev, name, cpu_units, steps, warmup, with_cpu):
+    """The decode step (kvq_decode_step) of one more workload: step and split
+    kernel rates, and the oracle's rate on a sample of its units."""
+    w = workloads.workload(name)
+    keep = {} if with_cpu else None
+    run = decode_run(torch, kvq, w, dev, warmup, steps, True, keep)
+    kern = float(np.mean(run["kern_ms"]))
+    kgbs = run["bytes_kern"] / (kern * 1e-3) / 1e9
+    sgbs = run["bytes_step"] / (run["ms_step"] * 1e-3) / 1e9
+    res = {"workload": describe(w), "cache_bytes_per_step": int(run["bytes_step"]),
+           "us_per_step": round(run["ms_step"] * 1e3, 2), "step_gbs": round(sgbs, 1),
+           "attention_kernel_us": percentiles(run["kern_ms"]), "kernel_gbs": round(kgbs, 1),
+           "pct_hbm_peak_kernel": round(100 * kgbs / HBM_PEAK_GBS, 2)}
+    if run["bytes_step"] < 256e6:
+        res["note"] = ("the cache fits the part's 256 MB last-level cache, so this rate is not an "
+                       "HBM rate")
+    log("%s: step %.1f us, kernel %.1f us, %.0f GB/s kernel" % (name, run["ms_step"] * 1e3,
+                                                              kern * 1e3, kgbs))
+    if with_cpu:
+        q_host = run["q0"].view(torch.int16).cpu().numpy().view(np.uint16)
+        units = unit_sample(w, cpu_units)
+        log("%s: cpu baseline on %d units" % (name, len(units)))
+        res["cpu_baseline"] = cpu_baseline(w, units, keep["k"], keep["v"], q_host, torch)
+    del run, keep
+    return res
 
 
 def percentiles(ms):
@@ -572,7 +640,7 @@ def prefill_bench(torch, kvq, dev, n_q=512):
     return res
 
 
-def bulk_append(torch, kvq, dev):
+def bulk_append(torch, kvq, dev, with_cpu=False, cpu_units=16):
     """Rotate-quantize-append of 32768 tokens per sequence in one call:
     batch 16, 8 KV heads, head_dim 128, K4 V4, no tail."""
     w = workloads.workload("mid")
@@ -597,6 +665,27 @@ def bulk_append(torch, kvq, dev):
            "gbs": round(moved / (ms * 1e-3) / 1e9, 1),
            "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
     log("bulk append", res)
+    if with_cpu:
+        # the oracle's append of a sample of the same units, one per process
+        import multiprocessing as mp
+        units = unit_sample(w, cpu_units, seed=1)
+        jobs = []
+        for b, g in units:
+            kk = k[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            vv = v[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            jobs.append((kk, vv, w))
+        par = min(len(os.sched_getaffinity(0)), CPU_WORKERS, len(jobs))
+        with mp.get_context("spawn").Pool(par) as pool:
+            r = pool.map(_oracle_append_unit, jobs)
+        wall = max(x[1] for x in r) - min(x[0] for x in r)
+        # a unit is one KV head of one sequence: n tokens x 1 head of the
+        # B x Hkv heads a token has, so tokens per second = n * units / Hkv
+        tok = n * len(jobs) / Hkv
+        res["cpu_baseline"] = {
+            "value": round(tok / wall / 1e6, 4), "unit": "Mtok/s", "cores": par, "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) units, %d tokens each, appended by the float32 "
+                      "oracle in one call per unit; %.1f s wall (a token is %d KV heads, so the rate "
+                      "counts units x tokens / %d)" % (len(jobs), B * Hkv, n, wall, Hkv, Hkv)}
     del k, v, cache
     return res
 

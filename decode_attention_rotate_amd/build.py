@@ -70,6 +70,34 @@ def _compile(job, incremental=False):
     return obj, r.returncode, msgs, cmd
 
 
+# Host-side sanitizer check of the C ABI (tests/asan/capi_check.cpp): the
+# library's host code built with AddressSanitizer and UBSan, linked with the
+# uninstrumented kernel objects; run by tests/test_capi_sanitizers.py.
+SAN_BIN = os.path.join(BUILD, "kvq_capi_asan")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LINK = ["-fsanitize=address,undefined", "-fno-gpu-sanitize"]
+
+
+def build_sanitizer_check(objs):
+    """Compile the host file and the check program with the sanitizers and
+    link them with the other objects into SAN_BIN."""
+    host = os.path.join(BUILD, "kvq_host_asan.o")
+    drv = os.path.join(BUILD, "capi_check_asan.o")
+    flags = ["-O1", "-g", "-std=c++17", "-fPIC", "-ffp-contract=off",
+             "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+    steps = [
+        [HIPCC] + flags + DEVICE + SAN_HOST + ["-x", "hip", "-c", os.path.join(CSRC, "kvq_host.cpp"), "-o", host],
+        [HIPCC] + flags + SAN_HOST + ["-c", os.path.join(ROOT, "tests", "asan", "capi_check.cpp"), "-o", drv],
+        [HIPCC, "--offload-arch=" + ARCH] + SAN_LINK + ["-o", SAN_BIN, drv, host] + objs,
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("sanitizer check build failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    return SAN_BIN
+
+
 def build(jobs=None, verbose=False, only=None, incremental=False):
     """Compile every unit and link libkvq.so; raises on any failure.
     only: compile just the units whose object name contains this string
@@ -102,6 +130,7 @@ def build(jobs=None, verbose=False, only=None, incremental=False):
     if r.returncode != 0:
         raise RuntimeError("ceiling library failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     shutil.move(tmp, CEILING_LIB)
+    build_sanitizer_check([o for o in objs if not o.endswith("kvq_host.o")])
     return LIB
 
 

@@ -268,6 +268,7 @@ size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane) {
     case KVQ_V_SCALES: return tiles * kTile * nb * sizeof(uint16_t) * (c.v_min ? 2 : 1);
     case KVQ_K_TAIL:
     case KVQ_V_TAIL: return units * (size_t)c.tail_len * c.head_dim * sizeof(uint16_t);
+    default: break;
   }
   return 0;
 }
@@ -619,6 +620,7 @@ const char* kvq_status_str(kvq_status s) {
     case KVQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case KVQ_ERR_HIP: return "HIP runtime error";
     case KVQ_ERR_WORKSPACE: return "decode workspace too small";
+    default: break;
   }
   return "unknown status";
 }

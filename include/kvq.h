@@ -126,14 +126,22 @@ typedef enum kvq_status {
   KVQ_ERR_CAPACITY = -3,     /* a sequence would exceed max_ctx */
   KVQ_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned */
   KVQ_ERR_HIP = -5,          /* the HIP runtime reported an error */
-  KVQ_ERR_WORKSPACE = -6     /* decode workspace smaller than required */
+  KVQ_ERR_WORKSPACE = -6,    /* decode workspace smaller than required */
+  /* Range markers, never returned: they make every int32 a representable
+   * value of the enum, so a caller passing an unknown value gets an error
+   * status instead of undefined behaviour (the same in the enums below). */
+  KVQ_STATUS_RANGE_MIN = -0x7FFFFFFF - 1, KVQ_STATUS_RANGE_MAX = 0x7FFFFFFF
 } kvq_status;
 
-typedef enum kvq_dtype { KVQ_BF16 = 0, KVQ_F32 = 1 } kvq_dtype;
+typedef enum kvq_dtype {
+  KVQ_BF16 = 0, KVQ_F32 = 1,
+  KVQ_DTYPE_RANGE_MIN = -0x7FFFFFFF - 1, KVQ_DTYPE_RANGE_MAX = 0x7FFFFFFF
+} kvq_dtype;
 
 typedef enum kvq_plane {
   KVQ_K_CODES = 0, KVQ_K_SCALES = 1, KVQ_V_CODES = 2,
-  KVQ_V_SCALES = 3, KVQ_K_TAIL = 4, KVQ_V_TAIL = 5
+  KVQ_V_SCALES = 3, KVQ_K_TAIL = 4, KVQ_V_TAIL = 5,
+  KVQ_PLANE_RANGE_MIN = -0x7FFFFFFF - 1, KVQ_PLANE_RANGE_MAX = 0x7FFFFFFF
 } kvq_plane;
 
 /* Largest batch a single call accepts (sequence lengths travel in the
