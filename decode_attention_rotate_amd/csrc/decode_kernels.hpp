@@ -275,8 +275,10 @@ void decode_split_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per wave");
   static_assert(!PF || G == 8, "prefill waves own 8 rows");
   constexpr int kGroupWaves = split_group_waves(D, KM || VM || PF);
-  // non-temporal cache loads at two waves per SIMD (see ld_cache)
-  constexpr bool kNT = split_waves_per_simd(D, KM || VM || PF) >= 2;
+  // non-temporal cache loads at two waves per SIMD (see ld_cache); not for
+  // prefill, whose waves all read every tile of their workgroup's range and
+  // find it in the caches after the first
+  constexpr bool kNT = !PF && split_waves_per_simd(D, KM || VM || PF) >= 2;
   // tiles whose bytes a wave keeps in registers ahead of the one computing:
   // at one wave per SIMD (d = 256) the wave alone must cover the latency, so
   // it keeps two where four step buffers fit the 512 registers with at most
