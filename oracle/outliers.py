@@ -125,3 +125,133 @@ def attention_outliers(q, k_parts, v_parts, k_idx, v_idx, k_bits, v_bits, sm_sca
     out = Rv.T @ (p @ vy)
     out[vi] += p @ vo
     return out
+
+
+# ---------------------------------------------------------------- the cache
+# Planes of the outlier parts, in the device byte layout (reading R25 with
+# the layouts of reading R11 at 32 channels):
+#   k_out_codes  per (b, g): [cap][32] 8-bit two's-complement codes (rows)
+#   v_out_codes  per (b, g): element-major 64-token tiles of the 32 outlier
+#                channels at 8 bits (offset codes u = c + 128), the V-tile
+#                layout of a 32-element head
+#   k_out_scales, v_out_scales  per (b, g): [cap] fp16 bits (one 32-block)
+
+class OutlierCache:
+    """Cache with an outlier set of 32 channels per plane and KV head
+    (reading R25), without a precision tail: the rest of every vector is
+    stored by the plain rules (an OracleCache of the zeroed-outlier rest
+    would hold the same planes), the outliers as one 8-bit absmax block in
+    the original space.  k_idx, v_idx: int [Hkv][32] channel lists."""
+
+    def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, max_ctx, k_idx, v_idx,
+                 rotate_k=True, rotate_v=True, sign_seed=0, k_min=False, v_min=False):
+        from .kvcache import OracleCache
+        from .blockquant import TILE
+        self.B, self.H, self.d = batch, n_kv_heads, head_dim
+        self.idx = {"k": np.asarray(k_idx, np.int64).reshape(n_kv_heads, BLOCK),
+                    "v": np.asarray(v_idx, np.int64).reshape(n_kv_heads, BLOCK)}
+        for p in ("k", "v"):
+            for g in range(n_kv_heads):
+                _index(self.idx[p][g], head_dim)
+        self.base = OracleCache(batch, n_kv_heads, head_dim, k_bits, v_bits, 0, max_ctx,
+                                rotate_k, rotate_v, sign_seed, k_min, v_min)
+        cap = self.base.cap
+        self.out_codes = {p: np.zeros((batch, n_kv_heads, cap, BLOCK), np.int8) for p in ("k", "v")}
+        self.out_scales = {p: np.zeros((batch, n_kv_heads, cap), np.uint16) for p in ("k", "v")}
+        self.v_out_u = np.zeros((batch, n_kv_heads, cap, BLOCK), np.uint8)
+        self.TILE = TILE
+
+    def append(self, k_new, v_new, lens, dtype="bf16"):
+        """Append n_new tokens per sequence ([B][n_new][Hkv][d]); lens are
+        the lengths before.  Returns the new lengths."""
+        from .kvcache import _widen
+        lens = np.asarray(lens, dtype=np.int64)
+        rests, outs = [], []
+        for p, new in (("k", k_new), ("v", v_new)):
+            x = _widen(new, dtype).astype(np.float32)            # [B][n][H][d]
+            rest = x.copy()
+            out = np.zeros(x.shape[:-1] + (BLOCK,), np.float32)
+            for g in range(self.H):
+                r, o = split_outliers(x[:, :, g, :], self.idx[p][g])
+                rest[:, :, g, :] = r
+                out[:, :, g, :] = o
+            rests.append(rest)
+            outs.append(out)
+        # the rest takes the plain path (rotation, block format)
+        new_lens = self.base.append(rests[0], rests[1], lens, dtype="f32")
+        n_new = np.asarray(k_new).shape[1]
+        for p, out in (("k", outs[0]), ("v", outs[1])):
+            codes, scales = quantize_blocks(out, 8)               # [B][n][H][32], [B][n][H][1]
+            for b in range(self.B):
+                for i in range(n_new):
+                    pos = int(lens[b]) + i
+                    self.out_codes[p][b, :, pos, :] = codes[b, i]
+                    self.out_scales[p][b, :, pos] = scales[b, i, :, 0]
+                    if p == "v":
+                        self.v_out_u[b, :, pos, :] = (codes[b, i].astype(np.int16) + 128).astype(np.uint8)
+        return new_lens
+
+    def physical(self):
+        """The plain planes of the rest plus the four outlier planes."""
+        from .blockquant import offset_codes_to_vtiles
+        out = self.base.physical()
+        cap = self.base.cap
+        out["k_out_codes"] = self.out_codes["k"].view(np.uint8).reshape(self.B, self.H, cap * BLOCK).copy()
+        vt = np.zeros((self.B, self.H, cap * BLOCK), np.uint8)
+        for b in range(self.B):
+            for g in range(self.H):
+                vt[b, g] = offset_codes_to_vtiles(self.v_out_u[b, g], 8)
+        out["v_out_codes"] = vt
+        out["k_out_scales"] = self.out_scales["k"].copy()
+        out["v_out_scales"] = self.out_scales["v"].copy()
+        return out
+
+
+def outlier_values(planes, p, b, g, n):
+    """Dequantized outlier values [n][32] (float32) of plane p ("k"/"v") of
+    sequence b, KV head g, read from the physical planes."""
+    from .blockquant import vtiles_to_codes, TILE
+    if p == "k":
+        codes = planes["k_out_codes"][b, g].view(np.int8).reshape(-1, BLOCK)[:n]
+    else:
+        n_t = (n + TILE - 1) // TILE * TILE
+        codes = vtiles_to_codes(planes["v_out_codes"][b, g], n_t, BLOCK, 8)[:n]
+    scales = planes[p + "_out_scales"][b, g][:n].reshape(n, 1)
+    return dequantize_blocks(codes, scales)
+
+
+def decode_reference_outliers(planes, q, lens, n_kv_heads, d, k_bits, v_bits, k_idx, v_idx,
+                              sm_scale=None, rotate_k=True, rotate_v=True, sign_seed=0,
+                              k_min=False, v_min=False):
+    """Decode attention [B][Hq][d] (float64) over a cache with outlier sets
+    (reading R25, no precision tail), in the split form of
+    attention_outliers, from the physical planes."""
+    from .kvcache import dequantize_rows
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, _ = q.shape
+    G = Hq // n_kv_heads
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    Rk = rotation_matrix(d, sign_seed) if rotate_k else np.eye(d)
+    Rv = rotation_matrix(d, sign_seed) if rotate_v else np.eye(d)
+    ki = np.asarray(k_idx, np.int64).reshape(n_kv_heads, BLOCK)
+    vi = np.asarray(v_idx, np.int64).reshape(n_kv_heads, BLOCK)
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        n = int(lens[b])
+        for g in range(n_kv_heads):
+            ky = dequantize_rows(planes["k_codes"][b, g], planes["k_scales"][b, g], d, k_bits, n, "k",
+                                 k_min).astype(np.float64)
+            vy = dequantize_rows(planes["v_codes"][b, g], planes["v_scales"][b, g], d, v_bits, n, "v",
+                                 v_min).astype(np.float64)
+            ko = outlier_values(planes, "k", b, g, n).astype(np.float64)
+            vo = outlier_values(planes, "v", b, g, n).astype(np.float64)
+            for h in range(g * G, (g + 1) * G):
+                s = sm_scale * (ky @ (Rk @ q[b, h]) + ko @ q[b, h][ki[g]])
+                s = s - np.max(s)
+                p = np.exp(s)
+                p = p / np.sum(p)
+                o = Rv.T @ (p @ vy)
+                o[vi[g]] += p @ vo
+                out[b, h] = o
+    return out

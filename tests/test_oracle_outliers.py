@@ -126,3 +126,76 @@ def test_split_attention_equals_attention_on_the_reconstruction(seed, rk, rv):
     V = reconstruct_f32(vp, vi, 5, rotate=rv, signs=signs)
     want = softmax_attention(q, K, V, 0.125)
     assert np.linalg.norm(got - want) <= 1e-5 * np.linalg.norm(want)
+
+
+# ------------------------------------------------------------ the cache
+def _cache_inputs(seed, B=2, n=130, H=2, d=128):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, n, H, d)).astype(np.float32)
+    v = rng.standard_normal((B, n, H, d)).astype(np.float32)
+    k[..., 9] *= 25.0
+    v[..., d - 28] *= 25.0
+    ki = np.stack([_set(d, [9], 10 + g) for g in range(H)])
+    vi = np.stack([_set(d, [d - 28], 20 + g) for g in range(H)])
+    return k, v, ki, vi
+
+
+@pytest.mark.parametrize("kb,vb,km,vm", [(4, 4, False, False), (8, 5, False, True), (5, 8, True, False)])
+def test_cache_rest_planes_are_the_plain_cache_of_the_zeroed_rest(kb, vb, km, vm):
+    from oracle import OracleCache
+    from oracle.outliers import OutlierCache
+    k, v, ki, vi = _cache_inputs(1)
+    B, n, H, d = k.shape
+    oc = OutlierCache(B, H, d, kb, vb, n + 3, ki, vi, k_min=km, v_min=vm)
+    oc.append(k, v, [0, 0], dtype="f32")
+    kr, vr = k.copy(), v.copy()
+    for g in range(H):
+        kr[:, :, g, ki[g]] = 0
+        vr[:, :, g, vi[g]] = 0
+    plain = OracleCache(B, H, d, kb, vb, 0, n + 3, k_min=km, v_min=vm)
+    plain.append(kr, vr, [0, 0], dtype="f32")
+    got, want = oc.physical(), plain.physical()
+    for key in want:
+        assert np.array_equal(got[key], want[key]), key
+
+
+def test_cache_outlier_planes_hold_the_8bit_blocks_of_the_gathered_channels():
+    from oracle.outliers import OutlierCache, outlier_values
+    k, v, ki, vi = _cache_inputs(2)
+    B, n, H, d = k.shape
+    oc = OutlierCache(B, H, d, 4, 4, n, ki, vi)
+    # two appends (chunking must not matter)
+    oc.append(k[:, :70], v[:, :70], [0, 0], dtype="f32")
+    oc.append(k[:, 70:], v[:, 70:], [70, 70], dtype="f32")
+    planes = oc.physical()
+    for b in range(B):
+        for g in range(H):
+            for p, x, idx in (("k", k, ki), ("v", v, vi)):
+                codes, scales = quantize_blocks(x[b, :, g][:, idx[g]], 8)
+                got = outlier_values(planes, p, b, g, n)
+                from oracle import dequantize_blocks
+                assert np.array_equal(got, dequantize_blocks(codes, scales))
+                assert np.array_equal(planes[p + "_out_scales"][b, g][:n], scales[:, 0])
+
+
+def test_cache_attention_equals_attention_on_the_reconstruction():
+    from oracle.outliers import OutlierCache, decode_reference_outliers, outlier_values
+    from oracle import dequantize_reference, rotation_matrix as rm
+    k, v, ki, vi = _cache_inputs(3, B=1, n=100, H=2, d=64)
+    B, n, H, d = k.shape
+    oc = OutlierCache(B, H, d, 4, 5, n, ki, vi, sign_seed=7)
+    oc.append(k, v, [0], dtype="f32")
+    planes = oc.physical()
+    q = np.random.default_rng(4).standard_normal((B, 2 * H, d))
+    got = decode_reference_outliers(planes, q, [n], H, d, 4, 5, ki, vi, sign_seed=7)
+    R = rm(d, 7)
+    from oracle.kvcache import dequantize_rows
+    for g in range(H):
+        # the full reconstruction: R^T rest + outliers at their channels
+        K = dequantize_rows(planes["k_codes"][0, g], planes["k_scales"][0, g], d, 4, n, "k") @ R
+        V = dequantize_rows(planes["v_codes"][0, g], planes["v_scales"][0, g], d, 5, n, "v") @ R
+        K[:, ki[g]] += outlier_values(planes, "k", 0, g, n)
+        V[:, vi[g]] += outlier_values(planes, "v", 0, g, n)
+        for h in (2 * g, 2 * g + 1):
+            want = softmax_attention(q[0, h], K, V, 1.0 / np.sqrt(d))
+            assert np.linalg.norm(got[0, h] - want) <= 1e-10 * np.linalg.norm(want)
