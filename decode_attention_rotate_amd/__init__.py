@@ -18,7 +18,8 @@ import math
 from . import _capi
 from ._capi import (KvqConfig, KvqCache, KvqError, KVQ_BF16, KVQ_F32,
                     KVQ_K_CODES, KVQ_K_SCALES, KVQ_V_CODES, KVQ_V_SCALES,
-                    KVQ_K_TAIL, KVQ_V_TAIL, KVQ_MAX_BATCH, KVQ_PAGE_TOKENS,
+                    KVQ_K_TAIL, KVQ_V_TAIL, KVQ_K_OUT_CODES, KVQ_K_OUT_SCALES,
+                    KVQ_V_OUT_CODES, KVQ_V_OUT_SCALES, KVQ_MAX_BATCH, KVQ_PAGE_TOKENS,
                     KVQ_STATIC_WORKSPACE_BYTES, LIB_PATH)
 
 __all__ = [
@@ -43,10 +44,12 @@ def kvq_config_default(batch, n_kv_heads, head_dim, max_ctx):
 
 def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
                tail_len=0, rotate_k=None, rotate_v=None, sign_seed=0, k_min=False,
-               v_min=False, page_pool=0):
+               v_min=False, page_pool=0, outliers=0):
     """kvq_config_default with fields overridden; validated by the library.
     k_min / v_min select scale-and-min blocks (q4_1 / q5_1 at 4 / 5 bits);
-    page_pool > 0 makes a paged cache of that many 64-position pages."""
+    page_pool > 0 makes a paged cache of that many 64-position pages;
+    outliers = 32 keeps 32 outlier channels per plane and KV head at 8 bits
+    (KVCache then needs their channel lists)."""
     c = kvq_config_default(batch, n_kv_heads, head_dim, max_ctx)
     c.k_bits, c.v_bits, c.tail_len = k_bits, v_bits, tail_len
     if rotate_k is not None:
@@ -56,6 +59,7 @@ def kvq_config(batch, n_kv_heads, head_dim, max_ctx, k_bits=4, v_bits=4,
     c.sign_seed = int(sign_seed) & 0xFFFFFFFF
     c.k_min, c.v_min = int(k_min), int(v_min)
     c.page_pool = int(page_pool)
+    c.outliers = int(outliers)
     _capi.check(_capi.lib().kvq_config_check(ctypes.byref(c)), "kvq_config")
     return c
 
@@ -118,9 +122,13 @@ class KVCache:
 
     PLANES = (("k_codes", KVQ_K_CODES), ("k_scales", KVQ_K_SCALES),
               ("v_codes", KVQ_V_CODES), ("v_scales", KVQ_V_SCALES),
-              ("k_tail", KVQ_K_TAIL), ("v_tail", KVQ_V_TAIL))
+              ("k_tail", KVQ_K_TAIL), ("v_tail", KVQ_V_TAIL),
+              ("k_out_codes", _capi.KVQ_K_OUT_CODES), ("k_out_scales", _capi.KVQ_K_OUT_SCALES),
+              ("v_out_codes", _capi.KVQ_V_OUT_CODES), ("v_out_scales", _capi.KVQ_V_OUT_SCALES))
 
-    def __init__(self, cfg, device="cuda", page_table=None):
+    def __init__(self, cfg, device="cuda", page_table=None, outlier_idx=None):
+        """outlier_idx (cfg.outliers > 0): the channel lists, int32 device
+        tensor [2][n_kv_heads][32] (K's, then V's)."""
         torch = _torch()
         self.cfg = cfg
         self.planes = {}
@@ -136,9 +144,21 @@ class KVCache:
                                  % (want,))
             self.page_table = page_table
             ptrs["page_table"] = page_table.data_ptr()
+        self.outlier_idx = None
+        if cfg.outliers > 0:
+            want = (2, cfg.n_kv_heads, cfg.outliers)
+            if (outlier_idx is None or outlier_idx.dtype != torch.int32
+                    or tuple(outlier_idx.shape) != want or not outlier_idx.is_cuda
+                    or not outlier_idx.is_contiguous()):
+                raise ValueError("outliers need outlier_idx, a contiguous int32 device tensor "
+                                 "of shape %s" % (want,))
+            self.outlier_idx = outlier_idx
+            ptrs["outlier_idx"] = outlier_idx.data_ptr()
         for name, pid in self.PLANES:
             nbytes = kvq_plane_bytes(cfg, pid)
-            if nbytes == 0 and name.endswith("tail") and cfg.tail_len == 0:
+            optional = (name.endswith("tail") and cfg.tail_len == 0) or \
+                ("_out_" in name and cfg.outliers == 0)
+            if nbytes == 0 and optional:
                 self.planes[name] = None
                 ptrs[name] = None
                 continue
@@ -171,6 +191,8 @@ class KVCache:
         view.planes = dict(self.planes)
         tail_bytes = cfg.n_kv_heads * cfg.tail_len * cfg.head_dim * 2
         ptrs = {"page_table": view.page_table.data_ptr()}
+        if self.outlier_idx is not None:
+            ptrs["outlier_idx"] = self.outlier_idx.data_ptr()
         for name, _ in self.PLANES:
             t = self.planes[name]
             if t is None:

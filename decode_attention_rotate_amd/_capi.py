@@ -22,6 +22,8 @@ KVQ_BF16 = 0
 KVQ_F32 = 1
 
 KVQ_K_CODES, KVQ_K_SCALES, KVQ_V_CODES, KVQ_V_SCALES, KVQ_K_TAIL, KVQ_V_TAIL = range(6)
+KVQ_K_OUT_CODES, KVQ_K_OUT_SCALES, KVQ_V_OUT_CODES, KVQ_V_OUT_SCALES = range(6, 10)
+OUTLIER_CHANNELS = 32
 KVQ_MAX_BATCH = 256
 KVQ_PAGE_TOKENS = 64
 
@@ -43,7 +45,8 @@ class KvqConfig(ctypes.Structure):
         "batch", "n_kv_heads", "head_dim", "k_bits", "v_bits", "tail_len",
         "max_ctx", "rotate_k", "rotate_v")] + [("sign_seed", ctypes.c_uint32),
                                                ("k_min", ctypes.c_int32), ("v_min", ctypes.c_int32),
-                                               ("page_pool", ctypes.c_int32)]
+                                               ("page_pool", ctypes.c_int32),
+                                               ("outliers", ctypes.c_int32)]
 
     def __repr__(self):
         return "KvqConfig(%s)" % ", ".join(
@@ -52,7 +55,8 @@ class KvqConfig(ctypes.Structure):
 
 class KvqCache(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
-        "k_codes", "k_scales", "v_codes", "v_scales", "k_tail", "v_tail", "page_table")]
+        "k_codes", "k_scales", "v_codes", "v_scales", "k_tail", "v_tail", "page_table",
+        "k_out_codes", "k_out_scales", "v_out_codes", "v_out_scales", "outlier_idx")]
 
 
 class KvqCeilingTilesArgs(ctypes.Structure):

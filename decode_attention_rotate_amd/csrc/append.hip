@@ -162,6 +162,15 @@ __device__ void quant_part(const AppendArgs& a, int bx, int g, int b, int pl, ui
 #pragma unroll
     for (int e = 0; e < 32; ++e) x[e] = 0.f;
   }
+  // outlier channels: the rest of the vector is rotated and quantized, the
+  // listed channels are stored apart (no tail with outliers)
+  if (a.outl) {
+    zero_masked(x, outlier_mask(a, pl, g, j));
+    if (active && store && j == 0) {
+      const size_t roff = ((size_t)(b * (size_t)a.n_new + (p - len)) * Hkv + g) * D;
+      store_outlier_block<D>(a, pl, g, (size_t)slot, p % kTile, a.src[pl], roff);
+    }
+  }
   // every lane takes part in the cross-lane stages
   if (a.rotate[pl]) {
     if (a.has_signs) apply_signs(x, a.signs[j]);

@@ -115,6 +115,60 @@ __device__ inline uint8_t* v_tile(const A& a, size_t slot, int bits) {
   return a.codes[1] + slot * (size_t)v_tile_bytes(D, bits);
 }
 
+// Outlier channels (a.outl == 32): the bits of block j's elements that are
+// in the list of plane pl, KV head g.
+template <typename A>
+__device__ inline uint32_t outlier_mask(const A& a, int pl, int g, int j) {
+  uint32_t m = 0;
+  if (!a.outl) return 0u;
+  const int32_t* li = a.out_idx + ((size_t)pl * a.Hkv + g) * kOutl;
+#pragma unroll 8
+  for (int o = 0; o < kOutl; ++o) {
+    const int ch = li[o];   // an entry outside [0, D) masks nothing
+    if (ch >= 0 && ch / kBlock == j) m |= 1u << (ch % kBlock);
+  }
+  return m;
+}
+__device__ inline void zero_masked(float (&x)[32], uint32_t m) {
+#pragma unroll
+  for (int e = 0; e < 32; ++e) x[e] = (m >> e) & 1u ? 0.f : x[e];
+}
+
+// Quantize and store the outlier block of one position of plane pl, KV
+// head g: the 32 listed channels of the input row at src + row_off (bf16
+// or float32 elements), one 8-bit absmax block.  slot, l: the position's
+// tile slot and place in it.  K: bytes [l][32] of the tile, two's
+// complement; V: the element-major 8-bit items of a 32-element head, offset
+// codes.
+template <int D, typename A>
+__device__ inline void store_outlier_block(const A& a, int pl, int g, size_t slot, int l, const void* src,
+                                           size_t row_off) {
+  const int32_t* li = a.out_idx + ((size_t)pl * a.Hkv + g) * kOutl;
+  float xo[32];
+#pragma unroll
+  for (int o = 0; o < kOutl; ++o) {
+    const size_t i = row_off + (size_t)outlier_channel(li, o, D);
+    xo[o] = a.dtype == KVQ_BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(src)[i] << 16)
+                                : static_cast<const float*>(src)[i];
+  }
+  uint32_t c[32];
+  const uint32_t s = quantize_block<8>(xo, c);   // offset codes u = c + 128
+  uint8_t* tile = a.out_codes[pl] + slot * (kTile * kOutl);
+  if (pl == 0) {
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = gather_low_bytes(c[4 * k], c[4 * k + 1], c[4 * k + 2], c[4 * k + 3]) ^ 0x80808080u;
+    uint4* dst = reinterpret_cast<uint4*>(tile + l * kOutl);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+#pragma unroll
+    for (int o = 0; o < kOutl; ++o) tile[8 * v_item(kOutl, l, o) + l % 8] = (uint8_t)(c[o] & 0xFFu);
+  }
+  a.out_scales[pl][slot * kTile + l] = (uint16_t)s;
+}
+
 // Positions [q0, q1) that become quantized and the first position of the
 // tail after the append of sequence b.
 struct AppendRange {
@@ -258,11 +312,15 @@ __device__ inline void append_one_finish(const OneArgs& a, int g, int b, int pl,
     for (int q = 0; q < 4; ++q) { r8[q] = L.rring[q]; r8[q + 4] = make_uint4(0u, 0u, 0u, 0u); }
     widen_bf16(r8, y);
   }
+  if (a.outl && o.new_lane) zero_masked(x, outlier_mask(a, pl, g, j));   // the rest only
   if (a.rotate[pl]) {                            // every lane takes part
     if (a.has_signs) apply_signs(x, a.signs[j]);
     if constexpr (FAST) rotate_row_for_absmax<D>(x, lane, a.cd);
     else rotate_row<D>(x, lane, a.cd);
   }
+  // outlier channels (no tail: the new token is the quantized position)
+  if (a.outl && store && lane == 0 && o.q_lane)
+    store_outlier_block<D>(a, pl, g, qs, pq % kTile, a.src[pl], o.unit * D);
   if (out_new && T > 0 && o.new_lane) {
 #pragma unroll
     for (int e = 0; e < 32; ++e) out_new[kBlock * j + e] = bf16_round(x[e]);

@@ -50,6 +50,16 @@ constexpr int kPGM = kPageAny;
 DecodeLauncher KVQ_TABLE[6][8] = {KVQ_ROW(4, false), KVQ_ROW(5, false), KVQ_ROW(6, false),
                                   KVQ_ROW(8, false), KVQ_ROW(4, true), KVQ_ROW(5, true)};
 
+// outlier-channel kernels (head_dim 128, absmax K and V): V q4_0..q8_0
+#if KVQ_INST_D == 128 && KVQ_INST_KM == 0
+#define KVQ_OTABLE KVQ_CAT(kvq_decode_otable, KVQ_INST_D, KVQ_INST_KB, KVQ_INST_KM)
+#define KVQ_LO(VB, G) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, G, false, false, false, kPGM, true>
+#define KVQ_OROW(VB) \
+  {KVQ_LO(VB, 1), KVQ_LO(VB, 2), KVQ_LO(VB, 3), KVQ_LO(VB, 4), \
+   KVQ_LO(VB, 5), KVQ_LO(VB, 6), KVQ_LO(VB, 7), KVQ_LO(VB, 8)}
+DecodeLauncher KVQ_OTABLE[4][8] = {KVQ_OROW(4), KVQ_OROW(5), KVQ_OROW(6), KVQ_OROW(8)};
+#endif
+
 // chunked prefill, same V order
 #define KVQ_P(VB, VM) launch_decode_split<KVQ_INST_D, KVQ_INST_KB, VB, 8, true, kKM, VM, kPGM>
 DecodeLauncher KVQ_PF_TABLE[6] = {KVQ_P(4, false), KVQ_P(5, false), KVQ_P(6, false),

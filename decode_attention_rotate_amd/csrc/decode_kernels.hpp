@@ -104,7 +104,7 @@ __device__ inline float half_of(uint32_t w, int hi) {
 
 // Cache bytes of one 32-token step held in registers.  KM / VM: K / V use
 // scale-and-min blocks, whose scale planes hold an (s, m) fp16 pair per block.
-template <int D, int KB, int VB, bool KM, bool VM>
+template <int D, int KB, int VB, bool KM, bool VM, bool OUT = false>
 struct StepRegs {
   static constexpr int NB = D / kBlock;
   static constexpr int NN = D / 16;
@@ -117,6 +117,11 @@ struct StepRegs {
   uint32_t ks[2][KSW], vs[2][VSW];           // [m] fp16 scales (pairs) of this lane's token
   u32x4 v[VB == 8 ? NN / 2 : NN / 4];        // V items (4 or 8 bytes each)
   uint32_t vh[VB == 5 ? NN / 4 : VB == 6 ? NN / 2 : 1];   // 5-bit bytes / 6-bit fields
+  // outlier channels: K codes (bytes 8r..8r+7 of the lane's tokens), the
+  // tokens' K and V outlier scales, the lane's two 8-bit V items
+  u32x2 ko[OUT ? 2 : 1];
+  uint32_t kos[OUT ? 2 : 1], vos[OUT ? 2 : 1];
+  u32x4 vo;
 
   // scale of block j of token-row half m, and the minimum of a pair block
   __device__ float k_scale(int m, int j) const { return KM ? half_of(ks[m][j], 0) : half_of(ks[m][j / 2], j % 2); }
@@ -128,10 +133,10 @@ struct StepRegs {
 // Largest fp16 V scale (as its bit pattern; scales are >= 0, so bit patterns
 // order like the values) of token-row half m of this lane.  Scale-and-min
 // words hold (s, m) pairs with s in the low half.
-template <int D, int KB, int VB, bool KM, bool VM>
-__device__ inline uint32_t v_scale_max_bits(const StepRegs<D, KB, VB, KM, VM>& R, int m) {
+template <int D, int KB, int VB, bool KM, bool VM, bool OUT>
+__device__ inline uint32_t v_scale_max_bits(const StepRegs<D, KB, VB, KM, VM, OUT>& R, int m) {
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  constexpr int VSW = StepRegs<D, KB, VB, KM, VM>::VSW;
+  constexpr int VSW = StepRegs<D, KB, VB, KM, VM, OUT>::VSW;
   u16x2 x = __builtin_bit_cast(u16x2, R.vs[m][0]);
 #pragma unroll
   for (int w = 1; w < VSW; ++w) x = __builtin_elementwise_max(x, __builtin_bit_cast(u16x2, R.vs[m][w]));
@@ -178,8 +183,8 @@ __device__ inline void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
 // token in the k-slot order of the query bytes (4/5/6-bit: elements
 // 0,2,4,6,1,3,5,7 of the lane's group of 8, widened to bytes; the high bits
 // come from one rotate of the block's high word).
-template <int D, int KB, int VB, bool KM, bool VM>
-__device__ inline long k_operand(const StepRegs<D, KB, VB, KM, VM>& R, int i, uint32_t rot_lo, uint32_t rot_hi) {
+template <int D, int KB, int VB, bool KM, bool VM, bool OUT>
+__device__ inline long k_operand(const StepRegs<D, KB, VB, KM, VM, OUT>& R, int i, uint32_t rot_lo, uint32_t rot_hi) {
   if constexpr (KB == 8) {
     return __builtin_bit_cast(long, R.k8[i]);
   } else {
@@ -201,8 +206,22 @@ __device__ inline long k_operand(const StepRegs<D, KB, VB, KM, VM>& R, int i, ui
 // B operand of P.V for output elements 16*nb..+15: this lane's element for
 // the 8 tokens of its k-slots, as exact fp16 codes (centred levels
 // u - 2^(VB-1) for scale-and-min blocks).
-template <int D, int KB, int VB, bool KM, bool VM>
-__device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, uint32_t magic) {
+// B operand of P.V from an 8-bit V item pair (items nb = 0, 1 of a u32x4):
+// the 8 offset codes u of item nb as exact fp16 values u - 128.
+__device__ inline h8_t v_operand8(const u32x4 q, int nb) {
+  const uint32_t x0 = nb ? q[2] : q[0];
+  const uint32_t x1 = nb ? q[3] : q[1];
+  const uint32_t c64 = 0x64646464u;
+  const h2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const h2_t d0 = as_h2(__builtin_amdgcn_perm(c64, x0, 0x04010400u)) + bias;
+  const h2_t d1 = as_h2(__builtin_amdgcn_perm(c64, x0, 0x04030402u)) + bias;
+  const h2_t d2 = as_h2(__builtin_amdgcn_perm(c64, x1, 0x04010400u)) + bias;
+  const h2_t d3 = as_h2(__builtin_amdgcn_perm(c64, x1, 0x04030402u)) + bias;
+  return h8_t{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+}
+
+template <int D, int KB, int VB, bool KM, bool VM, bool OUT>
+__device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM, OUT>& R, int nb, uint32_t magic) {
   const h2_t one16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   if constexpr (VB == 8) {
     const u32x4 q = R.v[nb / 2];
@@ -267,7 +286,11 @@ __device__ inline h8_t v_operand(const StepRegs<D, KB, VB, KM, VM>& R, int nb, u
 // PGM: where tiles live.  kPageAny decides at run time between contiguous
 // and paged planes; kPageFlat and kPagePaged fix it at compile time, for the
 // variants whose register budget is too tight to carry both.
-template <int D, int KB, int VB, int G, bool PF, bool KM, bool VM, int PGM>
+// OUT: outlier channels (32 per plane and KV head, 8-bit, original space;
+// no tail): one more i8 product per 16 tokens adds q[O_K] . x_O to the
+// scores, and two more f16 products accumulate the V outlier channels,
+// which the combine adds at their channels.
+template <int D, int KB, int VB, int G, bool PF, bool KM, bool VM, int PGM, bool OUT = false>
 __global__ __launch_bounds__(64 * split_group_waves(D, KM || VM || PF))
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(D, KM || VM || PF),
                                    split_waves_per_simd(D, KM || VM || PF))))
@@ -303,9 +326,11 @@ void decode_split_kernel(DecodeArgs a) {
   constexpr int LOROW = 8 * NB;
   constexpr int ZROW = 8 * NB + 8;
   constexpr int LOQ = 8 * NB + 9;
-  using Regs = StepRegs<D, KB, VB, KM, VM>;
+  constexpr int OROW = LOQ + (VM ? 8 * NB : 0);   // outlier weights of the 8 heads (OUT)
+  using Regs = StepRegs<D, KB, VB, KM, VM, OUT>;
+  static_assert(!OUT || (!PF && !KM && !VM), "outlier channels: decode with absmax blocks");
 
-  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9 + (VM ? 8 * NB : 0)) * WROW];
+  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9 + (VM ? 8 * NB : 0) + (OUT ? 8 : 0)) * WROW];
   __shared__ __align__(16) float alds_all[kGroupWaves][16];
   __shared__ uint32_t tile_ctr;
   // fused step: new K, new V, quantized K, quantized V values; the two
@@ -394,6 +419,10 @@ void decode_split_kernel(DecodeArgs a) {
   float mvA[VM ? NB : 1], mvB[VM ? NB : 1];
 #pragma unroll
   for (int j = 0; j < (VM ? NB : 1); ++j) mvA[j] = mvB[j] = 0.f;
+  // V outlier channels: slots 16 nb + col of the heads' rows (OUT)
+  f4_t acco[OUT ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < (OUT ? 2 : 1); ++i) acco[i] = f4_t{0.f, 0.f, 0.f, 0.f};
   // Weight factor of the quantized positions: their fp16 weights are
   // p * scale_v * 2^vfe, with 2^(11 - vfe) <= the largest V scale seen so far
   // < 2^(12 - vfe), so a weight never drops into fp16's subnormal range
@@ -517,6 +546,10 @@ void decode_split_kernel(DecodeArgs a) {
       const f4_t al = *reinterpret_cast<const f4_t*>(&alds[4 * r]) * vratio;
 #pragma unroll
       for (int i = 0; i < NN; ++i) acc[i] *= al;
+      if constexpr (OUT) {
+        acco[0] *= al;
+        acco[1] *= al;
+      }
       if constexpr (VM) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -711,6 +744,10 @@ void decode_split_kernel(DecodeArgs a) {
     long qop[NB];
     long qres[kQX ? NB : 1];
     float ckA, ckB;
+    // outlier channels: the unrotated query at K's channels in 16-bit fixed
+    // point of its own step, and that step's score factor per head
+    long qopo = 0;
+    float ckoA = 0.f, ckoB = 0.f;
     // head_dim 256 keeps the correction as two integers per block, added to
     // the combined sums (exact), to free registers for issuing the two token
     // halves' products together
@@ -749,6 +786,29 @@ void decode_split_kernel(DecodeArgs a) {
     const uint8_t* vpl = a.v_codes + unit * (size_t)(a.cap / kTile) * VTB;
     const uint16_t* vsc = a.v_scales + unit * (size_t)a.cap * VSE;
     auto load_step = [&](Regs& R, int s0) {
+      if constexpr (OUT) {
+        // outlier planes: [tile][64][32] K bytes, element-major V tiles of
+        // 2 KiB, [tile][64] scales; the tile's slot as for the other planes
+        size_t oslot = unit * (size_t)(a.cap / kTile) + s0 / kTile;
+        if (PGM == kPagePaged || (PGM == kPageAny && a.map.ptab != nullptr)) {
+          const int page = ((const __attribute__((address_space(4))) int32_t*)a.map.ptab)[(size_t)b * a.map.tiles +
+                                                                                            s0 / kTile];
+          oslot = (unsigned)page < (unsigned)a.map.n_pages ? (size_t)page * a.map.Hkv + g : (size_t)g;
+        }
+        const uint8_t* kot = a.out_codes[0] + oslot * (kTile * kOutl);
+        const uint8_t* vot = a.out_codes[1] + oslot * (kTile * kOutl);
+        const uint16_t* kos = a.out_scales[0] + oslot * kTile;
+        const uint16_t* vos = a.out_scales[1] + oslot * kTile;
+        const int l0 = s0 % kTile;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int l = l0 + 16 * m + col;
+          R.ko[m] = ld_cache<kNT, u32x2>(kot + l * kOutl + 8 * r);
+          R.kos[m] = ld_cache<kNT, uint16_t>(kos + l);
+          R.vos[m] = ld_cache<kNT, uint16_t>(vos + l);
+        }
+        R.vo = ld_cache<kNT, u32x4>(vot + ((l0 / kStep) * 64 + lane) * 16);
+      }
       const int j2 = (s0 / kStep) & 1;
       // s0's K and V tiles and its row of each scale plane
       const uint8_t* ktile = kpl + (size_t)(s0 / kTile) * kTile * RKP;
@@ -890,6 +950,17 @@ void decode_split_kernel(DecodeArgs a) {
           }
         }
       }
+      float soA[2] = {0.f, 0.f}, soB[2] = {0.f, 0.f};
+      if constexpr (OUT) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const i4_t e = __builtin_amdgcn_mfma_i32_16x16x32_i8(qopo, __builtin_bit_cast(long, R.ko[m]),
+                                                               i4_t{0, 0, 0, 0}, 0, 0, 0);
+          const float kso = half_of(R.kos[m], 0);
+          soA[m] = kso * (float)((e[0] << 8) + e[1]);
+          soB[m] = kso * (float)((e[2] << 8) + e[3]);
+        }
+      }
       float xA[2], xB[2], pA[2], pB[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -897,6 +968,10 @@ void decode_split_kernel(DecodeArgs a) {
         const bool validA = tok < nqr && (!PF || tok <= limA);
         const bool validB = tok < nqr && (!PF || tok <= limB);
         float ya = sA[m] * ckA, yb = sB[m] * ckB;
+        if constexpr (OUT) {
+          ya = __builtin_fmaf(soA[m], ckoA, ya);
+          yb = __builtin_fmaf(soB[m], ckoB, yb);
+        }
         asm volatile("" : "+v"(ya), "+v"(yb));   // selects, not branches
         xA[m] = validA && okA ? ya : -INFINITY;
         xB[m] = validB && okB ? yb : -INFINITY;
@@ -907,8 +982,14 @@ void decode_split_kernel(DecodeArgs a) {
       bool vtrig = false;
       float vratio = 1.f;
       {
-        const uint32_t l0 = s0 + col < nqr ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 0) : 0u;
-        const uint32_t l1 = s0 + 16 + col < nqr ? v_scale_max_bits<D, KB, VB, KM, VM>(R, 1) : 0u;
+        uint32_t l0 = v_scale_max_bits<D, KB, VB, KM, VM>(R, 0);
+        uint32_t l1 = v_scale_max_bits<D, KB, VB, KM, VM>(R, 1);
+        if constexpr (OUT) {
+          l0 = max(l0, R.vos[0] & 0xFFFFu);
+          l1 = max(l1, R.vos[1] & 0xFFFFu);
+        }
+        l0 = s0 + col < nqr ? l0 : 0u;
+        l1 = s0 + 16 + col < nqr ? l1 : 0u;
         const uint32_t lm = l0 > l1 ? l0 : l1;
         if (__builtin_amdgcn_ballot_w64(lm >= vthr) != 0) {
           const float mx = row16_max((float)__builtin_bit_cast(_Float16, (uint16_t)lm));
@@ -954,6 +1035,15 @@ void decode_split_kernel(DecodeArgs a) {
           }
         }
       }
+      if constexpr (OUT) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float vso = half_of(R.vos[m], 0);
+          const int t = 16 * m + col;
+          wl[(OROW + hA) * WROW + t] = __builtin_bit_cast(uint16_t, (_Float16)(pA[m] * vf * vso));
+          wl[(OROW + hB) * WROW + t] = __builtin_bit_cast(uint16_t, (_Float16)(pB[m] * vf * vso));
+        }
+      }
       if constexpr (VM) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -976,6 +1066,12 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 2 * j; i < 2 * j + 2; ++i)
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, v_operand<D, KB, VB, KM, VM>(R, i, magic), acc[i], 0, 0, 0);
+      }
+      if constexpr (OUT) {
+        const int row = col < 8 ? OROW + col : ZROW;
+        const h8_t wa = *reinterpret_cast<const h8_t*>(&wl[row * WROW + 8 * r]);
+        acco[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, v_operand8(R.vo, 0), acco[0], 0, 0, 0);
+        acco[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, v_operand8(R.vo, 1), acco[1], 0, 0, 0);
       }
     };
 
@@ -1013,6 +1109,38 @@ void decode_split_kernel(DecodeArgs a) {
       }
       amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, __shfl_xor(amax, 32));
+      if constexpr (OUT) {
+        // q at K's outlier channels 8r..8r+7 of the list (original space)
+        const int hq = col < 2 * G && row_ok(col / 2) ? col / 2 : 0;
+        const size_t qoff = row_vec(hq) * D;
+        const int32_t* kidx = a.out_idx + (size_t)g * kOutl + 8 * r;
+        float fo[8];
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int ch = outlier_channel(kidx, i, D);
+          fo[i] = a.q_dtype == KVQ_BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.q)[qoff + ch] << 16)
+                                        : static_cast<const float*>(a.q)[qoff + ch];
+          am = fmaxf(am, fabsf(fo[i]));
+        }
+        am = fmaxf(am, __shfl_xor(am, 16));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const float so = am > 0.f ? am / 32639.0f : 1.0f;
+        const float io = 1.0f / so;
+        uint64_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          int x = (int)rintf(fo[i] * io);
+          x = x > 32639 ? 32639 : (x < -32639 ? -32639 : x);
+          const int hi = (x + 128) >> 8;
+          const int byte = (col & 1) ? x - 256 * hi : hi;
+          w |= (uint64_t)(uint8_t)(int8_t)byte << (8 * i);
+        }
+        qopo = col < 2 * G && row_ok(col / 2) ? (long)w : 0;
+        const float cko = so * a.sm_scale * kLog2e;
+        ckoA = okA ? __shfl(cko, 4 * r) : 0.f;
+        ckoB = okB ? __shfl(cko, 4 * r + 2) : 0.f;
+      }
       const float step = amax > 0.f ? amax / 32639.0f : 1.0f;
       const float inv = 1.0f / step;
       const float ck = step * a.sm_scale * kLog2e;
@@ -1182,6 +1310,26 @@ void decode_split_kernel(DecodeArgs a) {
       }
     }
   }
+  if constexpr (OUT) {
+    const float inv = __uint_as_float((uint32_t)(127 - vfe) << 23);   // exact
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      acco[i] *= inv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acco[i][k] += __shfl_xor(acco[i][k], 32);
+    }
+    if (r < 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int h = 4 * r + k;
+        if (row_ok(h)) {
+          float* dst = a.part_out + (row_vec(h) * a.S + split) * kOutl + col;
+          dst[0] = acco[0][k];
+          dst[16] = acco[1][k];
+        }
+      }
+    }
+  }
   if (col == 0) {
     if (okA) {
       a.part_ml[(row_vec(hA) * a.S + split) * 2] = mA;
@@ -1195,10 +1343,10 @@ void decode_split_kernel(DecodeArgs a) {
 }
 
 template <int D, int KB, int VB, int G, bool PF = false, bool KM = false, bool VM = false,
-          int PGM = kPageAny>
+          int PGM = kPageAny, bool OUT = false>
 hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM, PGM>), grid,
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM, PGM, OUT>), grid,
                      dim3(64 * split_group_waves(D, KM || VM || PF)), 0, s, a);
   return hipGetLastError();
 }

@@ -21,6 +21,10 @@ KVQ_ALL_K(KVQ_DECLARE_TABLE, 192) KVQ_ALL_K(KVQ_DECLARE_TABLE, 256)
 #define KVQ_DECLARE_PTABLE(D, KB, KM) extern DecodeLauncher kvq_decode_ptable_##D##_##KB##_##KM[6][8]; \
   extern DecodeLauncher kvq_prefill_ptable_##D##_##KB##_##KM[6];
 KVQ_ALL_K(KVQ_DECLARE_PTABLE, 256)
+// outlier-channel kernels: head_dim 128, absmax K, [V format q4_0..q8_0][G-1]
+#define KVQ_DECLARE_OTABLE(D, KB, KM) extern DecodeLauncher kvq_decode_otable_##D##_##KB##_##KM[4][8];
+KVQ_DECLARE_OTABLE(128, 4, 0) KVQ_DECLARE_OTABLE(128, 5, 0) KVQ_DECLARE_OTABLE(128, 6, 0)
+KVQ_DECLARE_OTABLE(128, 8, 0)
 #undef KVQ_DECLARE_TABLE
 
 namespace {
@@ -30,9 +34,18 @@ int v_index(int vb, bool vm) {
 }
 }  // namespace
 
-DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, bool paged) {
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, bool paged,
+                               bool outliers) {
   const int vi = v_index(vb, vm);
   if (vi < 0 || gc < 1 || gc > 8) return nullptr;
+  if (outliers) {
+    if (D != 128 || km || vm || vi > 3) return nullptr;
+    if (kb == 4) return kvq_decode_otable_128_4_0[vi][gc - 1];
+    if (kb == 5) return kvq_decode_otable_128_5_0[vi][gc - 1];
+    if (kb == 6) return kvq_decode_otable_128_6_0[vi][gc - 1];
+    if (kb == 8) return kvq_decode_otable_128_8_0[vi][gc - 1];
+    return nullptr;
+  }
   if (paged && split_fixed_layout(D)) {
 #define KVQ_PICK(DD, KK, MM) \
   if (D == DD && kb == KK && (int)km == MM) return kvq_decode_ptable_##DD##_##KK##_##MM[vi][gc - 1];
@@ -114,6 +127,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     lsum += w * ml[2 * s + 1];
   }
   const float L = block_sum(lsum, red);   // its barriers also publish wgt
+  // outlier channels of V: thread t < 32 merges channel slot t the same way
+  float vo = 0.f;
+  if (a.part_out && t < kOutl) {
+    const float* po = a.part_out + (size_t)bh * S * kOutl + t;
+    for (int s2 = 0; s2 < S; ++s2) vo += wgt[s2] * po[(size_t)s2 * kOutl];
+  }
   const int e = t % D, ph = t / D;
   float v[U] = {};
   int s = t < P * D ? ph : S;
@@ -144,12 +163,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
   }
   const float scale = (a.rotate ? a.cd : 1.0f) / L;
+  float r = 0.f;
   if (t < D) {
-    float r = o[t] * scale;
+    r = o[t] * scale;
     if (a.rotate && a.has_signs)   // back by diag(s) H
       r = __uint_as_float(__float_as_uint(r) ^ (((a.signs[t / 32] >> (t % 32)) & 1u) << 31));
-    a.out[(size_t)bh * D + t] = r;
   }
+  if (a.part_out) {
+    // the outlier channels' part is added at V's channels (original space)
+    __syncthreads();   // every thread has read o[] for the rotation
+    if (t < D) o[t] = r;
+    __syncthreads();
+    if (t < kOutl) {
+      const int g = (bh % a.Hq) / a.G;
+      const int ch = outlier_channel(a.v_out_idx + (size_t)g * kOutl, t, D);
+      o[ch] = o[ch] + vo / L;   // the channels of a list are distinct
+    }
+    __syncthreads();
+    if (t < D) r = o[t];
+  }
+  if (t < D) a.out[(size_t)bh * D + t] = r;
 }
 
 }  // namespace

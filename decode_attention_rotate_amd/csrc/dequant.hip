@@ -80,6 +80,32 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   const int p = a.t0 + blockIdx.x * RPB + tid / LPR;
   const bool active = tid / LPR < RPB && p < a.t1;
   const size_t unit = (size_t)a.b * a.Hkv + g;
+  // outlier channels (space 1): the block's outlier values, and the list
+  // slot of each channel (-1: not an outlier), in LDS
+  __shared__ float oval[RPB][kOutl];
+  __shared__ int inv[D];
+  const bool outl = a.outl && a.space == 1;   // uniform
+  if (outl) {
+    for (int i = tid; i < D; i += 256) inv[i] = -1;
+    __syncthreads();
+    if (tid < kOutl) inv[outlier_channel(a.out_idx + (size_t)g * kOutl, tid, D)] = tid;
+    for (int it = tid; it < RPB * kOutl; it += 256) {
+      const int r = it / kOutl, o = it % kOutl;
+      const int pp = a.t0 + blockIdx.x * RPB + r;
+      float v = 0.f;
+      if (pp < a.t1 && pp < a.nq) {
+        const size_t slot = tile_slot_read(a.map, a.b, g, pp / kTile);
+        const int l = pp % kTile;
+        const float s = (float)__builtin_bit_cast(_Float16, a.out_scales[slot * kTile + l]);
+        const uint8_t* tile = a.out_codes + slot * kTile * kOutl;
+        const int c = a.which == 0 ? (int)(int8_t)tile[l * kOutl + o]
+                                   : (int)tile[8 * v_item(kOutl, l, o) + l % 8] - 128;
+        v = (float)c * s;
+      }
+      oval[r][o] = v;
+    }
+    __syncthreads();
+  }
   float x[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) x[e] = 0.f;
@@ -131,6 +157,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     if (a.has_signs) apply_signs(x, a.signs[j]);   // back by diag(s) H
   }
   if (!active) return;
+  if (outl) {
+    const int r = tid / LPR;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int k = inv[kBlock * j + e];
+      if (k >= 0) x[e] = x[e] + oval[r][k];
+    }
+  }
   float4* dst = reinterpret_cast<float4*>(a.out + ((size_t)(p - a.t0) * a.Hkv + g) * D + kBlock * j);
 #pragma unroll
   for (int q = 0; q < 8; ++q) dst[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);

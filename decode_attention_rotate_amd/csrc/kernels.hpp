@@ -24,9 +24,24 @@ struct AppendArgs {
   float cd;                  // fp32(1/sqrt(D))
   int32_t has_signs;         // rotate by H diag(s): flip element e's sign by bit e of signs
   uint32_t signs[8];
+  // outlier channels: outl (0 or 32) channels per plane and KV head, listed
+  // in out_idx [2][Hkv][outl]; their 8-bit codes and fp16 scales
+  int32_t outl;
+  const int32_t* out_idx;
+  uint8_t* out_codes[2];     // K: [tile][64][32] bytes; V: element-major 8-bit tiles
+  uint16_t* out_scales[2];   // [tile][64]
   int32_t len[KVQ_MAX_BATCH];  // lengths before the append
 };
 hipError_t launch_append(int D, const AppendArgs& a, int B, hipStream_t s);
+
+// Channels of an outlier set (one 32-element block).
+constexpr int kOutl = 32;
+// Entry o of an outlier list; an entry outside [0, D) reads channel 0 in its
+// place (results unspecified; every access stays inside the head vector).
+__device__ inline int outlier_channel(const int32_t* list, int o, int D) {
+  const int ch = list[o];
+  return (unsigned)ch < (unsigned)D ? ch : 0;
+}
 
 // What the one-token append of a decode step reads (AppendArgs without the
 // lengths, which the caller passes): the fused decode step carries it in its
@@ -44,6 +59,10 @@ struct OneArgs {
   float cd;
   int32_t has_signs;
   uint32_t signs[8];
+  int32_t outl;
+  const int32_t* out_idx;
+  uint8_t* out_codes[2];
+  uint16_t* out_scales[2];
 };
 __host__ __device__ inline OneArgs one_args(const AppendArgs& a) {
   OneArgs o;
@@ -63,6 +82,12 @@ __host__ __device__ inline OneArgs one_args(const AppendArgs& a) {
   o.cd = a.cd;
   o.has_signs = a.has_signs;
   for (int i = 0; i < 8; ++i) o.signs[i] = a.signs[i];
+  o.outl = a.outl;
+  o.out_idx = a.out_idx;
+  for (int p = 0; p < 2; ++p) {
+    o.out_codes[p] = a.out_codes[p];
+    o.out_scales[p] = a.out_scales[p];
+  }
   return o;
 }
 
@@ -79,6 +104,10 @@ struct DequantArgs {
   float cd;
   int32_t has_signs;         // space 1 rotates back by diag(s) H
   uint32_t signs[8];
+  int32_t outl;              // outlier channels: added back in space 1
+  const uint8_t* out_codes;
+  const uint16_t* out_scales;
+  const int32_t* out_idx;    // this plane's lists [Hkv][outl]
 };
 hipError_t launch_dequant(int D, const DequantArgs& a, hipStream_t s);
 
@@ -121,6 +150,12 @@ struct DecodeArgs {
   // lengths below then count it); step_on 0: plain decode over the cache
   int32_t step_on;
   OneArgs step;
+  // outlier channels (the OUT kernels): codes and scales of K's and V's
+  // outlier planes, the lists [2][Hkv][32], partial sums [B][Hq][S][32]
+  const uint8_t* out_codes[2];
+  const uint16_t* out_scales[2];
+  const int32_t* out_idx;
+  float* part_out;
   int32_t len[KVQ_MAX_BATCH];
 };
 using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
@@ -132,7 +167,8 @@ constexpr int kPageAny = 0, kPageFlat = 1, kPagePaged = 2;
 constexpr bool split_fixed_layout(int D) { return D == 256; }
 // Table lookup for (D, k_bits, v_bits, heads per chunk, K / V scale-and-min
 // blocks, paged planes); nullptr if absent.
-DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, bool paged);
+DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, bool paged,
+                               bool outliers = false);
 // The prefill variant of the split kernel for (D, k_bits, v_bits, km, vm, paged).
 DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm, bool paged);
 
@@ -147,6 +183,9 @@ struct CombineArgs {
   float cd;
   int32_t has_signs;         // rotate back by diag(s) H
   uint32_t signs[8];
+  const float* part_out;     // outlier channels' partials [B][Hq][S][32], or null
+  const int32_t* v_out_idx;  // V's outlier lists [Hkv][32]
+  int32_t G;                 // query heads per KV head
 };
 hipError_t launch_combine(int D, const CombineArgs& a, int B, hipStream_t s);
 

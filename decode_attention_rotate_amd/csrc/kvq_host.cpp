@@ -34,6 +34,7 @@ using namespace kvq;
 int target_waves(int D, bool wide) { return 256 * 4 * split_waves_per_simd(D, wide); }
 constexpr int kMaxSplits = kMaxSplitsDevice;
 constexpr int32_t kMaxCtx = 2147483647 - 2 * kTile;
+constexpr int32_t kOutlierChannels = 32;
 
 thread_local hipEvent_t g_ev_before = nullptr;
 thread_local hipEvent_t g_ev_after = nullptr;
@@ -58,6 +59,11 @@ kvq_status check_cfg(const kvq_config* c) {
   // lengths, capacities and plane offsets are int32 in the kernels: the
   // capacity rounded up to a whole tile, plus a tile of slack, must fit
   if (c->max_ctx > kMaxCtx) return KVQ_ERR_INVALID;
+  if (c->outliers != 0 && c->outliers != kOutlierChannels) return KVQ_ERR_INVALID;
+  // outlier channels are built without a tail, at head_dim 128, with absmax
+  // blocks for the rest
+  if (c->outliers && (c->tail_len != 0 || c->head_dim != 128 || c->k_min || c->v_min))
+    return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -75,6 +81,15 @@ kvq_status check_cache(const kvq_config& c, const kvq_cache* k) {
   if (c.page_pool > 0) {
     if (!k->page_table) return KVQ_ERR_INVALID;
     if ((reinterpret_cast<uintptr_t>(k->page_table) & 3u) != 0) return KVQ_ERR_ALIGN;
+  }
+  if (c.outliers) {
+    const void* out[4] = {k->k_out_codes, k->k_out_scales, k->v_out_codes, k->v_out_scales};
+    for (const void* p : out) {
+      if (!p) return KVQ_ERR_INVALID;
+      if (!aligned16(p)) return KVQ_ERR_ALIGN;
+    }
+    if (!k->outlier_idx) return KVQ_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(k->outlier_idx) & 3u) != 0) return KVQ_ERR_ALIGN;
   }
   return KVQ_OK;
 }
@@ -161,9 +176,10 @@ PrefillSchedule prefill_schedule(const kvq_config& c, int n_q_heads, int n_q, in
   return p;
 }
 
-// Workspace: (max, sum) pairs, then partial vectors, per split.
+// Workspace: (max, sum) pairs, then partial vectors, per split; with outlier
+// channels, then the partial sums of the 32 outlier channels of V.
 struct WsLayout {
-  size_t ml, acc, total;
+  size_t ml, acc, out, total;
 };
 WsLayout ws_layout(const kvq_config& c, int n_q_heads, int S) {
   WsLayout w;
@@ -171,7 +187,9 @@ WsLayout ws_layout(const kvq_config& c, int n_q_heads, int S) {
   w.ml = 0;
   const size_t ml_bytes = heads * (size_t)S * 2 * sizeof(float);
   w.acc = w.ml + (ml_bytes + 255) / 256 * 256;
-  w.total = w.acc + heads * (size_t)S * c.head_dim * sizeof(float);
+  const size_t acc_bytes = heads * (size_t)S * c.head_dim * sizeof(float);
+  w.out = w.acc + (acc_bytes + 255) / 256 * 256;
+  w.total = w.out + heads * (size_t)S * c.outliers * sizeof(float);
   return w;
 }
 
@@ -224,6 +242,14 @@ AppendArgs append_args(const kvq_config& c, const kvq_cache* cache, const void* 
   a.dtype = dtype;
   a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
   a.has_signs = sign_mask(c, a.signs);
+  a.outl = c.outliers;
+  if (c.outliers) {
+    a.out_idx = cache->outlier_idx;
+    a.out_codes[0] = static_cast<uint8_t*>(cache->k_out_codes);
+    a.out_codes[1] = static_cast<uint8_t*>(cache->v_out_codes);
+    a.out_scales[0] = static_cast<uint16_t*>(cache->k_out_scales);
+    a.out_scales[1] = static_cast<uint16_t*>(cache->v_out_scales);
+  }
   return a;
 }
 
@@ -232,7 +258,7 @@ AppendArgs append_args(const kvq_config& c, const kvq_cache* cache, const void* 
 extern "C" {
 
 kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t max_ctx) {
-  kvq_config c;
+  kvq_config c{};
   c.batch = batch;
   c.n_kv_heads = n_kv_heads;
   c.head_dim = head_dim;
@@ -247,6 +273,7 @@ kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads, int32_t head_di
   c.k_min = 0;
   c.v_min = 0;
   c.page_pool = 0;
+  c.outliers = 0;
   return c;
 }
 
@@ -268,6 +295,10 @@ size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane) {
     case KVQ_V_SCALES: return tiles * kTile * nb * sizeof(uint16_t) * (c.v_min ? 2 : 1);
     case KVQ_K_TAIL:
     case KVQ_V_TAIL: return units * (size_t)c.tail_len * c.head_dim * sizeof(uint16_t);
+    case KVQ_K_OUT_CODES:
+    case KVQ_V_OUT_CODES: return tiles * kTile * (size_t)c.outliers;
+    case KVQ_K_OUT_SCALES:
+    case KVQ_V_OUT_SCALES: return c.outliers ? tiles * kTile * sizeof(uint16_t) : 0;
     default: break;
   }
   return 0;
@@ -336,7 +367,7 @@ kvq_status plan_decode(const kvq_config* cfg, const kvq_cache* cache, const void
   if ((int64_t)c.n_kv_heads * plan->sc.nchunk > 65535) return KVQ_ERR_INVALID;
   plan->wl = ws_layout(c, n_q_heads, plan->sc.S);
   plan->fn = decode_launcher(c.head_dim, c.k_bits, c.v_bits, plan->sc.gc, c.k_min != 0, c.v_min != 0,
-                             c.page_pool > 0);
+                             c.page_pool > 0, c.outliers != 0);
   if (!plan->fn) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
@@ -379,6 +410,14 @@ kvq_status run_decode(const kvq_config& c, const kvq_cache* cache, const void* q
   da.cap = (int32_t)cap_tokens(c);
   da.map = tile_map(c, cache);
   da.S = sc.S;
+  if (c.outliers) {
+    da.out_codes[0] = static_cast<const uint8_t*>(cache->k_out_codes);
+    da.out_codes[1] = static_cast<const uint8_t*>(cache->v_out_codes);
+    da.out_scales[0] = static_cast<const uint16_t*>(cache->k_out_scales);
+    da.out_scales[1] = static_cast<const uint16_t*>(cache->v_out_scales);
+    da.out_idx = cache->outlier_idx;
+    da.part_out = reinterpret_cast<float*>(ws + wl.out);
+  }
   if (step) {
     da.step_on = 1;
     da.step = *step;
@@ -400,6 +439,9 @@ kvq_status run_decode(const kvq_config& c, const kvq_cache* cache, const void* q
   ca.cd = cd;
   ca.has_signs = da.has_signs;
   for (int i = 0; i < 8; ++i) ca.signs[i] = da.signs[i];
+  ca.part_out = da.part_out;
+  ca.v_out_idx = c.outliers ? cache->outlier_idx + (size_t)c.n_kv_heads * c.outliers : nullptr;
+  ca.G = n_q_heads / c.n_kv_heads;
   return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
 }
 
@@ -461,10 +503,11 @@ kvq_status kvq_decode_step(const kvq_config* cfg, const kvq_cache* cache, const 
   if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
   if (workspace_bytes < plan.wl.total) return KVQ_ERR_WORKSPACE;
   AppendArgs a = append_args(c, cache, k_new, v_new, kv_dtype, 1);
-  if (plan.sc.nchunk > 1) {
+  if (plan.sc.nchunk > 1 || c.outliers) {
     // a KV head's query heads span several chunks, each of which would
     // need the values of the position leaving the tail while another one
-    // overwrites it: append first, then attend
+    // overwrites it (or the cache has outlier channels, which the fused
+    // path does not carry): append first, then attend
     for (int b = 0; b < c.batch; ++b) a.len[b] = seq_len[b];
     if ((st = hip_status(launch_append(c.head_dim, a, c.batch, static_cast<hipStream_t>(stream)))) != KVQ_OK)
       return st;
@@ -508,6 +551,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   if (n_q_heads < c.n_kv_heads || n_q_heads % c.n_kv_heads != 0 || n_q < 1) return KVQ_ERR_INVALID;
   if ((int64_t)c.batch * n_q * n_q_heads > 2147483647 / 8) return KVQ_ERR_INVALID;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  if (c.outliers) return KVQ_ERR_UNSUPPORTED;   // prefill is built without outlier channels
   int max_len = 0;
   for (int b = 0; b < c.batch; ++b) {
     if (seq_len[b] < n_q) return KVQ_ERR_INVALID;
@@ -563,6 +607,9 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   ca.part_acc = da.part_acc;
   ca.out = out;
   ca.Hq = n_q * n_q_heads;   // rows [B][n_q][Hq] are combined like heads
+  ca.part_out = nullptr;
+  ca.v_out_idx = nullptr;
+  ca.G = 1;
   ca.S = ps.S;
   ca.rotate = c.rotate_v;
   ca.cd = cd;
@@ -608,6 +655,10 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache, int32_t
   a.nq = n - (c.tail_len > 0 ? std::min(n, (int)c.tail_len) : 0);
   a.cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
   a.has_signs = sign_mask(c, a.signs);
+  a.outl = c.outliers;
+  a.out_codes = static_cast<const uint8_t*>(which == 0 ? cache->k_out_codes : cache->v_out_codes);
+  a.out_scales = static_cast<const uint16_t*>(which == 0 ? cache->k_out_scales : cache->v_out_scales);
+  a.out_idx = c.outliers ? cache->outlier_idx + (size_t)which * c.n_kv_heads * c.outliers : nullptr;
   return hip_status(launch_dequant(c.head_dim, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -102,6 +102,19 @@
  *    x_hat = u * s + m
  * The code planes store u where the absmax formats store code + 2^(bits-1),
  * so their layouts are the same.
+ * Outlier channels (kvq_config.outliers = 32; the velog.io post, section
+ * "application and background", names the mixed precision that keeps only
+ * the outlier channels at 8 bits): each K and V head vector x splits before
+ * rotation into x_O = x[O] (the 32 listed channels, in list order) and the
+ * rest x_R = x with those channels zeroed.  x_R is rotated and stored by the
+ * rules above; x_O stays in the original space as one 8-bit absmax block
+ * (code = clamp(rint(x_O * r)), one fp16 scale).  Planes per (b, g), tiled
+ * by 64 positions like the others: K outlier codes [cap][32] two's-
+ * complement bytes; V outlier codes in element-major tiles of the V layout
+ * at 8 bits for a 32-element head (item ((t/32)*64 + 16*((t%32)/8) +
+ * o%16)*2 + o/16, byte t%8, u = code + 128); one fp16 scale per position
+ * in each scale plane.  Attention splits exactly: q.x = (R q).y_R + q[O].x_O,
+ * and the output is R^T (sum p y_V) plus sum p x_V,O added at V's channels.
  * The rotation is y = fp32(1/sqrt(d)) * FWHT(x) with the float32 butterfly
  * stages applied in the order h = 1, 2, 4, ..., d/2.  head_dim 192, a
  * multiple of 64 that is not a power of two (the velog.io post's rule turns
@@ -141,6 +154,8 @@ typedef enum kvq_dtype {
 typedef enum kvq_plane {
   KVQ_K_CODES = 0, KVQ_K_SCALES = 1, KVQ_V_CODES = 2,
   KVQ_V_SCALES = 3, KVQ_K_TAIL = 4, KVQ_V_TAIL = 5,
+  /* outlier channels (kvq_config.outliers > 0) */
+  KVQ_K_OUT_CODES = 6, KVQ_K_OUT_SCALES = 7, KVQ_V_OUT_CODES = 8, KVQ_V_OUT_SCALES = 9,
   KVQ_PLANE_RANGE_MIN = -0x7FFFFFFF - 1, KVQ_PLANE_RANGE_MAX = 0x7FFFFFFF
 } kvq_plane;
 
@@ -175,6 +190,10 @@ typedef struct kvq_config {
                         * owns max_ctx rounded up to 64 positions; > 0: the
                         * code and scale planes are a pool of this many pages
                         * of 64 positions, mapped by kvq_cache.page_table */
+  int32_t outliers;    /* 0, or 32: K and V each keep 32 caller-chosen
+                        * outlier channels per KV head at 8 bits in the
+                        * original space (see "Outlier channels" above);
+                        * needs tail_len 0, head_dim 128 and absmax blocks */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -194,12 +213,22 @@ typedef struct kvq_cache {
    * positions are unspecified).  Entries past a sequence's last tile are
    * never read. */
   const int32_t* page_table;
+  /* Outlier channels only (ignored when outliers == 0): the four outlier
+   * planes (kvq_plane_bytes of KVQ_K_OUT_CODES .. KVQ_V_OUT_SCALES) and the
+   * channel lists, device int32 [2][n_kv_heads][32] (K's lists, then V's),
+   * each list 32 distinct channels in [0, head_dim), 4-byte aligned, owned
+   * by the caller and fixed for the cache's life. */
+  void* k_out_codes;
+  void* k_out_scales;
+  void* v_out_codes;
+  void* v_out_scales;
+  const int32_t* outlier_idx;
 } kvq_cache;
 
 /* Defaults: 4-bit K and V, no tail, rotation on iff head_dim >= 64 and
  * head_dim % 64 == 0 (velog.io post, section "application and background"),
  * sign_seed 0, absmax blocks (k_min = v_min = 0), contiguous planes
- * (page_pool = 0). */
+ * (page_pool = 0), no outlier channels (outliers = 0). */
 kvq_config kvq_config_default(int32_t batch, int32_t n_kv_heads,
                               int32_t head_dim, int32_t max_ctx);
 
@@ -344,6 +373,9 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache,
  * for quantized positions, the stored bf16 value for tail positions.
  * space 0 returns the rotated values; space 1 rotates them back (the same
  * float32 transform as the append, since the matrix is its own inverse).
+ * With outlier channels, space 0 returns the rotated rest y_R and space 1
+ * the reconstruction: y_R rotated back, plus each outlier's dequantized
+ * value added at its channel (one float32 add).
  * seq_len is the host length array; 0 <= t0 <= t1 <= seq_len[b]. */
 kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache,
                           int32_t which, int32_t b, int32_t t0, int32_t t1,

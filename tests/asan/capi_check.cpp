@@ -23,7 +23,7 @@ static int failures = 0;
 static void* fake(uintptr_t a = 0x10000) { return reinterpret_cast<void*>(a); }
 
 static kvq_cache cache_of(uintptr_t codes = 0x10000, uintptr_t tail = 0x10000) {
-  kvq_cache c;
+  kvq_cache c{};
   c.k_codes = fake(codes);
   c.k_scales = fake();
   c.v_codes = fake();
@@ -127,6 +127,32 @@ int main() {
   nopt.page_table = nullptr;
   CHECK(kvq_decode_attention(&paged, &nopt, fake(), KVQ_BF16, 8, 0.1f, l_ok, out, fake(), 1 << 30, nullptr) ==
         KVQ_ERR_INVALID);
+  // outlier channels: 32 per plane and KV head, no tail, head_dim 128,
+  // absmax blocks; the lists and the four planes must be given
+  kvq_config oc = kvq_config_default(2, 4, 128, 1000);
+  oc.outliers = 32;
+  CHECK(kvq_config_check(&oc) == KVQ_OK);
+  CHECK(kvq_plane_bytes(&oc, KVQ_K_OUT_CODES) == (size_t)2 * 4 * 1024 * 32);
+  CHECK(kvq_plane_bytes(&oc, KVQ_V_OUT_SCALES) == (size_t)2 * 4 * 1024 * 2);
+  kvq_config oc_bad = oc;
+  oc_bad.outliers = 16;
+  CHECK(kvq_config_check(&oc_bad) == KVQ_ERR_INVALID);
+  oc_bad = oc;
+  oc_bad.tail_len = 8;
+  CHECK(kvq_config_check(&oc_bad) == KVQ_ERR_UNSUPPORTED);
+  kvq_cache och = cache_of(0x10000, 0);
+  CHECK(kvq_decode_attention(&oc, &och, fake(), KVQ_BF16, 8, 0.1f, l_ok, out, fake(), 1 << 30, nullptr) ==
+        KVQ_ERR_INVALID);   // no outlier planes
+  och.k_out_codes = fake();
+  och.k_out_scales = fake();
+  och.v_out_codes = fake();
+  och.v_out_scales = fake();
+  och.outlier_idx = reinterpret_cast<const int32_t*>(0x10002);
+  CHECK(kvq_decode_attention(&oc, &och, fake(), KVQ_BF16, 8, 0.1f, l_ok, out, fake(), 1 << 30, nullptr) ==
+        KVQ_ERR_ALIGN);
+  och.outlier_idx = reinterpret_cast<const int32_t*>(0x10000);
+  CHECK(kvq_prefill_attention(&oc, &och, fake(), KVQ_BF16, 8, 1, 0.1f, l_ok, out, fake(), 1 << 30, nullptr) ==
+        KVQ_ERR_UNSUPPORTED);
   for (int s = -6; s <= 0; ++s) CHECK(kvq_status_str((kvq_status)s) != nullptr);
   CHECK(kvq_status_str((kvq_status)-99) != nullptr);
   kvq_profile_decode_events(nullptr, nullptr);

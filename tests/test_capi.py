@@ -281,21 +281,82 @@ def test_plane_bytes_scale_and_min(d):
 
 
 def test_config_layout_and_sign_seed():
-    # thirteen 32-bit fields: sign_seed, then k_min, v_min, page_pool last;
-    # all 0 by default (plain Sylvester matrix, absmax blocks, contiguous)
-    assert ctypes.sizeof(_capi.KvqConfig) == 52
+    # fourteen 32-bit fields: sign_seed, then k_min, v_min, page_pool,
+    # outliers last; all 0 by default (plain Sylvester matrix, absmax blocks,
+    # contiguous, no outlier channels)
+    assert ctypes.sizeof(_capi.KvqConfig) == 56
     assert _capi.KvqConfig.sign_seed.offset == 36 and _capi.KvqConfig.v_min.offset == 44
-    assert _capi.KvqConfig.page_pool.offset == 48
+    assert _capi.KvqConfig.page_pool.offset == 48 and _capi.KvqConfig.outliers.offset == 52
     c = kvq.kvq_config_default(1, 1, 128, 64)
     assert c.sign_seed == 0 and c.k_min == 0 and c.v_min == 0 and c.page_pool == 0
+    assert c.outliers == 0
     c2 = kvq.kvq_config(1, 1, 128, 64, sign_seed=0xFFFFFFFF)
     assert c2.sign_seed == 0xFFFFFFFF
 
 
 def test_cache_struct_layout():
-    # six plane pointers, then the page table
-    assert ctypes.sizeof(_capi.KvqCache) == 7 * 8
+    # six plane pointers, the page table, four outlier planes, the lists
+    assert ctypes.sizeof(_capi.KvqCache) == 12 * 8
     assert _capi.KvqCache.page_table.offset == 48
+    assert _capi.KvqCache.k_out_codes.offset == 56 and _capi.KvqCache.outlier_idx.offset == 88
+
+
+@pytest.mark.parametrize("kb,vb", ((4, 4), (8, 4), (5, 6), (8, 8)))
+def test_outlier_config_and_planes(kb, vb):
+    # 32 channels per plane and KV head: K codes [tile][64][32] bytes, V
+    # codes in element-major 8-bit tiles of a 32-element head (the same
+    # size), one fp16 scale per position; the other planes keep their sizes
+    B, H, max_ctx = 3, 2, 1000
+    c = kvq.kvq_config(B, H, 128, max_ctx, kb, vb, outliers=32)
+    plain = kvq.kvq_config(B, H, 128, max_ctx, kb, vb)
+    cap = 1024
+    assert kvq.kvq_plane_bytes(c, _capi.KVQ_K_OUT_CODES) == B * H * cap * 32
+    assert kvq.kvq_plane_bytes(c, _capi.KVQ_V_OUT_CODES) == B * H * cap * 32
+    assert kvq.kvq_plane_bytes(c, _capi.KVQ_K_OUT_SCALES) == B * H * cap * 2
+    assert kvq.kvq_plane_bytes(c, _capi.KVQ_V_OUT_SCALES) == B * H * cap * 2
+    for p in (kvq.KVQ_K_CODES, kvq.KVQ_V_CODES, kvq.KVQ_K_SCALES, kvq.KVQ_V_SCALES):
+        assert kvq.kvq_plane_bytes(c, p) == kvq.kvq_plane_bytes(plain, p)
+    for p in (_capi.KVQ_K_OUT_CODES, _capi.KVQ_V_OUT_SCALES):
+        assert kvq.kvq_plane_bytes(plain, p) == 0
+    paged = kvq.kvq_config(B, H, 128, max_ctx, kb, vb, page_pool=37, outliers=32)
+    assert kvq.kvq_plane_bytes(paged, _capi.KVQ_K_OUT_CODES) == 37 * H * 64 * 32
+    assert kvq.kvq_plane_bytes(paged, _capi.KVQ_V_OUT_SCALES) == 37 * H * 64 * 2
+    # the workspace grows by the outlier channels' partial sums
+    assert kvq.kvq_decode_workspace_bytes(c, 8) > kvq.kvq_decode_workspace_bytes(plain, 8)
+
+
+def test_outlier_validation():
+    base = kvq.kvq_config_default(2, 2, 128, 100)
+    for field, val, want in (("outliers", 16, -1), ("outliers", -32, -1), ("outliers", 64, -1),
+                             ("tail_len", 8, -2), ("head_dim", 64, -2), ("k_min", 1, -2),
+                             ("v_min", 1, -2)):
+        c = kvq.kvq_config_default(2, 2, 128, 100)
+        c.outliers = 32
+        setattr(c, field, val)
+        assert kvq.kvq_config_check(c) == want, (field, val)
+    c = kvq.kvq_config(2, 2, 128, 100, outliers=32)
+    assert kvq.kvq_config_check(c) == 0 and kvq.kvq_config_check(base) == 0
+    ch = _cache(tail=0)
+    # no outlier planes or lists: refused before any launch
+    assert _append(c, ch, 1, _lens(0, 0)) == _capi.KVQ_ERR_INVALID
+    assert _decode(c, 4, _lens(1, 1), cache=ch) == _capi.KVQ_ERR_INVALID
+    for name in ("k_out_codes", "k_out_scales", "v_out_codes", "v_out_scales"):
+        setattr(ch, name, FAKE)
+    assert _decode(c, 4, _lens(1, 1), cache=ch) == _capi.KVQ_ERR_INVALID   # no lists
+    ch.outlier_idx = FAKE + 2
+    assert _decode(c, 4, _lens(1, 1), cache=ch) == _capi.KVQ_ERR_ALIGN
+    ch.v_out_codes = FAKE_MISALIGNED
+    ch.outlier_idx = FAKE
+    assert _decode(c, 4, _lens(1, 1), cache=ch) == _capi.KVQ_ERR_ALIGN
+    ch.v_out_codes = FAKE
+    # prefill is not built with outlier channels
+    assert L.kvq_prefill_attention(ctypes.byref(c), ctypes.byref(ch), FAKE, 0, 4, 1,
+                                   ctypes.c_float(0.1), _lens(1, 1), FAKE, FAKE, 1 << 40,
+                                   None) == _capi.KVQ_ERR_UNSUPPORTED
+    # n_new = 0 and an empty read-back queue nothing: accepted
+    assert _append(c, ch, 0, _lens(0, 0)) == 0
+    assert L.kvq_dequantize(ctypes.byref(c), ctypes.byref(ch), 1, 0, 0, 0, _lens(1, 1), 1, FAKE,
+                            None) == 0
 
 
 @pytest.mark.parametrize("d,kb,vb,km", [(64, 4, 4, 0), (128, 8, 4, 0), (192, 5, 6, 0),
