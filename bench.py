@@ -75,6 +75,9 @@ def cache_bytes_per_step(w, lens):
     d, T = w["d"], w["tail"]
     nb = d // 32
     scale_bytes = 2 * nb * ((2 if w.get("km") else 1) + (2 if w.get("vm") else 1))
+    if w.get("outliers"):
+        # outlier channels: 32 8-bit codes and one fp16 scale each for K and V
+        scale_bytes += 2 * (w["outliers"] + 2)
     tot = 0
     for n in lens:
         nt = min(n, T) if T > 0 else 0
@@ -88,9 +91,10 @@ def describe(w):
     # K8 V4: absmax blocks of those widths; "_1" marks scale-and-min blocks
     fk = "%d%s" % (w["k_bits"], "_1" if w.get("km") else "")
     fv = "%d%s" % (w["v_bits"], "_1" if w.get("vm") else "")
+    extra = (", %d outlier channels at 8 bits" % w["outliers"]) if w.get("outliers") else ""
     return ("%s: batch %d, %d query / %d KV heads, head_dim %d, context %d, K%s V%s, "
-            "bf16 tail %d, %s inputs" % (w["name"], w["B"], w["Hq"], w["Hkv"], w["d"], w["n"],
-                                        fk, fv, w["tail"], w["dist"]))
+            "bf16 tail %d, %s inputs%s" % (w["name"], w["B"], w["Hq"], w["Hkv"], w["d"], w["n"],
+                                          fk, fv, w["tail"], w["dist"], extra))
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -190,6 +194,8 @@ def main():
     ap.add_argument("--no-rotation-off", action="store_true",
                     help="skip the secondary run with rotation disabled")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-outliers", action="store_true",
+                    help="skip the secondary runs with and without outlier channels (no tail)")
     ap.add_argument("--paged", action="store_true",
                     help="run the main measurement on a paged cache (64-position pages in a "
                          "shuffled order) instead of the contiguous layout")
@@ -330,6 +336,26 @@ def main():
         del pg
 
 
+    if not args.no_outliers:
+        # outlier channels (32 per plane and KV head at 8 bits, the rest
+        # rotated and quantized) need a cache without a bf16 tail: the long
+        # workload with no tail, with and without them
+        res_o = {}
+        for key, extra in (("no_tail", {}), ("outliers", {"outliers": 32})):
+            wo = dict(w, tail=0, **extra)
+            r = decode_run(torch, kvq, wo, dev, args.warmup, args.steps, True, None)
+            kern = float(np.mean(r["kern_ms"]))
+            res_o[key] = {"workload": describe(wo), "us_per_step": round(r["ms_step"] * 1e3, 2),
+                          "step_gbs": round(r["bytes_step"] / (r["ms_step"] * 1e-3) / 1e9, 1),
+                          "attention_kernel_us": percentiles(r["kern_ms"]),
+                          "kernel_gbs": round(r["bytes_kern"] / (kern * 1e-3) / 1e9, 1)}
+            log("%s: step %.1f us, kernel %.1f us" % (key, r["ms_step"] * 1e3, kern * 1e3))
+            del r
+        res_o["kernel_cost_of_outliers_pct"] = round(
+            100 * (res_o["outliers"]["attention_kernel_us"]["median"]
+                   / res_o["no_tail"]["attention_kernel_us"]["median"] - 1), 2)
+        result["secondary"]["outlier_channels"] = res_o
+
     if not args.no_other_configs:
         # the other decode workloads, each with its own oracle baseline
         result["configs"] = {}
@@ -408,10 +434,12 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False, fus
         pool = B * tiles
         perm = np.random.default_rng(12345).permutation(pool).astype(np.int32)
         table = torch.from_numpy(perm.reshape(B, tiles)).to(dev)
+    outl = int(w.get("outliers", 0))
     cfg = kvq.kvq_config(B, Hkv, d, max_ctx, w["k_bits"], w["v_bits"], w["tail"],
                          rotate_k=rotate, rotate_v=rotate, k_min=w.get("km", False),
-                         v_min=w.get("vm", False), page_pool=pool)
-    cache = kvq.KVCache(cfg, dev, page_table=table)
+                         v_min=w.get("vm", False), page_pool=pool, outliers=outl)
+    idx = torch.from_numpy(workloads.outlier_lists(w)).to(dev) if outl else None
+    cache = kvq.KVCache(cfg, dev, page_table=table, outlier_idx=idx)
     if keep is not None:
         keep["k"] = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev)
         keep["v"] = torch.empty_like(keep["k"])

@@ -24,22 +24,6 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3
 
 
-def channel_lists(w, seed):
-    """[2][Hkv][32] int32: per plane and KV head, the channels the workload
-    makes large, then other channels, shuffled."""
-    Hkv, d = w["Hkv"], w["d"]
-    rng = np.random.default_rng(seed)
-    out = np.zeros((2, Hkv, 32), np.int32)
-    for pl, role in ((0, 1), (1, 2)):
-        big = workloads.outlier_scale(w, role) > 1
-        for g in range(Hkv):
-            must = [int(c) for c in np.flatnonzero(big[g])][:32]
-            rest = [int(c) for c in rng.permutation(d) if c not in must]
-            lst = np.array(must + rest[: 32 - len(must)], np.int32)
-            out[pl, g] = rng.permutation(lst)
-    return out
-
-
 class OutPair:
     """A device cache with outlier channels and the oracle's OutlierCache fed
     the same appends."""
@@ -145,7 +129,7 @@ CASES = [
 def _build(case, rotate=True, sign_seed=0, paged=False, extra=8):
     name, base, over, kb, vb, lens = case
     w = workloads.workload(base, **over)
-    lists = channel_lists(w, 11)
+    lists = workloads.outlier_lists(w)
     max_ctx = max(lens) + extra
     table, pool = None, 0
     B = len(lens)

@@ -82,6 +82,23 @@ def outlier_scale(w, role):
     return s
 
 
+def outlier_lists(w, seed=11, m=32):
+    """[2][Hkv][m] int32 channel lists for a cache with outlier channels
+    (K's, then V's): per KV head the channels outlier_scale makes large, then
+    seeded other channels, the list in a seeded order.  What a calibration
+    pass would pick for these inputs."""
+    Hkv, d = w["Hkv"], w["d"]
+    rng = np.random.default_rng((w["idx"], 7, seed))
+    out = np.zeros((2, Hkv, m), np.int32)
+    for pl, role in ((0, 1), (1, 2)):
+        big = outlier_scale(w, role) > 1
+        for g in range(Hkv):
+            must = [int(c) for c in np.flatnonzero(big[g])][:m]
+            rest = [int(c) for c in rng.permutation(d) if c not in must]
+            out[pl, g] = rng.permutation(np.array(must + rest[: m - len(must)], np.int32))
+    return out
+
+
 def amplitude(w, role):
     """Constant factor of K (role 1) or V (role 2) values: amp_k / amp_v, 1 if
     absent."""
