@@ -273,6 +273,139 @@ __global__ __launch_bounds__(256) void append_quant_kernel(AppendArgs a) {
   quant_part<D, FAST>(a, blockIdx.x, blockIdx.y, blockIdx.z >> 1, blockIdx.z & 1, vlds);
 }
 
+// Bulk quantization at head_dim 128 with absmax blocks in both planes, bf16
+// inputs and no outlier channels (the common shape of a long prompt's
+// append): the same arithmetic as quant_part, with the code widths fixed at
+// compile time and the work in tile-aligned passes.  A block takes up to
+// kBulkPasses 64-position tiles of one (sequence, KV head, plane); each pass
+// is one tile, one position per four lanes, and loads the next pass's rows
+// before its own arithmetic.  Whether a tile is stored, and which of its
+// eight-position groups are whole, is the same for every lane, so the V
+// items' masks and tile slots are scalar work.
+constexpr int kBulkPasses = 4;
+
+template <int KB, int VB>
+__global__ __launch_bounds__(256) void append_bulk_kernel(AppendArgs a) {
+  constexpr int D = 128, LPR = D / kBlock, NN = D / 16;
+  static_assert(rows_per_block(D) == kTile, "one tile per pass");
+  __shared__ __align__(16) uint8_t vlds[2][8 * D * 8];   // [pass & 1][group][e][slot]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = tid % LPR;
+  const int rho = tid / LPR;                             // position within the tile
+  const int g = blockIdx.y, b = blockIdx.z >> 1, pl = blockIdx.z & 1;
+  const AppendRange rg = append_range(a, b);
+  const int len = rg.len, q0 = rg.q0, q1 = rg.q1;
+  const int T = a.T;
+  const int Hkv = a.Hkv;
+  const int t_first = q0 / kTile + (int)blockIdx.x * kBulkPasses;
+  const int t_end = min((q1 + kTile - 1) / kTile, t_first + kBulkPasses);
+  if (q1 <= q0 || t_first >= t_end) return;             // uniform
+  const size_t unit = (size_t)b * Hkv + g;
+  const uint16_t* src = static_cast<const uint16_t*>(a.src[pl]);
+  // everything read from memory but the rows before the loop: the page
+  // table and the sign masks
+  long long slots[kBulkPasses];
+#pragma unroll
+  for (int k = 0; k < kBulkPasses; ++k) slots[k] = t_first + k < t_end ? tile_slot(a.map, b, g, t_first + k) : -1LL;
+  const bool signs = a.rotate[pl] && a.has_signs;
+  const uint32_t sgn = signs ? a.signs[j] : 0u;
+
+  // Raw bf16 words of this lane's block of position t * 64 + rho.  A row
+  // that is not an input row of this append (outside [len, len + n_new):
+  // a tail row, or past the range) reads input row 0 or n_new - 1 instead,
+  // whose values are never stored, so every load is unconditional and the
+  // next pass's loads stay in flight during this pass.
+  auto load = [&](int t, uint4 (&r)[4]) {
+    const int ip = min(max(t * kTile + rho - len, 0), a.n_new - 1);
+    const uint4* q = reinterpret_cast<const uint4*>(
+        src + ((size_t)(b * (size_t)a.n_new + ip) * Hkv + g) * D + (size_t)kBlock * j);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = q[k];
+  };
+  uint4 cur[4], nxt[4];
+  load(t_first, cur);
+#pragma unroll 1
+  for (int k = 0; k < kBulkPasses; ++k) {
+    const int t = t_first + k;
+    if (t >= t_end) break;                               // uniform
+    load(t + 1, nxt);
+    const int p = t * kTile + rho;
+    const bool active = p >= q0 && p < q1;
+    const bool from_ring = active && p < len;           // leaving the tail (T > 0)
+    long long kslot = slots[0];
+#pragma unroll
+    for (int i = 1; i < kBulkPasses; ++i) kslot = k == i ? slots[i] : kslot;
+    float x[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[q * 8 + 2 * i] = __uint_as_float(w[i] << 16);
+        x[q * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+    if (a.rotate[pl]) {
+      if (signs) {
+        // a fresh copy per pass: the 32 bit masks derived from it are not
+        // kept live across the unrolled passes
+        uint32_t sk = sgn;
+        asm volatile("" : "+v"(sk));
+        apply_signs(x, sk);
+      }
+      rotate_row_for_absmax<D>(x, lane, a.cd);
+    }
+    if (T > 0) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = bf16_round(x[e]);
+      if (from_ring) load_bf16_block(a.tail[pl] + (unit * T + p % T) * D + kBlock * j, x);
+    }
+    const long long slot = kslot;                        // the same for the whole pass
+    const bool store = slot >= 0;
+    const size_t st = store ? (size_t)slot : 0;
+    uint16_t* scales = a.scales[pl] + st * (size_t)kTile * LPR;
+    uint32_t c[32];
+    if (pl == 0) {
+      const uint32_t s = quantize_block<KB>(x, c);
+      if (store && active) {
+        store_k_row<D, KB>(c, a.codes[0] + st * (size_t)kTile * padded_row_bytes(D, KB), rho, j);
+        scales[rho * LPR + j] = (uint16_t)s;
+      }
+    } else {
+      const uint32_t s = quantize_block<VB>(x, c);
+      if (store && active) scales[rho * LPR + j] = (uint16_t)s;
+      uint8_t* buf = vlds[k & 1];
+      if (active) {
+        uint8_t* dst = buf + ((rho / 8) * D + kBlock * j) * 8 + rho % 8;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) dst[8 * e] = (uint8_t)c[e];   // offset code
+      }
+      // the buffer of pass k was last read in pass k - 2, before the
+      // barrier of pass k - 1
+      __syncthreads();
+      if (store) {
+        uint8_t* tile = a.codes[1] + st * (size_t)v_tile_bytes(D, VB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int it = tid + 256 * i;
+          const int grp = __builtin_amdgcn_readfirstlane(it / D);   // the same for a wave
+          const int idx = it % D;
+          const int e = 16 * (idx % NN) + idx / NN;
+          const int p0 = t * kTile + 8 * grp;
+          const int lo = max(q0 - p0, 0), hi = min(q1 - p0, 8);
+          if (lo >= hi) continue;
+          const uint32_t mask = (0xFFu >> (8 - hi)) & (0xFFu << lo);
+          const uint64_t u = *reinterpret_cast<const uint64_t*>(buf + (grp * D + e) * 8);
+          store_v_item<D, VB>(tile, v_item(D, 8 * grp, e), u, mask);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
   tail_part<D>(a, blockIdx.x, blockIdx.y, blockIdx.z >> 1, blockIdx.z & 1);
@@ -298,6 +431,34 @@ __global__ __launch_bounds__(64) void append_one_kernel(AppendArgs a) {
   append_one_load<D, VB>(o, blockIdx.x, blockIdx.y, blockIdx.z, a.len[blockIdx.y], true, L);
   append_one_finish<D, VB, FAST>(o, blockIdx.x, blockIdx.y, blockIdx.z, a.len[blockIdx.y], true, L, nullptr,
                                  nullptr);
+}
+
+template <int KB>
+void launch_bulk_k(const AppendArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.bits[1]) {
+    case 4: hipLaunchKernelGGL((append_bulk_kernel<KB, 4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((append_bulk_kernel<KB, 5>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((append_bulk_kernel<KB, 6>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((append_bulk_kernel<KB, 8>), grid, dim3(256), 0, s, a); break;
+  }
+}
+// Grid of append_bulk_kernel: enough blocks of kBulkPasses tiles for the
+// sequence whose quantized range spans the most tiles.
+void launch_bulk(const AppendArgs& a, int B, hipStream_t s) {
+  int tiles = 0;
+  for (int b = 0; b < B; ++b) {
+    const int len = a.len[b], n1 = len + a.n_new;
+    const int q0 = a.T > 0 ? max(0, len - a.T) : len;
+    const int q1 = a.T > 0 ? max(0, n1 - a.T) : n1;
+    if (q1 > q0) tiles = max(tiles, (q1 + kTile - 1) / kTile - q0 / kTile);
+  }
+  const dim3 grid((tiles + kBulkPasses - 1) / kBulkPasses, a.Hkv, 2 * B);
+  switch (a.bits[0]) {
+    case 4: launch_bulk_k<4>(a, grid, s); break;
+    case 5: launch_bulk_k<5>(a, grid, s); break;
+    case 6: launch_bulk_k<6>(a, grid, s); break;
+    default: launch_bulk_k<8>(a, grid, s); break;
+  }
 }
 
 template <int D>
@@ -336,7 +497,11 @@ hipError_t launch_append_d(const AppendArgs& a, int B, hipStream_t s) {
     const int q1 = a.T > 0 ? max(0, n1 - a.T) : n1;
     if (q1 > q0) quant_blocks = max(quant_blocks, (q1 - (q0 & ~7) + RPB - 1) / RPB);
   }
-  if (quant_blocks > 0) {
+  bool bulk = false;
+  if constexpr (D == 128) bulk = absmax && a.dtype == KVQ_BF16 && a.outl == 0;
+  if (quant_blocks > 0 && bulk) {
+    launch_bulk(a, B, s);
+  } else if (quant_blocks > 0) {
     const dim3 grid(quant_blocks, a.Hkv, 2 * B);
     if (absmax) hipLaunchKernelGGL((append_quant_kernel<D, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((append_quant_kernel<D, false>), grid, dim3(256), 0, s, a);
