@@ -35,7 +35,7 @@ DEVICE = [
 def units():
     """(source, object, extra flags) for every translation unit."""
     out = []
-    for name in ("append.hip", "dequant.hip", "decode_main.hip"):
+    for name in ("append.hip", "dequant.hip", "decode_main.hip", "prefill_mfma.hip"):
         out.append((os.path.join(CSRC, name), name.replace(".hip", ".o"), DEVICE))
     # K formats: (bits, scale-and-min) for q4_0 q5_0 q6_0 q8_0 q4_1 q5_1
     # (head_dim 256 also builds its paged-layout kernels as units of their own)

@@ -284,6 +284,42 @@ __device__ inline uint32_t quantize_block_min(const float (&x)[32], uint32_t (&m
   return (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, m16) << 16);
 }
 
+// Signed codes c of elements 32j..32j+31 of position p of one K tile (row
+// layout, 16-byte chunks placed by chunk_offset).
+template <int D, int BITS>
+__device__ inline void load_codes(const uint8_t* plane, int p, int j, int (&c)[32]) {
+  constexpr int RP = padded_row_bytes(D, BITS);
+  if constexpr (BITS == 8) {
+    const uint4 v0 = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, 2 * j, RP));
+    const uint4 v1 = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, 2 * j + 1, RP));
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) c[e] = (int)(int8_t)((w[e / 4] >> (8 * (e % 4))) & 0xFF);
+  } else {
+    constexpr int OFF = 1 << (BITS - 1);
+    const uint4 v = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, j, RP));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hw = 0, hw2[2] = {0u, 0u};
+    if constexpr (BITS == 5) {
+      const int byte = D / 2 + 4 * j;
+      hw = *reinterpret_cast<const uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
+    }
+    if constexpr (BITS == 6) {
+      const int byte = D / 2 + 8 * j;
+      const uint2 h = *reinterpret_cast<const uint2*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
+      hw2[0] = h.x;
+      hw2[1] = h.y;
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      int u = (int)((w[e / 8] >> (4 * (e % 8))) & 15);
+      if constexpr (BITS == 5) u |= (int)((hw >> hibit_pos(e)) & 1) << 4;
+      if constexpr (BITS == 6) u |= (int)((hw2[e / 16] >> hi2_pos(e)) & 3) << 4;
+      c[e] = u - OFF;
+    }
+  }
+}
+
 // Low bytes of a, b, c, d as one little-endian word.
 __device__ inline uint32_t gather_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);

@@ -12,40 +12,6 @@
 namespace kvq {
 namespace {
 
-template <int D, int BITS>
-__device__ inline void load_codes(const uint8_t* plane, int p, int j, int (&c)[32]) {
-  constexpr int RP = padded_row_bytes(D, BITS);
-  if constexpr (BITS == 8) {
-    const uint4 v0 = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, 2 * j, RP));
-    const uint4 v1 = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, 2 * j + 1, RP));
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int e = 0; e < 32; ++e) c[e] = (int)(int8_t)((w[e / 4] >> (8 * (e % 4))) & 0xFF);
-  } else {
-    constexpr int OFF = 1 << (BITS - 1);
-    const uint4 v = *reinterpret_cast<const uint4*>(plane + chunk_offset(p, j, RP));
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t hw = 0, hw2[2] = {0u, 0u};
-    if constexpr (BITS == 5) {
-      const int byte = D / 2 + 4 * j;
-      hw = *reinterpret_cast<const uint32_t*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
-    }
-    if constexpr (BITS == 6) {
-      const int byte = D / 2 + 8 * j;
-      const uint2 h = *reinterpret_cast<const uint2*>(plane + chunk_offset(p, byte / kChunk, RP) + byte % kChunk);
-      hw2[0] = h.x;
-      hw2[1] = h.y;
-    }
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      int u = (int)((w[e / 8] >> (4 * (e % 8))) & 15);
-      if constexpr (BITS == 5) u |= (int)((hw >> hibit_pos(e)) & 1) << 4;
-      if constexpr (BITS == 6) u |= (int)((hw2[e / 16] >> hi2_pos(e)) & 3) << 4;
-      c[e] = u - OFF;
-    }
-  }
-}
-
 // V codes of elements 32j..32j+31 of token p from the element-major tiles.
 template <int D, int BITS>
 __device__ inline void load_v_codes(const uint8_t* plane, int p, int j, int (&c)[32]) {

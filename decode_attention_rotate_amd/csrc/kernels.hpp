@@ -172,6 +172,44 @@ DecodeLauncher decode_launcher(int D, int kb, int vb, int gc, bool km, bool vm, 
 // The prefill variant of the split kernel for (D, k_bits, v_bits, km, vm, paged).
 DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm, bool paged);
 
+// ------------------------------------------------------- prefill (matrix)
+// Chunked prefill on the matrix cores at head_dim 128 with absmax blocks:
+// query rows prepared once (rotated, scaled to log2 units, split into fp16
+// hi + lo parts), then per workgroup of kPrefillRows rows of one KV head the
+// cache tiles are dequantized once into LDS and both products run as
+// 32x32x16 f16 matrix-core steps.  Partials as the split kernel's.
+constexpr int kPrefillRows = 128;
+struct PrefillArgs {
+  const uint8_t* k_codes;
+  const uint16_t* k_scales;
+  const uint8_t* v_codes;
+  const uint16_t* v_scales;
+  const uint16_t* k_tail;
+  const uint16_t* v_tail;
+  const void* q;             // [B][n_q][Hq][D] bf16 or float32, original space
+  uint16_t* q_hi;            // prepared rows [B][Hkv][rows_pad][D], fp16 bits
+  uint16_t* q_lo;
+  float* q_w;                // [B][Hkv][rows_pad]: 2^-f of each prepared row
+  float* part_ml;            // [B][n_q][Hq][S][2]
+  float* part_acc;           // [B][n_q][Hq][S][D], rotated space
+  int32_t Hkv, Hq, G, T, S, n_q, n_rb, rows_pad;
+  TileMap map;
+  int32_t q_dtype, rotate_k;
+  float cd, sm_scale;
+  int32_t has_signs;
+  uint32_t signs[8];
+  int32_t len[KVQ_MAX_BATCH];
+};
+// Whether the matrix-core prefill covers a configuration.
+constexpr bool prefill_mfma_supported(int D, int kb, int vb, bool km, bool vm) {
+  return D == 128 && !km && !vm && (kb == 4 || kb == 5 || kb == 6 || kb == 8) &&
+         (vb == 4 || vb == 5 || vb == 6 || vb == 8);
+}
+// Query preparation (grid: rows_pad / 64, Hkv, B), then the attention
+// kernel (grid: S, n_rb * Hkv, B).
+hipError_t launch_prefill_q(const PrefillArgs& a, int B, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int kb, int vb, int B, hipStream_t s);
+
 // Largest split count the host schedules (bounds the combine kernel's LDS).
 constexpr int kMaxSplitsDevice = 1024;
 

@@ -159,10 +159,14 @@ int max_splits(const kvq_config& c, int n_q_heads) {
 struct PrefillSchedule {
   int n_rb, S;
 };
+// The matrix-core prefill covers head_dim 128 with absmax blocks.
+bool prefill_on_mfma(const kvq_config& c) {
+  return prefill_mfma_supported(c.head_dim, c.k_bits, c.v_bits, c.k_min != 0, c.v_min != 0);
+}
 PrefillSchedule prefill_schedule(const kvq_config& c, int n_q_heads, int n_q, int max_len) {
   PrefillSchedule p;
   const int64_t G = n_q_heads / c.n_kv_heads;
-  const int64_t rows_per_block = 8 * split_group_waves(c.head_dim, true);
+  const int64_t rows_per_block = prefill_on_mfma(c) ? kPrefillRows : 8 * split_group_waves(c.head_dim, true);
   p.n_rb = (int)(((int64_t)n_q * G + rows_per_block - 1) / rows_per_block);
   const int64_t blocks = (int64_t)c.batch * c.n_kv_heads * p.n_rb;
   const int64_t tiles = std::max(1, (max_len + kTile - 1) / kTile);
@@ -529,12 +533,36 @@ kvq_status kvq_decode_attention_static(const kvq_config* cfg, const kvq_cache* c
   return run_decode(*cfg, cache, q, dtype, n_q_heads, sm_scale, seq_len, out, ws, plan, stream);
 }
 
+// Prefill workspace: the split partials, then (matrix-core path) the
+// prepared query rows, fp16 hi and lo parts and one factor per row.
+struct PrefillWs {
+  WsLayout parts;
+  size_t q_hi, q_lo, q_w, total;
+  int rows_pad;
+};
+PrefillWs prefill_ws(const kvq_config& c, int n_q_heads, int n_q, const PrefillSchedule& p) {
+  PrefillWs w;
+  w.parts = ws_layout(c, n_q * n_q_heads, p.S);
+  w.rows_pad = p.n_rb * kPrefillRows;
+  w.total = (w.parts.total + 255) / 256 * 256;
+  w.q_hi = w.q_lo = w.q_w = 0;
+  if (prefill_on_mfma(c)) {
+    const size_t rows = (size_t)c.batch * c.n_kv_heads * w.rows_pad;
+    const size_t half_bytes = (rows * c.head_dim * 2 + 255) / 256 * 256;
+    w.q_hi = w.total;
+    w.q_lo = w.q_hi + half_bytes;
+    w.q_w = w.q_lo + half_bytes;
+    w.total = w.q_w + rows * sizeof(float);
+  }
+  return w;
+}
+
 size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads, int32_t n_q) {
   if (check_cfg(cfg) != KVQ_OK) return 0;
   if (n_q_heads < cfg->n_kv_heads || n_q_heads % cfg->n_kv_heads != 0 || n_q < 1) return 0;
   if ((int64_t)n_q * n_q_heads > 2147483647 / 8) return 0;
   const PrefillSchedule p = prefill_schedule(*cfg, n_q_heads, n_q, cfg->max_ctx);
-  return ws_layout(*cfg, n_q * n_q_heads, p.S).total;
+  return prefill_ws(*cfg, n_q_heads, n_q, p).total;
 }
 
 kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q,
@@ -560,15 +588,68 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   }
   const PrefillSchedule ps = prefill_schedule(c, n_q_heads, n_q, max_len);
   if ((int64_t)c.n_kv_heads * ps.n_rb > 65535) return KVQ_ERR_INVALID;
-  const WsLayout wl = ws_layout(c, n_q * n_q_heads, ps.S);
-  if (workspace_bytes < wl.total) return KVQ_ERR_WORKSPACE;
-  const DecodeLauncher fn = prefill_launcher(c.head_dim, c.k_bits, c.v_bits, c.k_min != 0,
-                                             c.v_min != 0, c.page_pool > 0);
-  if (!fn) return KVQ_ERR_UNSUPPORTED;
+  const PrefillWs pw = prefill_ws(c, n_q_heads, n_q, ps);
+  const WsLayout& wl = pw.parts;
+  if (workspace_bytes < pw.total) return KVQ_ERR_WORKSPACE;
+  const bool mfma = prefill_on_mfma(c);
+  const DecodeLauncher fn = mfma ? nullptr
+                                 : prefill_launcher(c.head_dim, c.k_bits, c.v_bits, c.k_min != 0,
+                                                    c.v_min != 0, c.page_pool > 0);
+  if (!mfma && !fn) return KVQ_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const float cd = (float)(1.0 / std::sqrt((double)rot_block(c.head_dim)));
+
+  if (mfma) {
+    PrefillArgs pa;
+    std::memset(&pa, 0, sizeof(pa));
+    pa.k_codes = static_cast<const uint8_t*>(cache->k_codes);
+    pa.k_scales = static_cast<const uint16_t*>(cache->k_scales);
+    pa.v_codes = static_cast<const uint8_t*>(cache->v_codes);
+    pa.v_scales = static_cast<const uint16_t*>(cache->v_scales);
+    pa.k_tail = static_cast<const uint16_t*>(cache->k_tail);
+    pa.v_tail = static_cast<const uint16_t*>(cache->v_tail);
+    pa.q = q;
+    pa.q_dtype = dtype;
+    pa.q_hi = reinterpret_cast<uint16_t*>(ws + pw.q_hi);
+    pa.q_lo = reinterpret_cast<uint16_t*>(ws + pw.q_lo);
+    pa.q_w = reinterpret_cast<float*>(ws + pw.q_w);
+    pa.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+    pa.part_acc = reinterpret_cast<float*>(ws + wl.acc);
+    pa.Hkv = c.n_kv_heads;
+    pa.Hq = n_q_heads;
+    pa.G = n_q_heads / c.n_kv_heads;
+    pa.T = c.tail_len;
+    pa.S = ps.S;
+    pa.n_q = n_q;
+    pa.n_rb = ps.n_rb;
+    pa.rows_pad = pw.rows_pad;
+    pa.map = tile_map(c, cache);
+    pa.rotate_k = c.rotate_k;
+    pa.cd = cd;
+    pa.sm_scale = sm_scale;
+    pa.has_signs = sign_mask(c, pa.signs);
+    for (int b = 0; b < c.batch; ++b) pa.len[b] = seq_len[b];
+    if ((st = hip_status(launch_prefill_q(pa, c.batch, s))) != KVQ_OK) return st;
+    if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
+    if ((st = hip_status(launch_prefill_mfma(pa, c.k_bits, c.v_bits, c.batch, s))) != KVQ_OK) return st;
+    if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
+    CombineArgs ca;
+    ca.part_ml = pa.part_ml;
+    ca.part_acc = pa.part_acc;
+    ca.out = out;
+    ca.Hq = n_q * n_q_heads;   // rows [B][n_q][Hq] are combined like heads
+    ca.part_out = nullptr;
+    ca.v_out_idx = nullptr;
+    ca.G = 1;
+    ca.S = ps.S;
+    ca.rotate = c.rotate_v;
+    ca.cd = cd;
+    ca.has_signs = pa.has_signs;
+    for (int i = 0; i < 8; ++i) ca.signs[i] = pa.signs[i];
+    return hip_status(launch_combine(c.head_dim, ca, c.batch, s));
+  }
 
   DecodeArgs da;
   std::memset(&da, 0, sizeof(da));
