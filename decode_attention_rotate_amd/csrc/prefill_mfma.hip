@@ -292,16 +292,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) o[me][r] = 0.f;
   int fv_run = kNoScale;
 
+  // V scales of tile t into vsr, and the wave's smallest V exponent
+  // candidate into red: from the tile's raw words, after the previous
+  // tile's products (its loads have arrived by then), so the two barriers
+  // each tile has anyway publish them
   TileRaw raw;
-  if (t_begin < t_end) load_raw<KB, VB>(a, tile_slot_read(a.map, b, g, t_begin), t_begin, nq, raw);
+  auto v_scales = [&](int t) {
+    const int pl = tid >> 2, j = tid & 3;
+    const int p = t * kTile + pl;
+    int fvc = kNoScale;
+    float vs = 0.f;
+    if (p < nq) {
+      vs = fp16_bits_to_f32((uint16_t)(raw.scales >> 16));
+      if (vs > 0.f) fvc = 7 - exponent_of(vs);   // |c| < 2^7
+    } else if (p < len) {
+      const uint16_t* vr = a.v_tail + (unit * T + p % T) * PD + 32 * j;
+      float vm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) vm = fmaxf(vm, fabsf(bf16_to_f32(vr[e])));
+      if (vm > 0.f) fvc = 14 - exponent_of(vm);
+    }
+    vsr[pl * 4 + j] = vs;
+#pragma unroll
+    for (int mk = 1; mk < 64; mk <<= 1) fvc = min(fvc, __shfl_xor(fvc, mk));
+    if (lane == 0) red[wave] = fvc;
+  };
+  if (t_begin < t_end) {
+    load_raw<KB, VB>(a, tile_slot_read(a.map, b, g, t_begin), t_begin, nq, raw);
+    v_scales(t_begin);
+  }
+  __syncthreads();
   for (int t = t_begin; t < t_end; ++t) {
-    // ---- stage K' (hi, lo) and the V scales; each thread one 32-element
-    // block of one position
+    const int fv_tile = min(min(red[0], red[1]), min(red[2], red[3]));
+    const int fv_new = min(fv_run, fv_tile);
+    if (fv_run != kNoScale && fv_new < fv_run) {
+      const float f = pow2(fv_new - fv_run);   // exact power of two
+#pragma unroll
+      for (int me = 0; me < 4; ++me) o[me] *= f;
+    }
+    fv_run = fv_new;
+    const float vmul = pow2(fv_run == kNoScale ? 0 : fv_run);
+    // ---- stage K' (hi, lo); each thread one 32-element block of one
+    // position
     {
       const int pl = tid >> 2, j = tid & 3;
       const int p = t * kTile + pl;
-      int fkc = kNoScale, fvc = kNoScale;
-      float vs = 0.f;
+      int fkc = kNoScale;
       float x[32];
       if (p < nq) {
         int c[32];
@@ -310,20 +346,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (s > 0.f) fkc = 7 - exponent_of(s);   // |c| < 2^7: |x| < 2^(e+8)
 #pragma unroll
         for (int e = 0; e < 32; ++e) x[e] = (float)c[e] * s;
-        vs = fp16_bits_to_f32((uint16_t)(raw.scales >> 16));
-        if (vs > 0.f) fvc = 7 - exponent_of(vs);
       } else if (p < len) {
         const uint16_t* kr = a.k_tail + (unit * T + p % T) * PD + 32 * j;
-        const uint16_t* vr = a.v_tail + (unit * T + p % T) * PD + 32 * j;
-        float km = 0.f, vm = 0.f;
+        float km = 0.f;
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
           x[e] = bf16_to_f32(kr[e]);
           km = fmaxf(km, fabsf(x[e]));
-          vm = fmaxf(vm, fabsf(bf16_to_f32(vr[e])));
         }
         if (km > 0.f) fkc = 14 - exponent_of(km);
-        if (vm > 0.f) fvc = 14 - exponent_of(vm);
       } else {
 #pragma unroll
         for (int e = 0; e < 32; ++e) x[e] = 0.f;
@@ -347,22 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
       }
       if (j == 0) ku[pl] = pow2(-fk);
-      vsr[pl * 4 + j] = vs;
-      // the workgroup's smallest V exponent candidate
-#pragma unroll
-      for (int mk = 1; mk < 64; mk <<= 1) fvc = min(fvc, __shfl_xor(fvc, mk));
-      if (lane == 0) red[wave] = fvc;
     }
-    __syncthreads();
-    const int fv_tile = min(min(red[0], red[1]), min(red[2], red[3]));
-    const int fv_new = min(fv_run, fv_tile);
-    if (fv_run != kNoScale && fv_new < fv_run) {
-      const float f = pow2(fv_new - fv_run);   // exact power of two
-#pragma unroll
-      for (int me = 0; me < 4; ++me) o[me] *= f;
-    }
-    fv_run = fv_new;
-    const float vmul = pow2(fv_run == kNoScale ? 0 : fv_run);
     // ---- stage V'^T (hi, lo): each thread four items (eight positions of
     // one element)
 #pragma unroll
@@ -471,7 +487,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    __syncthreads();   // every wave has read this tile's LDS
+    if (t + 1 < t_end) v_scales(t + 1);
+    __syncthreads();   // every wave has read this tile's LDS and red; vsr, red are the next tile's
   }
 
   // ---- partials: row (b, i, g*G + h') in the [B][n_q][Hq] order of the output
