@@ -3,22 +3,27 @@
 One step is the decode hot path for one batch: rotate-quantize-append one new
 token per sequence (with tail graduation), then single-query decode attention
 over the whole cache, as one kvq_decode_step call (two launches: the split
-kernel, which also appends the token, and the combine).  Default workload "long": batch 8, 40 query / 8 KV
-heads, head_dim 128, 65536 cached tokens, K 8-bit / V 4-bit 32-element blocks
-with fp16 scales, newest 1024 tokens in a bf16 tail, Hadamard-128 rotation.
+kernel, which also appends the token, and the combine).  Default workload
+"long": batch 8, 40 query / 8 KV heads, head_dim 128, 65536 cached tokens,
+K 8-bit / V 4-bit 32-element blocks with fp16 scales, newest 1024 tokens in a
+bf16 tail, Hadamard-128 rotation.
 
 Prints one JSON line.  `value` is cache GB/s over the full step (algorithmic
 cache bytes read by the attention / step time, over the timed steps).
 `roofline` reports the split-K attention kernel alone, timed with HIP events
 that the library records on the call's stream around that kernel during a
 second run of as many steps (the event records stay out of the timed loop).
-`secondary` gives p10 / median / p90 of that kernel and of the one-token
-append, and the same step on a cache with rotation disabled.  `cpu_baseline`
-times the CPU oracle's decode attention on a bounded sample of (sequence, KV
-head) units of the same cache.
+`cpu_baseline` times the CPU oracle's decode attention on (sequence, KV head)
+units of the same cache, by wall time in a process pool.  Also reported:
+`configs` (the tiny, small, mid and huge decode workloads, each with an oracle
+baseline), `append` (bulk append of the mid workload), `prefill` (chunked
+prefill at 64k) and `secondary` (kernel percentiles, the step as two calls,
+rotation off, a paged cache, outlier channels).
 
   python bench.py [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
-                  [--no-append] [--no-rotation-off]
+                  [--no-append] [--no-prefill] [--no-other-configs] [--no-rotation-off]
+                  [--no-unfused] [--no-paged] [--no-outliers]
+  python bench.py --read-ceiling | --prefill-only | --append-only
 """
 
 import argparse
@@ -108,11 +113,13 @@ def _oracle_unit(args):
     from oracle.blockquant import bf16_bits_to_f32
     n, d = k.shape[0], w["d"]
     km, vm = bool(w.get("km")), bool(w.get("vm"))
+    dtype = "bf16" if k.dtype == np.uint16 else "f32"   # bf16 bit patterns or float32 values
+    qv = bf16_bits_to_f32(q) if dtype == "bf16" else q
     c = OracleCache(1, 1, d, w["k_bits"], w["v_bits"], w["tail"], n, k_min=km, v_min=vm)
-    c.append(k[None, :, None], v[None, :, None], [0], dtype="bf16")
+    c.append(k[None, :, None], v[None, :, None], [0], dtype=dtype)
     planes = c.physical()
     t0 = time.time()
-    decode_reference(planes, bf16_bits_to_f32(q)[None], [n], 1, d, w["k_bits"], w["v_bits"],
+    decode_reference(planes, qv[None], [n], 1, d, w["k_bits"], w["v_bits"],
                      w["tail"], k_min=km, v_min=vm)
     return t0, time.time()
 
@@ -146,9 +153,8 @@ def cpu_baseline(w, units, k_dev, v_dev, q_host, torch, scaled=False):
     G = w["Hq"] // w["Hkv"]
     jobs = []
     for b, g in units:
-        k = k_dev[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        v = v_dev[b, :, g].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        jobs.append((k, v, q_host[b, g * G:(g + 1) * G], w))
+        jobs.append((host_values(k_dev[b, :, g], torch), host_values(v_dev[b, :, g], torch),
+                     q_host[b, g * G:(g + 1) * G], w))
     ctx = mp.get_context("spawn")
     par = min(cores, len(jobs))
     with ctx.Pool(par) as pool:
@@ -163,7 +169,17 @@ def cpu_baseline(w, units, k_dev, v_dev, q_host, torch, scaled=False):
              if scaled or len(jobs) < total else ""))
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": par, "kind": "oracle",
             "sample": "%s; float64 attention over the oracle-built cache, %.1f s wall for the timed "
-                      "attention (%.1f s of CPU time over %d processes)" % (what, wall, busy, par)}
+                      "attention (%.1f s of CPU time over %d processes, %.3g s per unit on one core)"
+                      % (what, wall, busy, par, busy / len(jobs))}
+
+
+def host_values(t, torch):
+    """A device tensor of inputs as the oracle takes them: bf16 bit patterns
+    (uint16) or float32 values."""
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.float().cpu().numpy()
 
 
 def unit_sample(w, count, seed=0):
@@ -188,7 +204,7 @@ def main():
                     help="(sequence, KV head) units the CPU oracle times (all when >= batch * KV heads)")
     ap.add_argument("--no-append", action="store_true", help="skip the bulk append measurement")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the sub-results of the small, mid and huge decode workloads")
+                    help="skip the sub-results of the tiny, small, mid and huge decode workloads")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the secondary run with the append and the attention as two calls")
     ap.add_argument("--no-rotation-off", action="store_true",
@@ -369,7 +385,7 @@ def main():
         result["prefill"] = prefill_bench(torch, kvq, dev)
 
     if not args.no_cpu_baseline:
-        q_host = q0.view(torch.int16).cpu().numpy().view(np.uint16)
+        q_host = host_values(q0, torch)
         log("cpu baseline on %d units" % len(units))
         result["cpu_baseline"] = cpu_baseline(w, units, keep["k"], keep["v"], q_host, torch)
     print(json.dumps(result), flush=True)
@@ -378,8 +394,8 @@ def main():
 
 # Other decode workloads reported beside the main one, with the number of
 # (sequence, KV head) units their oracle baseline times (mid: 32 of 128 and
-# huge: 16 of 128 are seeded samples; small: all 8).
-OTHER_CONFIGS = (("small", 8), ("mid", 32), ("huge", 16))
+# huge: 16 of 128 are seeded samples; tiny: its one unit, small: all 8).
+OTHER_CONFIGS = (("tiny", 1), ("small", 8), ("mid", 32), ("huge", 16))
 
 
 def other_config(torch, kvq, dev, name, cpu_units, steps, warmup, with_cpu):
@@ -401,7 +417,7 @@ def other_config(torch, kvq, dev, name, cpu_units, steps, warmup, with_cpu):
     log("%s: step %.1f us, kernel %.1f us, %.0f GB/s kernel" % (name, run["ms_step"] * 1e3,
                                                               kern * 1e3, kgbs))
     if with_cpu:
-        q_host = run["q0"].view(torch.int16).cpu().numpy().view(np.uint16)
+        q_host = host_values(run["q0"], torch)
         units = unit_sample(w, cpu_units)
         log("%s: cpu baseline on %d units" % (name, len(units)))
         res["cpu_baseline"] = cpu_baseline(w, units, keep["k"], keep["v"], q_host, torch)
@@ -441,7 +457,8 @@ def decode_run(torch, kvq, w, dev, warmup, steps, rotate, keep, paged=False, fus
     idx = torch.from_numpy(workloads.outlier_lists(w)).to(dev) if outl else None
     cache = kvq.KVCache(cfg, dev, page_table=table, outlier_idx=idx)
     if keep is not None:
-        keep["k"] = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16, device=dev)
+        keep["k"] = torch.empty((B, n, Hkv, d), dtype=torch.bfloat16 if w["dtype"] == "bf16" else torch.float32,
+                                device=dev)
         keep["v"] = torch.empty_like(keep["k"])
     lens = [0] * B
     t_fill = 0.0
