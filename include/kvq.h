@@ -356,7 +356,8 @@ size_t kvq_prefill_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads,
  *            (KVQ_ERR_WORKSPACE otherwise), owned by the caller; contents
  *            need no initialisation.
  * Results are deterministic.  kvq_profile_decode_events instruments this
- * call's split kernel too.
+ * call's attention kernel too (the matrix-core kernel at head_dim 128 with
+ * absmax blocks, the split kernel's prefill variant otherwise).
  * Errors: KVQ_ERR_INVALID if n_q_heads is not a positive multiple of
  * n_kv_heads, n_q < 1, a length is below n_q, sm_scale is not finite or the
  * rows of one KV head exceed 65535 blocks of 64; KVQ_ERR_CAPACITY if a length
