@@ -244,7 +244,12 @@ size_t kvq_plane_bytes(const kvq_config* cfg, kvq_plane plane);
  * sequence; 0 for invalid arguments.  Depends only on the configuration. */
 size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t n_q_heads);
 
-/* Rotate, quantize and append n_new tokens to every sequence.
+/* Rotate, quantize and append n_new tokens to every sequence (velog.io post
+ * "fix KV cache quantization outliers", section "Hadamard rotation": K and V
+ * are rotated when they are stored; the block formats and their byte counts
+ * follow the aiwitness.kr table "Qwen 3.6 27B Q5_K_S + 64k context KLD
+ * results"; the tail follows aitrends.kr article 92204, glossary "Precision
+ * Tail").
  *  k_new, v_new: device [batch][n_new][n_kv_heads][head_dim] of `dtype`.
  *  seq_len:      host [batch], each sequence's length BEFORE the append;
  *                positions seq_len[b] .. seq_len[b]+n_new-1 are written.
@@ -370,7 +375,10 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache,
                                  void* stream);
 
 /* Read back positions [t0, t1) of sequence b from the K (which = 0) or V
- * (which = 1) cache as float32 [t1-t0][n_kv_heads][head_dim]: code * scale
+ * (which = 1) cache (velog.io post "fix KV cache quantization outliers",
+ * section "Hadamard rotation": the normalized matrix is its own inverse, so
+ * the stored values rotate back exactly in real arithmetic) as float32
+ * [t1-t0][n_kv_heads][head_dim]: code * scale
  * for quantized positions, the stored bf16 value for tail positions.
  * space 0 returns the rotated values; space 1 rotates them back (the same
  * float32 transform as the append, since the matrix is its own inverse).
