@@ -23,7 +23,8 @@ What the oracle computes, and where each step comes from:
   describe (reading R24); the functions only move whole 64-position tiles.
 * Outlier channels at 8 bits (oracle.outliers, reading R25): the mixed
   precision the velog.io post names in section "application and
-  background".  The GPU path does not build it yet.
+  background".  The GPU path builds it for 32 channels, no precision tail,
+  head_dim 128 and absmax blocks.
 
 Everything the pages leave open (Hadamard ordering, fp32 association of the
 transform, rounding of the scale, code encoding, memory layout) is a stated
