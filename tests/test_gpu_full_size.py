@@ -138,16 +138,84 @@ def test_full_size_sampled(name, units):
         planes = check_unit_attention(w, cache, cfg, out, q, b, g, n)
         check_unit_bytes(w, planes, b, g, n)
 
+    # decode steps as the benchmark runs them: one kvq_decode_step call
+    # appends the token and attends over the cache that holds it
     for s in range(1, steps + 1):
         say(name, "decode step", s)
-        kvq.kvq_rotate_quantize_append(cfg, cache, workloads.new_tokens_torch(w, 1, s, DEV, torch),
-                                       workloads.new_tokens_torch(w, 2, s, DEV, torch), lens)
-        lens = [x + 1 for x in lens]
         q = workloads.q_torch(w, s, DEV, torch)
-        kvq.kvq_decode_attention(cfg, cache, q, lens, out=out, workspace=ws)
+        kvq.kvq_decode_step(cfg, cache, workloads.new_tokens_torch(w, 1, s, DEV, torch),
+                            workloads.new_tokens_torch(w, 2, s, DEV, torch), q, lens, out=out,
+                            workspace=ws)
+        lens = [x + 1 for x in lens]
         torch.cuda.synchronize()
     for b, g in units:
         check_unit_attention(w, cache, cfg, out, q, b, g, n + steps)
+
+
+@pytest.mark.timeout(600)
+def test_outliers_full_size_sampled():
+    """The long workload without a tail and with 32 outlier channels per
+    plane and KV head, at full size: sampled windows of the rest's and the
+    outliers' codes and scales bit-exact against the oracle's split
+    quantizer, and the attention of sampled units within 1e-3 of the
+    float64 split-form reference on the device planes."""
+    from oracle.outliers import quantize_rows_outliers, decode_reference_outliers
+    w = workloads.workload("long", tail=0)
+    B, Hkv, Hq, d, n = w["B"], w["Hkv"], w["Hq"], w["d"], w["n"]
+    kb, vb = w["k_bits"], w["v_bits"]
+    lists = workloads.outlier_lists(w)
+    units = [(2, 7), (7, 1)]
+    steps = 2
+    cfg = kvq.kvq_config(B, Hkv, d, n + steps + 64, kb, vb, 0, outliers=32)
+    cache = kvq.KVCache(cfg, DEV, outlier_idx=torch.from_numpy(lists).to(DEV))
+    lens = [0] * B
+    for t0 in range(0, n, FILL):
+        t1 = min(n, t0 + FILL)
+        say("outliers fill", t0, t1)
+        kvq.kvq_rotate_quantize_append(cfg, cache, workloads.kv_torch(w, 1, t0, t1, DEV, torch),
+                                       workloads.kv_torch(w, 2, t0, t1, DEV, torch), lens)
+        lens = [x + (t1 - t0) for x in lens]
+    ws = torch.zeros(kvq.kvq_decode_workspace_bytes(cfg, Hq), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    for s in range(1, steps + 1):
+        say("outliers decode step", s)
+        q = workloads.q_torch(w, s, DEV, torch)
+        kvq.kvq_decode_step(cfg, cache, workloads.new_tokens_torch(w, 1, s, DEV, torch),
+                            workloads.new_tokens_torch(w, 2, s, DEV, torch), q, lens, out=out,
+                            workspace=ws)
+        lens = [x + 1 for x in lens]
+        torch.cuda.synchronize()
+    cap = (cfg.max_ctx + 63) // 64 * 64
+    G = Hq // Hkv
+    for b, g in units:
+        planes = unit_planes(cache, cfg, b, g)
+        for p in ("k", "v"):
+            planes[p + "_out_codes"] = cache[p + "_out_codes"].view(B, Hkv, -1)[b, g].cpu().numpy()[None, None]
+            planes[p + "_out_scales"] = (cache[p + "_out_scales"].view(B, Hkv, -1)[b, g].cpu().numpy()
+                                         .view(np.uint16).reshape(1, 1, cap))
+        # bytes of sampled windows of the fill
+        for role, p, bits, pl in ((1, "k", kb, 0), (2, "v", vb, 1)):
+            for t0 in (0, (n // 2) // 64 * 64, n - 64):
+                x = host_values(workloads.kv_torch(w, role, t0, t0 + 64, DEV, torch)[b, :, g])
+                parts = quantize_rows_outliers(x, lists[pl, g], bits)
+                got = window_codes(planes, p, d, bits, t0, t0 + 64)
+                assert np.array_equal(got, parts["rest_codes"]), (p, b, g, t0)
+                assert np.array_equal(planes[p + "_scales"][0, 0, t0:t0 + 64], parts["rest_scales"]), (p, b, g, t0)
+                assert np.array_equal(planes[p + "_out_scales"][0, 0, t0:t0 + 64], parts["out_scales"][:, 0]), \
+                    (p, b, g, t0, "outlier scales")
+                if p == "k":
+                    oc = planes["k_out_codes"][0, 0].view(np.int8).reshape(-1, 32)[t0:t0 + 64]
+                else:
+                    from oracle.blockquant import vtiles_to_codes
+                    oc = vtiles_to_codes(planes["v_out_codes"][0, 0], t0 + 64, 32, 8)[t0:t0 + 64]
+                assert np.array_equal(oc, parts["out_codes"]), (p, b, g, t0, "outlier codes")
+        qv = host_values(q[b, g * G:(g + 1) * G])[None]
+        ref = decode_reference_outliers(planes, qv, [n + steps], 1, d, kb, vb, lists[0, g:g + 1],
+                                        lists[1, g:g + 1])
+        got = out[b, g * G:(g + 1) * G].cpu().numpy()
+        err = np.linalg.norm(got - ref[0], axis=-1) / np.linalg.norm(ref[0], axis=-1)
+        say("outliers unit", (b, g), "worst rel L2 %.3e" % err.max())
+        assert err.max() <= TOL, (b, g, err)
 
 
 @pytest.mark.timeout(600)
