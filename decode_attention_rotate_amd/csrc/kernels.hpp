@@ -175,10 +175,11 @@ DecodeLauncher prefill_launcher(int D, int kb, int vb, bool km, bool vm, bool pa
 // ------------------------------------------------------- prefill (matrix)
 // Chunked prefill on the matrix cores at head_dim 128 with absmax blocks:
 // query rows prepared once (rotated, scaled to log2 units, split into fp16
-// hi + lo parts), then per workgroup of kPrefillRows rows of one KV head the
-// cache tiles are dequantized once into LDS and both products run as
-// 32x32x16 f16 matrix-core steps.  Partials as the split kernel's.
-constexpr int kPrefillRows = 128;
+// hi + lo parts), then per workgroup of kPrefillRows rows of one KV head
+// (eight waves) the cache tiles are dequantized once into double-buffered
+// LDS and both products run as 32x32x16 f16 matrix-core steps.  Partials as
+// the split kernel's.
+constexpr int kPrefillRows = 256;
 struct PrefillArgs {
   const uint8_t* k_codes;
   const uint16_t* k_scales;
@@ -207,7 +208,7 @@ constexpr bool prefill_mfma_supported(int D, int kb, int vb, bool km, bool vm) {
 }
 // Query preparation (grid: rows_pad / 64, Hkv, B), then the attention
 // kernel (grid: S, n_rb * Hkv, B).
-hipError_t launch_prefill_q(const PrefillArgs& a, int B, hipStream_t s);
+hipError_t launch_prefill_q(const PrefillArgs& a, int kb, int B, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int kb, int vb, int B, hipStream_t s);
 
 // Largest split count the host schedules (bounds the combine kernel's LDS).

@@ -631,7 +631,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
     pa.sm_scale = sm_scale;
     pa.has_signs = sign_mask(c, pa.signs);
     for (int b = 0; b < c.batch; ++b) pa.len[b] = seq_len[b];
-    if ((st = hip_status(launch_prefill_q(pa, c.batch, s))) != KVQ_OK) return st;
+    if ((st = hip_status(launch_prefill_q(pa, c.k_bits, c.batch, s))) != KVQ_OK) return st;
     if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
     if ((st = hip_status(launch_prefill_mfma(pa, c.k_bits, c.v_bits, c.batch, s))) != KVQ_OK) return st;
     if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
