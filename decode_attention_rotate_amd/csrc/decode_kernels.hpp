@@ -1344,10 +1344,15 @@ void decode_split_kernel(DecodeArgs a) {
 
 template <int D, int KB, int VB, int G, bool PF = false, bool KM = false, bool VM = false,
           int PGM = kPageAny, bool OUT = false>
-hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+hipError_t launch_decode_split(const DecodeArgs& a, dim3 grid, hipStream_t s, hipEvent_t t0,
+                               hipEvent_t t1) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM, PGM, OUT>), grid,
-                     dim3(64 * split_group_waves(D, KM || VM || PF)), 0, s, a);
+  const dim3 block(64 * split_group_waves(D, KM || VM || PF));
+  if (t0 || t1)
+    hipExtLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM, PGM, OUT>), grid, block, 0, s,
+                          t0, t1, 0, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, VB, G, PF, KM, VM, PGM, OUT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

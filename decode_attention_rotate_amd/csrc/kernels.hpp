@@ -2,6 +2,7 @@
 // units: argument blocks passed by value to the kernels, and launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -158,7 +159,9 @@ struct DecodeArgs {
   float* part_out;
   int32_t len[KVQ_MAX_BATCH];
 };
-using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t);
+// t0, t1: when non-null, events that take the kernel's own start and end
+// times (the instrumentation of kvq_profile_decode_events).
+using DecodeLauncher = hipError_t (*)(const DecodeArgs&, dim3, hipStream_t, hipEvent_t t0, hipEvent_t t1);
 // Page modes of the split kernel: tiles found at run time in contiguous or
 // paged planes (kPageAny), or fixed at compile time.  head_dim 256 builds
 // kPageFlat and kPagePaged: its two-tile pipeline fills the register file,
@@ -209,7 +212,8 @@ constexpr bool prefill_mfma_supported(int D, int kb, int vb, bool km, bool vm) {
 // Query preparation (grid: rows_pad / 64, Hkv, B), then the attention
 // kernel (grid: S, n_rb * Hkv, B).
 hipError_t launch_prefill_q(const PrefillArgs& a, int kb, int B, hipStream_t s);
-hipError_t launch_prefill_mfma(const PrefillArgs& a, int kb, int vb, int B, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int kb, int vb, int B, hipStream_t s,
+                               hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Largest split count the host schedules (bounds the combine kernel's LDS).
 constexpr int kMaxSplitsDevice = 1024;

@@ -429,9 +429,7 @@ kvq_status run_decode(const kvq_config& c, const kvq_cache* cache, const void* q
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
   const dim3 grid(sc.S / split_group_waves(c.head_dim, c.k_min || c.v_min), c.n_kv_heads * sc.nchunk,
                   c.batch);
-  if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
-  if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
-  if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
+  if ((st = hip_status(fn(da, grid, s, g_ev_before, g_ev_after))) != KVQ_OK) return st;
 
   CombineArgs ca;
   ca.part_ml = da.part_ml;
@@ -632,9 +630,9 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
     pa.has_signs = sign_mask(c, pa.signs);
     for (int b = 0; b < c.batch; ++b) pa.len[b] = seq_len[b];
     if ((st = hip_status(launch_prefill_q(pa, c.k_bits, c.batch, s))) != KVQ_OK) return st;
-    if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
-    if ((st = hip_status(launch_prefill_mfma(pa, c.k_bits, c.v_bits, c.batch, s))) != KVQ_OK) return st;
-    if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
+    if ((st = hip_status(launch_prefill_mfma(pa, c.k_bits, c.v_bits, c.batch, s, g_ev_before, g_ev_after))) !=
+        KVQ_OK)
+      return st;
     CombineArgs ca;
     ca.part_ml = pa.part_ml;
     ca.part_acc = pa.part_acc;
@@ -679,9 +677,7 @@ kvq_status kvq_prefill_attention(const kvq_config* cfg, const kvq_cache* cache, 
   da.n_rb = ps.n_rb;
   for (int b = 0; b < c.batch; ++b) da.len[b] = seq_len[b];
   const dim3 grid(ps.S, c.n_kv_heads * ps.n_rb, c.batch);
-  if (g_ev_before && hipEventRecord(g_ev_before, s) != hipSuccess) return KVQ_ERR_HIP;
-  if ((st = hip_status(fn(da, grid, s))) != KVQ_OK) return st;
-  if (g_ev_after && hipEventRecord(g_ev_after, s) != hipSuccess) return KVQ_ERR_HIP;
+  if ((st = hip_status(fn(da, grid, s, g_ev_before, g_ev_after))) != KVQ_OK) return st;
 
   CombineArgs ca;
   ca.part_ml = da.part_ml;

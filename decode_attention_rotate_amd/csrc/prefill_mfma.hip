@@ -716,24 +716,33 @@ hipError_t launch_prefill_q(const PrefillArgs& a, int kb, int B, hipStream_t s) 
   return hipGetLastError();
 }
 
+template <int KB, int VB>
+void launch_prefill_kv(const PrefillArgs& a, dim3 grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (t0 || t1)
+    hipExtLaunchKernelGGL((prefill_mfma_kernel<KB, VB>), grid, dim3(kThreads), 0, s, t0, t1, 0, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<KB, VB>), grid, dim3(kThreads), 0, s, a);
+}
+
 template <int KB>
-void launch_prefill_v(const PrefillArgs& a, int vb, dim3 grid, hipStream_t s) {
+void launch_prefill_v(const PrefillArgs& a, int vb, dim3 grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   switch (vb) {
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<KB, 4>), grid, dim3(kThreads), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((prefill_mfma_kernel<KB, 5>), grid, dim3(kThreads), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((prefill_mfma_kernel<KB, 6>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((prefill_mfma_kernel<KB, 8>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: launch_prefill_kv<KB, 4>(a, grid, s, t0, t1); break;
+    case 5: launch_prefill_kv<KB, 5>(a, grid, s, t0, t1); break;
+    case 6: launch_prefill_kv<KB, 6>(a, grid, s, t0, t1); break;
+    default: launch_prefill_kv<KB, 8>(a, grid, s, t0, t1); break;
   }
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, int kb, int vb, int B, hipStream_t s) {
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int kb, int vb, int B, hipStream_t s,
+                               hipEvent_t t0, hipEvent_t t1) {
   (void)hipGetLastError();
   const dim3 grid(a.S, a.n_rb * a.Hkv, B);
   switch (kb) {
-    case 4: launch_prefill_v<4>(a, vb, grid, s); break;
-    case 5: launch_prefill_v<5>(a, vb, grid, s); break;
-    case 6: launch_prefill_v<6>(a, vb, grid, s); break;
-    default: launch_prefill_v<8>(a, vb, grid, s); break;
+    case 4: launch_prefill_v<4>(a, vb, grid, s, t0, t1); break;
+    case 5: launch_prefill_v<5>(a, vb, grid, s, t0, t1); break;
+    case 6: launch_prefill_v<6>(a, vb, grid, s, t0, t1); break;
+    default: launch_prefill_v<8>(a, vb, grid, s, t0, t1); break;
   }
   return hipGetLastError();
 }

@@ -395,10 +395,11 @@ kvq_status kvq_dequantize(const kvq_config* cfg, const kvq_cache* cache,
 const char* kvq_status_str(kvq_status status);
 
 /* Instrumentation: when both are non-NULL, later kvq_decode_attention calls
- * on this host thread record `before` immediately before and `after`
- * immediately after the split-K attention kernel on the call's stream, so
- * that kernel can be timed on its own.  Both are hipEvent_t passed as void*;
- * the caller owns them.  NULL, NULL switches recording off. */
+ * on this host thread launch the split-K attention kernel with `before` and
+ * `after` bound to it (hipExtLaunchKernel), so they take that kernel's own
+ * start and end times on the call's stream.  Both are hipEvent_t created
+ * with timing, passed as void*; the caller owns them.  NULL, NULL switches
+ * this off. */
 void kvq_profile_decode_events(void* before, void* after);
 
 #ifdef __cplusplus
