@@ -528,6 +528,9 @@ __device__ inline void tile_products(const PrefillLds& sm, int bf, int t, int n,
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
     const _Float16* kh = khi + (32 * mt + n) * KROW + 8 * h;
     const _Float16* kl = klo + (32 * mt + n) * KROW + 8 * h;
+    // let the scheduler interleave the operand reads with the products, so
+    // later steps' LDS reads are in flight during earlier steps' products
+    __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const half8 ah = *reinterpret_cast<const half8*>(kh + 16 * ks);
@@ -583,6 +586,7 @@ __device__ inline void tile_products(const PrefillLds& sm, int bf, int t, int n,
     }
     // K order of slot j of half h: 16 s' + 8 (j/4) + 4 h + j%4, the
     // accumulator rows of the scores
+    __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int me = 0; me < 4; ++me) {
       const _Float16* vh = vth + (32 * me + n) * VROW + 32 * mt + 4 * h;
