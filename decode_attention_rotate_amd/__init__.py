@@ -90,8 +90,9 @@ def kvq_status_str(status):
 
 
 def kvq_profile_decode_events(before, after):
-    """Record two torch.cuda.Event objects around the split-K kernel of later
-    decode calls on this thread; pass None, None to stop."""
+    """Bind two torch.cuda.Event objects to the split-K (or matrix-core
+    prefill) kernel of later decode and prefill calls on this thread, so they
+    take that kernel's own start and end; pass None, None to stop."""
     if before is None or after is None:
         _capi.lib().kvq_profile_decode_events(None, None)
         return

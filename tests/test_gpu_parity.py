@@ -344,3 +344,51 @@ def test_decode_at_the_largest_batch():
     worst = max(errs.values())
     say("largest batch worst rel L2 %.3e" % worst)
     assert worst <= TOL
+
+
+def test_profiling_events_bound_to_the_kernels():
+    """kvq_profile_decode_events makes the decode split kernel and the
+    matrix-core prefill kernel launch with the two events bound to them; the
+    results stay those of the plain launch (against the oracle) and the
+    events give a positive elapsed time; switching them off restores plain
+    launches."""
+    import torch
+    import decode_attention_rotate_amd as kvq
+    w = workloads.workload("long", B=2, tail=64)
+    pair = Pair(2, 8, 128, 8, 4, 64, 2100)
+    _fill(pair, w, [2000, 700], "bf16")
+    lens = list(pair.lens)
+    q = workloads.q_numpy(w)
+    qd = to_device(q, "bf16")
+    planes = gpu_planes(pair.cache, pair.cfg)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        say("decode with profiling events")
+        kvq.kvq_profile_decode_events(e0, e1)
+        got = kvq.kvq_decode_attention(pair.cfg, pair.cache, qd, lens)
+        torch.cuda.synchronize()
+        ms = kvq.kernel_elapsed_ms(e0, e1)
+        assert np.isfinite(ms) and ms > 0, ms
+        errs = attention_errors(got.cpu().numpy().astype(np.float64), planes, to_values(q, "bf16"),
+                                lens, pair.cfg)
+        assert max(errs.values()) <= TOL, max(errs.values())
+        say("prefill with profiling events")
+        qp = workloads.prefill_q_numpy(w, 16)
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        kvq.kvq_profile_decode_events(e2, e3)
+        pre = kvq.kvq_prefill_attention(pair.cfg, pair.cache, to_device(qp, "bf16"), lens)
+        torch.cuda.synchronize()
+        ms = kvq.kernel_elapsed_ms(e2, e3)
+        assert np.isfinite(ms) and ms > 0, ms
+        ref = prefill_reference(planes, to_values(qp, "bf16"), lens, 8, 128, 8, 4, 64)
+        got = pre.cpu().numpy().astype(np.float64)
+        err = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+        assert err.max() <= TOL, err.max()
+    finally:
+        kvq.kvq_profile_decode_events(None, None)
+    say("decode after switching the events off")
+    got = kvq.kvq_decode_attention(pair.cfg, pair.cache, qd, lens)
+    torch.cuda.synchronize()
+    errs = attention_errors(got.cpu().numpy().astype(np.float64), planes, to_values(q, "bf16"),
+                            lens, pair.cfg)
+    assert max(errs.values()) <= TOL, max(errs.values())
