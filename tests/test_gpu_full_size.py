@@ -8,7 +8,9 @@ append one token and attend.  The oracle checks sampled outputs one by one:
 * the bf16 tail rows of those units, bit-exact;
 * the attention outputs of those units' query heads, relative L2 <= 1e-3
   against the float64 oracle evaluated on the device cache of the unit, after
-  the fill and after a decode step.
+  the fill and after a decode step;
+* the bulk append as the benchmark times it (32768 tokens per sequence in one
+  call): every code and scale of sampled units, bit-exact.
 
 Inputs come from the device generators of workloads.py; the windows the oracle
 needs are regenerated and copied to the host."""
@@ -255,3 +257,37 @@ def test_prefill_full_size_sampled():
             err = np.linalg.norm(got - ref[0, i, hl]) / np.linalg.norm(ref[0, i, hl])
             say("prefill full size row", (i, g * G + hl), "rel L2 %.3e" % err)
             assert err <= TOL, (i, g, hl, err)
+
+
+@pytest.mark.timeout(600)
+def test_bulk_append_full_size_sampled():
+    """The bulk append the benchmark times: batch 16, 8 KV heads, head_dim
+    128, K4 V4, no tail, 32768 new tokens per sequence in one call.  Every
+    code and scale of sampled (sequence, KV head) units, bit-exact against
+    the oracle quantizer on the same input values; a second call at the same
+    positions rewrites the same bytes."""
+    w = workloads.workload("mid")
+    B, Hkv, d, n = w["B"], w["Hkv"], w["d"], w["n"]
+    kb, vb = w["k_bits"], w["v_bits"]
+    cfg = kvq.kvq_config(B, Hkv, d, n, kb, vb, 0)
+    cache = kvq.KVCache(cfg, DEV)
+    k = workloads.kv_torch(w, 1, 0, n, DEV, torch)
+    v = workloads.kv_torch(w, 2, 0, n, DEV, torch)
+    say("bulk append", B, n)
+    kvq.kvq_rotate_quantize_append(cfg, cache, k, v, [0] * B)
+    torch.cuda.synchronize()
+    first = {p: cache[p].clone() for p in ("k_codes", "k_scales", "v_codes", "v_scales")}
+    say("bulk append again at the same positions")
+    kvq.kvq_rotate_quantize_append(cfg, cache, k, v, [0] * B)
+    torch.cuda.synchronize()
+    for p, t in first.items():
+        assert torch.equal(cache[p], t), p
+    for b, g in ((0, 0), (9, 5), (15, 7)):
+        planes = unit_planes(cache, cfg, b, g)
+        for src, p, bits in ((k, "k", kb), (v, "v", vb)):
+            say("unit", (b, g), p)
+            x = host_values(src[b, :, g])
+            codes, scales = quantize_blocks(rotate_f32(x), bits)
+            got = window_codes(planes, p, d, bits, 0, n)
+            assert np.array_equal(got, codes), (p, b, g)
+            assert np.array_equal(planes[p + "_scales"][0, 0, :n], scales), (p, b, g)
