@@ -574,7 +574,8 @@ def read_ceiling(torch, kvq, dev, reps=10):
       and 512 B per scale plane per tile), over splits per unit, tiles of
       loads in flight per wave, non-temporal loads, and contiguous ranges
       per workgroup against chunks of 8 tiles dealt round-robin.
-    Each configuration runs `reps` times after one warm-up; medians by HIP
+    Each configuration runs `reps` times after one warm-up (the sweep after
+    SETTLE_S seconds of the first stream configuration); medians by HIP
     events on the call's stream."""
     from decode_attention_rotate_amd import _capi
     import ctypes
@@ -597,6 +598,10 @@ def read_ceiling(torch, kvq, dev, reps=10):
     nbytes = cache_bytes // 4096 * 4096
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     stream_rows = []
+    # clock settling: the first configuration, repeated
+    sink0 = torch.empty(C.kvq_ceiling_sink_words(512, 1), dtype=torch.int32, device=dev)
+    settle(torch, lambda: C.kvq_ceiling_stream(buf.data_ptr(), nbytes, 512, 4, 1, sink0.data_ptr(), stream))
+    del sink0
     for blocks in (512, 1024, 2048, 4096, 8192):
         sink = torch.empty(C.kvq_ceiling_sink_words(blocks, 1), dtype=torch.int32, device=dev)
         for unroll in (4, 8, 16):
