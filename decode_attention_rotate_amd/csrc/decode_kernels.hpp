@@ -309,8 +309,16 @@ void decode_split_kernel(DecodeArgs a) {
   // prefill wave holds more state; contiguous planes only, a paged wave also
   // carries its page lookups and then spilled inside the loop).  The
   // one-wave d = 192 variants measured no faster with two.
+  // The query as 24-bit fixed point (three bytes: two in the rows of the
+  // Q.K product, the residual byte in a second product), in decode as in
+  // prefill: with heavy-tailed data the scores grow large enough that the
+  // 2^-16 relative step of a 16-bit query moved outputs by more than 1e-3
+  // (measured up to 1.2e-3 on the GPU and 2.2e-3 in a CPU emulation at head
+  // dims 64 to 256), against 1e-5 with 24 bits.  Its registers are those a
+  // second tile ahead would take at one wave per SIMD.
+  constexpr bool kQ24 = true;
   constexpr int kAhead =
-      split_waves_per_simd(D, KM || VM || PF) == 1 && D == 256 && !PF && !KM && !VM &&
+      !kQ24 && split_waves_per_simd(D, KM || VM || PF) == 1 && D == 256 && !PF && !KM && !VM &&
               PGM != kPagePaged && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
@@ -729,17 +737,17 @@ void decode_split_kernel(DecodeArgs a) {
   if (PF ? wq0 < wq1 : (int)blockIdx.x < ctq) {
     constexpr int KSE = KM ? 2 * NB : NB;   // 16-bit scale entries per token
     constexpr int VSE = VM ? 2 * NB : NB;
-    // A operand of Q.K: the rotated query in 16-bit fixed point (step
-    // amax / 32639 per head), high bytes in even rows, low bytes in odd rows;
+    // A operand of Q.K: the rotated query in fixed point (step amax / 32639
+    // per head), high bytes in even rows, low bytes in odd rows;
     // 4/5-bit codes widen to bytes in the order 0,2,4,6,1,3,5,7 of each group
     // of 8, so the query bytes follow that order.  Offset-binary codes need a
     // per-block correction -offset * sum(q_int), which seeds the low-byte rows
     // of the integer accumulators: cq[j] = {0, corr_hA, 0, corr_hB}.
-    // Prefill extends the query to 24 bits: a second product per block takes
+    // The query extends to 24 bits (kQ24): a second product per block takes
     // the residual byte rint(256 * (q / step - q_int)) in the odd rows (so its
-    // sums land in the same lanes), with its own offset correction.  Rows
-    // whose output nearly cancels need those bits on heavy-tailed data.
-    constexpr bool kQX = PF;
+    // sums land in the same lanes), with its own offset correction (seeded,
+    // or two integers per block where the main correction is).
+    constexpr bool kQX = kQ24;
     constexpr bool kOffset = KB != 8 && !KM;   // offset-binary codes
     long qop[NB];
     long qres[kQX ? NB : 1];
@@ -751,10 +759,11 @@ void decode_split_kernel(DecodeArgs a) {
     // head_dim 256 keeps the correction as two integers per block, added to
     // the combined sums (exact), to free registers for issuing the two token
     // halves' products together
-    constexpr bool kCorrInt = kOffset && D >= 192 && !kQX;
+    constexpr bool kCorrInt = kOffset && D >= 192;
     i4_t cq[kOffset && !kCorrInt ? NB : 1];
     int ciA[kCorrInt ? NB : 1], ciB[kCorrInt ? NB : 1];
-    i4_t cq2[kQX && kOffset ? NB : 1];
+    int ci2A[kCorrInt && kQX ? NB : 1], ci2B[kCorrInt && kQX ? NB : 1];
+    i4_t cq2[kQX && kOffset && !kCorrInt ? NB : 1];
     // K minima: sum of the fixed-point query over each block, heads hA, hB
     float bsA[KM ? NB : 1], bsB[KM ? NB : 1];
     // 5-bit K: bit 4 of the codes of this lane's group r sits at bits
@@ -866,22 +875,22 @@ void decode_split_kernel(DecodeArgs a) {
     };
 
     auto compute_step = [&](const Regs& R, int s0) {
-      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements
-      // (twice that for prefill's 24-bit queries).  Up to head_dim 128 all of
+      // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements,
+      // twice that with the residual bytes of the 24-bit query.  Up to head_dim 128 all of
       // them are issued before the first result is read, so their latencies
       // overlap instead of each product waiting out the last one's; the
-      // registers allow it there except for prefill with scale-and-min blocks
-      // or 5- and 6-bit K (their high-bit words), which then spilled.
+      // registers allow it there except with scale-and-min blocks or 5- and
+      // 6-bit K (their high-bit words), which then spilled.
       float sA[2] = {0.f, 0.f}, sB[2] = {0.f, 0.f};
       constexpr bool kIssueAll = NB <= 4 && !(kQX && (KM || VM || KB == 5 || KB == 6));
       // head_dim 256: the two token halves of one block together
-      constexpr bool kIssuePair = !kIssueAll && D >= 192 && !kQX;
+      constexpr bool kIssuePair = !kIssueAll && D >= 192;
       // blocks per issued group above head_dim 128: two at 256 (one wave per
       // SIMD, registers for it once the correction is two integers), one at
       // 192 (two waves per SIMD)
       constexpr int kPairBlocks = D == 256 ? 2 : 1;
       i4_t dq[kIssueAll ? NB : kPairBlocks][2];
-      i4_t dr[kIssueAll && kQX ? NB : 1][2];
+      i4_t dr[kQX ? (kIssueAll ? NB : (kIssuePair ? kPairBlocks : 1)) : 1][2];
       if constexpr (kIssueAll) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -892,7 +901,7 @@ void decode_split_kernel(DecodeArgs a) {
                 qop[j], kop, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
             if constexpr (kQX)
               dr[j][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                  qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+                  qres[j], kop, kOffset && !kCorrInt ? cq2[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
           }
         }
       }
@@ -912,6 +921,10 @@ void decode_split_kernel(DecodeArgs a) {
                 dq[jj % kPairBlocks][mm] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
                     qop[jj], kp, kOffset && !kCorrInt ? cq[kOffset && !kCorrInt ? jj : 0] : i4_t{0, 0, 0, 0},
                     0, 0, 0);
+                if constexpr (kQX)
+                  dr[jj % kPairBlocks][mm] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                      qres[jj], kp, kOffset && !kCorrInt ? cq2[kOffset && !kCorrInt ? jj : 0] : i4_t{0, 0, 0, 0},
+                      0, 0, 0);
               }
             }
             d = dq[j % kPairBlocks][m];
@@ -934,12 +947,19 @@ void decode_split_kernel(DecodeArgs a) {
             i4_t e;
             if constexpr (kIssueAll) {
               e = dr[j][m];
+            } else if constexpr (kIssuePair) {
+              e = dr[j % kPairBlocks][m];
             } else {
               e = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                  qres[j], kop, kOffset ? cq2[kOffset ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
+                  qres[j], kop, kOffset && !kCorrInt ? cq2[kOffset && !kCorrInt ? j : 0] : i4_t{0, 0, 0, 0}, 0, 0, 0);
             }
-            fA = __builtin_fmaf((float)e[1], 0.00390625f, fA);
-            fB = __builtin_fmaf((float)e[3], 0.00390625f, fB);
+            int eA = e[1], eB = e[3];
+            if constexpr (kCorrInt) {
+              eA += ci2A[j];
+              eB += ci2B[j];
+            }
+            fA = __builtin_fmaf((float)eA, 0.00390625f, fA);
+            fB = __builtin_fmaf((float)eB, 0.00390625f, fB);
           }
           sA[m] = __builtin_fmaf(ks, fA, sA[m]);
           sB[m] = __builtin_fmaf(ks, fB, sB[m]);
@@ -1205,7 +1225,13 @@ void decode_split_kernel(DecodeArgs a) {
             rsum += __shfl_xor(rsum, 16);
             rsum += __shfl_xor(rsum, 32);
             const int corr2 = -(1 << (KB - 1)) * rsum;
-            cq2[j] = i4_t{0, okA ? __shfl(corr2, 4 * r) : 0, 0, okB ? __shfl(corr2, 4 * r + 2) : 0};
+            const int c2A = okA ? __shfl(corr2, 4 * r) : 0, c2B = okB ? __shfl(corr2, 4 * r + 2) : 0;
+            if constexpr (kCorrInt) {
+              ci2A[j] = c2A;
+              ci2B[j] = c2B;
+            } else {
+              cq2[j] = i4_t{0, c2A, 0, c2B};
+            }
           }
         }
       }
