@@ -122,6 +122,11 @@ CASES = [
     ("k4v5", "mid", dict(B=2, Hq=8), 4, 5, [130, 130]),
     ("k6v6-G1", "small", dict(B=2, Hq=8), 6, 6, [97, 33]),
     ("k5v4-G12", "long", dict(B=2, Hq=96, tail=0), 5, 4, [150, 70]),
+    # heavy-tailed (Student-t) inputs: large scores magnify the query's
+    # fixed-point step, for the outlier channels' part as for the rest
+    ("t3-k8v4", "long", dict(B=2, tail=0, dist="t3"), 8, 4, [700, 350]),
+    ("t3-k4v4-G4", "mid", dict(B=2, dist="t3"), 4, 4, [600, 257]),
+    ("t3-k8v8-G8", "small", dict(B=2, Hq=64, dist="t3"), 8, 8, [400, 400]),
     ("f32-k8v8", "small", dict(B=2, dtype="f32"), 8, 8, [100, 100]),
 ]
 
