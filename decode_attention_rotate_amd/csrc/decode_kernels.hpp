@@ -328,17 +328,19 @@ void decode_split_kernel(DecodeArgs a) {
   // LDS weight rows of 32 tokens (+ pad), 16-bit: row 8*j + h holds head h's
   // weights for V block j; the tail keeps the low bf16 parts of its weights
   // in rows LOROW + h; row ZROW stays zero (A rows 8..15 of quantized steps
-  // with absmax V).  Scale-and-min V keeps the low fp16 parts of its
-  // weights in rows LOQ + 8*j + h, as A rows 8..15 (see the weights below).
+  // with absmax V).  Scale-and-min V, and prefill rows with either V
+  // block kind (kLoW), keep the low fp16 parts of their weights in rows
+  // LOQ + 8*j + h, as A rows 8..15 (see the weights below).
+  constexpr bool kLoW = VM || PF;
   constexpr int WROW = 48;
   constexpr int LOROW = 8 * NB;
   constexpr int ZROW = 8 * NB + 8;
   constexpr int LOQ = 8 * NB + 9;
-  constexpr int OROW = LOQ + (VM ? 8 * NB : 0);   // outlier weights of the 8 heads (OUT)
+  constexpr int OROW = LOQ + (kLoW ? 8 * NB : 0);   // outlier weights of the 8 heads (OUT)
   using Regs = StepRegs<D, KB, VB, KM, VM, OUT>;
   static_assert(!OUT || (!PF && !KM && !VM), "outlier channels: decode with absmax blocks");
 
-  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9 + (VM ? 8 * NB : 0) + (OUT ? 8 : 0)) * WROW];
+  __shared__ __align__(16) uint16_t wl_all[kGroupWaves][(8 * NB + 9 + (kLoW ? 8 * NB : 0) + (OUT ? 8 : 0)) * WROW];
   __shared__ __align__(16) float alds_all[kGroupWaves][16];
   __shared__ uint32_t tile_ctr;
   // fused step: new K, new V, quantized K, quantized V values; the two
@@ -1041,15 +1043,18 @@ void decode_split_kernel(DecodeArgs a) {
           const _Float16 wB = (_Float16)fB;
           wl[(8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, wA);
           wl[(8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, wB);
-          if constexpr (VM) {
+          if constexpr (kLoW) {
             // Scale-and-min blocks: a block whose range an outlier stretches
             // puts its ordinary elements far from the block's middle level,
             // so their centred levels are large against their values, and
             // the weight's fp16 rounding, common to the whole block, would
-            // not cancel in a sum that nearly does.  The low fp16 part of
-            // each weight goes in A rows 8..15 (otherwise zero), whose
-            // accumulator rows are added to rows 0..7 at the end: about 22
-            // significant bits for no extra matrix products.
+            // not cancel in a sum that nearly does.  Prefill rows: a row whose
+            // output nearly cancels magnifies the weights' rounding (a
+            // seeded sweep found 1.6e-3 at head_dim 64 with single fp16
+            // weights).  The low fp16 part of each weight goes in A rows
+            // 8..15 (otherwise zero), whose accumulator rows are added to
+            // rows 0..7 at the end: about 22 significant bits for no extra
+            // matrix products.
             wl[(LOQ + 8 * j + hA) * WROW + t] = __builtin_bit_cast(uint16_t, (_Float16)(fA - (float)wA));
             wl[(LOQ + 8 * j + hB) * WROW + t] = __builtin_bit_cast(uint16_t, (_Float16)(fB - (float)wB));
           }
@@ -1081,7 +1086,7 @@ void decode_split_kernel(DecodeArgs a) {
       // P.V on the matrix cores: NN products of 16 rows x 32 tokens x 16 elements
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int row = col < 8 ? 8 * j + col : (VM ? LOQ + 8 * j + col - 8 : ZROW);
+        const int row = col < 8 ? 8 * j + col : (kLoW ? LOQ + 8 * j + col - 8 : ZROW);
         const h8_t wa = *reinterpret_cast<const h8_t*>(&wl[row * WROW + 8 * r]);
 #pragma unroll
         for (int i = 2 * j; i < 2 * j + 2; ++i)

@@ -53,12 +53,18 @@ def _draw_cases(n=24, seed=20261203):
 
 
 CASES = _draw_cases()
+# Case 18 of the draw from seed 4242 (head_dim 64, K5 V4, bf16 tail 16, 6 query
+# heads per KV head, bf16): its prefill rows came out 1.6e-3 off the oracle
+# while the split kernel rounded each P.V weight to one fp16 value; kept as a
+# regression case for the high + low weight parts those rows now carry.
+CASES += [dict(c, tag="seed4242-") for c in _draw_cases(n=19, seed=4242)[18:19]]
 
 
 def _case_id(c):
     fk = "%d%s" % (c["kb"], "_1" if c["km"] else "")
     fv = "%d%s" % (c["vb"], "_1" if c["vm"] else "")
-    return "%d-d%d-K%s-V%s-T%d-G%d-%s" % (c["i"], c["d"], fk, fv, c["T"], c["G"], c["dtype"])
+    return "%s%d-d%d-K%s-V%s-T%d-G%d-%s" % (c.get("tag", ""), c["i"], c["d"], fk, fv, c["T"], c["G"],
+                                            c["dtype"])
 
 
 @pytest.mark.parametrize("c", CASES, ids=[_case_id(c) for c in CASES])
