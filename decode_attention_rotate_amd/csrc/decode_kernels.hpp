@@ -101,6 +101,12 @@ __device__ inline uint32_t rotr(uint32_t x, uint32_t s) { return __builtin_amdgc
 __device__ inline float half_of(uint32_t w, int hi) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(hi ? (w >> 16) : (w & 0xFFFFu)));
 }
+// In lanes 0..31, x of lane + 32 (one lane swap between the wave's halves;
+// lanes 32..63 get their own x back)
+__device__ inline float upper_half(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[1]);
+}
 
 // Cache bytes of one 32-token step held in registers.  KM / VM: K / V use
 // scale-and-min blocks, whose scale planes hold an (s, m) fp16 pair per block.
@@ -317,8 +323,12 @@ void decode_split_kernel(DecodeArgs a) {
   // dims 64 to 256), against 1e-5 with 24 bits.  Its registers are those a
   // second tile ahead would take at one wave per SIMD.
   constexpr bool kQ24 = true;
+  // Up to 4 heads per wave (decode) the hi / lo rows fill A rows 0..7 only,
+  // and the residual bytes take the odd rows 8..15 of the same product
+  // (kFold): no second product, and its registers free for a second tile.
+  constexpr bool kFold = kQ24 && !PF && G <= 4;
   constexpr int kAhead =
-      !kQ24 && split_waves_per_simd(D, KM || VM || PF) == 1 && D == 256 && !PF && !KM && !VM &&
+      (!kQ24 || kFold) && split_waves_per_simd(D, KM || VM || PF) == 1 && D == 256 && !PF && !KM && !VM &&
               PGM != kPagePaged && (KB == 4 || (VB == 4 && KB != 6)) ? 2 : 1;
   constexpr int NB = D / kBlock;
   constexpr int NN = D / 16;
@@ -449,7 +459,8 @@ void decode_split_kernel(DecodeArgs a) {
   // (h = 8, 16 exchange values with lanes 16 and 32 apart).  Lanes of absent
   // rows read row 0.
   auto load_query = [&](float (&f)[NB][8]) {
-    const int hq = col < 2 * G && row_ok(col / 2) ? col / 2 : 0;
+    const int qr = kFold && col >= 8 ? col - 8 : col;
+    const int hq = qr < 2 * G && row_ok(qr / 2) ? qr / 2 : 0;
     const size_t off = row_vec(hq) * D + 8 * r;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -745,11 +756,16 @@ void decode_split_kernel(DecodeArgs a) {
     // of 8, so the query bytes follow that order.  Offset-binary codes need a
     // per-block correction -offset * sum(q_int), which seeds the low-byte rows
     // of the integer accumulators: cq[j] = {0, corr_hA, 0, corr_hB}.
-    // The query extends to 24 bits (kQ24): a second product per block takes
-    // the residual byte rint(256 * (q / step - q_int)) in the odd rows (so its
-    // sums land in the same lanes), with its own offset correction (seeded,
-    // or two integers per block where the main correction is).
-    constexpr bool kQX = kQ24;
+    // The query extends to 24 bits (kQ24) by the residual byte
+    // rint(256 * (q / step - q_int)).  Up to 4 heads (kFold) lanes of A rows
+    // 8..15 hold the query of row - 8, and odd rows carry its residual bytes:
+    // their sums land 32 lanes above the hi / lo sums of the same token, each
+    // half sums its K-scaled blocks, and one lane swap adds the upper half's
+    // sum / 256.  Otherwise (kQX) a second product per block takes the
+    // residual bytes in the odd rows (so its sums land in the same lanes),
+    // with its own offset correction (seeded, or two integers per block where
+    // the main correction is).
+    constexpr bool kQX = kQ24 && !kFold;
     constexpr bool kOffset = KB != 8 && !KM;   // offset-binary codes
     long qop[NB];
     long qres[kQX ? NB : 1];
@@ -878,7 +894,8 @@ void decode_split_kernel(DecodeArgs a) {
 
     auto compute_step = [&](const Regs& R, int s0) {
       // Q.K on the matrix cores: 2 x NB products of 16 tokens x 32 elements,
-      // twice that with the residual bytes of the 24-bit query.  Up to head_dim 128 all of
+      // twice that where the residual bytes of the 24-bit query take a second
+      // product (kQX: more than 4 heads, or prefill).  Up to head_dim 128 all of
       // them are issued before the first result is read, so their latencies
       // overlap instead of each product waiting out the last one's; the
       // registers allow it there except with scale-and-min blocks or 5- and
@@ -970,6 +987,16 @@ void decode_split_kernel(DecodeArgs a) {
             sA[m] = __builtin_fmaf(km, bsA[j], sA[m]);
             sB[m] = __builtin_fmaf(km, bsB[j], sB[m]);
           }
+        }
+      }
+      if constexpr (kFold) {
+        // lanes 0..31 add the residual sums of lanes 32..63 (same tokens,
+        // same heads); the upper lanes hold no score head
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float uA = upper_half(sA[m]), uB = upper_half(sB[m]);
+          sA[m] = __builtin_fmaf(uA, 0.00390625f, sA[m]);
+          sB[m] = __builtin_fmaf(uB, 0.00390625f, sB[m]);
         }
       }
       float soA[2] = {0.f, 0.f}, soB[2] = {0.f, 0.f};
@@ -1184,7 +1211,7 @@ void decode_split_kernel(DecodeArgs a) {
           x = x > 32639 ? 32639 : (x < -32639 ? -32639 : x);
           v[i] = x;
           bsum += x;
-          if constexpr (kQX) {
+          if constexpr (kQ24) {
             int y = (int)rintf((t - (float)x) * 256.0f);
             y = y > 127 ? 127 : (y < -127 ? -127 : y);
             res[i] = y;
@@ -1198,16 +1225,21 @@ void decode_split_kernel(DecodeArgs a) {
           const int hi = (v[e] + 128) >> 8;
           const int byte = (col & 1) ? v[e] - 256 * hi : hi;
           w |= (uint64_t)(uint8_t)(int8_t)byte << (8 * i);
-          if constexpr (kQX) wr |= (uint64_t)(uint8_t)(int8_t)res[e] << (8 * i);
+          if constexpr (kQ24) wr |= (uint64_t)(uint8_t)(int8_t)res[e] << (8 * i);
         }
         const bool row_here = col < 2 * G && row_ok(col / 2);
-        qop[j] = row_here ? (long)w : 0;
+        if constexpr (kFold) {
+          const bool res_here = col >= 8 && (col & 1) && col - 8 < 2 * G && row_ok((col - 8) / 2);
+          qop[j] = row_here ? (long)w : (res_here ? (long)wr : 0);
+        } else {
+          qop[j] = row_here ? (long)w : 0;
+        }
         if constexpr (kQX) qres[j] = row_here && (col & 1) ? (long)wr : 0;
         if constexpr (KM) {
           bsum += __shfl_xor(bsum, 16);
           bsum += __shfl_xor(bsum, 32);
           float bf = (float)bsum;
-          if constexpr (kQX) {
+          if constexpr (kQ24) {
             rsum += __shfl_xor(rsum, 16);
             rsum += __shfl_xor(rsum, 32);
             bf = __builtin_fmaf((float)rsum, 0.00390625f, bf);
@@ -1218,8 +1250,17 @@ void decode_split_kernel(DecodeArgs a) {
         if constexpr (kOffset) {
           bsum += __shfl_xor(bsum, 16);
           bsum += __shfl_xor(bsum, 32);
-          const int corr = -(1 << (KB - 1)) * bsum;
-          const int cA = okA ? __shfl(corr, 4 * r) : 0, cB = okB ? __shfl(corr, 4 * r + 2) : 0;
+          int corr = -(1 << (KB - 1)) * bsum;
+          bool cokA = okA, cokB = okB;
+          if constexpr (kFold) {
+            // rows 8..15: the residual bytes' correction, for heads 2r - 4, 2r - 3
+            rsum += __shfl_xor(rsum, 16);
+            rsum += __shfl_xor(rsum, 32);
+            corr = col >= 8 ? -(1 << (KB - 1)) * rsum : corr;
+            cokA = r >= 2 ? row_ok(hA - 4) : okA;
+            cokB = r >= 2 ? row_ok(hB - 4) : okB;
+          }
+          const int cA = cokA ? __shfl(corr, 4 * r) : 0, cB = cokB ? __shfl(corr, 4 * r + 2) : 0;
           if constexpr (kCorrInt) {
             ciA[j] = cA;
             ciB[j] = cB;
