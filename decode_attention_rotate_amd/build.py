@@ -32,6 +32,15 @@ DEVICE = [
 ]
 
 
+# head_dim 256 runs one wave per SIMD with all 512 registers: left to itself
+# the compiler puts the matrix products' results in AGPRs and moves every one
+# to a VGPR (and the P.V accumulators back and forth each step), about a
+# quarter of the step's vector instructions; results kept in VGPRs measured
+# about 5% faster at 131k tokens.  Two waves per SIMD (head_dim <= 192)
+# leave no AGPRs in use, so nothing changes there.
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
 def units():
     """(source, object, extra flags) for every translation unit."""
     out = []
@@ -44,7 +53,8 @@ def units():
             out.append((os.path.join(CSRC, "decode_inst.hip"),
                         "decode_d%d_k%d_m%d%s.o" % (d, kb, km, "_paged" if paged else ""),
                         DEVICE + ["-DKVQ_INST_D=%d" % d, "-DKVQ_INST_KB=%d" % kb,
-                                  "-DKVQ_INST_KM=%d" % km] + (["-DKVQ_INST_PAGED=1"] if paged else [])))
+                                  "-DKVQ_INST_KM=%d" % km] + (["-DKVQ_INST_PAGED=1"] if paged else [])
+                        + (VGPR_MFMA if d == 256 else [])))
     out.append((os.path.join(CSRC, "kvq_host.cpp"), "kvq_host.o", DEVICE + ["-x", "hip"]))
     return out
 
