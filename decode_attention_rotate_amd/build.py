@@ -32,12 +32,14 @@ DEVICE = [
 ]
 
 
-# head_dim 256 runs one wave per SIMD with all 512 registers: left to itself
-# the compiler puts the matrix products' results in AGPRs and moves every one
-# to a VGPR (and the P.V accumulators back and forth each step), about a
-# quarter of the step's vector instructions; results kept in VGPRs measured
-# about 5% faster at 131k tokens.  Two waves per SIMD (head_dim <= 192)
-# leave no AGPRs in use, so nothing changes there.
+# head_dim 256, and head_dim 192 with scale-and-min blocks or prefill rows,
+# run one wave per SIMD with all 512 registers: left to itself the compiler
+# puts the matrix products' results in AGPRs and moves every one to a VGPR
+# (and the P.V accumulators back and forth each step), 89 of 693 vector
+# instructions per step at head_dim 256.  Results kept in VGPRs measured about
+# 5% faster at head_dim 256 (131k tokens) and 5-9% at head_dim 192 (64k
+# tokens, q4_1 V / q5_1 K).  Kernels at two waves per SIMD use no AGPRs and
+# compile the same either way.
 VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
@@ -54,7 +56,7 @@ def units():
                         "decode_d%d_k%d_m%d%s.o" % (d, kb, km, "_paged" if paged else ""),
                         DEVICE + ["-DKVQ_INST_D=%d" % d, "-DKVQ_INST_KB=%d" % kb,
                                   "-DKVQ_INST_KM=%d" % km] + (["-DKVQ_INST_PAGED=1"] if paged else [])
-                        + (VGPR_MFMA if d == 256 else [])))
+                        + (VGPR_MFMA if d >= 192 else [])))
     out.append((os.path.join(CSRC, "kvq_host.cpp"), "kvq_host.o", DEVICE + ["-x", "hip"]))
     return out
 
